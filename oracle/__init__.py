@@ -1,0 +1,28 @@
+"""CPU oracle for the W8A8 FP8 path.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path (the package
+``fp8_quantization_block_amd`` and its HIP library) imports, links or runs
+anything in this directory. Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may use it.
+
+It is a plain, slow, NumPy implementation written straight from the pages:
+
+* ``e4m3``  -- the OCP E4M3 value table and a table-driven round-to-nearest-even
+  encoder that saturates at +-448;
+* ``quant`` -- the amax / scale / cast quantizer for every group shape the path
+  uses (per tensor, 1x128, 128x128, KV head x 128 tokens) and the KV dequantizer;
+* ``gemm``  -- the block-scaled GEMM as dequantize-to-fp64 followed by a plain
+  fp64 matmul, plus the tolerance base |A|.|W|^T.
+
+Every function cites the page and section it follows. Pages are cited as
+
+* [FP8]   wangyu.me, "大语言模型量化技术（五）：FP8" (LLM quantization part 5: FP8)
+* [MIXED] charles2530.github.io, "量化：FP8 与混合精度推理：它不是一个 dtype 开关"
+* [LONG]  pwwt.cn, Llama-3 FP8 and long-context practice notes
+
+Parity status: every function here is pinned by tests under ``tests/``
+(``test_oracle_*.py``) against values the pages print, closed forms,
+invariants and brute force; none is "parity unpinned".
+"""
+
+from . import e4m3, quant, gemm  # noqa: F401

@@ -1,0 +1,69 @@
+"""Block-scaled FP8 GEMM (oracle; test infrastructure only).
+
+Follows [FP8] section "激活动态量化" (the full product becomes a sum over the
+128-wide K blocks j of s_x * s_{w,j} times the FP8 block product, with the
+scales multiplied back while accumulating) and section "FP8 矩阵乘" (weights in
+128x128 blocks, activations in per-token groups of 128, FP8 products with
+fp32 accumulation, partial results multiplied by their scales). [MIXED]
+section "混合精度才是生产形态" adds that low-precision products are summed in
+higher precision.
+
+Reading of the printed equation: it writes y = xW, but W is defined as
+N x K (N outputs, K inputs) with an ceil(N/128) x ceil(K/128) scale grid and
+activations may carry one scale per 128-channel group. So
+
+    y[m, n] = sum_j  s_a[m, j] * s_w[n // 128, j] * sum_{k in block j} qa[m, k] * qw[n, k]
+
+with qa, qw the decoded E4M3 values, i.e. y = A_hat . W_hat^T with
+A_hat = decode(qa) * s_a and W_hat = decode(qw) * s_w. With a per-tensor scale
+the scale is one number for the whole operand.
+
+The oracle is that definition written out: dequantize both operands to
+float64 (exact: 4 significant bits times 24), then one float64 matmul. It also
+returns the tolerance base T = |A_hat| . |W_hat|^T used by the acceptance bound
+|y - y_ref| <= 1e-3 * T.
+"""
+
+import numpy as np
+
+from . import quant
+
+PER_TENSOR = "per_tensor"
+GROUP_1x128 = "group_1x128"
+BLOCK_128x128 = "block_128x128"
+
+
+def dequant_activations(qa, sa, gran: str) -> np.ndarray:
+    """A_hat [M, K] in float64. gran: per_tensor (sa [1]) or group_1x128 (sa [M, ceil(K/128)])."""
+    if gran == PER_TENSOR:
+        return quant.dequantize_grid(qa, np.asarray(sa).reshape(1), 1, 1)
+    if gran == GROUP_1x128:
+        return quant.dequantize_grid(qa, sa, 1, quant.GROUP)
+    raise ValueError(gran)
+
+
+def dequant_weights(qw, sw, gran: str) -> np.ndarray:
+    """W_hat [N, K] in float64. gran: per_tensor (sw [1]) or block_128x128
+    (sw [ceil(N/128), ceil(K/128)])."""
+    if gran == PER_TENSOR:
+        return quant.dequantize_grid(qw, np.asarray(sw).reshape(1), 1, 1)
+    if gran == BLOCK_128x128:
+        return quant.dequantize_grid(qw, sw, quant.GROUP, quant.GROUP)
+    raise ValueError(gran)
+
+
+def block_gemm(qa, sa, gran_a: str, qw, sw, gran_w: str, rows=None, cols=None) -> tuple:
+    """Returns (y, T), both float64 [M, N] (or [len(rows), len(cols)] when
+    ``rows``/``cols`` select a subset of outputs).
+
+    y = A_hat . W_hat^T and T = |A_hat| . |W_hat|^T.
+    """
+    a = dequant_activations(qa, sa, gran_a)
+    w = dequant_weights(qw, sw, gran_w)
+    if rows is not None:
+        a = a[np.asarray(rows)]
+    if cols is not None:
+        w = w[np.asarray(cols)]
+    y = a @ w.T
+    t = np.abs(a) @ np.abs(w).T
+    return y, t
