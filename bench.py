@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the W8A8 FP8 hot path on one MI355X (gfx950).
+
+Workload (one "step"): the Llama-3-8B MLP up/gate prefill shape, M = 4096
+tokens, K = 4096, N = 14336:
+
+  1. dynamic activation quantization of a bf16 [4096, 4096] tensor with one
+     scale per 1 x 128 token group (fp8_quantize, K-block-major scales);
+  2. the block-scaled FP8 GEMM against E4M3 weights with 128 x 128 block
+     scales, fp32 accumulation, bf16 output (fp8_block_gemm).
+
+The weights are quantized once beforehand (offline, as the method prescribes)
+and that pass is timed separately. Inputs are seeded synthetic tensors of the
+workload's shapes and value structure (synth_inputs), resident in HBM before
+timing starts; activation buffers are rotated through 11 copies (> 256 MB
+Infinity Cache) so the quantize pass reads HBM.
+
+Printed: one JSON line. ``value`` is the step's throughput in TFLOP/s
+(2 M N K per step over the step time, quantize included); ``roofline`` is the
+GEMM kernel's achieved TFLOP/s against the dense FP8 MFMA peak, measured with
+HIP events on the launch stream; ``passes`` lists every pass of the path with
+its own time and GB/s or TFLOP/s (the KV-cache passes at [8, 131072, 128] and
+the decode-shaped GEMM 16 x 28672 x 8192 included); ``cpu_baseline`` times the
+CPU oracle on a bounded sample of the same step.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
+PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-secondary", action="store_true", help="skip the KV and decode passes")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["gemm", "quant", "kv", "decode"], default=None,
+                    help="time one pass only (for profiling runs)")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events on the current (launch) stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, iters: int, warmup: int = 2) -> float:
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for i in range(iters):
+            fn(i)
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters * 1e-3   # seconds per call
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards by rows / heads with no exchange, see the design notes", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth_inputs as syn
+    import fp8_quantization_block_amd as fp8
+
+    fp8.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    timer = Timer(torch)
+    c = syn.CONFIGS[2]
+    M, N, K = c["M"], c["N"], c["K"]
+    print(f"# bench: {c['workload']} on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+
+    # ---- inputs resident in HBM -------------------------------------------
+    a_host = syn.activations(2)
+    w = syn.weights(2).to(dev)
+    nsets = 11
+    a_sets = [a_host.to(dev) for _ in range(nsets)]
+    qa_sets = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    sa_sets = [torch.empty((K // 128, M), dtype=torch.float32, device=dev).t() for _ in range(nsets)]
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    qw = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    sw = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+
+    def quant_w(i):
+        fp8.fp8_quantize(w, "block_128x128", out=qw, scales=sw)
+
+    def quant_a(i):
+        j = i % nsets
+        fp8.fp8_quantize(a_sets[j], "group_1x128", out=qa_sets[j], scales=sa_sets[j])
+
+    def gemm(i):
+        j = i % nsets
+        fp8.fp8_block_gemm(qa_sets[j], sa_sets[j], "group_1x128", qw, sw, "block_128x128", out=out)
+
+    def step(i):
+        quant_a(i)
+        gemm(i)
+
+    quant_w(0)
+    for i in range(nsets):
+        quant_a(i)
+    torch.cuda.synchronize()
+
+    flops = 2.0 * M * N * K
+    passes = {}
+    if args.only in (None, "gemm"):
+        t_gemm = timer.run(gemm, max(args.steps, 10), warmup=args.warmup)
+        passes["gemm"] = {"us": t_gemm * 1e6, "TFLOP/s": flops / t_gemm / 1e12,
+                          "frac_fp8_peak": flops / t_gemm / 1e12 / PEAK_FP8_TFLOPS}
+    if args.only in (None, "quant"):
+        t_qa = timer.run(quant_a, max(args.steps, 22), warmup=args.warmup)
+        bytes_qa = M * K * 2 + M * K + M * (K // 128) * 4
+        passes["act_quant_1x128"] = {"us": t_qa * 1e6, "GB/s": bytes_qa / t_qa / 1e9,
+                                     "frac_hbm": bytes_qa / t_qa / 1e9 / PEAK_HBM_GBPS}
+        t_qw = timer.run(quant_w, 10, warmup=2)
+        bytes_qw = N * K * 2 + N * K + (N // 128) * (K // 128) * 4
+        passes["weight_quant_128x128_offline"] = {"us": t_qw * 1e6, "GB/s": bytes_qw / t_qw / 1e9,
+                                                  "frac_hbm": bytes_qw / t_qw / 1e9 / PEAK_HBM_GBPS}
+
+    # ---- the timed step: warmup, then exactly `steps` steps ---------------
+    t_step = None
+    if args.only is None:
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        e0.record(st)
+        for i in range(args.steps):
+            step(i)
+        e1.record(st)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        t_step = e0.elapsed_time(e1) * 1e-3 / args.steps
+        print(f"# timed {args.steps} steps: {t_step * 1e6:.1f} us/step (wall {wall:.3f} s)",
+              file=sys.stderr, flush=True)
+
+    # ---- secondary passes: KV cache and decode-shaped GEMM ------------------
+    if not args.no_secondary and args.only in (None, "kv"):
+        c5 = syn.CONFIGS[5]
+        kh, vh = syn.kv_pair(5)
+        kd, vd = kh.to(dev), vh.to(dev)
+        del kh, vh
+        H, T, D = c5["heads"], c5["tokens"], c5["head_dim"]
+        qk = torch.empty((H, T, D), dtype=torch.uint8, device=dev)
+        qv = torch.empty_like(qk)
+        sk = torch.empty((H, T // 128), dtype=torch.float32, device=dev)
+        sv = torch.empty_like(sk)
+        ok = torch.empty((H, T, D), dtype=torch.bfloat16, device=dev)
+        ov = torch.empty_like(ok)
+        lib = fp8.load_library()
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def kvq(i):
+            fp8._check(lib.fp8_kv_quantize(kd.data_ptr(), H, T, D, T * D, D, 128, 0, qk.data_ptr(), sk.data_ptr(), stream))
+            fp8._check(lib.fp8_kv_quantize(vd.data_ptr(), H, T, D, T * D, D, 128, 0, qv.data_ptr(), sv.data_ptr(), stream))
+
+        def kvd(i):
+            fp8._check(lib.fp8_kv_dequantize(qk.data_ptr(), sk.data_ptr(), H, T, D, 128, 0, ok.data_ptr(), stream))
+            fp8._check(lib.fp8_kv_dequantize(qv.data_ptr(), sv.data_ptr(), H, T, D, 128, 0, ov.data_ptr(), stream))
+
+        n = 2 * H * T * D
+        kv_bytes = n * 2 + n + 2 * H * (T // 128) * 4
+        t_kvq = timer.run(kvq, 20, warmup=3)
+        t_kvd = timer.run(kvd, 20, warmup=3)
+        passes["kv_quant_K+V"] = {"us": t_kvq * 1e6, "GB/s": kv_bytes / t_kvq / 1e9,
+                                  "frac_hbm": kv_bytes / t_kvq / 1e9 / PEAK_HBM_GBPS}
+        passes["kv_dequant_K+V"] = {"us": t_kvd * 1e6, "GB/s": kv_bytes / t_kvd / 1e9,
+                                    "frac_hbm": kv_bytes / t_kvd / 1e9 / PEAK_HBM_GBPS}
+        del kd, vd, qk, qv, ok, ov
+    if not args.no_secondary and args.only in (None, "decode"):
+        c3 = syn.CONFIGS[3]
+        m3, n3, k3 = c3["M"], c3["N"], c3["K"]
+        a3 = syn.activations(3).to(dev)
+        w3 = syn.weights(3).to(dev)
+        qa3, sa3 = fp8.fp8_quantize(a3, "group_1x128", scale_layout="kmajor")
+        qw3, sw3 = fp8.fp8_quantize(w3, "block_128x128")
+        del w3
+        o3 = torch.empty((m3, n3), dtype=torch.bfloat16, device=dev)
+
+        def dec(i):
+            fp8.fp8_block_gemm(qa3, sa3, "group_1x128", qw3, sw3, "block_128x128", out=o3)
+
+        t_dec = timer.run(dec, 50, warmup=5)
+        dec_bytes = m3 * k3 + n3 * k3 + 4 * (m3 * (k3 // 128) + (n3 // 128) * (k3 // 128)) + 2 * m3 * n3
+        passes["decode_gemm_16x28672x8192"] = {"us": t_dec * 1e6, "GB/s": dec_bytes / t_dec / 1e9,
+                                               "frac_hbm": dec_bytes / t_dec / 1e9 / PEAK_HBM_GBPS,
+                                               "TFLOP/s": 2.0 * m3 * n3 * k3 / t_dec / 1e12}
+        del qw3
+
+    # ---- CPU oracle on a bounded sample of the step -------------------------
+    cpu = None
+    if not args.no_cpu_baseline and args.only is None:
+        cpu = cpu_baseline(syn, M, N, K)
+
+    gemm_p = passes.get("gemm")
+    result = {
+        "metric": "block-scaled FP8 GEMM TFLOP/s (%FP8 MFMA peak) + quantize/KV GB/s (%HBM)",
+        "value": (flops / t_step / 1e12) if t_step else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": (t_step * 1e3) if t_step else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3-mfma/fp32-acc/bf16-out",
+        "data": "synthetic (seeded Llama-3-8B MLP-shaped activations with outlier channels, N(0,0.02) weights)",
+        "config": {"workload": c["workload"], "M": M, "N": N, "K": K,
+                   "act_scales": "1x128 dynamic", "weight_scales": "128x128", "parallelism": "single-gpu"},
+        "roofline": None if gemm_p is None else {
+            "kernel": "k_gemm_fp8_block (fp8_block_gemm)",
+            "bound": "mfma",
+            "achieved": gemm_p["TFLOP/s"],
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": gemm_p["TFLOP/s"] / PEAK_FP8_TFLOPS,
+            "traffic": None,
+        },
+        "passes": passes,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(syn, M, N, K):
+    """The oracle timed on a bounded sample of the step: 1x128 quantization of
+    the first 512 activation rows, then the oracle GEMM of those rows against
+    the first 3584 weight rows (weights quantized by the oracle beforehand,
+    untimed, as the offline pass)."""
+    import numpy as np
+    import threadpoolctl
+    from oracle import quant, gemm
+
+    ms, ns = 512, 3584
+    a = syn.activations(2)[:ms].float().numpy()
+    w = syn.weights(2)[:ns].float().numpy()
+    qw, sw = quant.quantize_block_128x128(w)
+    t0 = time.perf_counter()
+    qa, sa = quant.quantize_group_1x128(a)
+    gemm.block_gemm(qa, sa, "group_1x128", qw, sw, "block_128x128")
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
+    return {
+        "value": 2.0 * ms * ns * K / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"act quantize {ms}x{K} (1x128) + oracle GEMM {ms}x{ns}x{K} (fp64 dequant-matmul, y and T); "
+                  f"{dt:.2f} s; host os.cpu_count()={os.cpu_count()}",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+"""fp8_quantization_block_amd -- W8A8 FP8 quantization and block-scaled FP8 GEMM on MI355X.
+
+Thin ctypes binding over the C ABI of ``libfp8blk.so`` (``include/fp8blk.h``).
+The functions here only marshal arguments: they allocate outputs with torch
+on the tensors' device, pass raw pointers and the current HIP stream, and
+raise on a non-OK status. Every step of the computation runs in the HIP
+kernels; there is no CPU fallback, and a missing or unloadable library raises.
+
+Entry points (same names as the C ABI):
+
+* ``fp8_quantize(x, granularity, fmt="e4m3", scale_layout="row")`` -> (codes uint8, scales fp32)
+* ``fp8_block_gemm(qa, sa, gran_a, qw, sw, gran_w, out_dtype=torch.bfloat16, sa_layout=...)``
+* ``fp8_kv_quantize(kv, token_block=128)`` -> (codes uint8, scales fp32)
+* ``fp8_kv_dequantize(q, scales, token_block=128)`` -> bf16
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp8blk.so")
+
+OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP = 0, 1, 2, 3, 4
+E4M3, E5M2 = 0, 1
+PER_TENSOR, GROUP_1x128, BLOCK_128x128 = 0, 1, 2
+BF16, F32 = 0, 1
+
+_GRAN = {"per_tensor": PER_TENSOR, "group_1x128": GROUP_1x128, "block_128x128": BLOCK_128x128}
+_FMT = {"e4m3": E4M3, "e5m2": E5M2}
+
+_lib = None
+
+
+class Fp8BlkError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfp8blk.so once; raises if it is missing (build it with
+    ``python -m fp8_quantization_block_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libfp8blk.so not found at {path}; run python -m fp8_quantization_block_amd.build")
+    lib = ctypes.CDLL(path)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.fp8_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, vp, i64, vp, i64, i64, vp]
+    lib.fp8_block_gemm.argtypes = [i64, i64, i64, vp, i64, vp, i32, i64, i64, vp, i64, vp, i32,
+                                   i64, i64, i32, i32, vp, i32, i64, vp]
+    lib.fp8_kv_quantize.argtypes = [vp, i64, i64, i64, i64, i64, i64, i32, vp, vp, vp]
+    lib.fp8_kv_dequantize.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp, vp]
+    for f in ("fp8_quantize", "fp8_block_gemm", "fp8_kv_quantize", "fp8_kv_dequantize"):
+        getattr(lib, f).restype = i32
+    lib.fp8blk_status_string.argtypes = [i32]
+    lib.fp8blk_status_string.restype = ctypes.c_char_p
+    lib.fp8blk_last_error.argtypes = []
+    lib.fp8blk_last_error.restype = ctypes.c_char_p
+    lib.fp8blk_abi_version.argtypes = []
+    lib.fp8blk_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != OK:
+        lib = load_library()
+        raise Fp8BlkError(status, lib.fp8blk_last_error().decode())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("fp8_quantization_block_amd: tensors must be on the GPU")
+
+
+def fp8_quantize(x: torch.Tensor, granularity: str, fmt: str = "e4m3", scale_layout: str = "row",
+                 out: torch.Tensor = None, scales: torch.Tensor = None):
+    """Quantize a 2-D bf16/fp32 tensor to E4M3 codes (uint8) and fp32 scales.
+
+    granularity: "per_tensor" (scales [1]), "group_1x128" (scales [rows, ceil(cols/128)]),
+    "block_128x128" (scales [ceil(rows/128), ceil(cols/128)]).
+    scale_layout "kmajor" (group_1x128 only) stores the grid transposed,
+    [ceil(cols/128), rows] in memory, and returns it as a strided [rows, groups] view.
+    """
+    lib = load_library()
+    _require_cuda(x)
+    if x.dim() != 2:
+        raise ValueError("fp8_quantize expects a 2-D tensor")
+    if x.dtype == torch.bfloat16:
+        dt, esz = BF16, 2
+    elif x.dtype == torch.float32:
+        dt, esz = F32, 4
+    else:
+        raise ValueError("fp8_quantize: x must be bf16 or fp32")
+    if x.stride(1) != 1:
+        x = x.contiguous()
+    rows, cols = x.shape
+    gran = _GRAN[granularity]
+    if out is None:
+        ldq = ((cols + 15) // 16) * 16
+        out = torch.empty((rows, ldq), dtype=torch.uint8, device=x.device)[:, :cols]
+    if scales is None:
+        if gran == PER_TENSOR:
+            scales = torch.empty(1, dtype=torch.float32, device=x.device)
+        elif gran == GROUP_1x128:
+            g = (cols + 127) // 128
+            if scale_layout == "kmajor":
+                scales = torch.empty((g, rows), dtype=torch.float32, device=x.device).t()
+            else:
+                scales = torch.empty((rows, g), dtype=torch.float32, device=x.device)
+        else:
+            scales = torch.empty(((rows + 127) // 128, (cols + 127) // 128), dtype=torch.float32, device=x.device)
+    ss_r = scales.stride(0) if scales.dim() == 2 else 0
+    ss_c = scales.stride(1) if scales.dim() == 2 else 0
+    _check(lib.fp8_quantize(_ptr(x), dt, rows, cols, x.stride(0), gran, _FMT[fmt], _ptr(out),
+                            out.stride(0), _ptr(scales), ss_r, ss_c, _stream(x)))
+    return out, scales
+
+
+def fp8_block_gemm(qa: torch.Tensor, sa: torch.Tensor, gran_a: str, qw: torch.Tensor, sw: torch.Tensor,
+                   gran_w: str, out_dtype=torch.bfloat16, out: torch.Tensor = None):
+    """C = A . W^T from E4M3 codes: qa [M, K] uint8 with scales sa, qw [N, K]
+    uint8 with scales sw; returns C [M, N] in bf16 (or fp32)."""
+    lib = load_library()
+    _require_cuda(qa, sa, qw, sw)
+    M, K = qa.shape
+    N, K2 = qw.shape
+    if K != K2:
+        raise ValueError("fp8_block_gemm: K mismatch")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=qa.device)
+    cdt = BF16 if out.dtype == torch.bfloat16 else F32
+    ga, gw = _GRAN[gran_a], _GRAN[gran_w]
+    sam = sa.stride(0) if sa.dim() == 2 else 0
+    sak = sa.stride(1) if sa.dim() == 2 else 0
+    swn = sw.stride(0) if sw.dim() == 2 else 0
+    swk = sw.stride(1) if sw.dim() == 2 else 0
+    _check(lib.fp8_block_gemm(M, N, K, _ptr(qa), qa.stride(0), _ptr(sa), ga, sam, sak,
+                              _ptr(qw), qw.stride(0), _ptr(sw), gw, swn, swk, E4M3, E4M3,
+                              _ptr(out), cdt, out.stride(0), _stream(qa)))
+    return out
+
+
+def fp8_kv_quantize(kv: torch.Tensor, token_block: int = 128, fmt: str = "e4m3"):
+    """kv: bf16 [heads, tokens, head_dim] (head_dim contiguous). Returns
+    (codes uint8 [heads, tokens, head_dim], scales fp32 [heads, ceil(tokens/token_block)])."""
+    lib = load_library()
+    _require_cuda(kv)
+    if kv.dtype != torch.bfloat16 or kv.dim() != 3 or kv.stride(2) != 1:
+        raise ValueError("fp8_kv_quantize expects bf16 [heads, tokens, head_dim] with contiguous head_dim")
+    h, t, d = kv.shape
+    q = torch.empty((h, t, d), dtype=torch.uint8, device=kv.device)
+    s = torch.empty((h, (t + token_block - 1) // token_block), dtype=torch.float32, device=kv.device)
+    _check(lib.fp8_kv_quantize(_ptr(kv), h, t, d, kv.stride(0), kv.stride(1), token_block, _FMT[fmt],
+                               _ptr(q), _ptr(s), _stream(kv)))
+    return q, s
+
+
+def fp8_kv_dequantize(q: torch.Tensor, scales: torch.Tensor, token_block: int = 128, fmt: str = "e4m3"):
+    """Inverse of fp8_kv_quantize: bf16 [heads, tokens, head_dim] = bf16(dec(q) * s)."""
+    lib = load_library()
+    _require_cuda(q, scales)
+    h, t, d = q.shape
+    out = torch.empty((h, t, d), dtype=torch.bfloat16, device=q.device)
+    _check(lib.fp8_kv_dequantize(_ptr(q.contiguous()), _ptr(scales.contiguous()), h, t, d, token_block,
+                                 _FMT[fmt], _ptr(out), _stream(q)))
+    return out

@@ -1,0 +1,274 @@
+// C-ABI layer of libfp8blk.so: argument validation (host only, before any HIP
+// call or write), then dispatch to the kernel launchers. The interface and its
+// numerics are documented in include/fp8blk.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/fp8blk.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+fp8blk_status fail(fp8blk_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+fp8blk_status ok() {
+  g_last_error[0] = '\0';
+  return FP8BLK_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte range [lo, hi) of a strided 2-D array with rows >= 1 and cols >= 1.
+struct Range {
+  uintptr_t lo, hi;
+};
+Range range2d(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+  return {b, b + (uintptr_t)(((rows - 1) * ld + cols) * elem)};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Byte range covered by a scale grid [gr][gc] with element strides (sr, sc) >= 0.
+Range range_grid(const float* p, int64_t gr, int64_t gc, int64_t sr, int64_t sc) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+  const int64_t last = (gr - 1) * sr + (gc - 1) * sc;
+  return {b, b + (uintptr_t)((last + 1) * 4)};
+}
+
+fp8blk_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FP8BLK_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;   // indices are kept in 32 bits inside kernels
+
+fp8blk_status check_format(fp8blk_format fmt, const char* what) {
+  if (fmt == FP8BLK_E4M3) return FP8BLK_OK;
+  if (fmt == FP8BLK_E5M2) return fail(FP8BLK_EUNSUPPORTED, "%s: E5M2 is not implemented", what);
+  return fail(FP8BLK_EINVAL, "%s: unknown fp8 format %d", what, (int)fmt);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8blk_abi_version(void) { return FP8BLK_ABI_VERSION; }
+
+const char* fp8blk_last_error(void) { return g_last_error; }
+
+const char* fp8blk_status_string(fp8blk_status s) {
+  switch (s) {
+    case FP8BLK_OK: return "FP8BLK_OK";
+    case FP8BLK_EINVAL: return "FP8BLK_EINVAL";
+    case FP8BLK_EALIGN: return "FP8BLK_EALIGN";
+    case FP8BLK_EUNSUPPORTED: return "FP8BLK_EUNSUPPORTED";
+    case FP8BLK_EHIP: return "FP8BLK_EHIP";
+  }
+  return "FP8BLK_UNKNOWN";
+}
+
+fp8blk_status fp8_quantize(const void* x, fp8blk_dtype x_dtype, int64_t rows, int64_t cols,
+                           int64_t ld_x, fp8blk_granularity gran, fp8blk_format fmt, uint8_t* q,
+                           int64_t ld_q, float* scales, int64_t scale_stride_row,
+                           int64_t scale_stride_col, void* stream) {
+  const char* fn = "fp8_quantize";
+  if (!x || !q || !scales) return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
+  if (x_dtype != FP8BLK_BF16 && x_dtype != FP8BLK_F32)
+    return fail(FP8BLK_EINVAL, "%s: unknown input dtype %d", fn, (int)x_dtype);
+  if (gran != FP8BLK_PER_TENSOR && gran != FP8BLK_GROUP_1x128 && gran != FP8BLK_BLOCK_128x128)
+    return fail(FP8BLK_EINVAL, "%s: unknown granularity %d", fn, (int)gran);
+  if (fp8blk_status st = check_format(fmt, fn)) return st;
+  if (rows < 0 || cols < 0) return fail(FP8BLK_EINVAL, "%s: negative size", fn);
+  if (rows >= kMaxDim || cols >= kMaxDim || ld_x >= kMaxDim || ld_q >= kMaxDim)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: dimension above 2^31", fn);
+  if (ld_x < cols || ld_q < cols) return fail(FP8BLK_EINVAL, "%s: leading dimension < cols", fn);
+  if (scale_stride_row < 0 || scale_stride_col < 0)
+    return fail(FP8BLK_EINVAL, "%s: negative scale stride", fn);
+  const int64_t esz = x_dtype == FP8BLK_BF16 ? 2 : 4;
+  if (!aligned16(x) || !aligned16(q)) return fail(FP8BLK_EALIGN, "%s: x and q must be 16-byte aligned", fn);
+  if ((ld_x * esz) % 16 != 0 || ld_q % 16 != 0)
+    return fail(FP8BLK_EALIGN, "%s: ld_x * elem_size and ld_q must be multiples of 16 bytes", fn);
+  if (gran == FP8BLK_GROUP_1x128) {
+    const int64_t groups = rows * ((cols + 127) / 128);
+    if (groups >= kMaxDim) return fail(FP8BLK_EUNSUPPORTED, "%s: more than 2^31 groups", fn);
+  }
+  if (rows > 0 && cols > 0) {
+    const Range rx = range2d(x, rows, cols, ld_x, esz);
+    const Range rq = range2d(q, rows, cols, ld_q, 1);
+    int64_t gr = 1, gc = 1;
+    if (gran == FP8BLK_GROUP_1x128) { gr = rows; gc = (cols + 127) / 128; }
+    if (gran == FP8BLK_BLOCK_128x128) { gr = (rows + 127) / 128; gc = (cols + 127) / 128; }
+    const Range rs = gran == FP8BLK_PER_TENSOR ? range_grid(scales, 1, 1, 0, 0)
+                                               : range_grid(scales, gr, gc, scale_stride_row, scale_stride_col);
+    if (overlap(rx, rq) || overlap(rx, rs) || overlap(rq, rs))
+      return fail(FP8BLK_EINVAL, "%s: x, q and scales must not overlap", fn);
+    if (gran != FP8BLK_PER_TENSOR && (gr > 1 || gc > 1)) {
+      // distinct grid cells must be distinct floats
+      if ((gr > 1 && scale_stride_row == 0) || (gc > 1 && scale_stride_col == 0))
+        return fail(FP8BLK_EINVAL, "%s: zero scale stride on a grid axis longer than 1", fn);
+    }
+  } else if (gran != FP8BLK_PER_TENSOR) {
+    return ok();   // empty grid: nothing to write
+  }
+  fp8blk::QuantArgs a;
+  a.x = x;
+  a.x_dtype = (int)x_dtype;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld_x = ld_x;
+  a.gran = (int)gran;
+  a.q = q;
+  a.ld_q = ld_q;
+  a.scales = scales;
+  a.ss_row = scale_stride_row;
+  a.ss_col = scale_stride_col;
+  return hip_status(fp8blk::launch_quantize(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+fp8blk_status fp8_block_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                             const float* scale_a, fp8blk_granularity gran_a, int64_t sa_stride_m,
+                             int64_t sa_stride_k, const uint8_t* b, int64_t ldb,
+                             const float* scale_b, fp8blk_granularity gran_b, int64_t sb_stride_n,
+                             int64_t sb_stride_k, fp8blk_format fmt_a, fp8blk_format fmt_b,
+                             void* c, fp8blk_dtype c_dtype, int64_t ldc, void* stream) {
+  const char* fn = "fp8_block_gemm";
+  if (!a || !b || !scale_a || !scale_b || !c) return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
+  if (gran_a != FP8BLK_PER_TENSOR && gran_a != FP8BLK_GROUP_1x128)
+    return fail(FP8BLK_EINVAL, "%s: gran_a must be PER_TENSOR or GROUP_1x128", fn);
+  if (gran_b != FP8BLK_PER_TENSOR && gran_b != FP8BLK_BLOCK_128x128)
+    return fail(FP8BLK_EINVAL, "%s: gran_b must be PER_TENSOR or BLOCK_128x128", fn);
+  if (c_dtype != FP8BLK_BF16 && c_dtype != FP8BLK_F32)
+    return fail(FP8BLK_EINVAL, "%s: unknown output dtype %d", fn, (int)c_dtype);
+  if (fp8blk_status st = check_format(fmt_a, fn)) return st;
+  if (fp8blk_status st = check_format(fmt_b, fn)) return st;
+  if (M < 0 || N <= 0 || K <= 0) return fail(FP8BLK_EINVAL, "%s: need M >= 0, N > 0, K > 0", fn);
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: dimension above 2^31", fn);
+  if (N % 128 != 0 || K % 128 != 0)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: N and K must be multiples of 128", fn);
+  if (lda < K || ldb < K || ldc < N) return fail(FP8BLK_EINVAL, "%s: leading dimension too small", fn);
+  if (sa_stride_m < 0 || sa_stride_k < 0 || sb_stride_n < 0 || sb_stride_k < 0)
+    return fail(FP8BLK_EINVAL, "%s: negative scale stride", fn);
+  const int64_t csz = c_dtype == FP8BLK_BF16 ? 2 : 4;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c))
+    return fail(FP8BLK_EALIGN, "%s: a, b and c must be 16-byte aligned", fn);
+  if (lda % 16 != 0 || ldb % 16 != 0 || (ldc * csz) % 16 != 0)
+    return fail(FP8BLK_EALIGN, "%s: lda, ldb and ldc * elem_size must be multiples of 16 bytes", fn);
+  if (M == 0) return ok();
+  const Range rc = range2d(c, M, N, ldc, csz);
+  const Range ra = range2d(a, M, K, lda, 1);
+  const Range rb = range2d(b, N, K, ldb, 1);
+  const Range rsa = gran_a == FP8BLK_PER_TENSOR ? range_grid(scale_a, 1, 1, 0, 0)
+                                                : range_grid(scale_a, M, K / 128, sa_stride_m, sa_stride_k);
+  const Range rsb = gran_b == FP8BLK_PER_TENSOR ? range_grid(scale_b, 1, 1, 0, 0)
+                                                : range_grid(scale_b, N / 128, K / 128, sb_stride_n, sb_stride_k);
+  if (overlap(rc, ra) || overlap(rc, rb) || overlap(rc, rsa) || overlap(rc, rsb))
+    return fail(FP8BLK_EINVAL, "%s: c must not overlap the inputs", fn);
+  fp8blk::GemmArgs g;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.a = a;
+  g.lda = lda;
+  g.sa = scale_a;
+  g.gran_a = (int)gran_a;
+  g.sa_m = sa_stride_m;
+  g.sa_k = sa_stride_k;
+  g.b = b;
+  g.ldb = ldb;
+  g.sb = scale_b;
+  g.gran_b = (int)gran_b;
+  g.sb_n = sb_stride_n;
+  g.sb_k = sb_stride_k;
+  g.c = c;
+  g.c_dtype = (int)c_dtype;
+  g.ldc = ldc;
+  return hip_status(fp8blk::launch_block_gemm(g, static_cast<hipStream_t>(stream)), fn);
+}
+
+static fp8blk_status check_kv_common(const char* fn, int64_t heads, int64_t tokens, int64_t head_dim,
+                                     int64_t token_block, fp8blk_format fmt) {
+  if (fp8blk_status st = check_format(fmt, fn)) return st;
+  if (heads < 0 || tokens < 0) return fail(FP8BLK_EINVAL, "%s: negative size", fn);
+  if (head_dim <= 0 || token_block <= 0)
+    return fail(FP8BLK_EINVAL, "%s: head_dim and token_block must be positive", fn);
+  if (head_dim % 8 != 0) return fail(FP8BLK_EUNSUPPORTED, "%s: head_dim must be a multiple of 8", fn);
+  if (token_block * head_dim > 16384)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: token_block * head_dim must be <= 16384", fn);
+  if (heads >= 65536 || tokens >= kMaxDim || heads * tokens * head_dim >= ((int64_t)1 << 40))
+    return fail(FP8BLK_EUNSUPPORTED, "%s: tensor too large", fn);
+  if ((tokens + token_block - 1) / token_block >= kMaxDim)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: too many token blocks", fn);
+  return FP8BLK_OK;
+}
+
+fp8blk_status fp8_kv_quantize(const void* kv, int64_t heads, int64_t tokens, int64_t head_dim,
+                              int64_t stride_head, int64_t stride_token, int64_t token_block,
+                              fp8blk_format fmt, uint8_t* q, float* scales, void* stream) {
+  const char* fn = "fp8_kv_quantize";
+  if (!kv || !q || !scales) return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
+  if (fp8blk_status st = check_kv_common(fn, heads, tokens, head_dim, token_block, fmt)) return st;
+  if (stride_token < head_dim || stride_head < 0)
+    return fail(FP8BLK_EINVAL, "%s: stride_token must be >= head_dim and stride_head >= 0", fn);
+  if (!aligned16(kv) || !aligned16(q)) return fail(FP8BLK_EALIGN, "%s: kv and q must be 16-byte aligned", fn);
+  if (stride_head % 8 != 0 || stride_token % 8 != 0)
+    return fail(FP8BLK_EALIGN, "%s: strides must be multiples of 8 elements", fn);
+  if (heads == 0 || tokens == 0) return ok();
+  const int64_t nb = (tokens + token_block - 1) / token_block;
+  const uintptr_t kb = reinterpret_cast<uintptr_t>(kv);
+  const Range rkv = {kb, kb + (uintptr_t)(((heads - 1) * stride_head + (tokens - 1) * stride_token + head_dim) * 2)};
+  const Range rq = {reinterpret_cast<uintptr_t>(q), reinterpret_cast<uintptr_t>(q) + (uintptr_t)(heads * tokens * head_dim)};
+  const Range rs = range_grid(scales, heads, nb, nb, 1);
+  if (overlap(rkv, rq) || overlap(rkv, rs) || overlap(rq, rs))
+    return fail(FP8BLK_EINVAL, "%s: kv, q and scales must not overlap", fn);
+  fp8blk::KvArgs a = {};
+  a.kv = kv;
+  a.heads = heads;
+  a.tokens = tokens;
+  a.head_dim = head_dim;
+  a.stride_head = stride_head;
+  a.stride_token = stride_token;
+  a.token_block = token_block;
+  a.q = q;
+  a.scales = scales;
+  return hip_status(fp8blk::launch_kv_quantize(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+fp8blk_status fp8_kv_dequantize(const uint8_t* q, const float* scales, int64_t heads,
+                                int64_t tokens, int64_t head_dim, int64_t token_block,
+                                fp8blk_format fmt, void* out_bf16, void* stream) {
+  const char* fn = "fp8_kv_dequantize";
+  if (!q || !scales || !out_bf16) return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
+  if (fp8blk_status st = check_kv_common(fn, heads, tokens, head_dim, token_block, fmt)) return st;
+  if (!aligned16(q) || !aligned16(out_bf16))
+    return fail(FP8BLK_EALIGN, "%s: q and out must be 16-byte aligned", fn);
+  if (heads == 0 || tokens == 0) return ok();
+  const int64_t nb = (tokens + token_block - 1) / token_block;
+  const int64_t n = heads * tokens * head_dim;
+  const Range rq = {reinterpret_cast<uintptr_t>(q), reinterpret_cast<uintptr_t>(q) + (uintptr_t)n};
+  const Range ro = {reinterpret_cast<uintptr_t>(out_bf16), reinterpret_cast<uintptr_t>(out_bf16) + (uintptr_t)(2 * n)};
+  const Range rs = range_grid(scales, heads, nb, nb, 1);
+  if (overlap(ro, rq) || overlap(ro, rs)) return fail(FP8BLK_EINVAL, "%s: out must not overlap q or scales", fn);
+  fp8blk::KvArgs a = {};
+  a.q_in = q;
+  a.scales_in = scales;
+  a.heads = heads;
+  a.tokens = tokens;
+  a.head_dim = head_dim;
+  a.token_block = token_block;
+  a.out = out_bf16;
+  return hip_status(fp8blk::launch_kv_dequantize(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

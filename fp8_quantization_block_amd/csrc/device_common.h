@@ -1,0 +1,137 @@
+// Device helpers shared by the fp8blk HIP kernels (gfx950 only).
+//
+// E4M3 here is OCP E4M3 as fixed by [FP8] (wangyu.me, "大语言模型量化技术（五）：FP8"),
+// section "FP8 是什么": largest finite 448, smallest normal 2^-6, smallest
+// subnormal 2^-9, no infinity, saturation at +-448.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8blk {
+
+constexpr float kE4M3Max = 448.0f;
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32 bit helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---------------------------------------------------------------------------
+// Max reductions over non-negative fp32 bit patterns (which order like uints).
+// ---------------------------------------------------------------------------
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
+  uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)0, (int)v, kCtrl, 0xf, 0xf, false);
+  return o > v ? o : v;
+}
+
+// Max over the 16 lanes of a DPP row; every lane of the row gets the result.
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = dpp_max_step<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_step<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_step<0x141>(v);  // row_half_mirror
+  v = dpp_max_step<0x140>(v);  // row_mirror
+  return v;
+}
+
+// Max over the whole 64-lane wave; every lane gets the result.
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = row16_max(v);
+  uint32_t o = (uint32_t)__shfl_xor((int)v, 16);
+  v = o > v ? o : v;
+  o = (uint32_t)__shfl_xor((int)v, 32);
+  return o > v ? o : v;
+}
+
+// ---------------------------------------------------------------------------
+// fp32 -> E4M3 with round-to-nearest-even and saturation.
+//
+// The hardware conversion v_cvt_pk_fp8_f32 of gfx950 writes OCP E4M3 codes with
+// round-to-nearest-even; clamping to +-448 first (v_med3_f32) gives the
+// saturating behaviour the format requires. tests/test_gpu_quantize.py checks
+// this against the CPU oracle on every fp32 value in [-448, 448].
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float clamp448(float v) {
+  return __builtin_amdgcn_fmed3f(v, -kE4M3Max, kE4M3Max);
+}
+
+// Four fp32 values -> four E4M3 codes packed little-endian in one word.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+  w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), (int)w, true);
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// Group scale and the bit-exact cast of a group's elements.
+//
+// The code of x is E4M3(fl32(x / s)) with the IEEE correctly rounded fp32
+// quotient. Per element that division is replaced by two multiplications with
+// reciprocals nudged down and up: with r = fl32(1 / s),
+//   rl = fl32(r * (1 - 2^-21)),  rh = fl32(r * (1 + 2^-21)),
+// the products fl32(x * rl) and fl32(x * rh) bracket fl32(x / s) strictly in
+// magnitude (their relative offsets exceed 2^-21 - 3 * 2^-24 > 2^-24, the fp32
+// rounding bound) whenever the quotient is an fp32 normal. Round-to-nearest is
+// monotone, so when both brackets give the same code it is the code of
+// fl32(x / s); otherwise the element takes the exact division. Quotients below
+// the fp32 normal range give code 0 (signed) on every path. Groups whose scale
+// is an fp32 subnormal (r may overflow) always take the exact division.
+// ---------------------------------------------------------------------------
+struct GroupScale {
+  float s;    // fl32(amax / 448)
+  float rl;   // lower reciprocal bracket
+  float rh;   // upper reciprocal bracket
+  bool exact; // true: divide every element exactly (s is zero or subnormal)
+};
+
+__device__ __forceinline__ GroupScale make_group_scale(uint32_t amax_bits) {
+  GroupScale g;
+  g.s = __uint_as_float(amax_bits) / kE4M3Max;   // IEEE correctly rounded division
+  const float r = 1.0f / g.s;                    // IEEE correctly rounded division
+  g.rl = r * (1.0f - 0x1.0p-21f);
+  g.rh = r * (1.0f + 0x1.0p-21f);
+  g.exact = !(g.s >= 0x1.0p-126f);
+  return g;
+}
+
+// Exact path for one element: sign-only zero when s == 0.
+__device__ __forceinline__ float exact_quotient(float x, float s) {
+  if (s == 0.0f) return __uint_as_float(__float_as_uint(x) & 0x80000000u);
+  return x / s;   // IEEE correctly rounded division
+}
+
+// Codes of four elements of one group.
+__device__ __forceinline__ uint32_t cast4(const GroupScale& g, float a, float b, float c, float d) {
+  if (!g.exact) {
+    const uint32_t lo = e4m3x4(a * g.rl, b * g.rl, c * g.rl, d * g.rl);
+    const uint32_t hi = e4m3x4(a * g.rh, b * g.rh, c * g.rh, d * g.rh);
+    if (__builtin_expect(lo == hi, 1)) return lo;
+  }
+  return e4m3x4(exact_quotient(a, g.s), exact_quotient(b, g.s), exact_quotient(c, g.s),
+                exact_quotient(d, g.s));
+}
+
+// |x| bit patterns of eight bf16 values held in four words, as fp32 bit
+// patterns, reduced to their max.
+__device__ __forceinline__ uint32_t amax_bf16x8(uint4 w) {
+  uint32_t m = 0;
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = ws[i] & 0x7fff7fffu;
+    const uint32_t hi = a & 0xffff0000u;
+    const uint32_t lo = a << 16;
+    m = hi > m ? hi : m;
+    m = lo > m ? lo : m;
+  }
+  return m;
+}
+
+__device__ __forceinline__ uint32_t amax_f32(float v, uint32_t m) {
+  const uint32_t a = __float_as_uint(v) & 0x7fffffffu;
+  return a > m ? a : m;
+}
+
+}  // namespace fp8blk

@@ -1,0 +1,57 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernel
+// launchers (quantize.hip, gemm.hip). Arguments reaching a launcher have been
+// validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8blk {
+
+enum Gran : int { GRAN_PER_TENSOR = 0, GRAN_GROUP_1x128 = 1, GRAN_BLOCK_128x128 = 2 };
+enum DType : int { DTYPE_BF16 = 0, DTYPE_F32 = 1 };
+
+struct QuantArgs {
+  const void* x;
+  int x_dtype;
+  int64_t rows, cols, ld_x;
+  int gran;
+  uint8_t* q;
+  int64_t ld_q;
+  float* scales;
+  int64_t ss_row, ss_col;
+};
+
+struct KvArgs {
+  const void* kv;        // quantize input
+  const uint8_t* q_in;   // dequantize input
+  int64_t heads, tokens, head_dim, stride_head, stride_token, token_block;
+  uint8_t* q;            // quantize output
+  float* scales;         // quantize output / dequantize input
+  const float* scales_in;
+  void* out;             // dequantize output
+};
+
+struct GemmArgs {
+  int64_t M, N, K;
+  const uint8_t* a;
+  int64_t lda;
+  const float* sa;
+  int gran_a;
+  int64_t sa_m, sa_k;
+  const uint8_t* b;
+  int64_t ldb;
+  const float* sb;
+  int gran_b;
+  int64_t sb_n, sb_k;
+  void* c;
+  int c_dtype;
+  int64_t ldc;
+};
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
+hipError_t launch_kv_quantize(const KvArgs& a, hipStream_t st);
+hipError_t launch_kv_dequantize(const KvArgs& a, hipStream_t st);
+hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t st);
+
+}  // namespace fp8blk

@@ -1,0 +1,390 @@
+// Quantization kernels: per-tensor, 1x128 groups, 128x128 blocks, KV
+// (head x token block) groups, and the KV dequantizer.
+//
+// Method ([FP8] wangyu.me, "大语言模型量化技术（五）：FP8"): per group, amax = max|x|,
+// s = amax / 448, code = E4M3(x / s) rounded to nearest even and saturated
+// (section "什么是 FP8 量化"; section "权重量化：128×128 分块 FP8" for 128x128
+// blocks; section "激活动态量化" for per-token 1x128 groups). KV groups are one
+// head x 128 tokens x head_dim ([LONG] pwwt.cn Llama-3 FP8 notes, section 3).
+// Dequantization is x ~ q * s ([MIXED] charles2530.github.io, "量化：FP8 与混合精度推理",
+// section "E4M3 和 E5M2 是范围与格点的取舍").
+//
+// All passes are HBM-bound: 16-byte loads, a max reduction in registers / DPP
+// / LDS, then packed code stores.
+#include <hip/hip_bf16.h>
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace fp8blk {
+
+// ---------------------------------------------------------------------------
+// Eight consecutive input elements of one lane.
+// ---------------------------------------------------------------------------
+template <typename T>
+struct Vec8;
+
+template <>
+struct Vec8<__hip_bfloat16> {
+  uint4 w;
+  __device__ __forceinline__ void load(const __hip_bfloat16* p, uint32_t nvalid) {
+    if (nvalid >= 8) {
+      w = *reinterpret_cast<const uint4*>(p);
+    } else {
+      const uint16_t* h = reinterpret_cast<const uint16_t*>(p);
+      uint32_t e[8];
+#pragma unroll
+      for (uint32_t i = 0; i < 8; ++i) e[i] = i < nvalid ? (uint32_t)h[i] : 0u;
+      w.x = e[0] | (e[1] << 16);
+      w.y = e[2] | (e[3] << 16);
+      w.z = e[4] | (e[5] << 16);
+      w.w = e[6] | (e[7] << 16);
+    }
+  }
+  __device__ __forceinline__ void zero() { w = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ uint32_t amax_bits() const { return amax_bf16x8(w); }
+  __device__ __forceinline__ uint2 cast(const GroupScale& g) const {
+    uint2 r;
+    r.x = cast4(g, bf16_lo_to_f32(w.x), bf16_hi_to_f32(w.x), bf16_lo_to_f32(w.y), bf16_hi_to_f32(w.y));
+    r.y = cast4(g, bf16_lo_to_f32(w.z), bf16_hi_to_f32(w.z), bf16_lo_to_f32(w.w), bf16_hi_to_f32(w.w));
+    return r;
+  }
+};
+
+template <>
+struct Vec8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p, uint32_t nvalid) {
+    if (nvalid >= 8) {
+      a = reinterpret_cast<const float4*>(p)[0];
+      b = reinterpret_cast<const float4*>(p)[1];
+    } else {
+      float e[8];
+#pragma unroll
+      for (uint32_t i = 0; i < 8; ++i) e[i] = i < nvalid ? p[i] : 0.0f;
+      a = make_float4(e[0], e[1], e[2], e[3]);
+      b = make_float4(e[4], e[5], e[6], e[7]);
+    }
+  }
+  __device__ __forceinline__ void zero() {
+    a = make_float4(0, 0, 0, 0);
+    b = a;
+  }
+  __device__ __forceinline__ uint32_t amax_bits() const {
+    uint32_t m = 0;
+    m = amax_f32(a.x, m); m = amax_f32(a.y, m); m = amax_f32(a.z, m); m = amax_f32(a.w, m);
+    m = amax_f32(b.x, m); m = amax_f32(b.y, m); m = amax_f32(b.z, m); m = amax_f32(b.w, m);
+    return m;
+  }
+  __device__ __forceinline__ uint2 cast(const GroupScale& g) const {
+    uint2 r;
+    r.x = cast4(g, a.x, a.y, a.z, a.w);
+    r.y = cast4(g, b.x, b.y, b.z, b.w);
+    return r;
+  }
+};
+
+__device__ __forceinline__ void store_codes8(uint8_t* p, uint2 c, uint32_t nvalid) {
+  if (nvalid >= 8) {
+    *reinterpret_cast<uint2*>(p) = c;
+  } else {
+#pragma unroll
+    for (uint32_t i = 0; i < 8; ++i) {
+      const uint32_t word = i < 4 ? c.x : c.y;
+      if (i < nvalid) p[i] = (uint8_t)(word >> (8 * (i & 3)));
+    }
+  }
+}
+
+// Block-wide max over non-negative fp32 bit patterns (blockDim.x == 256).
+__device__ __forceinline__ uint32_t block256_max(uint32_t m) {
+  __shared__ uint32_t red[4];
+  m = wave_max(m);
+  const uint32_t wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63u) == 0) red[wave] = m;
+  __syncthreads();
+  uint32_t r = red[0];
+  r = red[1] > r ? red[1] : r;
+  r = red[2] > r ? red[2] : r;
+  r = red[3] > r ? red[3] : r;
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// 1x128 groups: 16 lanes (one DPP row) per group, 8 elements per lane,
+// kUnroll groups per lane with all loads issued before any arithmetic.
+// Group g of the flat (row, group) index space: row = g / ngroups.
+// ---------------------------------------------------------------------------
+template <typename T, int kUnroll>
+__global__ __launch_bounds__(256) void k_quant_group_1x128(
+    const T* __restrict__ x, int64_t ld_x, uint32_t cols, uint32_t ngroups, uint32_t total_groups,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ sc, int64_t ss_row, int64_t ss_col) {
+  const uint32_t lane16 = threadIdx.x & 15u;
+  const uint32_t slot = threadIdx.x >> 4;
+  Vec8<T> v[kUnroll];
+  uint32_t row[kUnroll], grp[kUnroll], nvalid[kUnroll];
+  bool live[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t g = (blockIdx.x * kUnroll + u) * 16u + slot;
+    live[u] = g < total_groups;
+    row[u] = live[u] ? g / ngroups : 0u;
+    grp[u] = g - row[u] * ngroups;
+    const uint32_t col0 = grp[u] * 128u + lane16 * 8u;
+    nvalid[u] = (live[u] && col0 < cols) ? min(8u, cols - col0) : 0u;
+    if (nvalid[u] > 0)
+      v[u].load(x + (int64_t)row[u] * ld_x + col0, nvalid[u]);
+    else
+      v[u].zero();
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t amax = row16_max(v[u].amax_bits());
+    const GroupScale gs = make_group_scale(amax);
+    const uint2 codes = v[u].cast(gs);
+    const uint32_t col0 = grp[u] * 128u + lane16 * 8u;
+    if (nvalid[u] > 0) store_codes8(q + (int64_t)row[u] * ld_q + col0, codes, nvalid[u]);
+    if (live[u] && lane16 == 0) sc[(int64_t)row[u] * ss_row + (int64_t)grp[u] * ss_col] = gs.s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tile groups held in registers by one 256-thread workgroup: a 128x128 weight
+// block, or one KV head x token block x head_dim. Up to 2048 chunks of 8
+// elements (16384 elements, 32 KB of bf16), 8 chunks per thread.
+// ---------------------------------------------------------------------------
+struct TileGroup {
+  int64_t in_off;      // element offset of the group's first element
+  int64_t in_ld;       // element stride between the group's rows
+  int64_t out_off;     // byte offset of the first code
+  int64_t out_ld;      // byte stride between rows of codes
+  int64_t scale_off;   // index of the group's scale
+  uint32_t rows;       // valid rows in this group
+  uint32_t cols;       // valid columns in this group
+};
+
+template <typename T>
+__device__ __forceinline__ void quant_tile_group(const T* __restrict__ x, uint8_t* __restrict__ q,
+                                                 float* __restrict__ sc, const TileGroup& tg) {
+  const uint32_t cpr = (tg.cols + 7u) >> 3;   // chunks per row
+  const uint32_t nchunks = tg.rows * cpr;
+  Vec8<T> v[8];
+  uint32_t r[8], cc[8], nv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c = threadIdx.x + 256u * i;
+    r[i] = c / cpr;
+    cc[i] = c - r[i] * cpr;
+    nv[i] = c < nchunks ? min(8u, tg.cols - cc[i] * 8u) : 0u;
+    if (nv[i] > 0)
+      v[i].load(x + tg.in_off + (int64_t)r[i] * tg.in_ld + cc[i] * 8u, nv[i]);
+    else
+      v[i].zero();
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t a = v[i].amax_bits();
+    m = a > m ? a : m;
+  }
+  const GroupScale gs = make_group_scale(block256_max(m));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (nv[i] > 0) store_codes8(q + tg.out_off + (int64_t)r[i] * tg.out_ld + cc[i] * 8u, v[i].cast(gs), nv[i]);
+  }
+  if (threadIdx.x == 0) sc[tg.scale_off] = gs.s;
+}
+
+// 128x128 blocks of a [rows][cols] matrix; grid (ceil(cols/128), ceil(rows/128)).
+template <typename T>
+__global__ __launch_bounds__(256) void k_quant_block_128x128(
+    const T* __restrict__ x, int64_t ld_x, uint32_t rows, uint32_t cols, uint8_t* __restrict__ q,
+    int64_t ld_q, float* __restrict__ sc, int64_t ss_row, int64_t ss_col) {
+  TileGroup tg;
+  const uint32_t gx = blockIdx.x, gy = blockIdx.y;
+  tg.in_off = (int64_t)gy * 128 * ld_x + (int64_t)gx * 128;
+  tg.in_ld = ld_x;
+  tg.out_off = (int64_t)gy * 128 * ld_q + (int64_t)gx * 128;
+  tg.out_ld = ld_q;
+  tg.scale_off = (int64_t)gy * ss_row + (int64_t)gx * ss_col;
+  tg.rows = min(128u, rows - gy * 128u);
+  tg.cols = min(128u, cols - gx * 128u);
+  quant_tile_group<T>(x, q, sc, tg);
+}
+
+// KV groups; grid (ceil(tokens/token_block), heads).
+__global__ __launch_bounds__(256) void k_kv_quant(
+    const __hip_bfloat16* __restrict__ kv, int64_t stride_head, int64_t stride_token,
+    uint32_t tokens, uint32_t head_dim, uint32_t token_block, uint8_t* __restrict__ q,
+    float* __restrict__ sc) {
+  TileGroup tg;
+  const uint32_t b = blockIdx.x, h = blockIdx.y, nb = gridDim.x;
+  const uint32_t t0 = b * token_block;
+  tg.in_off = (int64_t)h * stride_head + (int64_t)t0 * stride_token;
+  tg.in_ld = stride_token;
+  tg.out_off = ((int64_t)h * tokens + t0) * head_dim;
+  tg.out_ld = head_dim;
+  tg.scale_off = (int64_t)h * nb + b;
+  tg.rows = min(token_block, tokens - t0);
+  tg.cols = head_dim;
+  quant_tile_group<__hip_bfloat16>(kv, q, sc, tg);
+}
+
+// KV dequantize: one workgroup per group, 8 codes per chunk (contiguous run
+// of rows * head_dim codes in the dense layout), up to 2048 chunks per group.
+__global__ __launch_bounds__(256) void k_kv_dequant(
+    const uint8_t* __restrict__ q, const float* __restrict__ sc, uint32_t tokens,
+    uint32_t head_dim, uint32_t token_block, __hip_bfloat16* __restrict__ out) {
+  const uint32_t b = blockIdx.x, h = blockIdx.y, nb = gridDim.x;
+  const uint32_t t0 = b * token_block;
+  const uint32_t rows = min(token_block, tokens - t0);
+  const int64_t off = ((int64_t)h * tokens + t0) * head_dim;
+  const float s = sc[(int64_t)h * nb + b];
+  const uint32_t nchunks = (rows * head_dim) >> 3;   // head_dim % 8 == 0
+  const uint2* src = reinterpret_cast<const uint2*>(q + off);
+  uint4* dst = reinterpret_cast<uint4*>(out + off);
+  uint2 w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c = threadIdx.x + 256u * i;
+    w[i] = c < nchunks ? src[c] : make_uint2(0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c = threadIdx.x + 256u * i;
+    if (c >= nchunks) continue;
+    uint32_t o[4];
+    const uint32_t ws[2] = {w[i].x, w[i].y};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[k], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[k], true);
+      const __hip_bfloat16 e0 = __float2bfloat16(lo[0] * s);
+      const __hip_bfloat16 e1 = __float2bfloat16(lo[1] * s);
+      const __hip_bfloat16 e2 = __float2bfloat16(hi[0] * s);
+      const __hip_bfloat16 e3 = __float2bfloat16(hi[1] * s);
+      o[2 * k] = (uint32_t)__bfloat16_as_ushort(e0) | ((uint32_t)__bfloat16_as_ushort(e1) << 16);
+      o[2 * k + 1] = (uint32_t)__bfloat16_as_ushort(e2) | ((uint32_t)__bfloat16_as_ushort(e3) << 16);
+    }
+    dst[c] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per tensor: zero the accumulator, atomic max of |x| bits into scales[0],
+// cast with the scale derived from it, then store the scale itself.
+// ---------------------------------------------------------------------------
+__global__ void k_store_zero(float* __restrict__ p) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *reinterpret_cast<uint32_t*>(p) = 0u;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_amax_tensor(const T* __restrict__ x, int64_t ld_x,
+                                                     uint32_t cols, uint64_t nchunks,
+                                                     float* __restrict__ acc) {
+  const uint32_t cpr = (cols + 7u) >> 3;
+  uint32_t m = 0;
+  for (uint64_t c = (uint64_t)blockIdx.x * 256u + threadIdx.x; c < nchunks;
+       c += (uint64_t)gridDim.x * 256u) {
+    const uint64_t r = c / cpr;
+    const uint32_t cc = (uint32_t)(c - r * cpr);
+    Vec8<T> v;
+    v.load(x + (int64_t)r * ld_x + cc * 8u, min(8u, cols - cc * 8u));
+    const uint32_t a = v.amax_bits();
+    m = a > m ? a : m;
+  }
+  m = block256_max(m);
+  if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(acc), m);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_cast_tensor(const T* __restrict__ x, int64_t ld_x,
+                                                     uint32_t cols, uint64_t nchunks,
+                                                     const float* __restrict__ acc,
+                                                     uint8_t* __restrict__ q, int64_t ld_q) {
+  const GroupScale gs = make_group_scale(*reinterpret_cast<const uint32_t*>(acc));
+  const uint32_t cpr = (cols + 7u) >> 3;
+  for (uint64_t c = (uint64_t)blockIdx.x * 256u + threadIdx.x; c < nchunks;
+       c += (uint64_t)gridDim.x * 256u) {
+    const uint64_t r = c / cpr;
+    const uint32_t cc = (uint32_t)(c - r * cpr);
+    const uint32_t nv = min(8u, cols - cc * 8u);
+    Vec8<T> v;
+    v.load(x + (int64_t)r * ld_x + cc * 8u, nv);
+    store_codes8(q + (int64_t)r * ld_q + cc * 8u, v.cast(gs), nv);
+  }
+}
+
+__global__ void k_finalize_tensor_scale(float* __restrict__ acc) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    const uint32_t bits = *reinterpret_cast<const uint32_t*>(acc);
+    acc[0] = __uint_as_float(bits) / kE4M3Max;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers (arguments already validated by the API layer).
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kGroupUnroll = 4;
+
+template <typename T>
+hipError_t quantize_typed(const QuantArgs& a, hipStream_t st) {
+  const T* x = static_cast<const T*>(a.x);
+  const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
+  if (a.gran == GRAN_PER_TENSOR) {
+    hipLaunchKernelGGL(k_store_zero, dim3(1), dim3(64), 0, st, a.scales);
+    if (rows == 0 || cols == 0) return hipGetLastError();
+    const uint64_t nchunks = (uint64_t)rows * ((cols + 7u) >> 3);
+    const uint64_t want = (nchunks + 255) / 256;
+    const uint32_t grid = (uint32_t)(want < 4096 ? want : 4096);
+    hipLaunchKernelGGL(k_amax_tensor<T>, dim3(grid), dim3(256), 0, st, x, a.ld_x, cols, nchunks, a.scales);
+    hipLaunchKernelGGL(k_cast_tensor<T>, dim3(grid), dim3(256), 0, st, x, a.ld_x, cols, nchunks,
+                       a.scales, a.q, a.ld_q);
+    hipLaunchKernelGGL(k_finalize_tensor_scale, dim3(1), dim3(64), 0, st, a.scales);
+    return hipGetLastError();
+  }
+  if (rows == 0 || cols == 0) return hipSuccess;
+  if (a.gran == GRAN_GROUP_1x128) {
+    const uint32_t ngroups = (cols + 127u) / 128u;
+    const uint32_t total = rows * ngroups;
+    const uint32_t per_block = 16u * kGroupUnroll;
+    const uint32_t grid = (total + per_block - 1) / per_block;
+    hipLaunchKernelGGL((k_quant_group_1x128<T, kGroupUnroll>), dim3(grid), dim3(256), 0, st, x,
+                       a.ld_x, cols, ngroups, total, a.q, a.ld_q, a.scales, a.ss_row, a.ss_col);
+    return hipGetLastError();
+  }
+  // 128x128 blocks
+  const dim3 grid((cols + 127u) / 128u, (rows + 127u) / 128u);
+  hipLaunchKernelGGL(k_quant_block_128x128<T>, grid, dim3(256), 0, st, x, a.ld_x, rows, cols, a.q,
+                     a.ld_q, a.scales, a.ss_row, a.ss_col);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
+  if (a.x_dtype == DTYPE_BF16) return quantize_typed<__hip_bfloat16>(a, st);
+  return quantize_typed<float>(a, st);
+}
+
+hipError_t launch_kv_quantize(const KvArgs& a, hipStream_t st) {
+  if (a.heads == 0 || a.tokens == 0) return hipSuccess;
+  const dim3 grid((uint32_t)((a.tokens + a.token_block - 1) / a.token_block), (uint32_t)a.heads);
+  hipLaunchKernelGGL(k_kv_quant, grid, dim3(256), 0, st,
+                     static_cast<const __hip_bfloat16*>(a.kv), a.stride_head, a.stride_token,
+                     (uint32_t)a.tokens, (uint32_t)a.head_dim, (uint32_t)a.token_block, a.q,
+                     a.scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_dequantize(const KvArgs& a, hipStream_t st) {
+  if (a.heads == 0 || a.tokens == 0) return hipSuccess;
+  const dim3 grid((uint32_t)((a.tokens + a.token_block - 1) / a.token_block), (uint32_t)a.heads);
+  hipLaunchKernelGGL(k_kv_dequant, grid, dim3(256), 0, st, a.q_in, a.scales_in, (uint32_t)a.tokens,
+                     (uint32_t)a.head_dim, (uint32_t)a.token_block,
+                     static_cast<__hip_bfloat16*>(a.out));
+  return hipGetLastError();
+}
+
+}  // namespace fp8blk

@@ -1,0 +1,184 @@
+/*
+ * fp8blk -- W8A8 FP8 quantization and block-scaled FP8 GEMM for AMD MI355X (gfx950).
+ *
+ * C ABI of libfp8blk.so. Plain pointers and sizes only; every device pointer is
+ * caller-owned HIP device memory, every call is asynchronous on `stream`
+ * (a hipStream_t; NULL means the default stream) and stateless.
+ *
+ * Sources (the web pages this library implements):
+ *   [FP8]   wangyu.me, "大语言模型量化技术（五）：FP8" (LLM quantization part 5: FP8)
+ *   [MIXED] charles2530.github.io, "量化：FP8 与混合精度推理：它不是一个 dtype 开关"
+ *   [LONG]  pwwt.cn, Llama-3 FP8 and long-context practice notes
+ *
+ * Numerics shared by every entry point:
+ *   - FP8 format: OCP E4M3 (bias 7, subnormals, no infinity, S.1111.111 = NaN),
+ *     largest finite value 448 ([FP8] section "FP8 是什么", format table).
+ *   - Scale of a group: s = fl32(amax / 448), an IEEE fp32 correctly rounded
+ *     division; the stored scale is the dequantization multiplier, x ~ q * s
+ *     ([FP8] section "什么是 FP8 量化"; section "权重量化：128×128 分块 FP8").
+ *   - Code of an element: the E4M3 value nearest to fl32(x / s) (the IEEE fp32
+ *     correctly rounded quotient), ties to even, magnitudes >= 448 saturate to
+ *     +-448, the sign of a zero result is the sign of x. A group with s == 0
+ *     gets sign-only zero codes.
+ *   - Denormals are honoured, never flushed.
+ *   - Inputs must be finite; non-finite inputs give unspecified codes but never
+ *     out-of-bounds accesses.
+ *
+ * Error behaviour: every argument is checked on the host before any HIP call
+ * and before any write, so a call that returns an error leaves all outputs
+ * untouched. FP8BLK_EHIP reports a failed kernel launch; device faults surface
+ * at the caller's next synchronisation. fp8blk_last_error() gives a per-thread
+ * message for the last failing call. No C++ exception crosses this interface.
+ */
+#ifndef FP8BLK_H
+#define FP8BLK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8BLK_ABI_VERSION 1
+
+typedef enum fp8blk_status {
+  FP8BLK_OK = 0,
+  FP8BLK_EINVAL = 1,       /* null pointer, negative size, ld < cols, bad enum, aliasing */
+  FP8BLK_EALIGN = 2,       /* base pointer or leading dimension not 16-byte aligned */
+  FP8BLK_EUNSUPPORTED = 3, /* valid request this version does not implement (e.g. E5M2) */
+  FP8BLK_EHIP = 4          /* the HIP runtime rejected a launch */
+} fp8blk_status;
+
+/* FP8 encodings ([FP8] section "FP8 是什么"). Only E4M3 is implemented; E5M2
+ * is reserved and returns FP8BLK_EUNSUPPORTED. */
+typedef enum fp8blk_format { FP8BLK_E4M3 = 0, FP8BLK_E5M2 = 1 } fp8blk_format;
+
+/* Scale granularity ([MIXED] section "scale 是控制面"; [FP8] sections
+ * "权重量化：128×128 分块 FP8" and "激活动态量化"). */
+typedef enum fp8blk_granularity {
+  FP8BLK_PER_TENSOR = 0,    /* one scale for the whole tensor; grid [1] */
+  FP8BLK_GROUP_1x128 = 1,   /* one row x 128 consecutive columns; grid [rows][ceil(cols/128)] */
+  FP8BLK_BLOCK_128x128 = 2  /* 128 rows x 128 columns; grid [ceil(rows/128)][ceil(cols/128)] */
+} fp8blk_granularity;
+
+typedef enum fp8blk_dtype { FP8BLK_BF16 = 0, FP8BLK_F32 = 1 } fp8blk_dtype;
+
+/*
+ * fp8_quantize -- dynamic quantization of a 2-D tensor to E4M3 codes plus fp32 scales.
+ *
+ * Defined by [FP8] section "什么是 FP8 量化" (scale max|x|/448, divide, round to
+ * nearest, saturate, keep codes and scale), section "权重量化：128×128 分块 FP8"
+ * (128x128 weight blocks, ceil-sized scale grid, fp32 scales) and section
+ * "激活动态量化" (per-token activation scales, optionally one per 128-channel
+ * group, computed at run time).
+ *
+ *   x       device, [rows][cols] of x_dtype (bf16 or fp32), row stride ld_x elements.
+ *   q       device, uint8 E4M3 codes [rows][cols], row stride ld_q bytes.
+ *   scales  device, fp32 scale grid; element (i, j) of the grid lives at
+ *           scales[i * scale_stride_row + j * scale_stride_col] (strides in
+ *           elements; ignored for PER_TENSOR, whose single scale is scales[0]).
+ *           For GROUP_1x128, scale_stride_row = 1 and scale_stride_col = rows
+ *           gives the K-block-major layout fp8_block_gemm reads fastest.
+ *   Ragged edges (cols or rows not a multiple of 128) form smaller groups.
+ *   rows == 0 or cols == 0 is a no-op, except that PER_TENSOR sets scales[0] = 0.
+ *
+ * Requirements: x, q, scales non-null; rows, cols >= 0; ld_x >= cols and
+ * ld_q >= cols; x and q 16-byte aligned; ld_x * sizeof(x_dtype) and ld_q
+ * multiples of 16 (else FP8BLK_EALIGN); x, q and scales must not overlap.
+ * PER_TENSOR uses scales[0] as an atomic max accumulator during the call.
+ */
+fp8blk_status fp8_quantize(const void* x, fp8blk_dtype x_dtype, int64_t rows, int64_t cols,
+                           int64_t ld_x, fp8blk_granularity gran, fp8blk_format fmt,
+                           uint8_t* q, int64_t ld_q, float* scales, int64_t scale_stride_row,
+                           int64_t scale_stride_col, void* stream);
+
+/*
+ * fp8_block_gemm -- C[M][N] = A[M][K] . B[N][K]^T from E4M3 codes and their scales.
+ *
+ * Defined by [FP8] section "激活动态量化" (the product is a sum over 128-wide K
+ * blocks j of activation scale x weight-block scale x FP8 block product, the
+ * scales multiplied back while accumulating) and section "FP8 矩阵乘" (128x128
+ * weight blocks, 1x128 activation groups, FP8 products with fp32
+ * accumulation); [MIXED] section "混合精度才是生产形态" (low-precision products,
+ * higher-precision sums). Computed as
+ *   C[m][n] = sum_j s_a(m, j) * s_b(n / 128, j) * P_j[m][n],
+ *   P_j[m][n] = sum over the 128 k of block j of dec(a[m][k]) * dec(b[n][k]),
+ * with every P_j summed in fp32 from zero and promoted into an fp32 accumulator
+ * with one fused multiply-add per K block; the result is rounded once to c_dtype.
+ *
+ *   a       device, uint8 codes [M][K], row stride lda bytes (activations).
+ *   scale_a device, fp32. gran_a = PER_TENSOR: scale_a[0]. gran_a = GROUP_1x128:
+ *           s_a(m, j) = scale_a[m * sa_stride_m + j * sa_stride_k].
+ *   b       device, uint8 codes [N][K], row stride ldb bytes (weights W in R^{N x K}).
+ *   scale_b device, fp32. gran_b = PER_TENSOR: scale_b[0]. gran_b = BLOCK_128x128:
+ *           s_b(nb, j) = scale_b[nb * sb_stride_n + j * sb_stride_k]
+ *           (the ceil(N/128) x ceil(K/128) weight_scale_inv grid).
+ *   c       device, [M][N] of c_dtype (BF16 output, or F32 for verification),
+ *           row stride ldc elements.
+ *
+ * Requirements: pointers non-null; M >= 0 (M == 0 is a no-op); N > 0, K > 0,
+ * N % 128 == 0 and K % 128 == 0 (else FP8BLK_EUNSUPPORTED); lda, ldb >= K;
+ * ldc >= N; a, b, c 16-byte aligned and lda, ldb, ldc * sizeof(c_dtype)
+ * multiples of 16; gran_a in {PER_TENSOR, GROUP_1x128}; gran_b in {PER_TENSOR,
+ * BLOCK_128x128}; fmt_a = fmt_b = E4M3; c must not overlap the inputs.
+ */
+fp8blk_status fp8_block_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                             const float* scale_a, fp8blk_granularity gran_a, int64_t sa_stride_m,
+                             int64_t sa_stride_k, const uint8_t* b, int64_t ldb,
+                             const float* scale_b, fp8blk_granularity gran_b, int64_t sb_stride_n,
+                             int64_t sb_stride_k, fp8blk_format fmt_a, fp8blk_format fmt_b,
+                             void* c, fp8blk_dtype c_dtype, int64_t ldc, void* stream);
+
+/*
+ * fp8_kv_quantize -- FP8 KV-cache quantization with one scale per (head, token block).
+ *
+ * Defined by [LONG] section 1 (K and V quantized to FP8 with separate scales)
+ * and section 3 (finer KV granularity: per head and per 128-token block, so
+ * that small late-position keys keep their precision); [MIXED] section
+ * "scale 是控制面" (per-head scales). Same per-group arithmetic as fp8_quantize.
+ * Call once for K and once for V.
+ *
+ *   kv      device, bf16 [heads][tokens][head_dim]; element (h, t, d) at
+ *           kv[h * stride_head + t * stride_token + d] (strides in elements,
+ *           head_dim contiguous).
+ *   q       device, dense uint8 codes [heads][tokens][head_dim].
+ *   scales  device, dense fp32 [heads][ceil(tokens / token_block)].
+ *   A group is one head, token_block consecutive tokens (fewer in the ragged
+ *   last block) and all of head_dim.
+ *
+ * Requirements: pointers non-null; heads, tokens >= 0 (0 is a no-op);
+ * head_dim > 0 and a multiple of 8; token_block > 0 and token_block * head_dim
+ * <= 16384 (else FP8BLK_EUNSUPPORTED); kv and q 16-byte aligned; stride_head
+ * and stride_token multiples of 8 with stride_token >= head_dim; outputs must
+ * not overlap the input.
+ */
+fp8blk_status fp8_kv_quantize(const void* kv, int64_t heads, int64_t tokens, int64_t head_dim,
+                              int64_t stride_head, int64_t stride_token, int64_t token_block,
+                              fp8blk_format fmt, uint8_t* q, float* scales, void* stream);
+
+/*
+ * fp8_kv_dequantize -- out = bf16(fl32(dec(q) * s)), round to nearest even.
+ *
+ * Defined by [MIXED] section "E4M3 和 E5M2 是范围与格点的取舍" (dequantization
+ * multiplies the FP8 value by its scale) and [FP8] section "什么是 FP8 量化"
+ * (x ~ q * s). Layouts are those fp8_kv_quantize writes; out is dense bf16
+ * [heads][tokens][head_dim].
+ *
+ * Requirements as fp8_kv_quantize; out must not overlap q or scales.
+ */
+fp8blk_status fp8_kv_dequantize(const uint8_t* q, const float* scales, int64_t heads,
+                                int64_t tokens, int64_t head_dim, int64_t token_block,
+                                fp8blk_format fmt, void* out_bf16, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* fp8blk_status_string(fp8blk_status s);
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* fp8blk_last_error(void);
+/* FP8BLK_ABI_VERSION of the loaded library. */
+int fp8blk_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BLK_H */

@@ -56,14 +56,33 @@ def block_gemm(qa, sa, gran_a: str, qw, sw, gran_w: str, rows=None, cols=None) -
     """Returns (y, T), both float64 [M, N] (or [len(rows), len(cols)] when
     ``rows``/``cols`` select a subset of outputs).
 
-    y = A_hat . W_hat^T and T = |A_hat| . |W_hat|^T.
+    y = A_hat . W_hat^T and T = |A_hat| . |W_hat|^T. With a selection only the
+    selected rows of A_hat and W_hat are formed (each row is dequantized with
+    the scales of its own groups, as in the full computation).
     """
-    a = dequant_activations(qa, sa, gran_a)
-    w = dequant_weights(qw, sw, gran_w)
+    qa = np.asarray(qa)
+    qw = np.asarray(qw)
+    sa = np.asarray(sa, dtype=np.float32)
+    sw = np.asarray(sw, dtype=np.float32)
+    K = qa.shape[1]
+    g = quant.GROUP
     if rows is not None:
-        a = a[np.asarray(rows)]
+        rows = np.asarray(rows)
+        qa = qa[rows]
+        if gran_a == GROUP_1x128:
+            sa = sa[rows]
     if cols is not None:
-        w = w[np.asarray(cols)]
+        cols = np.asarray(cols)
+        qw = qw[cols]
+        if gran_w == BLOCK_128x128:
+            # one row of the block grid per selected weight row
+            w_scales = np.repeat(sw[cols // g], g, axis=1)[:, :K].astype(np.float64)
+            w = quant.e4m3.decode(qw) * w_scales
+        else:
+            w = dequant_weights(qw, sw, gran_w)
+    else:
+        w = dequant_weights(qw, sw, gran_w)
+    a = dequant_activations(qa, sa, gran_a)
     y = a @ w.T
     t = np.abs(a) @ np.abs(w).T
     return y, t

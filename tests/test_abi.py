@@ -1,0 +1,168 @@
+"""The C-ABI library loads on a machine without a GPU, exports every entry
+point declared in include/fp8blk.h, and rejects bad arguments on the host
+before any HIP call (so these tests make no GPU call at all).
+
+The pointers passed here are never dereferenced: every call fails validation.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8blk.h")
+LIB = os.path.join(ROOT, "fp8_quantization_block_amd", "libfp8blk.so")
+
+OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP = 0, 1, 2, 3, 4
+BF16, F32 = 0, 1
+PER_TENSOR, GROUP, BLOCK = 0, 1, 2
+E4M3, E5M2 = 0, 1
+
+# fake, aligned, never-dereferenced device addresses
+PA, PB, PC, PD = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libfp8blk.so not built (python -m fp8_quantization_block_amd.build)")
+    import fp8_quantization_block_amd as fp8
+    return fp8.load_library(LIB)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("fp8_quantize", "fp8_block_gemm", "fp8_kv_quantize", "fp8_kv_dequantize",
+              "fp8blk_status_string", "fp8blk_last_error", "fp8blk_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strings(lib):
+    assert lib.fp8blk_abi_version() == 1
+    assert lib.fp8blk_status_string(EALIGN) == b"FP8BLK_EALIGN"
+    assert lib.fp8blk_status_string(99) == b"FP8BLK_UNKNOWN"
+
+
+def q(lib, x=PA, dt=BF16, rows=4, cols=256, ldx=256, gran=GROUP, fmt=E4M3, qp=PB, ldq=256,
+      s=PC, ssr=2, ssc=1):
+    return lib.fp8_quantize(x, dt, rows, cols, ldx, gran, fmt, qp, ldq, s, ssr, ssc, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=0), EINVAL),
+    (dict(qp=0), EINVAL),
+    (dict(s=0), EINVAL),
+    (dict(rows=-1), EINVAL),
+    (dict(cols=-5), EINVAL),
+    (dict(ldx=100), EINVAL),
+    (dict(ldq=128), EINVAL),
+    (dict(dt=7), EINVAL),
+    (dict(gran=9), EINVAL),
+    (dict(fmt=5), EINVAL),
+    (dict(fmt=E5M2), EUNSUPPORTED),
+    (dict(x=PA + 2), EALIGN),
+    (dict(qp=PB + 8), EALIGN),
+    (dict(ldx=260, cols=256), EALIGN),
+    (dict(ldq=264, cols=256), EALIGN),
+    (dict(ssr=-1), EINVAL),
+    (dict(qp=PA + 256), EINVAL),           # q overlaps x
+    (dict(s=PB + 16), EINVAL),             # scales overlap q
+    (dict(ssr=0, ssc=1), EINVAL),          # grid rows collapse onto one float
+    (dict(rows=1 << 31), EUNSUPPORTED),
+])
+def test_quantize_rejects(lib, kw, status):
+    assert q(lib, **kw) == status
+    assert lib.fp8blk_last_error().decode().startswith("fp8_quantize")
+
+
+def test_quantize_empty_group_grid_is_a_noop(lib):
+    # no HIP call is made for an empty 1x128 or 128x128 grid
+    assert q(lib, rows=0) == OK
+    assert q(lib, cols=0, gran=BLOCK) == OK
+    assert lib.fp8blk_last_error() == b""
+
+
+def g(lib, M=256, N=256, K=256, a=PA, lda=256, sa=PB, ga=GROUP, sam=2, sak=1, b=PC, ldb=256,
+      sb=PB + 65536, gb=BLOCK, sbn=2, sbk=1, fa=E4M3, fb=E4M3, c=PD, cdt=BF16, ldc=256):
+    return lib.fp8_block_gemm(M, N, K, a, lda, sa, ga, sam, sak, b, ldb, sb, gb, sbn, sbk, fa, fb,
+                              c, cdt, ldc, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a=0), EINVAL),
+    (dict(sb=0), EINVAL),
+    (dict(c=0), EINVAL),
+    (dict(ga=BLOCK), EINVAL),
+    (dict(gb=GROUP), EINVAL),
+    (dict(cdt=3), EINVAL),
+    (dict(fa=E5M2), EUNSUPPORTED),
+    (dict(fb=4), EINVAL),
+    (dict(M=-1), EINVAL),
+    (dict(N=0), EINVAL),
+    (dict(N=200), EUNSUPPORTED),
+    (dict(K=200, lda=256, ldb=256), EUNSUPPORTED),
+    (dict(lda=128), EINVAL),
+    (dict(ldc=128), EINVAL),
+    (dict(a=PA + 4), EALIGN),
+    (dict(lda=264), EALIGN),
+    (dict(ldc=260), EALIGN),
+    (dict(c=PA + 1024), EINVAL),           # c overlaps a
+    (dict(sak=-2), EINVAL),
+])
+def test_gemm_rejects(lib, kw, status):
+    assert g(lib, **kw) == status
+    assert lib.fp8blk_last_error().decode().startswith("fp8_block_gemm")
+
+
+def test_gemm_empty_m_is_a_noop(lib):
+    assert g(lib, M=0) == OK
+
+
+def kvq(lib, kv=PA, h=2, t=300, d=128, sh=300 * 128, st=128, tb=128, fmt=E4M3, qp=PB, s=PC):
+    return lib.fp8_kv_quantize(kv, h, t, d, sh, st, tb, fmt, qp, s, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kv=0), EINVAL),
+    (dict(h=-1), EINVAL),
+    (dict(d=0), EINVAL),
+    (dict(tb=0), EINVAL),
+    (dict(d=100, st=104, sh=300 * 104), EUNSUPPORTED),
+    (dict(d=256, st=256, sh=300 * 256), EUNSUPPORTED),   # 128 x 256 > 16384 per group
+    (dict(st=64), EINVAL),
+    (dict(fmt=E5M2), EUNSUPPORTED),
+    (dict(kv=PA + 8), EALIGN),
+    (dict(st=132), EALIGN),
+    (dict(qp=PA + 4096), EINVAL),          # codes overlap the input
+])
+def test_kv_quantize_rejects(lib, kw, status):
+    assert kvq(lib, **kw) == status
+
+
+def test_kv_empty_is_a_noop(lib):
+    assert kvq(lib, t=0) == OK
+    assert lib.fp8_kv_dequantize(PB, PC, 0, 300, 128, 128, E4M3, PD, None) == OK
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, PC, 2, 300, 128, 128, E4M3, PD), EINVAL),
+    ((PB, PC, 2, 300, 128, 128, E5M2, PD), EUNSUPPORTED),
+    ((PB, PC, 2, 300, 100, 128, E4M3, PD), EUNSUPPORTED),
+    ((PB, PC, 2, 300, 128, 128, E4M3, PD + 2), EALIGN),
+    ((PB, PC, 2, 300, 128, 128, E4M3, PB + 64), EINVAL),   # out overlaps the codes
+])
+def test_kv_dequantize_rejects(lib, args, status):
+    assert lib.fp8_kv_dequantize(*args, None) == status

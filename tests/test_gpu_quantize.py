@@ -1,0 +1,223 @@
+"""GPU parity of fp8_quantize against the CPU oracle: codes and scales bit-exact.
+
+Covers: every fp32 value in [-448, 448] through the encoder (groups whose scale
+is exactly 1), fp32 quotients placed next to every kind of E4M3 midpoint,
+random bf16 groups over the whole bf16 range (subnormal to max), all three
+granularities on ragged shapes with padded leading dimensions, both input
+dtypes, both scale layouts, and the activation / weight tensors of every
+configuration at full size (weights sampled by 128-row slabs where the oracle
+would take minutes).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as syn
+from gpu_helpers import assert_codes_equal, assert_scales_equal, f32_of
+from oracle import e4m3, quant
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _oracle_code_boundaries():
+    """For c = 1..126: the smallest non-negative fp32 bit pattern the oracle
+    encodes to a code >= c (the oracle is monotone in the magnitude)."""
+    out = []
+    for c in range(1, 127):
+        lo, hi = 0, 0x43E00000
+        while lo < hi:
+            mid = (lo + hi) // 2
+            v = np.array([mid], dtype=np.uint32).view(np.float32)
+            if e4m3.encode(v)[0] >= c:
+                hi = mid
+            else:
+                lo = mid + 1
+        out.append(lo)
+    return np.array(out, dtype=np.int64)
+
+
+def test_encoder_every_fp32_value_up_to_448(gpu_lib):
+    """Every fp32 bit pattern with |x| <= 448 (and its negation) in groups of
+    127 next to one 448.0, so s == 1 and x / s == x. Expected codes come from
+    the oracle's own boundaries between consecutive codes."""
+    bounds = torch.tensor(_oracle_code_boundaries(), device=DEV)
+    total = 0x43E00000 + 1
+    per = 127
+    chunk_groups = 1 << 21
+    start = 0
+    while start < total:
+        ng = min(chunk_groups, (total - start + per - 1) // per)
+        pats = torch.arange(start, start + ng * per, device=DEV, dtype=torch.int64).clamp_(max=total - 1)
+        expect = torch.searchsorted(bounds, pats, right=True).to(torch.uint8).view(ng, per)
+        x = torch.empty((ng, 128), dtype=torch.float32, device=DEV)
+        x[:, 0] = 448.0
+        x[:, 1:] = pats.to(torch.int32).view(torch.float32).view(ng, per)
+        for sign in (1.0, -1.0):
+            q, s = gpu_lib.fp8_quantize(x * sign, "group_1x128")
+            assert bool(torch.all(s == 1.0))
+            want = expect if sign > 0 else (expect | 0x80)
+            bad = q[:, 1:] != want
+            if bool(bad.any()):
+                i = int(torch.nonzero(bad.view(-1))[0])
+                p = int(pats[i])
+                raise AssertionError(f"pattern 0x{p:08x} sign {sign}: gpu 0x{int(q[:, 1:].reshape(-1)[i]):02x} "
+                                     f"oracle 0x{int(want.reshape(-1)[i]):02x}")
+            assert bool(torch.all(q[:, 0] == (0x7E if sign > 0 else 0xFE)))
+        start += ng * per
+        del pats, expect, x
+    torch.cuda.synchronize()
+
+
+def test_fp32_quotients_next_to_midpoints(gpu_lib):
+    """x = fl32(m * s) nudged by -3..3 ulps for E4M3 midpoints m (normal and
+    subnormal range), under scales with full 24-bit mantissas."""
+    rng = np.random.default_rng(202)
+    G = 4096
+    # three quarters with normal scales, one quarter with fp32-subnormal scales
+    amax = np.exp2(np.concatenate([rng.uniform(-100, 100, size=3 * G // 4),
+                                   rng.uniform(-140, -118, size=G // 4)])).astype(np.float32)
+    s = quant.scale_of(amax)
+    mids = np.concatenate([e4m3.MIDPOINTS, e4m3.GRID[1:126]])
+    m = rng.choice(mids, size=(G, 127))
+    x = (m * s[:, None].astype(np.float64)).astype(np.float32)
+    k = rng.integers(-3, 4, size=(G, 127))
+    xi = np.maximum(x.view(np.int32) + k.astype(np.int32), 0)
+    x = xi.view(np.float32)
+    x = np.where(np.abs(x) <= amax[:, None], x, x * np.float32(0.5))
+    x *= np.where(rng.random((G, 127)) < 0.5, np.float32(-1), np.float32(1))
+    full = np.concatenate([amax[:, None], x], axis=1).astype(np.float32)
+    perm = rng.permuted(np.tile(np.arange(128), (G, 1)), axis=1)
+    full = np.take_along_axis(full, perm, axis=1)
+    qr, sr = quant.quantize_group_1x128(full)
+    qg, sg = gpu_lib.fp8_quantize(torch.from_numpy(full).to(DEV), "group_1x128")
+    assert_scales_equal(sg.cpu().numpy(), sr, "scales")
+    assert_codes_equal(qg.cpu().numpy(), qr, full, "codes")
+
+
+def _random_bf16_groups(rng, G):
+    """bf16 groups: one amax pattern per group; the rest have |x| <= amax,
+    half spread over every pattern below it, half within 16 binades of it."""
+    amax_bits = rng.integers(0x0001, 0x7F80, size=G).astype(np.int64)
+    u = rng.random((G, 127))
+    near = np.maximum(amax_bits[:, None] - (u * 2048).astype(np.int64), 0)
+    spread = (u * (amax_bits[:, None] + 1)).astype(np.int64)
+    mag = np.where((np.arange(G) % 2 == 0)[:, None], near, spread)
+    sign = (rng.random((G, 127)) < 0.5).astype(np.int64) << 15
+    bits = np.concatenate([amax_bits[:, None] | ((rng.random((G, 1)) < 0.5).astype(np.int64) << 15),
+                           mag | sign], axis=1).astype(np.uint16)
+    perm = rng.permuted(np.tile(np.arange(128), (G, 1)), axis=1)
+    bits = np.take_along_axis(bits, perm, axis=1)
+    return quant.bf16_bits_to_f32(bits)
+
+
+def test_bf16_groups_across_the_range(gpu_lib):
+    rng = np.random.default_rng(203)
+    x = _random_bf16_groups(rng, 1 << 15)
+    qr, sr = quant.quantize_group_1x128(x)
+    xt = torch.from_numpy(x).to(torch.bfloat16).to(DEV)
+    qg, sg = gpu_lib.fp8_quantize(xt, "group_1x128")
+    assert_scales_equal(sg.cpu().numpy(), sr, "scales")
+    assert_codes_equal(qg.cpu().numpy(), qr, x, "codes")
+
+
+def _padded(x32: np.ndarray, dtype, ld: int) -> torch.Tensor:
+    rows, cols = x32.shape
+    buf = torch.full((rows, ld), float("nan"), dtype=dtype)
+    buf[:, :cols] = torch.from_numpy(x32).to(dtype)
+    return buf.to(DEV)[:, :cols]
+
+
+ORACLE = {"per_tensor": quant.quantize_per_tensor, "group_1x128": quant.quantize_group_1x128,
+          "block_128x128": quant.quantize_block_128x128}
+
+
+@pytest.mark.parametrize("gran", ["per_tensor", "group_1x128", "block_128x128"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rows,cols,ld", [(1, 1, 8), (3, 8, 8), (5, 300, 304), (129, 131, 136),
+                                          (257, 1000, 1024), (130, 128, 128), (1, 4096, 4096)])
+def test_ragged_shapes(gpu_lib, gran, dtype, rows, cols, ld):
+    rng = np.random.default_rng(rows * 7919 + cols)
+    x = (rng.standard_normal((rows, cols)) * np.exp2(rng.uniform(-8, 8, size=(rows, 1)))).astype(np.float32)
+    x = torch.from_numpy(x).to(dtype).float().numpy()
+    xt = _padded(x, dtype, ld)
+    qr, sr = ORACLE[gran](x)
+    qg, sg = gpu_lib.fp8_quantize(xt, gran)
+    assert_scales_equal(sg.cpu().numpy(), sr, f"{gran} scales")
+    assert_codes_equal(qg.cpu().numpy(), qr, x, f"{gran} codes")
+
+
+@pytest.mark.parametrize("gran", ["per_tensor", "group_1x128", "block_128x128"])
+def test_special_values(gpu_lib, gran):
+    """Zero groups, negative zeros, bf16 subnormals, the largest bf16 values,
+    and groups mixing 2^-133 with 2^127."""
+    rows, cols = 256, 384
+    x = np.zeros((rows, cols), dtype=np.float32)
+    x[0:128, 0:128] = -0.0
+    sub = quant.bf16_bits_to_f32(np.arange(1, 129, dtype=np.uint16))
+    x[128:256, 0:128] = np.tile(sub, (128, 1)) * np.where(np.arange(128) % 2, -1, 1)[:, None]
+    big = quant.bf16_bits_to_f32(np.arange(0x7F00, 0x7F80, dtype=np.uint16))
+    x[0:128, 128:256] = np.tile(big, (128, 1))
+    x[128:256, 128:256] = np.where(np.arange(128)[None, :] % 2, 2.0 ** 127, 2.0 ** -133)
+    x[:, 256:] = np.linspace(-1, 1, 128)[None, :]
+    x[5, 300] = -0.0
+    xt = torch.from_numpy(x).to(torch.bfloat16).to(DEV)
+    x = f32_of(xt)
+    qr, sr = ORACLE[gran](x)
+    qg, sg = gpu_lib.fp8_quantize(xt, gran)
+    assert_scales_equal(sg.cpu().numpy(), sr, f"{gran} scales")
+    assert_codes_equal(qg.cpu().numpy(), qr, x, f"{gran} codes")
+
+
+def test_kmajor_scale_layout(gpu_lib):
+    x = syn.activations(2, M=300, K=1024)
+    qr, sr = quant.quantize_group_1x128(f32_of(x))
+    qg, sg = gpu_lib.fp8_quantize(x.to(DEV), "group_1x128", scale_layout="kmajor")
+    assert sg.stride(0) == 1 and sg.stride(1) == 300
+    assert_scales_equal(sg.cpu().numpy(), sr, "scales")
+    assert_codes_equal(qg.cpu().numpy(), qr, None, "codes")
+
+
+@pytest.mark.parametrize("config", [1, 2, 3, 4])
+def test_config_activations_full_size(gpu_lib, config):
+    c = syn.CONFIGS[config]
+    x = syn.activations(config)
+    x32 = f32_of(x)
+    qr, sr = ORACLE[c["gran_a"]](x32)
+    qg, sg = gpu_lib.fp8_quantize(x.to(DEV), c["gran_a"])
+    assert_scales_equal(sg.cpu().numpy(), sr, "scales")
+    assert_codes_equal(qg.cpu().numpy(), qr, None, "codes")
+
+
+@pytest.mark.parametrize("config", [1, 2, 3, 4])
+def test_config_weights_full_size(gpu_lib, config):
+    c = syn.CONFIGS[config]
+    w = syn.weights(config)
+    qg, sg = gpu_lib.fp8_quantize(w.to(DEV), c["gran_w"])
+    qg, sg = qg.cpu().numpy(), sg.cpu().numpy()
+    if c["gran_w"] == "per_tensor":
+        qr, sr = quant.quantize_per_tensor(f32_of(w))
+        assert_scales_equal(sg, sr, "scales")
+        assert_codes_equal(qg, qr, None, "codes")
+        return
+    n_slabs = c["N"] // 128
+    rng = np.random.default_rng(config)
+    slabs = sorted(set([0, n_slabs - 1] + list(rng.choice(n_slabs, size=min(n_slabs, 12), replace=False))))
+    for sl in slabs:
+        w32 = f32_of(w[sl * 128:(sl + 1) * 128])
+        qr, sr = quant.quantize_block_128x128(w32)
+        assert_scales_equal(sg[sl:sl + 1], sr, f"slab {sl} scales")
+        assert_codes_equal(qg[sl * 128:(sl + 1) * 128], qr, None, f"slab {sl} codes")
+
+
+def test_repeated_calls_and_scale_buffer_reuse(gpu_lib):
+    """The per-tensor scale slot doubles as the amax accumulator: a second call
+    with smaller values must not keep the first call's maximum."""
+    a = torch.full((64, 512), 3.0, dtype=torch.bfloat16, device=DEV)
+    b = torch.full((64, 512), 0.5, dtype=torch.bfloat16, device=DEV)
+    s = torch.empty(1, dtype=torch.float32, device=DEV)
+    gpu_lib.fp8_quantize(a, "per_tensor", scales=s)
+    q, s = gpu_lib.fp8_quantize(b, "per_tensor", scales=s)
+    assert float(s[0]) == float(np.float32(0.5) / np.float32(448))
+    assert bool(torch.all(q == 0x7E))
