@@ -250,14 +250,14 @@ def main():
 
 def cpu_baseline(syn, M, N, K):
     """The oracle timed on a bounded sample of the step: 1x128 quantization of
-    the first 512 activation rows, then the oracle GEMM of those rows against
-    the first 3584 weight rows (weights quantized by the oracle beforehand,
-    untimed, as the offline pass)."""
+    all 4096 activation rows, then the oracle GEMM of those rows against the
+    first 3584 weight rows (a quarter of N; the weights are quantized by the
+    oracle beforehand, untimed, as the offline pass)."""
     import numpy as np
     import threadpoolctl
     from oracle import quant, gemm
 
-    ms, ns = 512, 3584
+    ms, ns = 4096, 3584
     a = syn.activations(2)[:ms].float().numpy()
     w = syn.weights(2)[:ns].float().numpy()
     qw, sw = quant.quantize_block_128x128(w)

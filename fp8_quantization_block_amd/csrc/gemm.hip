@@ -222,6 +222,140 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode-shaped GEMM (M <= 64): bound by streaming the weights from HBM once.
+//
+// A workgroup owns 64 output columns (four 16-column subtiles) for every
+// row of C and splits K eight ways over its waves. Weight fragments go from
+// global memory straight into MFMA operand registers (each weight byte is
+// used once, so LDS staging would only add traffic); the next K block's
+// fragments are loaded while the current one is multiplied. The MFMA's first
+// operand is the weight subtile and its second the activations, so a lane's
+// four results share one activation row (one s_a) and the subtile shares one
+// s_b. The eight partial sums are added through LDS in a fixed order.
+// ---------------------------------------------------------------------------
+constexpr int kDecThreads = 512;
+constexpr int kDecSplit = kDecThreads / 64;
+constexpr int kDecBN = 64;
+
+template <int MT>
+struct DecFrags {
+  v8i w[4];
+  v8i a[MT];
+  float sa[MT];
+  float sw;
+};
+
+__device__ __forceinline__ v8i load_frag32(const uint8_t* p) {
+  const uint4 lo = reinterpret_cast<const uint4*>(p)[0];
+  const uint4 hi = reinterpret_cast<const uint4*>(p)[1];
+  v8i f;
+  f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
+  f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
+  return f;
+}
+
+template <int MT, bool kBf16Out>
+__global__ __launch_bounds__(kDecThreads) void k_gemm_fp8_decode(GemmParams p) {
+  __shared__ float red[kDecSplit][4 * MT * 64 * 4];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * kDecBN;
+  const int nk = p.K / 128;
+  const int kb0 = (nk * wave) / kDecSplit;
+  const int kb1 = (nk * (wave + 1)) / kDecSplit;
+  const int r16 = lane & 15;
+  const int kq = (lane >> 4) * 32;          // this lane's 32 bytes of a K block
+
+  const uint8_t* wrow[4];
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns) wrow[ns] = p.b + (int64_t)(n0 + ns * 16 + r16) * p.ldb + kq;
+  const uint8_t* arow[MT];
+  const float* sarow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = min(mt * 16 + r16, p.M - 1);
+    arow[mt] = p.a + (int64_t)m * p.lda + kq;
+    sarow[mt] = p.sa + (int64_t)m * p.sa_m;
+  }
+  const float* swrow = p.sb + (int64_t)(n0 >> 7) * p.sb_n;
+
+  auto load = [&](int kb) {
+    DecFrags<MT> f;
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) f.w[ns] = load_frag32(wrow[ns] + (int64_t)kb * 128);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f.a[mt] = load_frag32(arow[mt] + (int64_t)kb * 128);
+      f.sa[mt] = sarow[mt][(int64_t)kb * p.sa_k];
+    }
+    f.sw = swrow[(int64_t)kb * p.sb_k];
+    return f;
+  };
+
+  v4f acc[4][MT];
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[ns][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  if (kb0 < kb1) {
+    DecFrags<MT> cur = load(kb0);
+    for (int kb = kb0; kb < kb1; ++kb) {
+      DecFrags<MT> nxt = cur;
+      if (kb + 1 < kb1) nxt = load(kb + 1);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const float comb = cur.sa[mt] * cur.sw;
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) {
+          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur.w[ns], cur.a[mt], zero, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[ns][mt][v] = __builtin_fmaf(part[v], comb, acc[ns][mt][v]);
+        }
+      }
+      cur = nxt;
+    }
+  }
+
+  // partial sums to LDS: index ((ns * MT + mt) * 64 + lane) * 4 + v
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      *reinterpret_cast<v4f*>(&red[wave][((ns * MT + mt) * 64 + lane) * 4]) = acc[ns][mt];
+  __syncthreads();
+
+  for (int o = threadIdx.x; o < 4 * MT * 64 * 4; o += kDecThreads) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecSplit; ++w) sum += red[w][o];
+    const int v = o & 3;
+    const int ln = (o >> 2) & 63;
+    const int mt = (o >> 8) % MT;
+    const int ns = (o >> 8) / MT;
+    const int m = mt * 16 + (ln & 15);
+    const int n = n0 + ns * 16 + 4 * (ln >> 4) + v;
+    if (m < p.M) {
+      if (kBf16Out)
+        static_cast<__hip_bfloat16*>(p.c)[(int64_t)m * p.ldc + n] = __float2bfloat16(sum);
+      else
+        static_cast<float*>(p.c)[(int64_t)m * p.ldc + n] = sum;
+    }
+  }
+}
+
+template <int MT>
+void launch_decode(const GemmParams& p, bool bf16, hipStream_t st) {
+  const dim3 grid((unsigned)(p.N / kDecBN));
+  if (bf16)
+    hipLaunchKernelGGL((k_gemm_fp8_decode<MT, true>), grid, dim3(kDecThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((k_gemm_fp8_decode<MT, false>), grid, dim3(kDecThreads), 0, st, p);
+}
+
 }  // namespace
 
 hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t st) {
@@ -244,6 +378,19 @@ hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t st) {
   p.K = (int)g.K;
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
+  const bool bf16 = g.c_dtype == DTYPE_BF16;
+  if (p.M <= 16) {
+    launch_decode<1>(p, bf16, st);
+    return hipGetLastError();
+  }
+  if (p.M <= 32) {
+    launch_decode<2>(p, bf16, st);
+    return hipGetLastError();
+  }
+  if (p.M <= 64) {
+    launch_decode<4>(p, bf16, st);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
   if (g.c_dtype == DTYPE_BF16)
     hipLaunchKernelGGL(k_gemm_fp8_block<true>, grid, dim3(kThreads), 0, st, p);
