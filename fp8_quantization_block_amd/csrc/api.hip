@@ -52,6 +52,8 @@ fp8blk_status hip_status(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;   // indices are kept in 32 bits inside kernels
+// the GEMM addresses a 256-row operand tile with 32-bit byte offsets
+constexpr int64_t kMaxLdCodes = (int64_t)1 << 23;
 
 fp8blk_status check_format(fp8blk_format fmt, const char* what) {
   if (fmt == FP8BLK_E4M3) return FP8BLK_OK;
@@ -158,6 +160,8 @@ fp8blk_status fp8_block_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, 
   if (N % 128 != 0 || K % 128 != 0)
     return fail(FP8BLK_EUNSUPPORTED, "%s: N and K must be multiples of 128", fn);
   if (lda < K || ldb < K || ldc < N) return fail(FP8BLK_EINVAL, "%s: leading dimension too small", fn);
+  if (lda >= kMaxLdCodes || ldb >= kMaxLdCodes)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: lda and ldb must be below 2^23", fn);
   if (sa_stride_m < 0 || sa_stride_k < 0 || sb_stride_n < 0 || sb_stride_k < 0)
     return fail(FP8BLK_EINVAL, "%s: negative scale stride", fn);
   const int64_t csz = c_dtype == FP8BLK_BF16 ? 2 : 4;

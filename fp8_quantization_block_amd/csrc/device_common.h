@@ -69,15 +69,19 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
 //
 // The code of x is E4M3(fl32(x / s)) with the IEEE correctly rounded fp32
 // quotient. Per element that division is replaced by two multiplications with
-// reciprocals nudged down and up: with r = fl32(1 / s),
-//   rl = fl32(r * (1 - 2^-21)),  rh = fl32(r * (1 + 2^-21)),
+// reciprocals nudged down and up: with r ~ 1 / s to within 2^-22 relative
+// (v_rcp_f32 is accurate to 1 ulp),
+//   rl = r * (1 - 2^-20),  rh = r * (1 + 2^-20),
 // the products fl32(x * rl) and fl32(x * rh) bracket fl32(x / s) strictly in
-// magnitude (their relative offsets exceed 2^-21 - 3 * 2^-24 > 2^-24, the fp32
-// rounding bound) whenever the quotient is an fp32 normal. Round-to-nearest is
-// monotone, so when both brackets give the same code it is the code of
-// fl32(x / s); otherwise the element takes the exact division. Quotients below
-// the fp32 normal range give code 0 (signed) on every path. Groups whose scale
-// is an fp32 subnormal (r may overflow) always take the exact division.
+// magnitude (their relative offsets exceed 2^-20 - 2^-22 - 3 * 2^-24 > 2^-24,
+// the fp32 rounding bound) whenever the quotient is an fp32 normal.
+// Round-to-nearest is monotone, so when both brackets give the same code it is
+// the code of fl32(x / s); otherwise the element takes the exact division.
+// The lower bracket never exceeds 448 (|x| <= amax), where the hardware
+// conversion is exact; the upper one may exceed it by a hair, and if the
+// conversion then disagrees the exact path decides. Quotients below the fp32
+// normal range give code 0 (signed) on every path. Groups whose scale is zero
+// or an fp32 subnormal (r may overflow) always take the exact division.
 // ---------------------------------------------------------------------------
 struct GroupScale {
   float s;    // fl32(amax / 448)
@@ -89,9 +93,9 @@ struct GroupScale {
 __device__ __forceinline__ GroupScale make_group_scale(uint32_t amax_bits) {
   GroupScale g;
   g.s = __uint_as_float(amax_bits) / kE4M3Max;   // IEEE correctly rounded division
-  const float r = 1.0f / g.s;                    // IEEE correctly rounded division
-  g.rl = r * (1.0f - 0x1.0p-21f);
-  g.rh = r * (1.0f + 0x1.0p-21f);
+  const float r = __builtin_amdgcn_rcpf(g.s);    // 1 ulp
+  g.rl = r * (1.0f - 0x1.0p-20f);
+  g.rh = r * (1.0f + 0x1.0p-20f);
   g.exact = !(g.s >= 0x1.0p-126f);
   return g;
 }
@@ -102,15 +106,42 @@ __device__ __forceinline__ float exact_quotient(float x, float s) {
   return x / s;   // IEEE correctly rounded division
 }
 
+// Four fp32 values (|v| <= 448 or slightly above) -> four E4M3 codes, no clamp.
+__device__ __forceinline__ uint32_t e4m3x4_raw(float a, float b, float c, float d) {
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
+  return w;
+}
+
 // Codes of four elements of one group.
 __device__ __forceinline__ uint32_t cast4(const GroupScale& g, float a, float b, float c, float d) {
   if (!g.exact) {
-    const uint32_t lo = e4m3x4(a * g.rl, b * g.rl, c * g.rl, d * g.rl);
-    const uint32_t hi = e4m3x4(a * g.rh, b * g.rh, c * g.rh, d * g.rh);
+    const uint32_t lo = e4m3x4_raw(a * g.rl, b * g.rl, c * g.rl, d * g.rl);
+    const uint32_t hi = e4m3x4_raw(a * g.rh, b * g.rh, c * g.rh, d * g.rh);
     if (__builtin_expect(lo == hi, 1)) return lo;
   }
   return e4m3x4(exact_quotient(a, g.s), exact_quotient(b, g.s), exact_quotient(c, g.s),
                 exact_quotient(d, g.s));
+}
+
+// Max over the 8 lanes of each half of a DPP row; every lane of the half gets it.
+__device__ __forceinline__ uint32_t row8_max(uint32_t v) {
+  v = dpp_max_step<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_step<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_step<0x141>(v);  // row_half_mirror
+  return v;
+}
+
+// q = n / d for n < 2^31 with a precomputed multiplier (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", PLDI
+// 1994): l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1, and
+// q = (umulhi(m, n) + n) >> l; the sum cannot overflow because n < 2^31.
+struct FastDiv {
+  uint32_t m;
+  uint32_t l;
+};
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, FastDiv d) {
+  return (__umulhi(d.m, n) + n) >> d.l;
 }
 
 // |x| bit patterns of eight bf16 values held in four words, as fp32 bit

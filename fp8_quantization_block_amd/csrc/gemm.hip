@@ -16,10 +16,13 @@
 //   owning 64 rows x 128 columns (so a wave's columns are exactly one weight
 //   scale block and s_b is one scalar per K block).
 // * A and B tiles (and the K block's 256 activation scales and 2 weight-block
-//   scales) are copied
-//   global -> LDS with global_load_lds_dwordx4 / _dword, double buffered, one
-//   barrier per K block. Rows are stored with their eight 16-byte chunks
-//   XOR-swizzled by (row & 7) so the MFMA operand reads are conflict free.
+//   scales) are double buffered in LDS, one barrier per K block. The next
+//   block's tiles travel through 16 registers per thread in two halves: the A
+//   tile is loaded while the first half of the block's MFMAs run and written
+//   to LDS after them, then the B tile the same way around the second half.
+//   (Direct global-to-LDS copies did not overlap with the MFMA work on this
+//   chip; the register route does.) Rows are stored with their eight 16-byte
+//   chunks XOR-swizzled so the MFMA operand reads are conflict free.
 // * Workgroup ids are remapped so that neighbouring tiles (which share A rows
 //   or B columns) run on the same XCD and share its L2.
 #include <hip/hip_bf16.h>
@@ -31,8 +34,6 @@ namespace fp8blk {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
 namespace {
 
@@ -54,43 +55,22 @@ struct GemmParams {
   int tiles_m, tiles_n;
 };
 
-__device__ __forceinline__ void lds_copy16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_copy4(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds, 4, 0, 0);
+// A 128-byte operand row holds eight 16-byte chunks; logical chunk c of row r
+// is stored at physical chunk c ^ swz(r). Any 16 consecutive rows then hit 16
+// distinct (row parity, chunk) pairs and any 8 consecutive rows 8 distinct
+// chunks, so the fragment reads (16 rows, same logical chunk) and the tile
+// writes (8 lanes per row) are free of bank conflicts whether the LDS serves
+// 8 or 16 lanes of a 128-bit access per cycle.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// Buffer resource over `bytes` bytes from `base` (raw, untyped loads; reads
+// at or past `bytes` return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Issue the copies of K block kb into one LDS stage. Each wave instruction
-// fills 1 KB = 8 rows of 128 bytes; lane l fills physical chunk l % 8 of row
-// l / 8, which holds logical chunk (l % 8) ^ (row & 7).
-struct Stage {
-  uint8_t* a;      // [256][128] codes, swizzled
-  uint8_t* b;      // [256][128] codes, swizzled
-  float* s;        // [256] activation scales, then 2 weight-block scales
-};
-
-__device__ __forceinline__ void issue_stage(const GemmParams& p, const Stage& stage, int m0, int n0,
-                                            int kb, int wave, int lane) {
-  const int sub_row = lane >> 3;
-  const int pchunk = lane & 7;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int blk = wave * 4 + i;                // 0..31
-    const int row = blk * 8 + sub_row;           // 0..255
-    const int lchunk = pchunk ^ (row & 7);
-    const int ra = min(m0 + row, p.M - 1);
-    const int rb = min(n0 + row, p.N - 1);
-    lds_copy16(p.a + (int64_t)ra * p.lda + (int64_t)kb * BK + lchunk * 16, stage.a + blk * 1024);
-    lds_copy16(p.b + (int64_t)rb * p.ldb + (int64_t)kb * BK + lchunk * 16, stage.b + blk * 1024);
-  }
-  if (wave < 4) {
-    const int r = min(m0 + wave * 64 + lane, p.M - 1);
-    lds_copy4(p.sa + (int64_t)r * p.sa_m + (int64_t)kb * p.sa_k, stage.s + wave * 64);
-  } else if (wave == 4 && lane < 2) {
-    const int nb = min((n0 >> 7) + lane, (p.N >> 7) - 1);
-    lds_copy4(p.sb + (int64_t)nb * p.sb_n + (int64_t)kb * p.sb_k, stage.s + 256);
-  }
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
 // Operand fragment of one 16-row (or 16-column) subtile: lane l takes row
@@ -98,7 +78,7 @@ __device__ __forceinline__ void issue_stage(const GemmParams& p, const Stage& st
 // same K assignment, so the MFMA sums exactly the 128 products of the block.
 __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int lane) {
   const int lc0 = (lane >> 4) * 2;
-  const int sw = row & 7;
+  const int sw = swz(row);
   const uint4 lo = *reinterpret_cast<const uint4*>(tile + row * 128 + ((lc0 ^ sw) << 4));
   const uint4 hi = *reinterpret_cast<const uint4*>(tile + row * 128 + (((lc0 + 1) ^ sw) << 4));
   v8i f;
@@ -107,58 +87,125 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int lane)
   return f;
 }
 
-// One K block: prefetch block kb + 1 into `next` (if any), then multiply the
-// tiles of block kb held in `cur` and promote into acc.
-struct WaveCtx {
-  int m0, n0, wave, lane, wm, wn;
-  bool active;
-};
-
-__device__ __forceinline__ void k_block_step(const GemmParams& p, const WaveCtx& w, int kb, int nk,
-                                             const Stage& cur, const Stage& next, v4f (&acc)[4][8]) {
-  if (kb + 1 < nk) issue_stage(p, next, w.m0, w.n0, kb + 1, w.wave, w.lane);
-  if (w.active) {
-    const float sbv = cur.s[256 + w.wn];
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    const uint8_t* ta = cur.a;
-    const uint8_t* tb = cur.b;
-    const float* ssa = cur.s;
-    const int lane = w.lane;
-    v8i af[4];
-    v4f comb[4];
+// Multiply the four 16-column subtiles ni0 .. ni0 + 3 of this wave against
+// its four 16-row A fragments and promote every 16 x 16 partial into acc.
+template <int ni0>
+__device__ __forceinline__ void mma_half(const uint8_t* tb, int wn, int lane, const v8i (&af)[4],
+                                         const v4f (&comb)[4], v4f (&acc)[4][8]) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ni = ni0; ni < ni0 + 4; ++ni) {
+    const v8i bf = read_frag(tb, wn * 128 + ni * 16 + (lane & 15), lane);
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
-      af[mi] = read_frag(ta, w.wm * 64 + mi * 16 + (lane & 15), lane);
-      const v4f s4 = *reinterpret_cast<const v4f*>(ssa + w.wm * 64 + mi * 16 + 4 * (lane >> 4));
-      comb[mi] = s4 * sbv;
-    }
+      const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf, zero, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-    for (int ni = 0; ni < 8; ++ni) {
-      const v8i bf = read_frag(tb, w.wn * 128 + ni * 16 + (lane & 15), lane);
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf, zero, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[mi][ni][v] = __builtin_fmaf(part[v], comb[mi][v], acc[mi][ni][v]);
-      }
+      for (int v = 0; v < 4; ++v) acc[mi][ni][v] = __builtin_fmaf(part[v], comb[mi][v], acc[mi][ni][v]);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's prefetch landed
-  __syncthreads();                      // ... and every other wave's
+}
+
+// One K block's operands in flight in registers: thread t holds chunks
+// c = t + 512 i (i = 0..3) of the A and the B tile (row c / 8, logical chunk
+// c % 8), and one scale (an activation scale for t < 256, a weight-block
+// scale for t = 256, 257).
+struct Regs {
+  uint4 a[4];
+  uint4 b[4];
+  float s;
+};
+
+// Per-thread copy plan. Global offsets are relative to the tile's first row
+// (so they fit 32 bits: 256 * ld < 2^31 is checked on the host); rows past the
+// operand's end fall outside the buffer resource and read as zero. The four
+// LDS destinations of a thread are 64 rows apart, which keeps the same swizzle,
+// so one offset plus immediates addresses them.
+struct Copier {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t goa[4], gob[4];
+  uint32_t loff;      // LDS byte offset of chunk 0; chunk i adds 8192 * i
+  const float* sp;    // this thread's scale for K block 0 (threads 0..257)
+  int64_t s_kstep;    // element step of that scale per K block
+  int tid;
+};
+
+__device__ __forceinline__ void load_a(const Copier& c, int kb, Regs& r) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.a[i] = buf_load16(c.ra, c.goa[i], (uint32_t)kb * BK);
+}
+__device__ __forceinline__ void load_b(const Copier& c, int kb, Regs& r) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.b[i] = buf_load16(c.rb, c.gob[i], (uint32_t)kb * BK);
+  r.s = c.tid < 258 ? c.sp[(int64_t)kb * c.s_kstep] : 0.f;
+}
+__device__ __forceinline__ void store_a(const Copier& c, const Regs& r, uint8_t* ta) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(ta + c.loff + 8192 * i) = r.a[i];
+}
+__device__ __forceinline__ void store_b(const Copier& c, const Regs& r, uint8_t* tb, float* ts) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(tb + c.loff + 8192 * i) = r.b[i];
+  if (c.tid < 258) ts[c.tid] = r.s;
+}
+
+// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt left at their maxima).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier that waits for this wave's LDS writes but not for its
+// global loads in flight; the empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  wait_lds();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One K block. On entry `r` holds block kb + 1 (loaded during the previous
+// block) and stage nxt_* is free. The A half of r goes to LDS and is reloaded
+// with block kb + 2, the first half of block kb's MFMAs runs, then the B half
+// and the scales move the same way before the second half of the MFMAs. The
+// LDS writes thus arrive as two 32 KB bursts between fragment reads, and every
+// load has a whole block of work to arrive. Block indices are clamped to the
+// last block (the tail re-copies it into a stage nobody reads again), so every
+// step has the same shape.
+__device__ __forceinline__ void block_step(const Copier& cp, Regs& r, int kb, int nk, int wm,
+                                           int wn, int lane, bool active, const uint8_t* cur_a,
+                                           const uint8_t* cur_b, const float* cur_s,
+                                           uint8_t* nxt_a, uint8_t* nxt_b, float* nxt_s,
+                                           v4f (&acc)[4][8]) {
+  const int kl = min(kb + 2, nk - 1);
+  v8i af[4];
+  v4f comb[4];
+  if (active) {
+    const float sbv = cur_s[256 + wn];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      af[mi] = read_frag(cur_a, wm * 64 + mi * 16 + (lane & 15), lane);
+      const v4f s4 = *reinterpret_cast<const v4f*>(cur_s + wm * 64 + mi * 16 + 4 * (lane >> 4));
+      comb[mi] = s4 * sbv;
+    }
+  }
+  store_a(cp, r, nxt_a);
+  load_a(cp, kl, r);
+  __builtin_amdgcn_sched_barrier(0);
+  if (active) mma_half<0>(cur_b, wn, lane, af, comb, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  store_b(cp, r, nxt_b, nxt_s);
+  load_b(cp, kl, r);
+  __builtin_amdgcn_sched_barrier(0);
+  if (active) mma_half<4>(cur_b, wn, lane, af, comb, acc);
+  lds_barrier();
 }
 
 template <bool kBf16Out>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
-  // two LDS stages as distinct objects, so the compiler can tell reads of one
-  // stage from the asynchronous copies into the other
   __shared__ __attribute__((aligned(1024))) uint8_t a0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t b0[kTileBytes];
   __shared__ __attribute__((aligned(16))) float s0[BM + 4];
   __shared__ __attribute__((aligned(1024))) uint8_t a1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t b1[kTileBytes];
   __shared__ __attribute__((aligned(16))) float s1[BM + 4];
-  const Stage stage0 = {a0, b0, s0};
-  const Stage stage1 = {a1, b1, s1};
 
   // ---- tile assignment: XCD-major remap, then grouped row-major order ----
   const int nwg = p.tiles_m * p.tiles_n;
@@ -169,19 +216,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
   const int first_m = group * kGroupM;
   const int gm = min(p.tiles_m - first_m, kGroupM);
   const int in_group = bid - group * kGroupM * p.tiles_n;
-  const int tm = first_m + in_group % gm;
-  const int tn = in_group / gm;
+  const int m0 = (first_m + in_group % gm) * BM;
+  const int n0 = (in_group / gm) * BN;
 
-  WaveCtx w;
-  w.m0 = tm * BM;
-  w.n0 = tn * BN;
-  w.lane = threadIdx.x & 63;
-  w.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
-  w.wm = w.wave >> 1;          // 0..3 : 64-row slab
-  w.wn = w.wave & 1;           // 0..1 : 128-column slab
-  w.active = (w.n0 + w.wn * 128) < p.N;
-  const int m0 = w.m0, n0 = w.n0, lane = w.lane, wm = w.wm, wn = w.wn;
-  const bool wave_active = w.active;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+  const int wm = wave >> 1;          // 0..3 : 64-row slab
+  const int wn = wave & 1;           // 0..1 : 128-column slab
+  const bool active = (n0 + wn * 128) < p.N;
+
+  Copier cp;
+  cp.tid = tid;
+  const int rows_a = min(p.M - m0, BM), rows_b = min(p.N - n0, BN);
+  cp.ra = make_rsrc(p.a + (int64_t)m0 * p.lda, (uint32_t)(rows_a * p.lda));
+  cp.rb = make_rsrc(p.b + (int64_t)n0 * p.ldb, (uint32_t)(rows_b * p.ldb));
+  {
+    const int row = tid >> 3, lc = tid & 7;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      cp.goa[i] = (uint32_t)((row + 64 * i) * (int)p.lda + lc * 16);
+      cp.gob[i] = (uint32_t)((row + 64 * i) * (int)p.ldb + lc * 16);
+    }
+    cp.loff = (uint32_t)(row * 128 + ((lc ^ swz(row)) << 4));
+  }
+  // scales: threads 0..255 copy the activation scale of tile row tid, threads
+  // 256 and 257 the weight-block scales of the tile's two 128-column halves
+  if (tid < 256) {
+    cp.sp = p.sa + (int64_t)min(m0 + tid, p.M - 1) * p.sa_m;
+    cp.s_kstep = p.sa_k;
+  } else {
+    cp.sp = p.sb + (int64_t)min((n0 >> 7) + (tid - 256), (p.N >> 7) - 1) * p.sb_n;
+    cp.s_kstep = p.sb_k;
+  }
 
   v4f acc[4][8];
 #pragma unroll
@@ -190,16 +257,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
     for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const int nk = p.K / BK;
-  issue_stage(p, stage0, m0, n0, 0, w.wave, lane);
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies landed
-  __syncthreads();
+  Regs r;
+  load_a(cp, 0, r);
+  load_b(cp, 0, r);
+  store_a(cp, r, a0);
+  store_b(cp, r, b0, s0);
+  load_a(cp, min(1, nk - 1), r);
+  load_b(cp, min(1, nk - 1), r);
+  lds_barrier();
 
   for (int kb = 0; kb < nk; kb += 2) {
-    k_block_step(p, w, kb, nk, stage0, stage1, acc);
-    if (kb + 1 < nk) k_block_step(p, w, kb + 1, nk, stage1, stage0, acc);
+    block_step(cp, r, kb, nk, wm, wn, lane, active, a0, b0, s0, a1, b1, s1, acc);
+    if (kb + 1 < nk) block_step(cp, r, kb + 1, nk, wm, wn, lane, active, a1, b1, s1, a0, b0, s0, acc);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no load outstanding past the loop
 
-  if (!wave_active) return;
+  if (!active) return;
   // ---- epilogue: lane holds rows 4 * (lane / 16) + v, column lane % 16 ----
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {

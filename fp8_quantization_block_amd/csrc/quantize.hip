@@ -112,40 +112,49 @@ __device__ __forceinline__ uint32_t block256_max(uint32_t m) {
 }
 
 // ---------------------------------------------------------------------------
-// 1x128 groups: 16 lanes (one DPP row) per group, 8 elements per lane,
+// 1x128 groups: 8 lanes (half a DPP row) per group, 16 elements per lane in
+// two 16-byte chunks (elements 8 l .. 8 l + 7 and 64 + 8 l .. 64 + 8 l + 7),
 // kUnroll groups per lane with all loads issued before any arithmetic.
 // Group g of the flat (row, group) index space: row = g / ngroups.
 // ---------------------------------------------------------------------------
 template <typename T, int kUnroll>
 __global__ __launch_bounds__(256) void k_quant_group_1x128(
     const T* __restrict__ x, int64_t ld_x, uint32_t cols, uint32_t ngroups, uint32_t total_groups,
-    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ sc, int64_t ss_row, int64_t ss_col) {
-  const uint32_t lane16 = threadIdx.x & 15u;
-  const uint32_t slot = threadIdx.x >> 4;
-  Vec8<T> v[kUnroll];
-  uint32_t row[kUnroll], grp[kUnroll], nvalid[kUnroll];
+    FastDiv div_groups, uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ sc,
+    int64_t ss_row, int64_t ss_col) {
+  const uint32_t lane8 = threadIdx.x & 7u;
+  const uint32_t slot = threadIdx.x >> 3;
+  Vec8<T> v[kUnroll][2];
+  uint32_t row[kUnroll], grp[kUnroll], nv[kUnroll][2];
   bool live[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
-    const uint32_t g = (blockIdx.x * kUnroll + u) * 16u + slot;
+    const uint32_t g = (blockIdx.x * kUnroll + u) * 32u + slot;
     live[u] = g < total_groups;
-    row[u] = live[u] ? g / ngroups : 0u;
+    row[u] = live[u] ? fastdiv(g, div_groups) : 0u;
     grp[u] = g - row[u] * ngroups;
-    const uint32_t col0 = grp[u] * 128u + lane16 * 8u;
-    nvalid[u] = (live[u] && col0 < cols) ? min(8u, cols - col0) : 0u;
-    if (nvalid[u] > 0)
-      v[u].load(x + (int64_t)row[u] * ld_x + col0, nvalid[u]);
-    else
-      v[u].zero();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t col0 = grp[u] * 128u + h * 64u + lane8 * 8u;
+      nv[u][h] = (live[u] && col0 < cols) ? min(8u, cols - col0) : 0u;
+      if (nv[u][h] > 0)
+        v[u][h].load(x + (int64_t)row[u] * ld_x + col0, nv[u][h]);
+      else
+        v[u][h].zero();
+    }
   }
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
-    const uint32_t amax = row16_max(v[u].amax_bits());
+    const uint32_t a0 = v[u][0].amax_bits(), a1 = v[u][1].amax_bits();
+    const uint32_t amax = row8_max(a0 > a1 ? a0 : a1);
     const GroupScale gs = make_group_scale(amax);
-    const uint2 codes = v[u].cast(gs);
-    const uint32_t col0 = grp[u] * 128u + lane16 * 8u;
-    if (nvalid[u] > 0) store_codes8(q + (int64_t)row[u] * ld_q + col0, codes, nvalid[u]);
-    if (live[u] && lane16 == 0) sc[(int64_t)row[u] * ss_row + (int64_t)grp[u] * ss_col] = gs.s;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint2 codes = v[u][h].cast(gs);
+      const uint32_t col0 = grp[u] * 128u + h * 64u + lane8 * 8u;
+      if (nv[u][h] > 0) store_codes8(q + (int64_t)row[u] * ld_q + col0, codes, nv[u][h]);
+    }
+    if (live[u] && lane8 == 0) sc[(int64_t)row[u] * ss_row + (int64_t)grp[u] * ss_col] = gs.s;
   }
 }
 
@@ -327,7 +336,17 @@ __global__ void k_finalize_tensor_scale(float* __restrict__ acc) {
 // Host launchers (arguments already validated by the API layer).
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kGroupUnroll = 4;
+constexpr int kGroupUnroll = 2;
+
+// Multiplier and shift for fastdiv by d >= 1 (see device_common.h).
+FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  FastDiv f;
+  f.m = (uint32_t)((((1ull << l) - d) << 32) / d + 1);
+  f.l = l;
+  return f;
+}
 
 template <typename T>
 hipError_t quantize_typed(const QuantArgs& a, hipStream_t st) {
@@ -349,10 +368,11 @@ hipError_t quantize_typed(const QuantArgs& a, hipStream_t st) {
   if (a.gran == GRAN_GROUP_1x128) {
     const uint32_t ngroups = (cols + 127u) / 128u;
     const uint32_t total = rows * ngroups;
-    const uint32_t per_block = 16u * kGroupUnroll;
+    const uint32_t per_block = 32u * kGroupUnroll;
     const uint32_t grid = (total + per_block - 1) / per_block;
     hipLaunchKernelGGL((k_quant_group_1x128<T, kGroupUnroll>), dim3(grid), dim3(256), 0, st, x,
-                       a.ld_x, cols, ngroups, total, a.q, a.ld_q, a.scales, a.ss_row, a.ss_col);
+                       a.ld_x, cols, ngroups, total, make_fastdiv(ngroups), a.q, a.ld_q, a.scales,
+                       a.ss_row, a.ss_col);
     return hipGetLastError();
   }
   // 128x128 blocks

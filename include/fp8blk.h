@@ -117,7 +117,8 @@ fp8blk_status fp8_quantize(const void* x, fp8blk_dtype x_dtype, int64_t rows, in
  *           row stride ldc elements.
  *
  * Requirements: pointers non-null; M >= 0 (M == 0 is a no-op); N > 0, K > 0,
- * N % 128 == 0 and K % 128 == 0 (else FP8BLK_EUNSUPPORTED); lda, ldb >= K;
+ * N % 128 == 0 and K % 128 == 0 (else FP8BLK_EUNSUPPORTED); lda, ldb >= K and
+ * below 2^23 (else FP8BLK_EUNSUPPORTED);
  * ldc >= N; a, b, c 16-byte aligned and lda, ldb, ldc * sizeof(c_dtype)
  * multiples of 16; gran_a in {PER_TENSOR, GROUP_1x128}; gran_b in {PER_TENSOR,
  * BLOCK_128x128}; fmt_a = fmt_b = E4M3; c must not overlap the inputs.

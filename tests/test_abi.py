@@ -166,3 +166,7 @@ def test_kv_empty_is_a_noop(lib):
 ])
 def test_kv_dequantize_rejects(lib, args, status):
     assert lib.fp8_kv_dequantize(*args, None) == status
+
+
+def test_gemm_rejects_huge_leading_dimension(lib):
+    assert g(lib, lda=1 << 23) == EUNSUPPORTED

@@ -221,3 +221,18 @@ def test_repeated_calls_and_scale_buffer_reuse(gpu_lib):
     q, s = gpu_lib.fp8_quantize(b, "per_tensor", scales=s)
     assert float(s[0]) == float(np.float32(0.5) / np.float32(448))
     assert bool(torch.all(q == 0x7E))
+
+
+@pytest.mark.parametrize("ngroups", [5, 7, 13, 33, 64, 65, 127])
+def test_group_index_division(gpu_lib, ngroups):
+    """Row / group decomposition of the flat group index for many group counts
+    (the kernel divides by the group count with a multiply and shift)."""
+    rng = np.random.default_rng(ngroups)
+    rows, cols = 67, 128 * ngroups - 40
+    x = (rng.standard_normal((rows, cols)) * np.exp2(rng.uniform(-4, 4, size=(rows, 1)))).astype(np.float32)
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    x = xt.float().numpy()
+    qr, sr = quant.quantize_group_1x128(x)
+    qg, sg = gpu_lib.fp8_quantize(xt.to(DEV), "group_1x128")
+    assert_scales_equal(sg.cpu().numpy(), sr, "scales")
+    assert_codes_equal(qg.cpu().numpy(), qr, x, "codes")
