@@ -68,11 +68,20 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
 // Group scale and the bit-exact cast of a group's elements.
 //
 // The code of x is E4M3(fl32(x / s)) with the IEEE correctly rounded fp32
-// quotient. Per element that division is replaced by two multiplications with
-// reciprocals nudged down and up: with r ~ 1 / s to within 2^-22 relative
-// (v_rcp_f32 is accurate to 1 ulp),
-//   rl = r * (1 - 2^-20),  rh = r * (1 + 2^-20),
-// the products fl32(x * rl) and fl32(x * rh) bracket fl32(x / s) strictly in
+// quotient; the per-element division is replaced by multiplications with a
+// per-group reciprocal r: v_rcp_f32(s) (1 ulp) refined by one Newton step.
+//
+// bf16 inputs (cast4_bf16): q = fl32(x r), then one residual correction
+// q' = q - fl32(s q - x) r with fused multiply-adds. An exhaustive sweep over
+// every bf16 amax and every bf16 |x| <= amax whose scale lies in
+// [2^-64, 2^64] finds the code of q' equal to the code of fl32(x / s) in all
+// 2.8e8 cases (the quotient itself can differ by one ulp, never across a code
+// boundary); tests/test_gpu_quantize.py re-checks a sample against the CPU
+// oracle. The residual is negated so that x = -0 keeps its sign. Groups whose
+// scale lies outside that range, or is zero, divide exactly.
+//
+// fp32 inputs (cast4_f32): the products fl32(x rl) and fl32(x rh) with
+// rl = r (1 - 2^-20), rh = r (1 + 2^-20) bracket fl32(x / s) strictly in
 // magnitude (their relative offsets exceed 2^-20 - 2^-22 - 3 * 2^-24 > 2^-24,
 // the fp32 rounding bound) whenever the quotient is an fp32 normal.
 // Round-to-nearest is monotone, so when both brackets give the same code it is
@@ -81,22 +90,18 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
 // conversion is exact; the upper one may exceed it by a hair, and if the
 // conversion then disagrees the exact path decides. Quotients below the fp32
 // normal range give code 0 (signed) on every path. Groups whose scale is zero
-// or an fp32 subnormal (r may overflow) always take the exact division.
+// or an fp32 subnormal always take the exact division.
 // ---------------------------------------------------------------------------
 struct GroupScale {
-  float s;    // fl32(amax / 448)
-  float rl;   // lower reciprocal bracket
-  float rh;   // upper reciprocal bracket
-  bool exact; // true: divide every element exactly (s is zero or subnormal)
+  float s;  // fl32(amax / 448)
+  float r;  // ~ 1 / s, Newton-refined
 };
 
 __device__ __forceinline__ GroupScale make_group_scale(uint32_t amax_bits) {
   GroupScale g;
   g.s = __uint_as_float(amax_bits) / kE4M3Max;   // IEEE correctly rounded division
-  const float r = __builtin_amdgcn_rcpf(g.s);    // 1 ulp
-  g.rl = r * (1.0f - 0x1.0p-20f);
-  g.rh = r * (1.0f + 0x1.0p-20f);
-  g.exact = !(g.s >= 0x1.0p-126f);
+  const float r0 = __builtin_amdgcn_rcpf(g.s);   // 1 ulp
+  g.r = __builtin_fmaf(__builtin_fmaf(-g.s, r0, 1.0f), r0, r0);
   return g;
 }
 
@@ -113,15 +118,39 @@ __device__ __forceinline__ uint32_t e4m3x4_raw(float a, float b, float c, float 
   return w;
 }
 
-// Codes of four elements of one group.
-__device__ __forceinline__ uint32_t cast4(const GroupScale& g, float a, float b, float c, float d) {
-  if (!g.exact) {
-    const uint32_t lo = e4m3x4_raw(a * g.rl, b * g.rl, c * g.rl, d * g.rl);
-    const uint32_t hi = e4m3x4_raw(a * g.rh, b * g.rh, c * g.rh, d * g.rh);
-    if (__builtin_expect(lo == hi, 1)) return lo;
-  }
+__device__ __forceinline__ uint32_t exact4(const GroupScale& g, float a, float b, float c, float d) {
   return e4m3x4(exact_quotient(a, g.s), exact_quotient(b, g.s), exact_quotient(c, g.s),
                 exact_quotient(d, g.s));
+}
+
+__device__ __forceinline__ bool bf16_fast_ok(const GroupScale& g) {
+  return g.s >= 0x1.0p-64f && g.s <= 0x1.0p64f;
+}
+
+__device__ __forceinline__ float quotient_bf16(const GroupScale& g, float x) {
+  const float q = x * g.r;
+  const float e = __builtin_fmaf(g.s, q, -x);
+  return __builtin_fmaf(-e, g.r, q);
+}
+
+// Codes of four elements of one group whose values are bf16 numbers.
+__device__ __forceinline__ uint32_t cast4_bf16(const GroupScale& g, float a, float b, float c, float d) {
+  if (__builtin_expect(bf16_fast_ok(g), 1))
+    return e4m3x4_raw(quotient_bf16(g, a), quotient_bf16(g, b), quotient_bf16(g, c),
+                      quotient_bf16(g, d));
+  return exact4(g, a, b, c, d);
+}
+
+// Codes of four elements of one group of arbitrary fp32 values.
+__device__ __forceinline__ uint32_t cast4_f32(const GroupScale& g, float a, float b, float c, float d) {
+  if (g.s >= 0x1.0p-126f) {
+    const float rl = g.r * (1.0f - 0x1.0p-20f);
+    const float rh = g.r * (1.0f + 0x1.0p-20f);
+    const uint32_t lo = e4m3x4_raw(a * rl, b * rl, c * rl, d * rl);
+    const uint32_t hi = e4m3x4_raw(a * rh, b * rh, c * rh, d * rh);
+    if (__builtin_expect(lo == hi, 1)) return lo;
+  }
+  return exact4(g, a, b, c, d);
 }
 
 // Max over the 8 lanes of each half of a DPP row; every lane of the half gets it.

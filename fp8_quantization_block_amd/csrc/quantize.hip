@@ -46,8 +46,8 @@ struct Vec8<__hip_bfloat16> {
   __device__ __forceinline__ uint32_t amax_bits() const { return amax_bf16x8(w); }
   __device__ __forceinline__ uint2 cast(const GroupScale& g) const {
     uint2 r;
-    r.x = cast4(g, bf16_lo_to_f32(w.x), bf16_hi_to_f32(w.x), bf16_lo_to_f32(w.y), bf16_hi_to_f32(w.y));
-    r.y = cast4(g, bf16_lo_to_f32(w.z), bf16_hi_to_f32(w.z), bf16_lo_to_f32(w.w), bf16_hi_to_f32(w.w));
+    r.x = cast4_bf16(g, bf16_lo_to_f32(w.x), bf16_hi_to_f32(w.x), bf16_lo_to_f32(w.y), bf16_hi_to_f32(w.y));
+    r.y = cast4_bf16(g, bf16_lo_to_f32(w.z), bf16_hi_to_f32(w.z), bf16_lo_to_f32(w.w), bf16_hi_to_f32(w.w));
     return r;
   }
 };
@@ -79,8 +79,8 @@ struct Vec8<float> {
   }
   __device__ __forceinline__ uint2 cast(const GroupScale& g) const {
     uint2 r;
-    r.x = cast4(g, a.x, a.y, a.z, a.w);
-    r.y = cast4(g, b.x, b.y, b.z, b.w);
+    r.x = cast4_f32(g, a.x, a.y, a.z, a.w);
+    r.y = cast4_f32(g, b.x, b.y, b.z, b.w);
     return r;
   }
 };

@@ -122,6 +122,38 @@ def test_bf16_groups_across_the_range(gpu_lib):
     assert_codes_equal(qg.cpu().numpy(), qr, x, "codes")
 
 
+def test_bf16_every_value_below_sampled_amax(gpu_lib):
+    """For sampled bf16 amax patterns A, every bf16 pattern |x| <= A (both
+    signs, and -0) appears in a 1x128 group whose amax is A. The samples include
+    the patterns whose scale amax / 448 sits at either side of 2^-64 and 2^64
+    and the smallest and largest finite ones."""
+    rng = np.random.default_rng(211)
+    edges = []
+    for e in (-64.0, 64.0):
+        a = np.float32(np.ldexp(448.0, int(e)))
+        b = int(np.array([a], np.float32).view(np.uint32)[0] >> 16)
+        edges += [b - 2, b - 1, b, b + 1, b + 2]
+    amax_bits = np.unique(np.concatenate([
+        np.array(edges + [0x0001, 0x0002, 0x0080, 0x3F80, 0x43E0, 0x7F7F], np.int64),
+        rng.integers(0x0001, 0x7F80, size=200)]))
+    rows = []
+    for A in amax_bits:
+        mags = np.arange(A + 1, dtype=np.int64)
+        sign = (np.arange(A + 1) & 1).astype(np.int64) << 15
+        pat = np.concatenate([mags | sign, [0x8000]])
+        pad = (-len(pat)) % 127
+        pat = np.concatenate([pat, np.zeros(pad, np.int64)]).reshape(-1, 127)
+        head = np.full((pat.shape[0], 1), A, np.int64)
+        rows.append(np.concatenate([head, pat], axis=1))
+    bits = np.concatenate(rows).astype(np.uint16)
+    x = quant.bf16_bits_to_f32(bits)
+    qr, sr = quant.quantize_group_1x128(x)
+    xt = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    qg, sg = gpu_lib.fp8_quantize(xt, "group_1x128")
+    assert_scales_equal(sg.cpu().numpy(), sr, "scales")
+    assert_codes_equal(qg.cpu().numpy(), qr, x, "codes")
+
+
 def _padded(x32: np.ndarray, dtype, ld: int) -> torch.Tensor:
     rows, cols = x32.shape
     buf = torch.full((rows, ld), float("nan"), dtype=dtype)
