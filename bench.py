@@ -44,18 +44,24 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-secondary", action="store_true", help="skip the KV and decode passes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["gemm", "quant", "kv", "decode"], default=None,
-                    help="time one pass only (for profiling runs)")
+    ap.add_argument("--only", choices=["gemm", "quant", "kv", "decode", "copy"], default=None,
+                    help="time one pass only (for profiling runs); 'copy' times a plain 512 MB "
+                         "device copy, the calibration kernel for the HBM byte counters")
     return ap.parse_args()
 
 
 class Timer:
-    """HIP events on the current (launch) stream."""
+    """HIP events on the current stream, which is the stream every fp8blk call
+    is launched on (the binding passes torch's current stream)."""
 
     def __init__(self, torch):
         self.torch = torch
+        self.stats = {}
 
-    def run(self, fn, iters: int, warmup: int = 2) -> float:
+    def run(self, fn, iters: int, warmup: int = 2, name: str = None) -> float:
+        """Mean seconds per call over `iters` back-to-back calls bracketed by one
+        event pair; with `name`, a second loop with an event pair around every
+        call records median / min / p90 under self.stats[name]."""
         torch = self.torch
         for i in range(warmup):
             fn(i)
@@ -68,7 +74,49 @@ class Timer:
             fn(i)
         e1.record(st)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / iters * 1e-3   # seconds per call
+        mean = e0.elapsed_time(e1) / iters * 1e-3
+        if name is not None:
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(iters)]
+            for i, (a, b) in enumerate(ev):
+                a.record(st)
+                fn(i)
+                b.record(st)
+            torch.cuda.synchronize()
+            t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+            self.stats[name] = {"median_us": t[len(t) // 2], "min_us": t[0],
+                                "p90_us": t[min(len(t) - 1, (9 * len(t)) // 10)], "calls": len(t)}
+        return mean
+
+
+# HBM bytes per launch of the prefill GEMM kernel (M = 4096, N = 14336, K = 4096),
+# read from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) and scaled by
+# what the same counters read for a plain device copy of known size (FETCH_SIZE
+# x 2.0, WRITE_SIZE x 1.0). Valid only for the kernel source they were taken on:
+# the key is the SHA-256 of the GEMM source files; any other source gives null.
+GEMM_COUNTERS = {
+    "sources_sha256": "998e64508fb2a7fd7b607ce8b872c53297e9ecb711a061985b66bf0561c50ae4",
+    "fetch_kib": 192749.6,
+    "write_kib": 114688.0,
+}
+FETCH_FACTOR = 2.0
+WRITE_FACTOR = 1.0
+
+
+def gemm_source_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "device_common.h", "internal.h"):
+        with open(os.path.join(ROOT, "fp8_quantization_block_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def gemm_traffic_bytes():
+    c = GEMM_COUNTERS
+    if c["sources_sha256"] is None or c["sources_sha256"] != gemm_source_sha256():
+        return None
+    return (c["fetch_kib"] * FETCH_FACTOR + c["write_kib"] * WRITE_FACTOR) * 1024.0
 
 
 def main():
@@ -90,6 +138,9 @@ def main():
     timer = Timer(torch)
     c = syn.CONFIGS[2]
     M, N, K = c["M"], c["N"], c["K"]
+    if args.only == "copy":
+        copy_calibration(torch, timer, dev)
+        return
     print(f"# bench: {c['workload']} on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
 
     # ---- inputs resident in HBM -------------------------------------------
@@ -126,15 +177,15 @@ def main():
     flops = 2.0 * M * N * K
     passes = {}
     if args.only in (None, "gemm"):
-        t_gemm = timer.run(gemm, max(args.steps, 10), warmup=args.warmup)
+        t_gemm = timer.run(gemm, max(args.steps, 10), warmup=args.warmup, name="gemm")
         passes["gemm"] = {"us": t_gemm * 1e6, "TFLOP/s": flops / t_gemm / 1e12,
                           "frac_fp8_peak": flops / t_gemm / 1e12 / PEAK_FP8_TFLOPS}
     if args.only in (None, "quant"):
-        t_qa = timer.run(quant_a, max(args.steps, 22), warmup=args.warmup)
+        t_qa = timer.run(quant_a, max(args.steps, 22), warmup=args.warmup, name="act_quant_1x128")
         bytes_qa = M * K * 2 + M * K + M * (K // 128) * 4
         passes["act_quant_1x128"] = {"us": t_qa * 1e6, "GB/s": bytes_qa / t_qa / 1e9,
                                      "frac_hbm": bytes_qa / t_qa / 1e9 / PEAK_HBM_GBPS}
-        t_qw = timer.run(quant_w, 10, warmup=2)
+        t_qw = timer.run(quant_w, 10, warmup=2, name="weight_quant_128x128_offline")
         bytes_qw = N * K * 2 + N * K + (N // 128) * (K // 128) * 4
         passes["weight_quant_128x128_offline"] = {"us": t_qw * 1e6, "GB/s": bytes_qw / t_qw / 1e9,
                                                   "frac_hbm": bytes_qw / t_qw / 1e9 / PEAK_HBM_GBPS}
@@ -185,8 +236,8 @@ def main():
 
         n = 2 * H * T * D
         kv_bytes = n * 2 + n + 2 * H * (T // 128) * 4
-        t_kvq = timer.run(kvq, 20, warmup=3)
-        t_kvd = timer.run(kvd, 20, warmup=3)
+        t_kvq = timer.run(kvq, 20, warmup=3, name="kv_quant_K+V")
+        t_kvd = timer.run(kvd, 20, warmup=3, name="kv_dequant_K+V")
         passes["kv_quant_K+V"] = {"us": t_kvq * 1e6, "GB/s": kv_bytes / t_kvq / 1e9,
                                   "frac_hbm": kv_bytes / t_kvq / 1e9 / PEAK_HBM_GBPS}
         passes["kv_dequant_K+V"] = {"us": t_kvd * 1e6, "GB/s": kv_bytes / t_kvd / 1e9,
@@ -205,7 +256,7 @@ def main():
         def dec(i):
             fp8.fp8_block_gemm(qa3, sa3, "group_1x128", qw3, sw3, "block_128x128", out=o3)
 
-        t_dec = timer.run(dec, 50, warmup=5)
+        t_dec = timer.run(dec, 50, warmup=5, name="decode_gemm_16x28672x8192")
         dec_bytes = m3 * k3 + n3 * k3 + 4 * (m3 * (k3 // 128) + (n3 // 128) * (k3 // 128)) + 2 * m3 * n3
         passes["decode_gemm_16x28672x8192"] = {"us": t_dec * 1e6, "GB/s": dec_bytes / t_dec / 1e9,
                                                "frac_hbm": dec_bytes / t_dec / 1e9 / PEAK_HBM_GBPS,
@@ -240,39 +291,55 @@ def main():
             "peak": PEAK_FP8_TFLOPS,
             "unit": "TFLOP/s",
             "frac": gemm_p["TFLOP/s"] / PEAK_FP8_TFLOPS,
-            "traffic": None,
+            "traffic": gemm_traffic_bytes(),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
+            "algorithmic_bytes": float(M * K + N * K + 2 * M * N + 4 * (M * (K // 128) + (N // 128) * (K // 128))),
         },
         "passes": passes,
+        "per_call": timer.stats,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
 
 
+def copy_calibration(torch, timer, dev):
+    """A plain device-to-device copy of 512 MB (torch copy_), the reference
+    kernel for scaling the HBM byte counters, and the achievable-bandwidth
+    context for the HBM-bound passes."""
+    n = 256 * 1024 * 1024
+    x = torch.ones(n, device=dev, dtype=torch.bfloat16)
+    y = torch.empty_like(x)
+    t = timer.run(lambda i: y.copy_(x), 20, warmup=3, name="copy_512MB")
+    print(json.dumps({"copy_512MB": {"us": t * 1e6, "GB/s": 2 * 2 * n / t / 1e9,
+                                     "bytes_read": 2 * n, "bytes_written": 2 * n},
+                      "per_call": timer.stats}), flush=True)
+
+
 def cpu_baseline(syn, M, N, K):
-    """The oracle timed on a bounded sample of the step: 1x128 quantization of
-    all 4096 activation rows, then the oracle GEMM of those rows against the
-    first 3584 weight rows (a quarter of N; the weights are quantized by the
-    oracle beforehand, untimed, as the offline pass)."""
-    import numpy as np
+    """The oracle timed on the whole step at full size: 1x128 quantization of
+    the [4096, 4096] activations, then the oracle GEMM 4096 x 14336 x 4096
+    (dequantize to fp64 and one fp64 matmul, plus the tolerance base). The
+    weights are quantized by the oracle beforehand, untimed, as the offline
+    pass."""
     import threadpoolctl
     from oracle import quant, gemm
 
-    ms, ns = 4096, 3584
-    a = syn.activations(2)[:ms].float().numpy()
-    w = syn.weights(2)[:ns].float().numpy()
+    a = syn.activations(2).float().numpy()
+    w = syn.weights(2).float().numpy()
     qw, sw = quant.quantize_block_128x128(w)
+    del w
     t0 = time.perf_counter()
     qa, sa = quant.quantize_group_1x128(a)
     gemm.block_gemm(qa, sa, "group_1x128", qw, sw, "block_128x128")
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
     return {
-        "value": 2.0 * ms * ns * K / dt / 1e12,
+        "value": 2.0 * M * N * K / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"act quantize {ms}x{K} (1x128) + oracle GEMM {ms}x{ns}x{K} (fp64 dequant-matmul, y and T); "
-                  f"{dt:.2f} s; host os.cpu_count()={os.cpu_count()}",
+        "sample": f"the whole step: act quantize {M}x{K} (1x128) + oracle GEMM {M}x{N}x{K} "
+                  f"(fp64 dequant-matmul, y and T); {dt:.2f} s; host os.cpu_count()={os.cpu_count()}",
     }
 
 
