@@ -22,6 +22,9 @@ FLAGS = [
     "-shared",
     # packed fp32 VALU ops are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the GEMM promotes every partial product with VALU
+    # FMAs, which cannot read AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"),

@@ -8,21 +8,26 @@
 // multiplied by their scales); [MIXED] charles2530.github.io, "量化：FP8 与混合精度推理",
 // section "混合精度才是生产形态" (low-precision products, higher-precision sums).
 //
-// Design (gfx950):
+// Prefill kernel design (gfx950):
 // * One v_mfma_f32_16x16x128_f8f6f4 covers exactly one 128-deep scale block,
 //   so every MFMA starts from zero and its 16x16 fp32 result is promoted into
 //   the fp32 accumulator with one FMA per element: acc += P_j * s_a * s_b.
-// * Workgroup tile 256 x 256, K step 128; 8 waves in a 4 x 2 grid, each wave
-//   owning 64 rows x 128 columns (so a wave's columns are exactly one weight
-//   scale block and s_b is one scalar per K block).
-// * A and B tiles (and the K block's 256 activation scales and 2 weight-block
-//   scales) are double buffered in LDS, one barrier per K block. The next
-//   block's tiles travel through 16 registers per thread in two halves: the A
-//   tile is loaded while the first half of the block's MFMAs run and written
-//   to LDS after them, then the B tile the same way around the second half.
-//   (Direct global-to-LDS copies did not overlap with the MFMA work on this
-//   chip; the register route does.) Rows are stored with their eight 16-byte
-//   chunks XOR-swizzled so the MFMA operand reads are conflict free.
+// * Workgroup tile 256 x 256 (the largest whose fp32 accumulators fit the
+//   register file next to the operands: 256 KB per CU), K step 128; 8 waves in
+//   a 4 x 2 grid, each owning 64 rows x 128 columns (one weight scale block,
+//   so s_b is one scalar per wave and K block).
+// * Both operand tiles (32 KB each) and the K block's scales go global -> LDS
+//   by direct copies (no staging registers), double buffered: the copies of
+//   block kb + 1 are issued at the start of block kb and waited for at its
+//   end, one barrier per block.
+// * The 32 products of a wave's K block are software pipelined: the MFMA of
+//   product t is issued before the promotion FMAs of product t - 2, so the
+//   FMAs run under the matrix unit's work.
+// * Fragment K order: lane group q = lane / 16 holds K bytes [16q, 16q + 16)
+//   and [64 + 16q, 64 + 16q + 16) of the block for both operands, so the MFMA
+//   sums exactly the block's 128 products.
+// * LDS rows hold eight 16-byte chunks, logical chunk c of row r at physical
+//   chunk c ^ swz(r), so the operand reads are free of bank conflicts.
 // * Workgroup ids are remapped so that neighbouring tiles (which share A rows
 //   or B columns) run on the same XCD and share its L2.
 #include <hip/hip_bf16.h>
@@ -34,6 +39,7 @@ namespace fp8blk {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 namespace {
 
@@ -41,7 +47,8 @@ constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 128;
 constexpr int kThreads = 512;
-constexpr int kTileBytes = BM * BK;                 // one operand tile, 32 KB
+constexpr int kTileBytes = BM * BK;    // one operand tile, 32 KB
+constexpr int kScaleSlots = BM + 64;   // 256 activation scales, then 64 weight-scale slots
 
 struct GemmParams {
   const uint8_t* a;
@@ -55,157 +62,173 @@ struct GemmParams {
   int tiles_m, tiles_n;
 };
 
-// A 128-byte operand row holds eight 16-byte chunks; logical chunk c of row r
-// is stored at physical chunk c ^ swz(r). Any 16 consecutive rows then hit 16
-// distinct (row parity, chunk) pairs and any 8 consecutive rows 8 distinct
-// chunks, so the fragment reads (16 rows, same logical chunk) and the tile
-// writes (8 lanes per row) are free of bank conflicts whether the LDS serves
-// 8 or 16 lanes of a 128-bit access per cycle.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-// Buffer resource over `bytes` bytes from `base` (raw, untyped loads; reads
-// at or past `bytes` return zero).
+// Buffer resource over `bytes` bytes from `base` (raw loads; reads at or past
+// `bytes` return zero).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+// Direct global -> LDS copy through a buffer resource: lane l writes `size`
+// bytes at lds + size * l (lds must be wave-uniform); reads past the
+// resource's end write zeros.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
 }
 
-// Operand fragment of one 16-row (or 16-column) subtile: lane l takes row
-// base + l % 16 and the 32 bytes at K offset 32 * (l / 16). A and B use the
-// same K assignment, so the MFMA sums exactly the 128 products of the block.
-__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int lane) {
-  const int lc0 = (lane >> 4) * 2;
-  const int sw = swz(row);
-  const uint4 lo = *reinterpret_cast<const uint4*>(tile + row * 128 + ((lc0 ^ sw) << 4));
-  const uint4 hi = *reinterpret_cast<const uint4*>(tile + row * 128 + (((lc0 + 1) ^ sw) << 4));
+__device__ __forceinline__ v8i pack_frag(uint4 lo, uint4 hi) {
   v8i f;
   f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
   f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
   return f;
 }
 
-// Multiply the four 16-column subtiles ni0 .. ni0 + 3 of this wave against
-// its four 16-row A fragments and promote every 16 x 16 partial into acc.
-template <int ni0>
-__device__ __forceinline__ void mma_half(const uint8_t* tb, int wn, int lane, const v8i (&af)[4],
-                                         const v4f (&comb)[4], v4f (&acc)[4][8]) {
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ni = ni0; ni < ni0 + 4; ++ni) {
-    const v8i bf = read_frag(tb, wn * 128 + ni * 16 + (lane & 15), lane);
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf, zero, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[mi][ni][v] = __builtin_fmaf(part[v], comb[mi][v], acc[mi][ni][v]);
-    }
-  }
+// Fragment of a 16-row subtile from an LDS tile: lane l takes the row at
+// byte offset `row_off` (subtile base + l % 16, precomputed with its
+// swizzled chunk offsets lo/hi for chunks q and 4 + q, q = l / 16).
+__device__ __forceinline__ v8i read_frag(const uint8_t* tile, uint32_t lo_off, uint32_t hi_off) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(tile + lo_off);
+  const uint4 hi = *reinterpret_cast<const uint4*>(tile + hi_off);
+  return pack_frag(lo, hi);
 }
 
-// One K block's operands in flight in registers: thread t holds chunks
-// c = t + 512 i (i = 0..3) of the A and the B tile (row c / 8, logical chunk
-// c % 8), and one scale (an activation scale for t < 256, a weight-block
-// scale for t = 256, 257).
-struct Regs {
-  uint4 a[4];
-  uint4 b[4];
-  float s;
-};
-
-// Per-thread copy plan. Global offsets are relative to the tile's first row
-// (so they fit 32 bits: 256 * ld < 2^31 is checked on the host); rows past the
-// operand's end fall outside the buffer resource and read as zero. The four
-// LDS destinations of a thread are 64 rows apart, which keeps the same swizzle,
-// so one offset plus immediates addresses them.
-struct Copier {
-  __amdgpu_buffer_rsrc_t ra, rb;
-  uint32_t goa[4], gob[4];
-  uint32_t loff;      // LDS byte offset of chunk 0; chunk i adds 8192 * i
-  const float* sp;    // this thread's scale for K block 0 (threads 0..257)
-  int64_t s_kstep;    // element step of that scale per K block
-  int tid;
-};
-
-__device__ __forceinline__ void load_a(const Copier& c, int kb, Regs& r) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r.a[i] = buf_load16(c.ra, c.goa[i], (uint32_t)kb * BK);
-}
-__device__ __forceinline__ void load_b(const Copier& c, int kb, Regs& r) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r.b[i] = buf_load16(c.rb, c.gob[i], (uint32_t)kb * BK);
-  r.s = c.tid < 258 ? c.sp[(int64_t)kb * c.s_kstep] : 0.f;
-}
-__device__ __forceinline__ void store_a(const Copier& c, const Regs& r, uint8_t* ta) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(ta + c.loff + 8192 * i) = r.a[i];
-}
-__device__ __forceinline__ void store_b(const Copier& c, const Regs& r, uint8_t* tb, float* ts) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(tb + c.loff + 8192 * i) = r.b[i];
-  if (c.tid < 258) ts[c.tid] = r.s;
+// s_waitcnt with vmcnt(n) only (expcnt and lgkmcnt left at their maxima).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(((n >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (n & 15));
 }
 
-// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt left at their maxima).
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-// Workgroup barrier that waits for this wave's LDS writes but not for its
-// global loads in flight; the empty asm statements keep the compiler from
-// moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  wait_lds();
+// Workgroup barrier; the empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void raw_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// One K block. On entry `r` holds block kb + 1 (loaded during the previous
-// block) and stage nxt_* is free. The A half of r goes to LDS and is reloaded
-// with block kb + 2, the first half of block kb's MFMAs runs, then the B half
-// and the scales move the same way before the second half of the MFMAs. The
-// LDS writes thus arrive as two 32 KB bursts between fragment reads, and every
-// load has a whole block of work to arrive. Block indices are clamped to the
-// last block (the tail re-copies it into a stage nobody reads again), so every
-// step has the same shape.
-__device__ __forceinline__ void block_step(const Copier& cp, Regs& r, int kb, int nk, int wm,
-                                           int wn, int lane, bool active, const uint8_t* cur_a,
-                                           const uint8_t* cur_b, const float* cur_s,
-                                           uint8_t* nxt_a, uint8_t* nxt_b, float* nxt_s,
-                                           v4f (&acc)[4][8]) {
-  const int kl = min(kb + 2, nk - 1);
-  v8i af[4];
-  v4f comb[4];
-  if (active) {
-    const float sbv = cur_s[256 + wn];
+// Per-thread copy and read plan.
+// * Operand tiles, K block kb, into an LDS stage: wave w fills rows 32 w ..
+//   32 w + 31 of each tile, 8 rows (1 KB) per instruction; lane l fills
+//   physical chunk l % 8 of row 8 (4 w + i) + l / 8, i.e. logical chunk
+//   (l % 8) ^ swz(row). Activation rows past M read as zero.
+// * Scales of K block kb: lane l of wave w < 4 copies the activation scale of
+//   tile row 64 w + l (rows past M re-read row M - 1; their results are never
+//   stored) into slot 64 w + l; lane l of wave 4 copies the weight-block scale
+//   of the tile's 128-column half l % 2 into slot 256 + l; waves 5..7 copy the
+//   same into a sink (so that every wave issues the same instructions).
+struct Plan {
+  uint32_t a_voff[4];   // byte offset of this lane's activation chunk, per copy instruction (block 0)
+  uint32_t b_voff[4];   // byte offset of this lane's weight chunk, per copy instruction (block 0)
+  uint32_t s_voff;      // byte offset of this lane's scale (block 0)
+  uint32_t s_kstep;     // bytes between consecutive K blocks' scales
+  uint32_t a_lo, a_hi;  // this lane's activation fragment chunks (subtile 0 of its slab)
+  uint32_t b_lo, b_hi;  // this lane's weight fragment chunks (subtile 0 of its slab)
+  uint32_t s_rd;        // this lane's four activation scales (subtile 0)
+  uint32_t w_rd;        // the wave's weight-block scale slot
+  int wave;
+};
+
+// Copies of K block kb into one stage: 4 + 4 + 1 vector memory instructions.
+__device__ __forceinline__ void issue(const Plan& pl, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                      __amdgpu_buffer_rsrc_t rs, int kb, uint8_t* ta, uint8_t* tb,
+                                      float* ts, float* sink) {
+  const uint32_t soff = (uint32_t)kb * BK;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      af[mi] = read_frag(cur_a, wm * 64 + mi * 16 + (lane & 15), lane);
-      const v4f s4 = *reinterpret_cast<const v4f*>(cur_s + wm * 64 + mi * 16 + 4 * (lane >> 4));
-      comb[mi] = s4 * sbv;
-    }
+  for (int i = 0; i < 4; ++i) {
+    dma16(ra, pl.a_voff[i], soff, ta + (pl.wave * 4 + i) * 1024);
+    dma16(rb, pl.b_voff[i], soff, tb + (pl.wave * 4 + i) * 1024);
   }
-  store_a(cp, r, nxt_a);
-  load_a(cp, kl, r);
-  __builtin_amdgcn_sched_barrier(0);
-  if (active) mma_half<0>(cur_b, wn, lane, af, comb, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  store_b(cp, r, nxt_b, nxt_s);
-  load_b(cp, kl, r);
-  __builtin_amdgcn_sched_barrier(0);
-  if (active) mma_half<4>(cur_b, wn, lane, af, comb, acc);
-  lds_barrier();
+  float* sdst = pl.wave <= 4 ? ts + pl.wave * 64 : sink;
+  dma4(rs, pl.s_voff, (uint32_t)kb * pl.s_kstep, sdst);
+}
+
+// One K block of a wave: 4 activation subtiles x 8 weight subtiles.
+// Software pipeline over the 32 products t = (ni, mi) = (t / 4, t % 4): step
+// t issues the MFMA of product t into one of three rotating partial registers
+// and promotes product t - 2; the weight fragment of subtile ni + 1 is read
+// while subtile ni is in use.
+__device__ __forceinline__ void mma_block(const Plan& pl, const uint8_t* ta, const uint8_t* tb,
+                                          const float* ts, v4f (&acc)[4][8]) {
+  v8i af[4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) af[mi] = read_frag(ta, pl.a_lo + mi * 2048, pl.a_hi + mi * 2048);
+  const float sw = ts[pl.w_rd];
+  v4f comb[4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) comb[mi] = *reinterpret_cast<const v4f*>(ts + pl.s_rd + mi * 16) * sw;
+  v8i bf[2];
+  bf[0] = read_frag(tb, pl.b_lo, pl.b_hi);
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  v4f part[3];
+#pragma unroll
+  for (int t = 0; t < 34; ++t) {
+    const int ni = t >> 2, mi = t & 3;
+    if (t < 32 && mi == 0 && ni < 7)
+      bf[(ni + 1) & 1] = read_frag(tb, pl.b_lo + (ni + 1) * 2048, pl.b_hi + (ni + 1) * 2048);
+    if (t < 32)
+      part[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf[ni & 1], zero, 0, 0, 0, 0, 0, 0);
+    if (t >= 2) {
+      const int u = t - 2;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        acc[u & 3][u >> 2][v] = __builtin_fmaf(part[u % 3][v], comb[u & 3][v], acc[u & 3][u >> 2][v]);
+    }
+    if (t < 32 && mi == 0 && ni < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // fragment reads
+    if (t < 32) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // the MFMA
+    if (t >= 2) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                      // four FMAs
+  }
+}
+
+// One K block kb: copy block kb + 1 into the other stage, multiply block kb,
+// wait for the copies (the only vector memory operations in flight), barrier.
+// The block index of the copy is clamped to the last block (the tail copy
+// lands in a stage nobody reads again).
+__device__ __forceinline__ void k_step(const Plan& pl, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                       __amdgpu_buffer_rsrc_t rs, int kb, int nk, const uint8_t* ca,
+                                       const uint8_t* cb, const float* cs, uint8_t* na, uint8_t* nb,
+                                       float* ns, float* sink, bool active, v4f (&acc)[4][8]) {
+  issue(pl, ra, rb, rs, min(kb + 1, nk - 1), na, nb, ns, sink);
+  if (active) mma_block(pl, ca, cb, cs, acc);
+  wait_vm<0>();
+  raw_barrier();
+}
+
+// The K loop over the two stages. Every pointer the copies touch (both
+// stages' tiles and scale slots, the sink, and the arrays they read) is a
+// distinct non-aliasing parameter, so that the compiler can tell that reading
+// one stage does not depend on the copies in flight into the other.
+__device__ __forceinline__ void k_loop(const Plan& pl, const uint8_t* __restrict__ ga, uint32_t ga_bytes,
+                                       const uint8_t* __restrict__ gb, uint32_t gb_bytes,
+                                       const float* __restrict__ gs, uint32_t gs_bytes,
+                                       uint8_t* __restrict__ a0, uint8_t* __restrict__ a1,
+                                       uint8_t* __restrict__ b0, uint8_t* __restrict__ b1,
+                                       float* __restrict__ s0, float* __restrict__ s1,
+                                       float* __restrict__ sink, int nk, bool active, v4f (&acc)[4][8]) {
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(ga, ga_bytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(gb, gb_bytes);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(gs, gs_bytes);
+  issue(pl, ra, rb, rs, 0, a0, b0, s0, sink);
+  wait_vm<0>();
+  raw_barrier();
+  int kb = 0;
+  for (; kb + 1 < nk; kb += 2) {
+    k_step(pl, ra, rb, rs, kb, nk, a0, b0, s0, a1, b1, s1, sink, active, acc);
+    k_step(pl, ra, rb, rs, kb + 1, nk, a1, b1, s1, a0, b0, s0, sink, active, acc);
+  }
+  if (kb < nk) k_step(pl, ra, rb, rs, kb, nk, a0, b0, s0, a1, b1, s1, sink, active, acc);
 }
 
 template <bool kBf16Out>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t a0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t b0[kTileBytes];
-  __shared__ __attribute__((aligned(16))) float s0[BM + 4];
-  __shared__ __attribute__((aligned(1024))) uint8_t a1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t b1[kTileBytes];
-  __shared__ __attribute__((aligned(16))) float s1[BM + 4];
+  __shared__ __attribute__((aligned(1024))) uint8_t ta[2][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t tb[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) float ts[2][kScaleSlots];
+  __shared__ float sink[64];
 
   // ---- tile assignment: XCD-major remap, then grouped row-major order ----
   const int nwg = p.tiles_m * p.tiles_n;
@@ -225,29 +248,46 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
   const int wm = wave >> 1;          // 0..3 : 64-row slab
   const int wn = wave & 1;           // 0..1 : 128-column slab
   const bool active = (n0 + wn * 128) < p.N;
-
-  Copier cp;
-  cp.tid = tid;
+  const int nk = p.K / BK;
   const int rows_a = min(p.M - m0, BM), rows_b = min(p.N - n0, BN);
-  cp.ra = make_rsrc(p.a + (int64_t)m0 * p.lda, (uint32_t)(rows_a * p.lda));
-  cp.rb = make_rsrc(p.b + (int64_t)n0 * p.ldb, (uint32_t)(rows_b * p.ldb));
+
+  Plan pl;
+  pl.wave = wave;
   {
-    const int row = tid >> 3, lc = tid & 7;
+    const int sub_row = lane >> 3, pchunk = lane & 7;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      cp.goa[i] = (uint32_t)((row + 64 * i) * (int)p.lda + lc * 16);
-      cp.gob[i] = (uint32_t)((row + 64 * i) * (int)p.ldb + lc * 16);
+      const int row = (wave * 4 + i) * 8 + sub_row;
+      const int chunk = (pchunk ^ swz(row)) << 4;
+      pl.a_voff[i] = (uint32_t)(row * (int)p.lda + chunk);
+      pl.b_voff[i] = (uint32_t)(row * (int)p.ldb + chunk);
     }
-    cp.loff = (uint32_t)(row * 128 + ((lc ^ swz(row)) << 4));
+    const int rrow = lane & 15, q = lane >> 4;
+    const uint32_t lo = (uint32_t)(rrow * 128 + ((q ^ swz(rrow)) << 4));
+    const uint32_t hi = (uint32_t)(rrow * 128 + (((4 + q) ^ swz(rrow)) << 4));
+    pl.a_lo = lo + wm * 64 * 128;
+    pl.a_hi = hi + wm * 64 * 128;
+    pl.b_lo = lo + wn * 128 * 128;
+    pl.b_hi = hi + wn * 128 * 128;
+    pl.s_rd = (uint32_t)(wm * 64 + 4 * q);
+    pl.w_rd = (uint32_t)(BM + wn);
   }
-  // scales: threads 0..255 copy the activation scale of tile row tid, threads
-  // 256 and 257 the weight-block scales of the tile's two 128-column halves
-  if (tid < 256) {
-    cp.sp = p.sa + (int64_t)min(m0 + tid, p.M - 1) * p.sa_m;
-    cp.s_kstep = p.sa_k;
+  // scale copy plan: waves 0..3 activation scales, waves 4..7 weight-block scales
+  const float* gs;
+  uint32_t gs_bytes;
+  if (wave < 4) {
+    const int64_t s_last = (int64_t)(p.M - 1) * p.sa_m + (int64_t)(nk - 1) * p.sa_k;
+    gs = p.sa;
+    gs_bytes = (uint32_t)((s_last + 1) * 4);
+    pl.s_voff = (uint32_t)((int64_t)min(m0 + wave * 64 + lane, p.M - 1) * p.sa_m * 4);
+    pl.s_kstep = (uint32_t)(p.sa_k * 4);
   } else {
-    cp.sp = p.sb + (int64_t)min((n0 >> 7) + (tid - 256), (p.N >> 7) - 1) * p.sb_n;
-    cp.s_kstep = p.sb_k;
+    const int nblk = p.N >> 7;
+    const int64_t s_last = (int64_t)(nblk - 1) * p.sb_n + (int64_t)(nk - 1) * p.sb_k;
+    gs = p.sb;
+    gs_bytes = (uint32_t)((s_last + 1) * 4);
+    pl.s_voff = (uint32_t)((int64_t)min((n0 >> 7) + (lane & 1), nblk - 1) * p.sb_n * 4);
+    pl.s_kstep = (uint32_t)(p.sb_k * 4);
   }
 
   v4f acc[4][8];
@@ -256,21 +296,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
 #pragma unroll
     for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = p.K / BK;
-  Regs r;
-  load_a(cp, 0, r);
-  load_b(cp, 0, r);
-  store_a(cp, r, a0);
-  store_b(cp, r, b0, s0);
-  load_a(cp, min(1, nk - 1), r);
-  load_b(cp, min(1, nk - 1), r);
-  lds_barrier();
-
-  for (int kb = 0; kb < nk; kb += 2) {
-    block_step(cp, r, kb, nk, wm, wn, lane, active, a0, b0, s0, a1, b1, s1, acc);
-    if (kb + 1 < nk) block_step(cp, r, kb + 1, nk, wm, wn, lane, active, a1, b1, s1, a0, b0, s0, acc);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no load outstanding past the loop
+  k_loop(pl, p.a + (int64_t)m0 * p.lda, (uint32_t)(rows_a * (int)p.lda), p.b + (int64_t)n0 * p.ldb,
+         (uint32_t)(rows_b * (int)p.ldb), gs, gs_bytes, ta[0], ta[1], tb[0], tb[1], ts[0], ts[1], sink, nk,
+         active, acc);
 
   if (!active) return;
   // ---- epilogue: lane holds rows 4 * (lane / 16) + v, column lane % 16 ----
