@@ -122,8 +122,8 @@ __device__ __forceinline__ void raw_barrier() {
 //   of the tile's 128-column half l % 2 into slot 256 + l; waves 5..7 copy the
 //   same into a sink (so that every wave issues the same instructions).
 struct Plan {
-  uint32_t a_voff[4];   // byte offset of this lane's activation chunk, per copy instruction (block 0)
-  uint32_t b_voff[4];   // byte offset of this lane's weight chunk, per copy instruction (block 0)
+  uint32_t a_voff[2], b_voff[2];   // byte offset of this lane's chunk in copy instructions 0 and 1 (block 0)
+  uint32_t a_istep, b_istep;       // bytes between copy instructions i and i + 2 (16 rows)
   uint32_t s_voff;      // byte offset of this lane's scale (block 0)
   uint32_t s_kstep;     // bytes between consecutive K blocks' scales
   uint32_t a_lo, a_hi;  // this lane's activation fragment chunks (subtile 0 of its slab)
@@ -140,8 +140,8 @@ __device__ __forceinline__ void issue(const Plan& pl, __amdgpu_buffer_rsrc_t ra,
   const uint32_t soff = (uint32_t)kb * BK;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    dma16(ra, pl.a_voff[i], soff, ta + (pl.wave * 4 + i) * 1024);
-    dma16(rb, pl.b_voff[i], soff, tb + (pl.wave * 4 + i) * 1024);
+    dma16(ra, pl.a_voff[i & 1], soff + (uint32_t)(i >> 1) * pl.a_istep, ta + (pl.wave * 4 + i) * 1024);
+    dma16(rb, pl.b_voff[i & 1], soff + (uint32_t)(i >> 1) * pl.b_istep, tb + (pl.wave * 4 + i) * 1024);
   }
   float* sdst = pl.wave <= 4 ? ts + pl.wave * 64 : sink;
   dma4(rs, pl.s_voff, (uint32_t)kb * pl.s_kstep, sdst);
@@ -149,9 +149,11 @@ __device__ __forceinline__ void issue(const Plan& pl, __amdgpu_buffer_rsrc_t ra,
 
 // One K block of a wave: 4 activation subtiles x 8 weight subtiles.
 // Software pipeline over the 32 products t = (ni, mi) = (t / 4, t % 4): step
-// t issues the MFMA of product t into one of three rotating partial registers
-// and promotes product t - 2; the weight fragment of subtile ni + 1 is read
-// while subtile ni is in use.
+// t issues the MFMA of product t into one of kLag + 1 rotating partial
+// registers and promotes product t - kLag, so the promotion FMAs of a product
+// run kLag MFMAs after it was issued, with no wait on its result; the weight
+// fragment of subtile ni + 1 is read while subtile ni is in use.
+constexpr int kLag = 5;
 __device__ __forceinline__ void mma_block(const Plan& pl, const uint8_t* ta, const uint8_t* tb,
                                           const float* ts, v4f (&acc)[4][8]) {
   v8i af[4];
@@ -164,23 +166,23 @@ __device__ __forceinline__ void mma_block(const Plan& pl, const uint8_t* ta, con
   v8i bf[2];
   bf[0] = read_frag(tb, pl.b_lo, pl.b_hi);
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  v4f part[3];
+  v4f part[kLag + 1];
 #pragma unroll
-  for (int t = 0; t < 34; ++t) {
+  for (int t = 0; t < 32 + kLag; ++t) {
     const int ni = t >> 2, mi = t & 3;
     if (t < 32 && mi == 0 && ni < 7)
       bf[(ni + 1) & 1] = read_frag(tb, pl.b_lo + (ni + 1) * 2048, pl.b_hi + (ni + 1) * 2048);
     if (t < 32)
-      part[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf[ni & 1], zero, 0, 0, 0, 0, 0, 0);
-    if (t >= 2) {
-      const int u = t - 2;
+      part[t % (kLag + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf[ni & 1], zero, 0, 0, 0, 0, 0, 0);
+    if (t >= kLag) {
+      const int u = t - kLag;
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        acc[u & 3][u >> 2][v] = __builtin_fmaf(part[u % 3][v], comb[u & 3][v], acc[u & 3][u >> 2][v]);
+        acc[u & 3][u >> 2][v] = __builtin_fmaf(part[u % (kLag + 1)][v], comb[u & 3][v], acc[u & 3][u >> 2][v]);
     }
-    if (t < 32 && mi == 0 && ni < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // fragment reads
-    if (t < 32) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // the MFMA
-    if (t >= 2) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                      // four FMAs
+    // keep the program order: the scheduler would otherwise pair FMAs with the
+    // MFMA that produces their operand and stall on it
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -254,14 +256,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
   Plan pl;
   pl.wave = wave;
   {
+    // rows 8 (4 w + i) + l / 8 of copy instruction i: swz(row) = (l / 8) ^ (i & 1),
+    // so instructions i and i + 2 share the chunk pattern and are 16 rows apart
     const int sub_row = lane >> 3, pchunk = lane & 7;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const int row = (wave * 4 + i) * 8 + sub_row;
       const int chunk = (pchunk ^ swz(row)) << 4;
       pl.a_voff[i] = (uint32_t)(row * (int)p.lda + chunk);
       pl.b_voff[i] = (uint32_t)(row * (int)p.ldb + chunk);
     }
+    pl.a_istep = (uint32_t)(16 * p.lda);
+    pl.b_istep = (uint32_t)(16 * p.ldb);
     const int rrow = lane & 15, q = lane >> 4;
     const uint32_t lo = (uint32_t)(rrow * 128 + ((q ^ swz(rrow)) << 4));
     const uint32_t hi = (uint32_t)(rrow * 128 + (((4 + q) ^ swz(rrow)) << 4));
