@@ -147,38 +147,60 @@ __device__ __forceinline__ void issue(const Plan& pl, __amdgpu_buffer_rsrc_t ra,
   dma4(rs, pl.s_voff, (uint32_t)kb * pl.s_kstep, sdst);
 }
 
-// One K block of a wave: 4 activation subtiles x 8 weight subtiles.
-// Software pipeline over the 32 products t = (ni, mi) = (t / 4, t % 4): step
-// t issues the MFMA of product t into one of kLag + 1 rotating partial
-// registers and promotes product t - kLag, so the promotion FMAs of a product
-// run kLag MFMAs after it was issued, with no wait on its result; the weight
-// fragment of subtile ni + 1 is read while subtile ni is in use.
+// The MFMA / promotion pipeline of a wave, continuous across K blocks.
+// Products are numbered t = 0..31 per block, (ni, mi) = (t / 4, t % 4). Step t
+// issues the MFMA of product t into partial register t % kRing and promotes
+// the product issued kLag steps earlier (for t < kLag the last products of the
+// previous block, with that block's scales), so a promotion never waits for
+// its MFMA and the matrix unit keeps running across the block boundary, while
+// the first LDS reads of the new block are in flight.
 constexpr int kLag = 5;
+constexpr int kRing = 8;   // > kLag and a divisor of 32: ring slots are the same in every block
+
+struct Pipe {
+  v4f part[kRing];
+  v4f comb[4];   // scales of the block whose products are being promoted
+};
+
+__device__ __forceinline__ void promote(const Pipe& pp, const v4f (&comb)[4], int u, v4f (&acc)[4][8]) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+    acc[u & 3][u >> 2][v] = __builtin_fmaf(pp.part[u % kRing][v], comb[u & 3][v], acc[u & 3][u >> 2][v]);
+}
+
+// One K block of a wave: 4 activation subtiles x 8 weight subtiles. `first`:
+// no previous block to finish.
+template <bool first>
 __device__ __forceinline__ void mma_block(const Plan& pl, const uint8_t* ta, const uint8_t* tb,
-                                          const float* ts, v4f (&acc)[4][8]) {
-  v8i af[4];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) af[mi] = read_frag(ta, pl.a_lo + mi * 2048, pl.a_hi + mi * 2048);
-  const float sw = ts[pl.w_rd];
-  v4f comb[4];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) comb[mi] = *reinterpret_cast<const v4f*>(ts + pl.s_rd + mi * 16) * sw;
-  v8i bf[2];
+                                          const float* ts, Pipe& pp, v4f (&acc)[4][8]) {
+  // reads for the first MFMA first, then the rest of the activation fragments
+  // and the scales; the weight fragment of subtile ni + 1 is read while
+  // subtile ni is in use
+  v8i af[4], bf[2];
+  af[0] = read_frag(ta, pl.a_lo, pl.a_hi);
   bf[0] = read_frag(tb, pl.b_lo, pl.b_hi);
+#pragma unroll
+  for (int mi = 1; mi < 4; ++mi) af[mi] = read_frag(ta, pl.a_lo + mi * 2048, pl.a_hi + mi * 2048);
+  v4f s4[4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) s4[mi] = *reinterpret_cast<const v4f*>(ts + pl.s_rd + mi * 16);
+  const float sw = ts[pl.w_rd];
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  v4f part[kLag + 1];
 #pragma unroll
-  for (int t = 0; t < 32 + kLag; ++t) {
+  for (int t = 0; t < 32; ++t) {
     const int ni = t >> 2, mi = t & 3;
-    if (t < 32 && mi == 0 && ni < 7)
+    if (mi == 0 && ni < 7)
       bf[(ni + 1) & 1] = read_frag(tb, pl.b_lo + (ni + 1) * 2048, pl.b_hi + (ni + 1) * 2048);
-    if (t < 32)
-      part[t % (kLag + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf[ni & 1], zero, 0, 0, 0, 0, 0, 0);
+    pp.part[t % kRing] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf[ni & 1], zero, 0, 0, 0, 0, 0, 0);
     if (t >= kLag) {
-      const int u = t - kLag;
+      promote(pp, pp.comb, t - kLag, acc);
+    } else if (!first) {
+      promote(pp, pp.comb, t - kLag + 32, acc);   // previous block's product, its scales
+    }
+    if (t == kLag - 1) {
+      // from here on the promotions belong to this block
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        acc[u & 3][u >> 2][v] = __builtin_fmaf(part[u % (kLag + 1)][v], comb[u & 3][v], acc[u & 3][u >> 2][v]);
+      for (int m = 0; m < 4; ++m) pp.comb[m] = s4[m] * sw;
     }
     // keep the program order: the scheduler would otherwise pair FMAs with the
     // MFMA that produces their operand and stall on it
@@ -186,16 +208,23 @@ __device__ __forceinline__ void mma_block(const Plan& pl, const uint8_t* ta, con
   }
 }
 
+// Promotions of the last block's final kLag products.
+__device__ __forceinline__ void drain(const Pipe& pp, v4f (&acc)[4][8]) {
+#pragma unroll
+  for (int u = 32 - kLag; u < 32; ++u) promote(pp, pp.comb, u, acc);
+}
+
 // One K block kb: copy block kb + 1 into the other stage, multiply block kb,
 // wait for the copies (the only vector memory operations in flight), barrier.
 // The block index of the copy is clamped to the last block (the tail copy
 // lands in a stage nobody reads again).
+template <bool first>
 __device__ __forceinline__ void k_step(const Plan& pl, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                        __amdgpu_buffer_rsrc_t rs, int kb, int nk, const uint8_t* ca,
                                        const uint8_t* cb, const float* cs, uint8_t* na, uint8_t* nb,
-                                       float* ns, float* sink, bool active, v4f (&acc)[4][8]) {
+                                       float* ns, float* sink, bool active, Pipe& pp, v4f (&acc)[4][8]) {
   issue(pl, ra, rb, rs, min(kb + 1, nk - 1), na, nb, ns, sink);
-  if (active) mma_block(pl, ca, cb, cs, acc);
+  if (active) mma_block<first>(pl, ca, cb, cs, pp, acc);
   wait_vm<0>();
   raw_barrier();
 }
@@ -214,15 +243,18 @@ __device__ __forceinline__ void k_loop(const Plan& pl, const uint8_t* __restrict
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(ga, ga_bytes);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(gb, gb_bytes);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(gs, gs_bytes);
+  Pipe pp;
   issue(pl, ra, rb, rs, 0, a0, b0, s0, sink);
   wait_vm<0>();
   raw_barrier();
-  int kb = 0;
+  k_step<true>(pl, ra, rb, rs, 0, nk, a0, b0, s0, a1, b1, s1, sink, active, pp, acc);
+  int kb = 1;
   for (; kb + 1 < nk; kb += 2) {
-    k_step(pl, ra, rb, rs, kb, nk, a0, b0, s0, a1, b1, s1, sink, active, acc);
-    k_step(pl, ra, rb, rs, kb + 1, nk, a1, b1, s1, a0, b0, s0, sink, active, acc);
+    k_step<false>(pl, ra, rb, rs, kb, nk, a1, b1, s1, a0, b0, s0, sink, active, pp, acc);
+    k_step<false>(pl, ra, rb, rs, kb + 1, nk, a0, b0, s0, a1, b1, s1, sink, active, pp, acc);
   }
-  if (kb < nk) k_step(pl, ra, rb, rs, kb, nk, a0, b0, s0, a1, b1, s1, sink, active, acc);
+  if (kb < nk) k_step<false>(pl, ra, rb, rs, kb, nk, a1, b1, s1, a0, b0, s0, sink, active, pp, acc);
+  if (active) drain(pp, acc);
 }
 
 template <bool kBf16Out>
