@@ -39,6 +39,7 @@ namespace fp8blk {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 namespace {
@@ -49,6 +50,12 @@ constexpr int BK = 128;
 constexpr int kThreads = 512;
 constexpr int kTileBytes = BM * BK;    // one operand tile, 32 KB
 constexpr int kScaleSlots = BM + 64;   // 256 activation scales, then 64 weight-scale slots
+// bf16 output staging after the K loop: per wave 64 rows of 128 values with a
+// 272-byte pitch (16 bytes of padding against LDS bank conflicts)
+constexpr int kOutPitch = 272;
+constexpr int kLoopSmem = 4 * kTileBytes + (2 * kScaleSlots + 64) * 4;
+constexpr int kOutSmem = 8 * 64 * kOutPitch;
+constexpr int kSmemBytes = kLoopSmem > kOutSmem ? kLoopSmem : kOutSmem;
 
 struct GemmParams {
   const uint8_t* a;
@@ -60,6 +67,11 @@ struct GemmParams {
   int64_t sa_m, sa_k, sb_n, sb_k;
   int M, N, K;
   int tiles_m, tiles_n;
+  // Tail balancing: the last n_half tiles (in tile order) are computed as two
+  // 256 x 128 halves by two workgroups each, so that a last round that would
+  // occupy only part of the chip fills it. n_full + n_half = tiles; when
+  // n_half > 0 both n_full and 2 n_half are multiples of 8 (one share per XCD).
+  int n_full, n_half;
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
@@ -259,31 +271,55 @@ __device__ __forceinline__ void k_loop(const Plan& pl, const uint8_t* __restrict
 
 template <bool kBf16Out>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ta[2][kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t tb[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) float ts[2][kScaleSlots];
-  __shared__ float sink[64];
+  // LDS: two stages of operand tiles and scales during the K loop; afterwards
+  // the same memory stages the bf16 output for coalesced stores
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemBytes];
+  uint8_t* const ta0 = smem;
+  uint8_t* const ta1 = smem + kTileBytes;
+  uint8_t* const tb0 = smem + 2 * kTileBytes;
+  uint8_t* const tb1 = smem + 3 * kTileBytes;
+  float* const ts0 = reinterpret_cast<float*>(smem + 4 * kTileBytes);
+  float* const ts1 = ts0 + kScaleSlots;
+  float* const sink = ts1 + kScaleSlots;
 
-  // ---- tile assignment: XCD-major remap, then grouped row-major order ----
-  const int nwg = p.tiles_m * p.tiles_n;
-  int bid = blockIdx.x;
-  if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);
+  // ---- tile assignment --------------------------------------------------
+  // Workgroups are dispatched round-robin over the 8 XCDs (id % 8); each XCD
+  // is given a contiguous share of the tile order (neighbouring tiles share A
+  // rows or B columns in its L2): first its full tiles, then its halves.
+  int bid = blockIdx.x, half = -1;
+  if (p.n_half == 0) {
+    const int nwg = p.tiles_m * p.tiles_n;
+    if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);
+  } else {
+    const int x = bid & 7, pos = bid >> 3;
+    const int fpx = p.n_full >> 3, hpx = (2 * p.n_half) >> 3;
+    if (pos < fpx) {
+      bid = x * fpx + pos;
+    } else {
+      const int h = x * hpx + (pos - fpx);
+      bid = p.n_full + (h >> 1);
+      half = h & 1;
+    }
+  }
+  // grouped row-major order: 8 tile rows at a time
   constexpr int kGroupM = 8;
   const int group = bid / (kGroupM * p.tiles_n);
   const int first_m = group * kGroupM;
   const int gm = min(p.tiles_m - first_m, kGroupM);
   const int in_group = bid - group * kGroupM * p.tiles_n;
   const int m0 = (first_m + in_group % gm) * BM;
-  const int n0 = (in_group / gm) * BN;
+  // a half tile is the 256 x 128 block n0 + 128 half .. + 127, computed by the
+  // waves of column slab 0 (one on each SIMD); the other four idle
+  const int n0 = (in_group / gm) * BN + (half > 0 ? 128 : 0);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-  const int wm = wave >> 1;          // 0..3 : 64-row slab
-  const int wn = wave & 1;           // 0..1 : 128-column slab
-  const bool active = (n0 + wn * 128) < p.N;
+  const int wm = wave & 3;           // 0..3 : 64-row slab (waves 4 apart share a SIMD)
+  const int wn = wave >> 2;          // 0..1 : 128-column slab
+  const bool active = (n0 + wn * 128) < p.N && (half < 0 || wn == 0);
   const int nk = p.K / BK;
-  const int rows_a = min(p.M - m0, BM), rows_b = min(p.N - n0, BN);
+  const int rows_a = min(p.M - m0, BM), rows_b = min(p.N - n0, half < 0 ? BN : 128);
 
   Plan pl;
   pl.wave = wave;
@@ -335,27 +371,44 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
     for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
 
   k_loop(pl, p.a + (int64_t)m0 * p.lda, (uint32_t)(rows_a * (int)p.lda), p.b + (int64_t)n0 * p.ldb,
-         (uint32_t)(rows_b * (int)p.ldb), gs, gs_bytes, ta[0], ta[1], tb[0], tb[1], ts[0], ts[1], sink, nk,
-         active, acc);
+         (uint32_t)(rows_b * (int)p.ldb), gs, gs_bytes, ta0, ta1, tb0, tb1, ts0, ts1, sink, nk, active, acc);
 
   if (!active) return;
   // ---- epilogue: lane holds rows 4 * (lane / 16) + v, column lane % 16 ----
+  const int q = lane >> 4, c16 = lane & 15;
+  if (kBf16Out) {
+    // Every wave is past the loop's last barrier and no copy is in flight, so
+    // the LDS is free: stage the wave's 64 x 128 block as bf16, then store it
+    // row by row, 16 bytes per lane (16 lanes per 256-byte row).
+    uint8_t* const ep = smem + wave * (64 * kOutPitch);
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = m0 + wm * 64 + mi * 16 + 4 * (lane >> 4) + v;
-      if (row >= p.M) continue;
+      for (int ni = 0; ni < 8; ++ni)
 #pragma unroll
-      for (int ni = 0; ni < 8; ++ni) {
-        const int col = n0 + wn * 128 + ni * 16 + (lane & 15);
-        if (kBf16Out) {
-          __hip_bfloat16* c = static_cast<__hip_bfloat16*>(p.c);
-          c[(int64_t)row * p.ldc + col] = __float2bfloat16(acc[mi][ni][v]);
-        } else {
-          float* c = static_cast<float*>(p.c);
-          c[(int64_t)row * p.ldc + col] = acc[mi][ni][v];
-        }
+        for (int v = 0; v < 4; ++v)
+          *reinterpret_cast<__hip_bfloat16*>(ep + (mi * 16 + 4 * q + v) * kOutPitch + (ni * 16 + c16) * 2) =
+              __float2bfloat16(acc[mi][ni][v]);
+    __hip_bfloat16* const c = static_cast<__hip_bfloat16*>(p.c);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int idx = i * 64 + lane;
+      const int r = idx >> 4, ch = idx & 15;
+      const v4i val = *reinterpret_cast<const v4i*>(ep + r * kOutPitch + ch * 16);
+      const int row = m0 + wm * 64 + r;
+      if (row < p.M)
+        __builtin_nontemporal_store(val, reinterpret_cast<v4i*>(c + (int64_t)row * p.ldc + n0 + wn * 128 + ch * 8));
+    }
+  } else {
+    float* const c = static_cast<float*>(p.c);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = m0 + wm * 64 + mi * 16 + 4 * q + v;
+        if (row >= p.M) continue;
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni) c[(int64_t)row * p.ldc + n0 + wn * 128 + ni * 16 + c16] = acc[mi][ni][v];
       }
     }
   }
@@ -497,6 +550,19 @@ void launch_decode(const GemmParams& p, bool bf16, hipStream_t st) {
 
 }  // namespace
 
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t st) {
   if (g.M == 0) return hipSuccess;
   GemmParams p;
@@ -530,7 +596,17 @@ hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t st) {
     launch_decode<4>(p, bf16, st);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+  // tail balancing (see GemmParams)
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int cus = device_cu_count();
+  const int rem = cus > 0 ? tiles % cus : 0;
+  p.n_full = tiles;
+  p.n_half = 0;
+  if (rem > 0 && 2 * rem <= cus && rem % 4 == 0 && (tiles - rem) % 8 == 0) {
+    p.n_full = tiles - rem;
+    p.n_half = rem;
+  }
+  const dim3 grid((unsigned)(p.n_full + 2 * p.n_half));
   if (g.c_dtype == DTYPE_BF16)
     hipLaunchKernelGGL(k_gemm_fp8_block<true>, grid, dim3(kThreads), 0, st, p);
   else

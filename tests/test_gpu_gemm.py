@@ -129,3 +129,15 @@ def test_config_full_size_sampled(gpu_lib, config):
     cols = _sample(N, rng, [0, 15, 16, 127, 128, 255, 256, 383, 511, N - 129, N - 128, N - 1])
     literal = _compare(gpu_lib, qa, sa, ga, qw, sw, gw, rows=rows, cols=cols, what=f"config {config}")
     print(f"config {config}: {literal} sampled bf16 outputs exceed the literal 1e-3*T bound (output rounding)")
+
+
+def test_tail_balanced_grid(gpu_lib):
+    """13 x 20 = 260 tiles of 256 x 256: on a 256-CU device the last 4 tiles
+    run as 256 x 128 halves next to 256 full tiles. Sampled rows and columns
+    cover the first, a middle and the last tiles (and both halves of these)."""
+    M, N, K = 13 * 256, 20 * 256, 256
+    qa, sa, ga, qw, sw, gw = _quantized(gpu_lib, 2, M=M, N=N, K=K, variant=7)
+    rng = np.random.default_rng(77)
+    rows = _sample(M, rng, [0, 255, 256, M - 257, M - 256, M - 129, M - 1])
+    cols = _sample(N, rng, [0, 127, 128, 255, N - 257, N - 256, N - 129, N - 128, N - 1])
+    _compare(gpu_lib, qa, sa, ga, qw, sw, gw, rows=rows, cols=cols, what="tail-balanced grid")
