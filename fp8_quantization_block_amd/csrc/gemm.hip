@@ -147,6 +147,7 @@ struct Plan {
   // weight copies carry the 8-row step of instruction i in the scalar offset.
   uint32_t a_voff[4], b_voff;
   uint32_t b_istep;            // bytes between consecutive weight copy instructions (8 rows)
+  uint32_t warm_voff;          // row of this lane's L2 warm-up read (block 0)
   uint32_t s_voff;      // byte offset of this lane's scale (block 0)
   uint32_t s_kstep;     // bytes between consecutive K blocks' scales
   uint32_t a_lo, a_hi;  // this lane's activation fragment chunks (subtile 0 of its slab)
@@ -168,6 +169,16 @@ __device__ __forceinline__ void issue(const Plan& pl, __amdgpu_buffer_rsrc_t ra,
   }
   float* sdst = pl.wave <= 4 ? ts + pl.wave * 64 : sink;
   dma4(rs, pl.s_voff, (uint32_t)kb * pl.s_kstep, sdst);
+}
+
+// L2 warm-up of K block kb: one 4-byte read of each of the block's 512
+// operand lines (128 bytes of one row; waves 0..3 the 256 activation rows,
+// waves 4..7 the 256 weight rows), landing in the sink. Issued after the
+// copies of the block before it, it brings the lines that miss L2 in from
+// the Infinity Cache or HBM one block ahead of their copies. 1 instruction.
+__device__ __forceinline__ void warm(const Plan& pl, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                     int kb, float* sink) {
+  dma4(pl.wave < 4 ? ra : rb, pl.warm_voff, (uint32_t)kb * BK, sink);
 }
 
 // The MFMA / promotion pipeline of a wave, continuous across K blocks.
@@ -237,18 +248,20 @@ __device__ __forceinline__ void drain(const Pipe& pp, v4f (&acc)[4][8]) {
   for (int u = 32 - kLag; u < 32; ++u) promote(pp, pp.comb, u, acc);
 }
 
-// One K block kb: copy block kb + 1 into the other stage, multiply block kb,
-// wait for the copies (the only vector memory operations in flight), barrier.
-// The block index of the copy is clamped to the last block (the tail copy
-// lands in a stage nobody reads again).
+// One K block kb: copy block kb + 1 into the other stage and warm block
+// kb + 2 in L2, multiply block kb, wait for the copies (everything but the
+// warm-up, the only later vector memory operation), barrier. Block indices
+// past the end are clamped to the last block (such a copy lands in a stage
+// nobody reads again).
 template <bool first>
 __device__ __forceinline__ void k_step(const Plan& pl, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                        __amdgpu_buffer_rsrc_t rs, int kb, int nk, const uint8_t* ca,
                                        const uint8_t* cb, const float* cs, uint8_t* na, uint8_t* nb,
                                        float* ns, float* sink, bool active, Pipe& pp, v4f (&acc)[4][8]) {
   issue(pl, ra, rb, rs, min(kb + 1, nk - 1), na, nb, ns, sink);
+  warm(pl, ra, rb, min(kb + 2, nk - 1), sink);
   if (active) mma_block<first>(pl, ca, cb, cs, pp, acc);
-  wait_vm<0>();
+  wait_vm<1>();
   raw_barrier();
 }
 
@@ -268,7 +281,8 @@ __device__ __forceinline__ void k_loop(const Plan& pl, const uint8_t* __restrict
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(gs, gs_bytes);
   Pipe pp;
   issue(pl, ra, rb, rs, 0, a0, b0, s0, sink);
-  wait_vm<0>();
+  warm(pl, ra, rb, min(1, nk - 1), sink);
+  wait_vm<1>();
   raw_barrier();
   k_step<true>(pl, ra, rb, rs, 0, nk, a0, b0, s0, a1, b1, s1, sink, active, pp, acc);
   int kb = 1;
@@ -277,6 +291,7 @@ __device__ __forceinline__ void k_loop(const Plan& pl, const uint8_t* __restrict
     k_step<false>(pl, ra, rb, rs, kb + 1, nk, a0, b0, s0, a1, b1, s1, sink, active, pp, acc);
   }
   if (kb < nk) k_step<false>(pl, ra, rb, rs, kb, nk, a1, b1, s1, a0, b0, s0, sink, active, pp, acc);
+  wait_vm<0>();   // the last warm-up too: nothing may be in flight into the LDS past the loop
   if (active) drain(pp, acc);
 }
 
@@ -344,6 +359,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
     for (int i = 0; i < 4; ++i) pl.a_voff[i] = (uint32_t)((row0 + 8 * i) * (int)p.lda + chunk);
     pl.b_voff = (uint32_t)(row0 * (int)p.ldb + chunk);
     pl.b_istep = (uint32_t)(8 * p.ldb);
+    pl.warm_voff = (uint32_t)(((wave & 3) * 64 + lane) * (int)(wave < 4 ? p.lda : p.ldb));
     const int rrow = lane & 15, q = lane >> 4;
     const uint32_t lo = (uint32_t)(rrow * 128 + ((q ^ swz(rrow)) << 4));
     const uint32_t hi = (uint32_t)(rrow * 128 + (((4 + q) ^ swz(rrow)) << 4));
