@@ -316,6 +316,13 @@ __device__ __forceinline__ void drain(const Pipe& pp, v4f (&acc)[4][8]) {
   for (int u = 32 - kLag; u < 32; ++u) promote(pp, pp.comb, u, acc);
 }
 
+// Distance in K blocks between a block's L2 warm-up and its multiplication.
+// With in-order vector memory counters a warm-up can stay in flight for about
+// two blocks (the end-of-block wait covers everything issued before the next
+// block's copies), so a warm-up three blocks ahead has landed in L2 a block
+// before the copy of its block is issued.
+constexpr int kWarm = 3;
+
 // One K block kb of tile `cur`, reading stage S. It first copies the next
 // block into the other stage (block kb + 1 of this tile, else block 0 of the
 // next work item, else a repeat of this block that nobody reads) and warms the
@@ -330,16 +337,20 @@ __device__ __forceinline__ void k_step(const Plan& pl, const Tile& cur, const Ti
   const float* const rds = S ? ss1 : ss0;
   uint8_t* const wr = S ? st0 : st1;
   float* const wrs = S ? ss0 : ss1;
-  if (kb + 1 < nk) {
+  if (kb + 1 < nk)
     issue(pl, cur, kb + 1, wr, wrs, sink);
-    warm(pl, cur, min(kb + 2, nk - 1), sink);
-  } else if (nxt.valid) {
+  else if (nxt.valid)
     issue(pl, nxt, 0, wr, wrs, sink);
-    warm(pl, nxt, min(1, nk - 1), sink);
-  } else {
+  else
     issue(pl, cur, kb, wr, wrs, sink);
-    warm(pl, cur, kb, sink);
-  }
+  // warm-up target: kWarm blocks ahead, in this item or the next one
+  const int w = kb + kWarm;
+  if (w < nk)
+    warm(pl, cur, w, sink);
+  else if (nxt.valid)
+    warm(pl, nxt, min(w - nk, nk - 1), sink);
+  else
+    warm(pl, cur, nk - 1, sink);
   if (cur.active) mma_block<first>(pl, rd, rd + kTileBytes, rds, pp, acc);
   wait_vm<1>();
   raw_barrier();
@@ -441,9 +452,12 @@ __device__ __forceinline__ void run(const GemmParams& p, const Plan& pl, const u
   const int nk = p.K / BK;
   Tile cur = make_tile(p, pl, 0, ga, gb, gsa, gsb);
   if (!cur.valid) return;
+  // prologue: block 0's copies, then warm-ups of blocks 1 .. kWarm - 1 (the
+  // steps warm kWarm on); wait for the copies only
   issue(pl, cur, 0, st0, ss0, sink);
-  warm(pl, cur, min(1, nk - 1), sink);
-  wait_vm<1>();
+#pragma unroll
+  for (int j = 1; j < kWarm; ++j) warm(pl, cur, min(j, nk - 1), sink);
+  wait_vm<kWarm - 1>();
   raw_barrier();
   int par = 0;   // stage holding the current item's first block
   for (int k = 0; cur.valid; ++k) {
