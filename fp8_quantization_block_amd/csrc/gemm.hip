@@ -351,9 +351,16 @@ __device__ __forceinline__ void k_step(const Plan& pl, const Tile& cur, const Ti
     warm(pl, nxt, min(w - nk, nk - 1), sink);
   else
     warm(pl, cur, nk - 1, sink);
+  // Everything after the copy issue runs at raised wave priority, lowered
+  // again after the barrier (measured 15% faster than no priority change, 8%
+  // faster than raising it for the MFMAs only): a wave issuing the next
+  // block's copies does not take issue cycles from waves that have MFMAs or
+  // promotions ready.
+  __builtin_amdgcn_s_setprio(3);
   if (cur.active) mma_block<first>(pl, rd, rd + kTileBytes, rds, pp, acc);
   wait_vm<1>();
   raw_barrier();
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Output of one work item. bf16: the wave's 64 x 128 block goes through the
