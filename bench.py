@@ -95,9 +95,9 @@ class Timer:
 # x 2.0, WRITE_SIZE x 1.0). Valid only for the kernel source they were taken on:
 # the key is the SHA-256 of the GEMM source files; any other source gives null.
 GEMM_COUNTERS = {
-    "sources_sha256": "4536aa184459160ef4928b456cd63bb9cdb4c460ff944d9f641a616745f980d9",
-    "fetch_kib": 192686.7,
-    "write_kib": 114757.2,
+    "sources_sha256": "8b8bcf76c49d631aa895c23a6602a07a2e5a3730c6d1e026d8dc44f5f1b76c53",
+    "fetch_kib": 193727.5,
+    "write_kib": 115749.1,
 }
 FETCH_FACTOR = 2.0
 WRITE_FACTOR = 1.0
