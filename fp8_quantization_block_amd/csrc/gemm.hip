@@ -55,7 +55,7 @@ constexpr int kScaleSlots = BM + 64;   // 256 activation scales, then 64 weight-
 // LDS read)
 constexpr int kOutPitch = 256;
 constexpr int kLoopSmem = 4 * kTileBytes + (2 * kScaleSlots + 64) * 4;
-constexpr int kOutSmem = 8 * 32 * kOutPitch;   // one pass of the output staging (fits one stage)
+constexpr int kOutSmem = 8 * 64 * kOutPitch;
 constexpr int kSmemBytes = kLoopSmem > kOutSmem ? kLoopSmem : kOutSmem;
 
 struct GemmParams {
@@ -73,7 +73,6 @@ struct GemmParams {
   // occupy only part of the chip fills it. n_full + n_half = tiles; when
   // n_half > 0 both n_full and 2 n_half are multiples of 8 (one share per XCD).
   int n_full, n_half;
-  int remap;   // XCD-aware work order (needs n_full and 2 n_half divisible by 8)
 };
 
 // LDS rows are 128 bytes (eight 16-byte chunks); logical chunk c of row r is
@@ -130,7 +129,7 @@ __device__ __forceinline__ void raw_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Per-thread copy and read plan, the same for every tile.
+// Per-thread copy and read plan.
 // * Operand tiles, K block kb, into an LDS stage: wave w fills rows 32 w ..
 //   32 w + 31 of each tile, 8 rows (1 KB) per instruction; lane l fills
 //   physical chunk l % 8 of row 8 (4 w + i) + l / 8, i.e. logical chunk
@@ -148,108 +147,27 @@ struct Plan {
   // weight copies carry the 8-row step of instruction i in the scalar offset.
   uint32_t a_voff[4], b_voff;
   uint32_t b_istep;            // bytes between consecutive weight copy instructions (8 rows)
-  uint32_t warm_voff;          // row of this lane's L2 warm-up read (block 0)
-  uint32_t s_kstep;            // bytes between consecutive K blocks' scales
-  uint32_t a_lo, a_hi;         // this lane's activation fragment chunks (subtile 0 of its slab)
-  uint32_t b_lo, b_hi;         // this lane's weight fragment chunks (subtile 0 of its slab)
-  uint32_t s_rd;               // this lane's four activation scales (subtile 0)
-  uint32_t w_rd;               // the wave's weight-block scale slot
-  int wave, wm, wn, lane;
+  uint32_t s_voff;      // byte offset of this lane's scale (block 0)
+  uint32_t s_kstep;     // bytes between consecutive K blocks' scales
+  uint32_t a_lo, a_hi;  // this lane's activation fragment chunks (subtile 0 of its slab)
+  uint32_t b_lo, b_hi;  // this lane's weight fragment chunks (subtile 0 of its slab)
+  uint32_t s_rd;        // this lane's four activation scales (subtile 0)
+  uint32_t w_rd;        // the wave's weight-block scale slot
+  int wave;
 };
 
-// One work item: a 256 x 256 tile, or one 256 x 128 half of it (then only the
-// waves of column slab 0 compute; they sit on the four SIMDs).
-struct Tile {
-  __amdgpu_buffer_rsrc_t ra, rb, rs;
-  uint32_t s_voff;   // this lane's scale (block 0)
-  int m0, n0;
-  bool active;       // this wave computes (and stores) part of the tile
-  bool valid;        // the work item exists
-};
-
-// Work item k of this workgroup. Workgroups are dispatched round-robin over
-// the 8 XCDs (id % 8). With the XCD remap each XCD owns a contiguous share of
-// the tile order (its full tiles, then its half tiles), so that the tiles
-// running at the same time on one XCD share A rows and B columns in its L2;
-// the workgroups of an XCD take its items in turn. Within the tile order,
-// tiles are grouped 8 tile rows at a time.
-__device__ __forceinline__ bool item_of(const GemmParams& p, int k, int& tile, int& half) {
-  const int b = blockIdx.x, P = gridDim.x;
-  half = -1;
-  if (!p.remap) {
-    tile = b + k * P;
-    return tile < p.n_full;
-  }
-  const int x = b & 7, J = P >> 3;
-  const int pos = (b >> 3) + k * J;
-  const int fpx = p.n_full >> 3, hpx = (2 * p.n_half) >> 3;
-  if (pos < fpx) {
-    tile = x * fpx + pos;
-    return true;
-  }
-  if (pos < fpx + hpx) {
-    const int h = x * hpx + (pos - fpx);
-    tile = p.n_full + (h >> 1);
-    half = h & 1;
-    return true;
-  }
-  return false;
-}
-
-__device__ __forceinline__ Tile make_tile(const GemmParams& p, const Plan& pl, int k, const uint8_t* __restrict__ ga,
-                                          const uint8_t* __restrict__ gb, const float* __restrict__ gsa,
-                                          const float* __restrict__ gsb) {
-  Tile t;
-  int tile, half;
-  t.valid = item_of(p, k, tile, half);
-  if (!t.valid) tile = 0;
-  constexpr int kGroupM = 8;
-  const int group = tile / (kGroupM * p.tiles_n);
-  const int first_m = group * kGroupM;
-  const int gm = min(p.tiles_m - first_m, kGroupM);
-  const int in_group = tile - group * kGroupM * p.tiles_n;
-  t.m0 = (first_m + in_group % gm) * BM;
-  t.n0 = (in_group / gm) * BN + (half > 0 ? 128 : 0);
-  t.active = t.valid && (t.n0 + pl.wn * 128) < p.N && (half < 0 || pl.wn == 0);
-  const int rows_a = min(p.M - t.m0, BM), rows_b = min(p.N - t.n0, half < 0 ? BN : 128);
-  t.ra = make_rsrc(ga + (int64_t)t.m0 * p.lda, (uint32_t)(rows_a * (int)p.lda));
-  t.rb = make_rsrc(gb + (int64_t)t.n0 * p.ldb, (uint32_t)(rows_b * (int)p.ldb));
-  const int nk = p.K / BK;
-  if (pl.wave < 4) {
-    const int64_t s_last = (int64_t)(p.M - 1) * p.sa_m + (int64_t)(nk - 1) * p.sa_k;
-    t.rs = make_rsrc(gsa, (uint32_t)((s_last + 1) * 4));
-    t.s_voff = (uint32_t)((int64_t)min(t.m0 + pl.wave * 64 + pl.lane, p.M - 1) * p.sa_m * 4);
-  } else {
-    const int nblk = p.N >> 7;
-    const int64_t s_last = (int64_t)(nblk - 1) * p.sb_n + (int64_t)(nk - 1) * p.sb_k;
-    t.rs = make_rsrc(gsb, (uint32_t)((s_last + 1) * 4));
-    t.s_voff = (uint32_t)((int64_t)min((t.n0 >> 7) + (pl.lane & 1), nblk - 1) * p.sb_n * 4);
-  }
-  return t;
-}
-
-// Copies of K block kb of tile t into one stage (activation tile at st,
-// weight tile at st + 32 KB, scales at ss): 4 + 4 + 1 vector memory
-// instructions.
-__device__ __forceinline__ void issue(const Plan& pl, const Tile& t, int kb, uint8_t* st, float* ss,
-                                      float* sink) {
+// Copies of K block kb into one stage: 4 + 4 + 1 vector memory instructions.
+__device__ __forceinline__ void issue(const Plan& pl, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                      __amdgpu_buffer_rsrc_t rs, int kb, uint8_t* ta, uint8_t* tb,
+                                      float* ts, float* sink) {
   const uint32_t soff = (uint32_t)kb * BK;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    dma16(t.ra, pl.a_voff[i], soff, st + (pl.wave * 4 + i) * 1024);
-    dma16(t.rb, pl.b_voff, soff + (uint32_t)i * pl.b_istep, st + kTileBytes + (pl.wave * 4 + i) * 1024);
+    dma16(ra, pl.a_voff[i], soff, ta + (pl.wave * 4 + i) * 1024);
+    dma16(rb, pl.b_voff, soff + (uint32_t)i * pl.b_istep, tb + (pl.wave * 4 + i) * 1024);
   }
-  float* sdst = pl.wave <= 4 ? ss + pl.wave * 64 : sink;
-  dma4(t.rs, t.s_voff, (uint32_t)kb * pl.s_kstep, sdst);
-}
-
-// L2 warm-up of K block kb of tile t: one 4-byte read of each of the block's
-// 512 operand lines (128 bytes of one row; waves 0..3 the 256 activation rows,
-// waves 4..7 the 256 weight rows), landing in the sink. Issued after the
-// copies of the block before it, it brings the lines that miss L2 in from
-// the Infinity Cache or HBM one block ahead of their copies. 1 instruction.
-__device__ __forceinline__ void warm(const Plan& pl, const Tile& t, int kb, float* sink) {
-  dma4(pl.wave < 4 ? t.ra : t.rb, pl.warm_voff, (uint32_t)kb * BK, sink);
+  float* sdst = pl.wave <= 4 ? ts + pl.wave * 64 : sink;
+  dma4(rs, pl.s_voff, (uint32_t)kb * pl.s_kstep, sdst);
 }
 
 // The MFMA / promotion pipeline of a wave, continuous across K blocks.
@@ -278,15 +196,18 @@ __device__ __forceinline__ void promote(const Pipe& pp, const v4f (&comb)[4], in
 template <bool first>
 __device__ __forceinline__ void mma_block(const Plan& pl, const uint8_t* ta, const uint8_t* tb,
                                           const float* ts, Pipe& pp, v4f (&acc)[4][8]) {
-  // reads for the first MFMA first, then the rest of the activation fragments;
-  // the weight fragment of subtile ni + 1 is read while subtile ni is in use
+  // reads for the first MFMA first, then the rest of the activation fragments
+  // and the scales; the weight fragment of subtile ni + 1 is read while
+  // subtile ni is in use
   v8i af[4], bf[2];
   af[0] = read_frag(ta, pl.a_lo, pl.a_hi);
   bf[0] = read_frag(tb, pl.b_lo, pl.b_hi);
 #pragma unroll
   for (int mi = 1; mi < 4; ++mi) af[mi] = read_frag(ta, pl.a_lo + mi * 2048, pl.a_hi + mi * 2048);
-  // the weight-block scale is one value for the whole wave: keep it in an SGPR
-  const float sw = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ts[pl.w_rd])));
+  v4f s4[4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) s4[mi] = *reinterpret_cast<const v4f*>(ts + pl.s_rd + mi * 16);
+  const float sw = ts[pl.w_rd];
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int t = 0; t < 32; ++t) {
@@ -299,11 +220,11 @@ __device__ __forceinline__ void mma_block(const Plan& pl, const uint8_t* ta, con
     } else if (!first) {
       promote(pp, pp.comb, t - kLag + 32, acc);   // previous block's product, its scales
     }
-    // the scales of subtile row m = t - 1 are replaced by this block's once the
-    // previous block's last promotion with them (product 28 + m) is done; the
-    // first promotion with the new ones is product m, kLag - 1 steps later
-    if (t >= 1 && t <= 4)
-      pp.comb[t - 1] = *reinterpret_cast<const v4f*>(ts + pl.s_rd + (t - 1) * 16) * sw;
+    if (t == kLag - 1) {
+      // from here on the promotions belong to this block
+#pragma unroll
+      for (int m = 0; m < 4; ++m) pp.comb[m] = s4[m] * sw;
+    }
     // keep the program order: the scheduler would otherwise pair FMAs with the
     // MFMA that produces their operand and stall on it
     __builtin_amdgcn_sched_barrier(0);
@@ -316,191 +237,106 @@ __device__ __forceinline__ void drain(const Pipe& pp, v4f (&acc)[4][8]) {
   for (int u = 32 - kLag; u < 32; ++u) promote(pp, pp.comb, u, acc);
 }
 
-// Distance in K blocks between a block's L2 warm-up and its multiplication.
-// With in-order vector memory counters a warm-up can stay in flight for about
-// two blocks (the end-of-block wait covers everything issued before the next
-// block's copies), so a warm-up three blocks ahead has landed in L2 a block
-// before the copy of its block is issued.
-constexpr int kWarm = 3;
-
-// One K block kb of tile `cur`, reading stage S. It first copies the next
-// block into the other stage (block kb + 1 of this tile, else block 0 of the
-// next work item, else a repeat of this block that nobody reads) and warms the
-// block after that in L2, then multiplies, waits for the copies (everything
-// but the warm-up, the only later vector memory operation) and ends with a
-// barrier.
-template <int S, bool first>
-__device__ __forceinline__ void k_step(const Plan& pl, const Tile& cur, const Tile& nxt, int kb, int nk,
-                                       uint8_t* st0, uint8_t* st1, float* ss0, float* ss1, float* sink,
-                                       Pipe& pp, v4f (&acc)[4][8]) {
-  uint8_t* const rd = S ? st1 : st0;
-  const float* const rds = S ? ss1 : ss0;
-  uint8_t* const wr = S ? st0 : st1;
-  float* const wrs = S ? ss0 : ss1;
-  if (kb + 1 < nk)
-    issue(pl, cur, kb + 1, wr, wrs, sink);
-  else if (nxt.valid)
-    issue(pl, nxt, 0, wr, wrs, sink);
-  else
-    issue(pl, cur, kb, wr, wrs, sink);
-  // warm-up target: kWarm blocks ahead, in this item or the next one
-  const int w = kb + kWarm;
-  if (w < nk)
-    warm(pl, cur, w, sink);
-  else if (nxt.valid)
-    warm(pl, nxt, min(w - nk, nk - 1), sink);
-  else
-    warm(pl, cur, nk - 1, sink);
-  // Everything after the copy issue runs at raised wave priority, lowered
-  // again after the barrier (measured 15% faster than no priority change, 8%
-  // faster than raising it for the MFMAs only): a wave issuing the next
-  // block's copies does not take issue cycles from waves that have MFMAs or
-  // promotions ready.
-  __builtin_amdgcn_s_setprio(3);
-  if (cur.active) mma_block<first>(pl, rd, rd + kTileBytes, rds, pp, acc);
-  wait_vm<1>();
+// One K block kb: copy block kb + 1 into the other stage, multiply block kb,
+// wait for the copies (the only vector memory operations in flight), barrier.
+// The block index of the copy is clamped to the last block (the tail copy
+// lands in a stage nobody reads again).
+template <bool first>
+__device__ __forceinline__ void k_step(const Plan& pl, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                       __amdgpu_buffer_rsrc_t rs, int kb, int nk, const uint8_t* ca,
+                                       const uint8_t* cb, const float* cs, uint8_t* na, uint8_t* nb,
+                                       float* ns, float* sink, bool active, Pipe& pp, v4f (&acc)[4][8]) {
+  issue(pl, ra, rb, rs, min(kb + 1, nk - 1), na, nb, ns, sink);
+  if (active) mma_block<first>(pl, ca, cb, cs, pp, acc);
+  wait_vm<0>();
   raw_barrier();
-  __builtin_amdgcn_s_setprio(0);
 }
 
-// Output of one work item. bf16: the wave's 64 x 128 block goes through the
-// free 64 KB stage `ep` in two passes of 32 rows (8 KB per wave, 256 bytes per
-// row) and leaves as 16-byte row-contiguous stores. fp32 (verification): direct
-// stores.
-template <bool kBf16Out>
-__device__ __forceinline__ void store_tile(const GemmParams& p, const Plan& pl, const Tile& t, uint8_t* ep,
-                                           const v4f (&acc)[4][8]) {
-  const int q = pl.lane >> 4, c16 = pl.lane & 15;
-  if (kBf16Out) {
-    uint8_t* const w = ep + pl.wave * (32 * kOutPitch);
-    __hip_bfloat16* const c = static_cast<__hip_bfloat16*>(p.c);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int mh = 0; mh < 2; ++mh)
-#pragma unroll
-        for (int ni = 0; ni < 8; ++ni)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            *reinterpret_cast<__hip_bfloat16*>(w + (mh * 16 + 4 * q + v) * kOutPitch + (ni * 16 + c16) * 2) =
-                __float2bfloat16(acc[2 * h + mh][ni][v]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int idx = i * 64 + pl.lane;
-        const int r = idx >> 4, ch = idx & 15;
-        const v4i val = *reinterpret_cast<const v4i*>(w + r * kOutPitch + ch * 16);
-        const int row = t.m0 + pl.wm * 64 + 32 * h + r;
-        if (row < p.M)
-          __builtin_nontemporal_store(val, reinterpret_cast<v4i*>(c + (int64_t)row * p.ldc + t.n0 + pl.wn * 128 + ch * 8));
-      }
-    }
-  } else {
-    float* const c = static_cast<float*>(p.c);
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = t.m0 + pl.wm * 64 + mi * 16 + 4 * q + v;
-        if (row >= p.M) continue;
-#pragma unroll
-        for (int ni = 0; ni < 8; ++ni)
-          c[(int64_t)row * p.ldc + t.n0 + pl.wn * 128 + ni * 16 + c16] = acc[mi][ni][v];
-      }
-    }
-  }
-}
-
-// One work item whose first K block sits in stage P0: the K loop (stages
-// alternate, so it is unrolled by two with static stages), the promotion of
-// the last products and the output. Returns with the next item's first block
-// landed in stage (P0 + nk) % 2.
-template <bool kBf16Out, int P0>
-__device__ __forceinline__ void run_item(const GemmParams& p, const Plan& pl, const Tile& cur, const Tile& nxt,
-                                         int nk, uint8_t* st0, uint8_t* st1, float* ss0, float* ss1,
-                                         float* sink) {
-  constexpr int P1 = 1 - P0;
-  v4f acc[4][8];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
+// The K loop over the two stages. Every pointer the copies touch (both
+// stages' tiles and scale slots, the sink, and the arrays they read) is a
+// distinct non-aliasing parameter, so that the compiler can tell that reading
+// one stage does not depend on the copies in flight into the other.
+__device__ __forceinline__ void k_loop(const Plan& pl, const uint8_t* __restrict__ ga, uint32_t ga_bytes,
+                                       const uint8_t* __restrict__ gb, uint32_t gb_bytes,
+                                       const float* __restrict__ gs, uint32_t gs_bytes,
+                                       uint8_t* __restrict__ a0, uint8_t* __restrict__ a1,
+                                       uint8_t* __restrict__ b0, uint8_t* __restrict__ b1,
+                                       float* __restrict__ s0, float* __restrict__ s1,
+                                       float* __restrict__ sink, int nk, bool active, v4f (&acc)[4][8]) {
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(ga, ga_bytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(gb, gb_bytes);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(gs, gs_bytes);
   Pipe pp;
-  k_step<P0, true>(pl, cur, nxt, 0, nk, st0, st1, ss0, ss1, sink, pp, acc);
+  issue(pl, ra, rb, rs, 0, a0, b0, s0, sink);
+  wait_vm<0>();
+  raw_barrier();
+  k_step<true>(pl, ra, rb, rs, 0, nk, a0, b0, s0, a1, b1, s1, sink, active, pp, acc);
   int kb = 1;
   for (; kb + 1 < nk; kb += 2) {
-    k_step<P1, false>(pl, cur, nxt, kb, nk, st0, st1, ss0, ss1, sink, pp, acc);
-    k_step<P0, false>(pl, cur, nxt, kb + 1, nk, st0, st1, ss0, ss1, sink, pp, acc);
+    k_step<false>(pl, ra, rb, rs, kb, nk, a1, b1, s1, a0, b0, s0, sink, active, pp, acc);
+    k_step<false>(pl, ra, rb, rs, kb + 1, nk, a0, b0, s0, a1, b1, s1, sink, active, pp, acc);
   }
-  const bool odd_tail = kb < nk;   // nk even: one more block, in stage P1
-  if (odd_tail) k_step<P1, false>(pl, cur, nxt, kb, nk, st0, st1, ss0, ss1, sink, pp, acc);
-  if (cur.active) {
-    drain(pp, acc);
-    // the stage of the last block is free (the next item's first block has
-    // landed in the other one): stage the output there
-    uint8_t* const ep = (odd_tail ? P1 : P0) ? st1 : st0;
-    store_tile<kBf16Out>(p, pl, cur, ep, acc);
-  }
-  raw_barrier();   // the staging area is the stage the next copy refills
-}
-
-// All work items of this workgroup, the K blocks of one running straight into
-// the next: the last K block of an item copies the first block of the next
-// one, so only the output staging of each item is not overlapped with loads.
-// Every pointer the copies touch (the two stages, their scale slots, the sink
-// and the arrays they read) is a distinct non-aliasing parameter, so that the
-// compiler can tell that reading one stage does not depend on the copies in
-// flight into the other.
-template <bool kBf16Out>
-__device__ __forceinline__ void run(const GemmParams& p, const Plan& pl, const uint8_t* __restrict__ ga,
-                                    const uint8_t* __restrict__ gb, const float* __restrict__ gsa,
-                                    const float* __restrict__ gsb, uint8_t* __restrict__ st0,
-                                    uint8_t* __restrict__ st1, float* __restrict__ ss0,
-                                    float* __restrict__ ss1, float* __restrict__ sink) {
-  const int nk = p.K / BK;
-  Tile cur = make_tile(p, pl, 0, ga, gb, gsa, gsb);
-  if (!cur.valid) return;
-  // prologue: block 0's copies, then warm-ups of blocks 1 .. kWarm - 1 (the
-  // steps warm kWarm on); wait for the copies only
-  issue(pl, cur, 0, st0, ss0, sink);
-#pragma unroll
-  for (int j = 1; j < kWarm; ++j) warm(pl, cur, min(j, nk - 1), sink);
-  wait_vm<kWarm - 1>();
-  raw_barrier();
-  int par = 0;   // stage holding the current item's first block
-  for (int k = 0; cur.valid; ++k) {
-    const Tile nxt = make_tile(p, pl, k + 1, ga, gb, gsa, gsb);
-    if (par == 0)
-      run_item<kBf16Out, 0>(p, pl, cur, nxt, nk, st0, st1, ss0, ss1, sink);
-    else
-      run_item<kBf16Out, 1>(p, pl, cur, nxt, nk, st0, st1, ss0, ss1, sink);
-    par ^= nk & 1;
-    cur = nxt;
-  }
-  wait_vm<0>();   // nothing may be in flight into the LDS past the kernel
+  if (kb < nk) k_step<false>(pl, ra, rb, rs, kb, nk, a1, b1, s1, a0, b0, s0, sink, active, pp, acc);
+  if (active) drain(pp, acc);
 }
 
 template <bool kBf16Out>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
-  // LDS: two stages of operand tiles (activation tile, then weight tile) and
-  // scales; after a work item's K loop the stage it last read stages its bf16
-  // output
+  // LDS: two stages of operand tiles and scales during the K loop; afterwards
+  // the same memory stages the bf16 output for coalesced stores
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemBytes];
-  uint8_t* const st0 = smem;
-  uint8_t* const st1 = smem + 2 * kTileBytes;
-  float* const ss0 = reinterpret_cast<float*>(smem + 4 * kTileBytes);
-  float* const ss1 = ss0 + kScaleSlots;
-  float* const sink = ss1 + kScaleSlots;
+  uint8_t* const ta0 = smem;
+  uint8_t* const ta1 = smem + kTileBytes;
+  uint8_t* const tb0 = smem + 2 * kTileBytes;
+  uint8_t* const tb1 = smem + 3 * kTileBytes;
+  float* const ts0 = reinterpret_cast<float*>(smem + 4 * kTileBytes);
+  float* const ts1 = ts0 + kScaleSlots;
+  float* const sink = ts1 + kScaleSlots;
+
+  // ---- tile assignment --------------------------------------------------
+  // Workgroups are dispatched round-robin over the 8 XCDs (id % 8); each XCD
+  // is given a contiguous share of the tile order (neighbouring tiles share A
+  // rows or B columns in its L2): first its full tiles, then its halves.
+  int bid = blockIdx.x, half = -1;
+  if (p.n_half == 0) {
+    const int nwg = p.tiles_m * p.tiles_n;
+    if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);
+  } else {
+    const int x = bid & 7, pos = bid >> 3;
+    const int fpx = p.n_full >> 3, hpx = (2 * p.n_half) >> 3;
+    if (pos < fpx) {
+      bid = x * fpx + pos;
+    } else {
+      const int h = x * hpx + (pos - fpx);
+      bid = p.n_full + (h >> 1);
+      half = h & 1;
+    }
+  }
+  // grouped row-major order: 8 tile rows at a time
+  constexpr int kGroupM = 8;
+  const int group = bid / (kGroupM * p.tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = min(p.tiles_m - first_m, kGroupM);
+  const int in_group = bid - group * kGroupM * p.tiles_n;
+  const int m0 = (first_m + in_group % gm) * BM;
+  // a half tile is the 256 x 128 block n0 + 128 half .. + 127, computed by the
+  // waves of column slab 0 (one on each SIMD); the other four idle
+  const int n0 = (in_group / gm) * BN + (half > 0 ? 128 : 0);
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+  const int wm = wave & 3;           // 0..3 : 64-row slab (waves 4 apart share a SIMD)
+  const int wn = wave >> 2;          // 0..1 : 128-column slab
+  const bool active = (n0 + wn * 128) < p.N && (half < 0 || wn == 0);
+  const int nk = p.K / BK;
+  const int rows_a = min(p.M - m0, BM), rows_b = min(p.N - n0, half < 0 ? BN : 128);
+
   Plan pl;
-  pl.lane = tid & 63;
-  pl.wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-  pl.wm = pl.wave & 3;    // 0..3 : 64-row slab (waves 4 apart share a SIMD)
-  pl.wn = pl.wave >> 2;   // 0..1 : 128-column slab
+  pl.wave = wave;
   {
     // copy instruction i fills rows 8 (4 w + i) + l / 8, whose swizzle is
     // l / 8: every instruction uses the same chunk pattern, 8 rows further on
-    const int lane = pl.lane, wave = pl.wave;
     const int sub_row = lane >> 3, pchunk = lane & 7;
     const int row0 = wave * 32 + sub_row;
     const int chunk = (pchunk ^ swz(row0)) << 4;
@@ -508,19 +344,82 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
     for (int i = 0; i < 4; ++i) pl.a_voff[i] = (uint32_t)((row0 + 8 * i) * (int)p.lda + chunk);
     pl.b_voff = (uint32_t)(row0 * (int)p.ldb + chunk);
     pl.b_istep = (uint32_t)(8 * p.ldb);
-    pl.warm_voff = (uint32_t)(((wave & 3) * 64 + lane) * (int)(wave < 4 ? p.lda : p.ldb));
-    pl.s_kstep = (uint32_t)((wave < 4 ? p.sa_k : p.sb_k) * 4);
     const int rrow = lane & 15, q = lane >> 4;
     const uint32_t lo = (uint32_t)(rrow * 128 + ((q ^ swz(rrow)) << 4));
     const uint32_t hi = (uint32_t)(rrow * 128 + (((4 + q) ^ swz(rrow)) << 4));
-    pl.a_lo = lo + pl.wm * 64 * 128;
-    pl.a_hi = hi + pl.wm * 64 * 128;
-    pl.b_lo = lo + pl.wn * 128 * 128;
-    pl.b_hi = hi + pl.wn * 128 * 128;
-    pl.s_rd = (uint32_t)(pl.wm * 64 + 4 * q);
-    pl.w_rd = (uint32_t)(BM + pl.wn);
+    pl.a_lo = lo + wm * 64 * 128;
+    pl.a_hi = hi + wm * 64 * 128;
+    pl.b_lo = lo + wn * 128 * 128;
+    pl.b_hi = hi + wn * 128 * 128;
+    pl.s_rd = (uint32_t)(wm * 64 + 4 * q);
+    pl.w_rd = (uint32_t)(BM + wn);
   }
-  run<kBf16Out>(p, pl, p.a, p.b, p.sa, p.sb, st0, st1, ss0, ss1, sink);
+  // scale copy plan: waves 0..3 activation scales, waves 4..7 weight-block scales
+  const float* gs;
+  uint32_t gs_bytes;
+  if (wave < 4) {
+    const int64_t s_last = (int64_t)(p.M - 1) * p.sa_m + (int64_t)(nk - 1) * p.sa_k;
+    gs = p.sa;
+    gs_bytes = (uint32_t)((s_last + 1) * 4);
+    pl.s_voff = (uint32_t)((int64_t)min(m0 + wave * 64 + lane, p.M - 1) * p.sa_m * 4);
+    pl.s_kstep = (uint32_t)(p.sa_k * 4);
+  } else {
+    const int nblk = p.N >> 7;
+    const int64_t s_last = (int64_t)(nblk - 1) * p.sb_n + (int64_t)(nk - 1) * p.sb_k;
+    gs = p.sb;
+    gs_bytes = (uint32_t)((s_last + 1) * 4);
+    pl.s_voff = (uint32_t)((int64_t)min((n0 >> 7) + (lane & 1), nblk - 1) * p.sb_n * 4);
+    pl.s_kstep = (uint32_t)(p.sb_k * 4);
+  }
+
+  v4f acc[4][8];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  k_loop(pl, p.a + (int64_t)m0 * p.lda, (uint32_t)(rows_a * (int)p.lda), p.b + (int64_t)n0 * p.ldb,
+         (uint32_t)(rows_b * (int)p.ldb), gs, gs_bytes, ta0, ta1, tb0, tb1, ts0, ts1, sink, nk, active, acc);
+
+  if (!active) return;
+  // ---- epilogue: lane holds rows 4 * (lane / 16) + v, column lane % 16 ----
+  const int q = lane >> 4, c16 = lane & 15;
+  if (kBf16Out) {
+    // Every wave is past the loop's last barrier and no copy is in flight, so
+    // the LDS is free: stage the wave's 64 x 128 block as bf16, then store it
+    // row by row, 16 bytes per lane (16 lanes per 256-byte row).
+    uint8_t* const ep = smem + wave * (64 * kOutPitch);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 8; ++ni)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          *reinterpret_cast<__hip_bfloat16*>(ep + (mi * 16 + 4 * q + v) * kOutPitch + (ni * 16 + c16) * 2) =
+              __float2bfloat16(acc[mi][ni][v]);
+    __hip_bfloat16* const c = static_cast<__hip_bfloat16*>(p.c);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int idx = i * 64 + lane;
+      const int r = idx >> 4, ch = idx & 15;
+      const v4i val = *reinterpret_cast<const v4i*>(ep + r * kOutPitch + ch * 16);
+      const int row = m0 + wm * 64 + r;
+      if (row < p.M)
+        __builtin_nontemporal_store(val, reinterpret_cast<v4i*>(c + (int64_t)row * p.ldc + n0 + wn * 128 + ch * 8));
+    }
+  } else {
+    float* const c = static_cast<float*>(p.c);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = m0 + wm * 64 + mi * 16 + 4 * q + v;
+        if (row >= p.M) continue;
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni) c[(int64_t)row * p.ldc + n0 + wn * 128 + ni * 16 + c16] = acc[mi][ni][v];
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -705,8 +604,7 @@ hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t st) {
     launch_decode<4>(p, bf16, st);
     return hipGetLastError();
   }
-  // Work items: tiles, with tail balancing (see GemmParams). The grid is
-  // persistent, one workgroup per compute unit, each looping over its items.
+  // tail balancing (see GemmParams)
   const int tiles = p.tiles_m * p.tiles_n;
   const int cus = device_cu_count();
   const int rem = cus > 0 ? tiles % cus : 0;
@@ -716,11 +614,7 @@ hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t st) {
     p.n_full = tiles - rem;
     p.n_half = rem;
   }
-  const int items = p.n_full + 2 * p.n_half;
-  p.remap = (p.n_full % 8 == 0) && (p.n_half % 4 == 0) ? 1 : 0;
-  int wgs = items;
-  if (cus >= 8 && items > cus) wgs = p.remap ? (cus & ~7) : cus;
-  const dim3 grid((unsigned)wgs);
+  const dim3 grid((unsigned)(p.n_full + 2 * p.n_half));
   if (g.c_dtype == DTYPE_BF16)
     hipLaunchKernelGGL(k_gemm_fp8_block<true>, grid, dim3(kThreads), 0, st, p);
   else
