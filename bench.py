@@ -279,6 +279,13 @@ def main():
                                                "TFLOP/s": 2.0 * m3 * n3 * k3 / t_dec / 1e12}
         del qw3
 
+    # ---- measured MFMA ceiling on the workload's own codes --------------------
+    ceiling = None
+    if args.only is None:
+        ceiling = mfma_ceiling(torch, dev, qa_sets[0], qw)
+        if ceiling and passes.get("gemm"):
+            ceiling["gemm_frac_of_mfma_plus_4_fma"] = passes["gemm"]["TFLOP/s"] / ceiling["mfma_plus_4_fma"]
+
     # ---- CPU oracle on a bounded sample of the step -------------------------
     cpu = None
     if not args.no_cpu_baseline and args.only is None:
@@ -312,6 +319,7 @@ def main():
             "algorithmic_bytes": float(M * K + N * K + 2 * M * N + 4 * (M * (K // 128) + (N // 128) * (K // 128))),
         },
         "passes": passes,
+        "mfma_ceiling": ceiling,
         "per_call": timer.stats,
         "cpu_baseline": cpu,
     }
@@ -329,6 +337,52 @@ def copy_calibration(torch, timer, dev):
     print(json.dumps({"copy_512MB": {"us": t * 1e6, "GB/s": 2 * 2 * n / t / 1e9,
                                      "bytes_read": 2 * n, "bytes_written": 2 * n},
                       "per_call": timer.stats}), flush=True)
+
+
+def mfma_ceiling(torch, dev, qa, qw):
+    """Throughput of the GEMM's FP8 MFMA with no memory traffic, on 2 KB of
+    the workload's own activation and weight codes, alone and with the 4
+    independent fp32 FMAs per MFMA that the per-K-block promotion issues, and
+    (for contrast) on all-zero operands. 2 waves per SIMD, as the GEMM. The
+    chip's clock under MFMA load is power-limited and power depends on the
+    operand bits, so this, not the nominal peak, is what the GEMM can reach."""
+    import ctypes
+    path = os.path.join(ROOT, "fp8_quantization_block_amd", "libfp8blk_bench.so")
+    if not os.path.exists(path):
+        print("bench.py: libfp8blk_bench.so not built; skipping the MFMA ceiling", file=sys.stderr)
+        return None
+    lib = ctypes.CDLL(path)
+    f = lib.fp8blk_bench_mfma_ceiling
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    a_codes = qa.reshape(-1)[:2048].contiguous().view(torch.int32)
+    b_codes = qw.reshape(-1)[:2048].contiguous().view(torch.int32)
+    zeros = torch.zeros(512, dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 2 * cus, 2000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    flops = blocks * 4 * iters * 8 * 16 * 16 * 128 * 2.0
+    res = {}
+    for name, a, b, fmas in (("mfma_only", a_codes, b_codes, 0), ("mfma_plus_4_fma", a_codes, b_codes, 4),
+                             ("mfma_only_zero_operands", zeros, zeros, 0)):
+        best = None
+        for rep in range(4):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rc = f(a.data_ptr(), b.data_ptr(), out.data_ptr(), fmas, blocks, iters, stream)
+            e1.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"fp8blk_bench_mfma_ceiling returned {rc}")
+            t = e0.elapsed_time(e1) * 1e-3
+            if rep > 0:
+                best = t if best is None else min(best, t)
+        res[name] = flops / best / 1e12
+    res["unit"] = "TFLOP/s"
+    res["operands"] = "first 2 KB of the quantized activations and weights"
+    return res
 
 
 def cpu_baseline(syn, M, N, K):

@@ -12,6 +12,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfp8blk.so")
 SOURCES = ["api.hip", "quantize.hip", "gemm.hip"]
+# measurement-only kernels, loaded by bench.py alone (kept out of the product library)
+BENCH_LIB = os.path.join(PKG, "libfp8blk_bench.so")
+BENCH_SOURCES = ["bench_ceiling.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -32,9 +35,15 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into one shared library; returns its path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+    """Compile the product library (every HIP source of the path) and the
+    measurement-only library; returns the product library's path."""
+    _compile(BENCH_SOURCES, BENCH_LIB, verbose)
+    return _compile(SOURCES, LIB, verbose)
+
+
+def _compile(sources, lib, verbose):
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = lib + ".tmp"
     cmd = [HIPCC] + FLAGS + srcs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -45,8 +54,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
