@@ -9,6 +9,7 @@ It is a plain, slow, NumPy implementation written straight from the pages:
 
 * ``e4m3``  -- the OCP E4M3 value table and a table-driven round-to-nearest-even
   encoder that saturates at +-448;
+* ``e5m2``  -- the same for OCP E5M2 (largest value 57344, saturating);
 * ``quant`` -- the amax / scale / cast quantizer for every group shape the path
   uses (per tensor, 1x128, 128x128, KV head x 128 tokens) and the KV dequantizer;
 * ``gemm``  -- the block-scaled GEMM as dequantize-to-fp64 followed by a plain
@@ -25,4 +26,4 @@ Parity status: every function here is pinned by tests under ``tests/``
 invariants and brute force; none is "parity unpinned".
 """
 
-from . import e4m3, quant, gemm  # noqa: F401
+from . import e4m3, e5m2, quant, gemm  # noqa: F401

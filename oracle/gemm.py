@@ -14,7 +14,8 @@ activations may carry one scale per 128-channel group. So
 
     y[m, n] = sum_j  s_a[m, j] * s_w[n // 128, j] * sum_{k in block j} qa[m, k] * qw[n, k]
 
-with qa, qw the decoded E4M3 values, i.e. y = A_hat . W_hat^T with
+with qa, qw the decoded FP8 values (E4M3, or E5M2 for either operand: [FP8]
+section "FP8 是什么", format table), i.e. y = A_hat . W_hat^T with
 A_hat = decode(qa) * s_a and W_hat = decode(qw) * s_w. With a per-tensor scale
 the scale is one number for the whole operand.
 
@@ -33,26 +34,27 @@ GROUP_1x128 = "group_1x128"
 BLOCK_128x128 = "block_128x128"
 
 
-def dequant_activations(qa, sa, gran: str) -> np.ndarray:
+def dequant_activations(qa, sa, gran: str, fmt: str = "e4m3") -> np.ndarray:
     """A_hat [M, K] in float64. gran: per_tensor (sa [1]) or group_1x128 (sa [M, ceil(K/128)])."""
     if gran == PER_TENSOR:
-        return quant.dequantize_grid(qa, np.asarray(sa).reshape(1), 1, 1)
+        return quant.dequantize_grid(qa, np.asarray(sa).reshape(1), 1, 1, fmt)
     if gran == GROUP_1x128:
-        return quant.dequantize_grid(qa, sa, 1, quant.GROUP)
+        return quant.dequantize_grid(qa, sa, 1, quant.GROUP, fmt)
     raise ValueError(gran)
 
 
-def dequant_weights(qw, sw, gran: str) -> np.ndarray:
+def dequant_weights(qw, sw, gran: str, fmt: str = "e4m3") -> np.ndarray:
     """W_hat [N, K] in float64. gran: per_tensor (sw [1]) or block_128x128
     (sw [ceil(N/128), ceil(K/128)])."""
     if gran == PER_TENSOR:
-        return quant.dequantize_grid(qw, np.asarray(sw).reshape(1), 1, 1)
+        return quant.dequantize_grid(qw, np.asarray(sw).reshape(1), 1, 1, fmt)
     if gran == BLOCK_128x128:
-        return quant.dequantize_grid(qw, sw, quant.GROUP, quant.GROUP)
+        return quant.dequantize_grid(qw, sw, quant.GROUP, quant.GROUP, fmt)
     raise ValueError(gran)
 
 
-def block_gemm(qa, sa, gran_a: str, qw, sw, gran_w: str, rows=None, cols=None) -> tuple:
+def block_gemm(qa, sa, gran_a: str, qw, sw, gran_w: str, rows=None, cols=None,
+               fmt_a: str = "e4m3", fmt_w: str = "e4m3") -> tuple:
     """Returns (y, T), both float64 [M, N] (or [len(rows), len(cols)] when
     ``rows``/``cols`` select a subset of outputs).
 
@@ -77,12 +79,12 @@ def block_gemm(qa, sa, gran_a: str, qw, sw, gran_w: str, rows=None, cols=None) -
         if gran_w == BLOCK_128x128:
             # one row of the block grid per selected weight row
             w_scales = np.repeat(sw[cols // g], g, axis=1)[:, :K].astype(np.float64)
-            w = quant.e4m3.decode(qw) * w_scales
+            w = quant.fmt_module(fmt_w).decode(qw) * w_scales
         else:
-            w = dequant_weights(qw, sw, gran_w)
+            w = dequant_weights(qw, sw, gran_w, fmt_w)
     else:
-        w = dequant_weights(qw, sw, gran_w)
-    a = dequant_activations(qa, sa, gran_a)
+        w = dequant_weights(qw, sw, gran_w, fmt_w)
+    a = dequant_activations(qa, sa, gran_a, fmt_a)
     y = a @ w.T
     t = np.abs(a) @ np.abs(w).T
     return y, t

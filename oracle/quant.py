@@ -34,25 +34,42 @@ Readings taken where the pages are silent:
 * Denormals are kept (no flush to zero).
 * The KV dequantizer computes fl32(decode(q) * s) and rounds that to bf16
   with round-to-nearest-even.
+
+Formats: every function takes ``fmt`` = "e4m3" (default) or "e5m2". E5M2 ([FP8]
+section "FP8 是什么", format table; [LONG] section 1, E5M2 KV cache) runs the same
+steps with its own largest value: s = a / 57344 and codes from the E5M2 grid.
 """
 
 import numpy as np
 
-from . import e4m3
+from . import e4m3, e5m2
+
+FORMATS = {"e4m3": e4m3, "e5m2": e5m2}
+FORMAT_MAX = {"e4m3": e4m3.E4M3_MAX, "e5m2": e5m2.E5M2_MAX}
+
+
+def fmt_module(fmt: str):
+    """The table module of an FP8 format name."""
+    if fmt not in FORMATS:
+        raise ValueError(f"unknown fp8 format {fmt!r}")
+    return FORMATS[fmt]
 
 GROUP = 128
 
 
-def scale_of(amax) -> np.ndarray:
-    """s = fl32(amax / 448) as a correctly rounded fp32 division."""
-    return np.asarray(amax, dtype=np.float32) / np.float32(e4m3.E4M3_MAX)
+def scale_of(amax, fmt: str = "e4m3") -> np.ndarray:
+    """s = fl32(amax / max_fmt) (448 for E4M3, 57344 for E5M2) as a correctly
+    rounded fp32 division."""
+    fmt_module(fmt)
+    return np.asarray(amax, dtype=np.float32) / np.float32(FORMAT_MAX[fmt])
 
 
-def cast(x32: np.ndarray, s32: np.ndarray) -> np.ndarray:
+def cast(x32: np.ndarray, s32: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
     """Codes of fl32(x / s), elementwise; ``s`` broadcasts against ``x``.
 
     Where s == 0 the code is the sign of x with a zero magnitude.
     """
+    enc = fmt_module(fmt).encode
     x32 = np.asarray(x32, dtype=np.float32)
     s32 = np.broadcast_to(np.asarray(s32, dtype=np.float32), x32.shape)
     out = np.empty(x32.shape, dtype=np.uint8)
@@ -67,7 +84,7 @@ def cast(x32: np.ndarray, s32: np.ndarray) -> np.ndarray:
         with np.errstate(divide="ignore", invalid="ignore"):
             quot = xs / np.where(zero, np.float32(1), ss)   # fp32 / fp32, IEEE
         quot = np.where(zero, np.where(np.signbit(xs), np.float32(-0.0), np.float32(0.0)), quot)
-        flat_o[lo:lo + step] = e4m3.encode(quot)
+        flat_o[lo:lo + step] = enc(quot)
     return out
 
 
@@ -83,15 +100,15 @@ def _pad_to(a: np.ndarray, axis: int, mult: int) -> np.ndarray:
     return np.pad(a, widths)
 
 
-def quantize_per_tensor(x) -> tuple:
+def quantize_per_tensor(x, fmt: str = "e4m3") -> tuple:
     """One scale for the whole tensor. Returns (codes uint8 like x, s float32 [1])."""
     x32 = np.asarray(x, dtype=np.float32)
     amax = np.max(np.abs(x32)) if x32.size else np.float32(0)
-    s = scale_of(amax).reshape(1)
-    return cast(x32, s[0]), s
+    s = scale_of(amax, fmt).reshape(1)
+    return cast(x32, s[0], fmt), s
 
 
-def quantize_group_1x128(x) -> tuple:
+def quantize_group_1x128(x, fmt: str = "e4m3") -> tuple:
     """x: [rows, cols]. Group = one row x 128 consecutive columns.
 
     Returns (codes uint8 [rows, cols], s float32 [rows, ceil(cols/128)]).
@@ -101,12 +118,12 @@ def quantize_group_1x128(x) -> tuple:
     g = -(-cols // GROUP)
     xp = _pad_to(x32, 1, GROUP).reshape(rows, g, GROUP)
     amax = np.max(np.abs(xp), axis=2)
-    s = scale_of(amax)
+    s = scale_of(amax, fmt)
     s_full = np.repeat(s, GROUP, axis=1)[:, :cols]
-    return cast(x32, s_full), s
+    return cast(x32, s_full, fmt), s
 
 
-def quantize_block_128x128(x) -> tuple:
+def quantize_block_128x128(x, fmt: str = "e4m3") -> tuple:
     """x: [rows, cols] (a weight W in R^{N x K}). Group = 128 x 128 block.
 
     Returns (codes uint8 [rows, cols], s float32 [ceil(rows/128), ceil(cols/128)]).
@@ -116,12 +133,12 @@ def quantize_block_128x128(x) -> tuple:
     gr, gc = -(-rows // GROUP), -(-cols // GROUP)
     xp = _pad_to(_pad_to(x32, 0, GROUP), 1, GROUP).reshape(gr, GROUP, gc, GROUP)
     amax = np.max(np.abs(xp), axis=(1, 3))
-    s = scale_of(amax)
+    s = scale_of(amax, fmt)
     s_full = np.repeat(np.repeat(s, GROUP, axis=0), GROUP, axis=1)[:rows, :cols]
-    return cast(x32, s_full), s
+    return cast(x32, s_full, fmt), s
 
 
-def kv_quantize(kv, token_block: int = GROUP) -> tuple:
+def kv_quantize(kv, token_block: int = GROUP, fmt: str = "e4m3") -> tuple:
     """kv: [heads, tokens, head_dim]. Group = one head x ``token_block``
     consecutive tokens x all of head_dim.
 
@@ -133,9 +150,9 @@ def kv_quantize(kv, token_block: int = GROUP) -> tuple:
     nb = -(-t // token_block)
     xp = _pad_to(x32, 1, token_block).reshape(h, nb, token_block, d)
     amax = np.max(np.abs(xp), axis=(2, 3))
-    s = scale_of(amax)
+    s = scale_of(amax, fmt)
     s_full = np.repeat(s, token_block, axis=1)[:, :t, None]
-    return cast(x32, s_full), s
+    return cast(x32, s_full, fmt), s
 
 
 def f32_to_bf16_bits(x32) -> np.ndarray:
@@ -166,7 +183,7 @@ def bf16_bits_to_f32(b) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def kv_dequantize(q, s, token_block: int = GROUP) -> np.ndarray:
+def kv_dequantize(q, s, token_block: int = GROUP, fmt: str = "e4m3") -> np.ndarray:
     """bf16(fl32(decode(q) * s)) with the scale of each (head, token block).
 
     q: uint8 [heads, tokens, head_dim]; s: float32 [heads, ceil(tokens/token_block)].
@@ -177,18 +194,19 @@ def kv_dequantize(q, s, token_block: int = GROUP) -> np.ndarray:
     q = np.asarray(q, dtype=np.uint8)
     h, t, d = q.shape
     s_full = np.repeat(np.asarray(s, dtype=np.float32), token_block, axis=1)[:, :t, None]
-    prod = (e4m3.decode(q) * s_full.astype(np.float64)).astype(np.float32)
+    prod = (fmt_module(fmt).decode(q) * s_full.astype(np.float64)).astype(np.float32)
     return f32_to_bf16_bits(prod)
 
 
-def dequantize_grid(q, s, group_rows: int, group_cols: int) -> np.ndarray:
+def dequantize_grid(q, s, group_rows: int, group_cols: int, fmt: str = "e4m3") -> np.ndarray:
     """fp64 x_hat = decode(q) * s for a 2-D code array with a scale grid of
     ``group_rows`` x ``group_cols`` groups (a per-tensor grid is one group
     spanning everything). Exact in float64."""
     q = np.asarray(q, dtype=np.uint8)
     rows, cols = q.shape
     s = np.asarray(s, dtype=np.float32).astype(np.float64)
+    dec = fmt_module(fmt).decode
     if s.size == 1:
-        return e4m3.decode(q) * s.reshape(())
+        return dec(q) * s.reshape(())
     s_full = np.repeat(np.repeat(s, group_rows, axis=0), group_cols, axis=1)[:rows, :cols]
-    return e4m3.decode(q) * s_full
+    return dec(q) * s_full

@@ -171,3 +171,52 @@ def test_tolerance_base_dominates():
     ref_t = t[np.ix_([5, 0], [129, 3])]
     assert np.all(np.abs(sub_y - y[np.ix_([5, 0], [129, 3])]) <= 1e-13 * ref_t)
     assert np.all(np.abs(sub_t - ref_t) <= 1e-13 * ref_t)
+
+
+def _rand_codes_fmt(rng, shape, fmt):
+    c = rng.integers(0, 256, size=shape, dtype=np.int64)
+    if fmt == "e4m3":
+        c = np.where((c & 0x7F) == 0x7F, c ^ 0x01, c)
+    else:
+        c = np.where((c & 0x7F) >= 0x7C, c & 0xBB, c)   # no inf / NaN codes
+    return c.astype(np.uint8)
+
+
+@pytest.mark.parametrize("fmt_a,fmt_w", [("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3")])
+def test_bruteforce_exact_rational_e5m2_operands(fmt_a, fmt_w):
+    """E5M2 operands ([FP8] section "FP8 是什么", format table): the same block sum
+    with each operand decoded from its own format, against exact fractions."""
+    from oracle import quant
+    rng = np.random.default_rng(24)
+    M, N, K = 3, 4, 256
+    qa = _rand_codes_fmt(rng, (M, K), fmt_a)
+    qw = _rand_codes_fmt(rng, (N, K), fmt_w)
+    sa = _rand_scales(rng, (M, 2))
+    sw = _rand_scales(rng, (1, 2))
+    y, t = gemm.block_gemm(qa, sa, gemm.GROUP_1x128, qw, sw, gemm.BLOCK_128x128, fmt_a=fmt_a, fmt_w=fmt_w)
+    da = quant.fmt_module(fmt_a).decode(qa)
+    dw = quant.fmt_module(fmt_w).decode(qw)
+    assert np.all(np.isfinite(da)) and np.all(np.isfinite(dw))
+    for m in range(M):
+        for n in range(N):
+            tot = Fraction(0)
+            for j in range(2):
+                p = sum((Fraction(float(da[m, k])) * Fraction(float(dw[n, k])) for k in range(128 * j, 128 * (j + 1))),
+                        Fraction(0))
+                tot += Fraction(float(sa[m, j])) * Fraction(float(sw[0, j])) * p
+            assert abs(Fraction(float(y[m, n])) - tot) <= Fraction(float(t[m, n])) * Fraction(1, 1 << 45)
+
+
+def test_identity_weight_reproduces_every_e5m2_code():
+    """E4M3 identity weight (0x38 = 1.0) times E5M2 activations holding all 248
+    finite codes reproduces their decoded values exactly."""
+    from oracle import e5m2
+    codes = e5m2.finite_codes()
+    K = 256
+    qa = np.zeros((1, K), dtype=np.uint8)
+    qa[0, :codes.size] = codes
+    qw = np.zeros((K, K), dtype=np.uint8)
+    np.fill_diagonal(qw, 0x38)
+    one = np.ones(1, dtype=np.float32)
+    y, _ = gemm.block_gemm(qa, one, gemm.PER_TENSOR, qw, one, gemm.PER_TENSOR, fmt_a="e5m2", fmt_w="e4m3")
+    assert np.array_equal(y[0, :codes.size], e5m2.DECODE[codes])
