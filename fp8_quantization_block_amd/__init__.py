@@ -9,9 +9,11 @@ kernels; there is no CPU fallback, and a missing or unloadable library raises.
 Entry points (same names as the C ABI):
 
 * ``fp8_quantize(x, granularity, fmt="e4m3", scale_layout="row")`` -> (codes uint8, scales fp32)
-* ``fp8_block_gemm(qa, sa, gran_a, qw, sw, gran_w, out_dtype=torch.bfloat16, sa_layout=...)``
-* ``fp8_kv_quantize(kv, token_block=128)`` -> (codes uint8, scales fp32)
-* ``fp8_kv_dequantize(q, scales, token_block=128)`` -> bf16
+* ``fp8_block_gemm(qa, sa, gran_a, qw, sw, gran_w, out_dtype=torch.bfloat16, fmt_a="e4m3", fmt_w="e4m3")``
+* ``fp8_kv_quantize(kv, token_block=128, fmt="e4m3")`` -> (codes uint8, scales fp32)
+* ``fp8_kv_dequantize(q, scales, token_block=128, fmt="e4m3")`` -> bf16
+
+``fmt`` is "e4m3" (largest value 448) or "e5m2" (largest value 57344).
 """
 
 import ctypes
@@ -88,7 +90,7 @@ def _require_cuda(*ts):
 
 def fp8_quantize(x: torch.Tensor, granularity: str, fmt: str = "e4m3", scale_layout: str = "row",
                  out: torch.Tensor = None, scales: torch.Tensor = None):
-    """Quantize a 2-D bf16/fp32 tensor to E4M3 codes (uint8) and fp32 scales.
+    """Quantize a 2-D bf16/fp32 tensor to FP8 codes of format ``fmt`` (uint8) and fp32 scales.
 
     granularity: "per_tensor" (scales [1]), "group_1x128" (scales [rows, ceil(cols/128)]),
     "block_128x128" (scales [ceil(rows/128), ceil(cols/128)]).
@@ -131,9 +133,11 @@ def fp8_quantize(x: torch.Tensor, granularity: str, fmt: str = "e4m3", scale_lay
 
 
 def fp8_block_gemm(qa: torch.Tensor, sa: torch.Tensor, gran_a: str, qw: torch.Tensor, sw: torch.Tensor,
-                   gran_w: str, out_dtype=torch.bfloat16, out: torch.Tensor = None):
-    """C = A . W^T from E4M3 codes: qa [M, K] uint8 with scales sa, qw [N, K]
-    uint8 with scales sw; returns C [M, N] in bf16 (or fp32)."""
+                   gran_w: str, out_dtype=torch.bfloat16, out: torch.Tensor = None,
+                   fmt_a: str = "e4m3", fmt_w: str = "e4m3"):
+    """C = A . W^T from FP8 codes: qa [M, K] uint8 (format fmt_a) with scales
+    sa, qw [N, K] uint8 (format fmt_w) with scales sw; returns C [M, N] in bf16
+    (or fp32)."""
     lib = load_library()
     _require_cuda(qa, sa, qw, sw)
     M, K = qa.shape
@@ -149,7 +153,7 @@ def fp8_block_gemm(qa: torch.Tensor, sa: torch.Tensor, gran_a: str, qw: torch.Te
     swn = sw.stride(0) if sw.dim() == 2 else 0
     swk = sw.stride(1) if sw.dim() == 2 else 0
     _check(lib.fp8_block_gemm(M, N, K, _ptr(qa), qa.stride(0), _ptr(sa), ga, sam, sak,
-                              _ptr(qw), qw.stride(0), _ptr(sw), gw, swn, swk, E4M3, E4M3,
+                              _ptr(qw), qw.stride(0), _ptr(sw), gw, swn, swk, _FMT[fmt_a], _FMT[fmt_w],
                               _ptr(out), cdt, out.stride(0), _stream(qa)))
     return out
 

@@ -56,8 +56,7 @@ constexpr int64_t kMaxDim = (int64_t)1 << 31;   // indices are kept in 32 bits i
 constexpr int64_t kMaxLdCodes = (int64_t)1 << 23;
 
 fp8blk_status check_format(fp8blk_format fmt, const char* what) {
-  if (fmt == FP8BLK_E4M3) return FP8BLK_OK;
-  if (fmt == FP8BLK_E5M2) return fail(FP8BLK_EUNSUPPORTED, "%s: E5M2 is not implemented", what);
+  if (fmt == FP8BLK_E4M3 || fmt == FP8BLK_E5M2) return FP8BLK_OK;
   return fail(FP8BLK_EINVAL, "%s: unknown fp8 format %d", what, (int)fmt);
 }
 
@@ -130,6 +129,7 @@ fp8blk_status fp8_quantize(const void* x, fp8blk_dtype x_dtype, int64_t rows, in
   a.cols = cols;
   a.ld_x = ld_x;
   a.gran = (int)gran;
+  a.fmt = (int)fmt;
   a.q = q;
   a.ld_q = ld_q;
   a.scales = scales;
@@ -198,6 +198,8 @@ fp8blk_status fp8_block_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, 
   g.c = c;
   g.c_dtype = (int)c_dtype;
   g.ldc = ldc;
+  g.fmt_a = (int)fmt_a;
+  g.fmt_b = (int)fmt_b;
   return hip_status(fp8blk::launch_block_gemm(g, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -244,6 +246,7 @@ fp8blk_status fp8_kv_quantize(const void* kv, int64_t heads, int64_t tokens, int
   a.stride_head = stride_head;
   a.stride_token = stride_token;
   a.token_block = token_block;
+  a.fmt = (int)fmt;
   a.q = q;
   a.scales = scales;
   return hip_status(fp8blk::launch_kv_quantize(a, static_cast<hipStream_t>(stream)), fn);
@@ -271,6 +274,7 @@ fp8blk_status fp8_kv_dequantize(const uint8_t* q, const float* scales, int64_t h
   a.tokens = tokens;
   a.head_dim = head_dim;
   a.token_block = token_block;
+  a.fmt = (int)fmt;
   a.out = out_bf16;
   return hip_status(fp8blk::launch_kv_dequantize(a, static_cast<hipStream_t>(stream)), fn);
 }

@@ -1,16 +1,22 @@
 // Device helpers shared by the fp8blk HIP kernels (gfx950 only).
 //
-// E4M3 here is OCP E4M3 as fixed by [FP8] (wangyu.me, "大语言模型量化技术（五）：FP8"),
-// section "FP8 是什么": largest finite 448, smallest normal 2^-6, smallest
-// subnormal 2^-9, no infinity, saturation at +-448.
+// The FP8 formats are OCP E4M3 and OCP E5M2 as fixed by [FP8] (wangyu.me,
+// "大语言模型量化技术（五）：FP8"), section "FP8 是什么", format table: E4M3 has
+// largest finite 448, smallest normal 2^-6, smallest subnormal 2^-9, no
+// infinity, saturation at +-448; E5M2 has largest finite 57344, smallest
+// normal 2^-14, smallest subnormal 2^-16 (its infinity and NaN codes are never
+// produced: the quantizer saturates at +-57344 as well).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "internal.h"
+
 namespace fp8blk {
 
 constexpr float kE4M3Max = 448.0f;
+constexpr float kE5M2Max = 57344.0f;
 
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32 bit helpers
@@ -46,32 +52,65 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 }
 
 // ---------------------------------------------------------------------------
-// fp32 -> E4M3 with round-to-nearest-even and saturation.
+// fp32 -> FP8 with round-to-nearest-even and saturation, and FP8 -> fp32.
 //
-// The hardware conversion v_cvt_pk_fp8_f32 of gfx950 writes OCP E4M3 codes with
-// round-to-nearest-even; clamping to +-448 first (v_med3_f32) gives the
-// saturating behaviour the format requires. tests/test_gpu_quantize.py checks
-// this against the CPU oracle on every fp32 value in [-448, 448].
+// The hardware conversions v_cvt_pk_fp8_f32 (E4M3) and v_cvt_pk_bf8_f32 (E5M2)
+// of gfx950 write OCP codes with round-to-nearest-even; clamping to the
+// format's largest value first (v_med3_f32) gives the saturating behaviour of
+// the quantizer. tests/test_gpu_quantize.py and tests/test_gpu_e5m2.py check
+// this against the CPU oracle on every fp32 value in [-448, 448] and
+// [-57344, 57344]. v_cvt_pk_f32_fp8 / v_cvt_pk_f32_bf8 decode codes exactly.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float clamp448(float v) {
-  return __builtin_amdgcn_fmed3f(v, -kE4M3Max, kE4M3Max);
+template <int kFmt>
+struct Fp8;
+
+template <>
+struct Fp8<FMT_E4M3> {
+  static constexpr float kMax = kE4M3Max;
+  // four values with |v| <= 448 (or a hair above) -> four codes, no clamp
+  static __device__ __forceinline__ uint32_t pack4_raw(float a, float b, float c, float d) {
+    uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
+  }
+  // codes 0,1 (kHi = false) or 2,3 (kHi = true) of a word -> fp32
+  template <bool kHi>
+  static __device__ __forceinline__ auto decode2(uint32_t w) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, kHi);
+  }
+};
+
+template <>
+struct Fp8<FMT_E5M2> {
+  static constexpr float kMax = kE5M2Max;
+  static __device__ __forceinline__ uint32_t pack4_raw(float a, float b, float c, float d) {
+    uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, d, (int)w, true);
+  }
+  template <bool kHi>
+  static __device__ __forceinline__ auto decode2(uint32_t w) {
+    return __builtin_amdgcn_cvt_pk_f32_bf8((int)w, kHi);
+  }
+};
+
+template <int kFmt>
+__device__ __forceinline__ float clamp_max(float v) {
+  return __builtin_amdgcn_fmed3f(v, -Fp8<kFmt>::kMax, Fp8<kFmt>::kMax);
 }
 
-// Four fp32 values -> four E4M3 codes packed little-endian in one word.
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
-  w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), (int)w, true);
-  return w;
+// Four fp32 values -> four codes packed little-endian in one word, saturating.
+template <int kFmt>
+__device__ __forceinline__ uint32_t pack4_sat(float a, float b, float c, float d) {
+  return Fp8<kFmt>::pack4_raw(clamp_max<kFmt>(a), clamp_max<kFmt>(b), clamp_max<kFmt>(c), clamp_max<kFmt>(d));
 }
 
 // ---------------------------------------------------------------------------
 // Group scale and the bit-exact cast of a group's elements.
 //
-// The code of x is E4M3(fl32(x / s)) with the IEEE correctly rounded fp32
+// The code of x is FP8(fl32(x / s)) with the IEEE correctly rounded fp32
 // quotient; the per-element division is replaced by multiplications with a
 // per-group reciprocal r: v_rcp_f32(s) (1 ulp) refined by one Newton step.
 //
-// bf16 inputs (cast4_bf16): q = fl32(x r), then one residual correction
+// bf16 inputs to E4M3 (cast4_bf16): q = fl32(x r), then one residual correction
 // q' = q - fl32(s q - x) r with fused multiply-adds. An exhaustive sweep over
 // every bf16 amax and every bf16 |x| <= amax whose scale lies in
 // [2^-64, 2^64] finds the code of q' equal to the code of fl32(x / s) in all
@@ -80,26 +119,31 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
 // oracle. The residual is negated so that x = -0 keeps its sign. Groups whose
 // scale lies outside that range, or is zero, divide exactly.
 //
-// fp32 inputs (cast4_f32): the products fl32(x rl) and fl32(x rh) with
+// fp32 inputs, and every input to E5M2 (cast4_f32): the products fl32(x rl) and fl32(x rh) with
 // rl = r (1 - 2^-20), rh = r (1 + 2^-20) bracket fl32(x / s) strictly in
 // magnitude (their relative offsets exceed 2^-20 - 2^-22 - 3 * 2^-24 > 2^-24,
 // the fp32 rounding bound) whenever the quotient is an fp32 normal.
 // Round-to-nearest is monotone, so when both brackets give the same code it is
 // the code of fl32(x / s); otherwise the element takes the exact division.
-// The lower bracket never exceeds 448 (|x| <= amax), where the hardware
-// conversion is exact; the upper one may exceed it by a hair, and if the
-// conversion then disagrees the exact path decides. Quotients below the fp32
+// For E4M3 the brackets are converted without a clamp: the lower one never
+// exceeds 448 (|x| <= amax), where the hardware conversion is exact; the upper
+// one may exceed it by a hair, and if the conversion then disagrees the exact
+// path decides. For E5M2 both are clamped to +-57344 first (a monotone,
+// saturating conversion), so the argument holds unchanged. The E5M2 fast path
+// for bf16 inputs is this bracket too: the residual-corrected quotient's code
+// equality was established for the E4M3 grid only. Quotients below the fp32
 // normal range give code 0 (signed) on every path. Groups whose scale is zero
 // or an fp32 subnormal always take the exact division.
 // ---------------------------------------------------------------------------
 struct GroupScale {
-  float s;  // fl32(amax / 448)
+  float s;  // fl32(amax / max_fmt)
   float r;  // ~ 1 / s, Newton-refined
 };
 
+template <int kFmt>
 __device__ __forceinline__ GroupScale make_group_scale(uint32_t amax_bits) {
   GroupScale g;
-  g.s = __uint_as_float(amax_bits) / kE4M3Max;   // IEEE correctly rounded division
+  g.s = __uint_as_float(amax_bits) / Fp8<kFmt>::kMax;   // IEEE correctly rounded division
   const float r0 = __builtin_amdgcn_rcpf(g.s);   // 1 ulp
   g.r = __builtin_fmaf(__builtin_fmaf(-g.s, r0, 1.0f), r0, r0);
   return g;
@@ -111,16 +155,10 @@ __device__ __forceinline__ float exact_quotient(float x, float s) {
   return x / s;   // IEEE correctly rounded division
 }
 
-// Four fp32 values (|v| <= 448 or slightly above) -> four E4M3 codes, no clamp.
-__device__ __forceinline__ uint32_t e4m3x4_raw(float a, float b, float c, float d) {
-  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
-  return w;
-}
-
+template <int kFmt>
 __device__ __forceinline__ uint32_t exact4(const GroupScale& g, float a, float b, float c, float d) {
-  return e4m3x4(exact_quotient(a, g.s), exact_quotient(b, g.s), exact_quotient(c, g.s),
-                exact_quotient(d, g.s));
+  return pack4_sat<kFmt>(exact_quotient(a, g.s), exact_quotient(b, g.s), exact_quotient(c, g.s),
+                         exact_quotient(d, g.s));
 }
 
 __device__ __forceinline__ bool bf16_fast_ok(const GroupScale& g) {
@@ -133,24 +171,36 @@ __device__ __forceinline__ float quotient_bf16(const GroupScale& g, float x) {
   return __builtin_fmaf(-e, g.r, q);
 }
 
-// Codes of four elements of one group whose values are bf16 numbers.
-__device__ __forceinline__ uint32_t cast4_bf16(const GroupScale& g, float a, float b, float c, float d) {
-  if (__builtin_expect(bf16_fast_ok(g), 1))
-    return e4m3x4_raw(quotient_bf16(g, a), quotient_bf16(g, b), quotient_bf16(g, c),
-                      quotient_bf16(g, d));
-  return exact4(g, a, b, c, d);
-}
-
 // Codes of four elements of one group of arbitrary fp32 values.
+template <int kFmt>
 __device__ __forceinline__ uint32_t cast4_f32(const GroupScale& g, float a, float b, float c, float d) {
   if (g.s >= 0x1.0p-126f) {
     const float rl = g.r * (1.0f - 0x1.0p-20f);
     const float rh = g.r * (1.0f + 0x1.0p-20f);
-    const uint32_t lo = e4m3x4_raw(a * rl, b * rl, c * rl, d * rl);
-    const uint32_t hi = e4m3x4_raw(a * rh, b * rh, c * rh, d * rh);
+    uint32_t lo, hi;
+    if constexpr (kFmt == FMT_E4M3) {
+      lo = Fp8<kFmt>::pack4_raw(a * rl, b * rl, c * rl, d * rl);
+      hi = Fp8<kFmt>::pack4_raw(a * rh, b * rh, c * rh, d * rh);
+    } else {
+      lo = pack4_sat<kFmt>(a * rl, b * rl, c * rl, d * rl);
+      hi = pack4_sat<kFmt>(a * rh, b * rh, c * rh, d * rh);
+    }
     if (__builtin_expect(lo == hi, 1)) return lo;
   }
-  return exact4(g, a, b, c, d);
+  return exact4<kFmt>(g, a, b, c, d);
+}
+
+// Codes of four elements of one group whose values are bf16 numbers.
+template <int kFmt>
+__device__ __forceinline__ uint32_t cast4_bf16(const GroupScale& g, float a, float b, float c, float d) {
+  if constexpr (kFmt == FMT_E4M3) {
+    if (__builtin_expect(bf16_fast_ok(g), 1))
+      return Fp8<kFmt>::pack4_raw(quotient_bf16(g, a), quotient_bf16(g, b), quotient_bf16(g, c),
+                                  quotient_bf16(g, d));
+    return exact4<kFmt>(g, a, b, c, d);
+  } else {
+    return cast4_f32<kFmt>(g, a, b, c, d);
+  }
 }
 
 // Max over the 8 lanes of each half of a DPP row; every lane of the half gets it.

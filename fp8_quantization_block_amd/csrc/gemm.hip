@@ -8,6 +8,10 @@
 // multiplied by their scales); [MIXED] charles2530.github.io, "量化：FP8 与混合精度推理",
 // section "混合精度才是生产形态" (low-precision products, higher-precision sums).
 //
+// Operands are E4M3 or E5M2 codes, each operand in its own format ([FP8]
+// section "FP8 是什么", format table): the f8f6f4 MFMA decodes either format, so
+// the kernels are instantiated per (format of A, format of B) pair.
+//
 // Prefill kernel design (gfx950):
 // * One v_mfma_f32_16x16x128_f8f6f4 covers exactly one 128-deep scale block,
 //   so every MFMA starts from zero and its 16x16 fp32 result is promoted into
@@ -193,7 +197,7 @@ __device__ __forceinline__ void promote(const Pipe& pp, const v4f (&comb)[4], in
 
 // One K block of a wave: 4 activation subtiles x 8 weight subtiles. `first`:
 // no previous block to finish.
-template <bool first>
+template <bool first, int kFa, int kFb>
 __device__ __forceinline__ void mma_block(const Plan& pl, const uint8_t* ta, const uint8_t* tb,
                                           const float* ts, Pipe& pp, v4f (&acc)[4][8]) {
   // reads for the first MFMA first, then the rest of the activation fragments
@@ -214,7 +218,7 @@ __device__ __forceinline__ void mma_block(const Plan& pl, const uint8_t* ta, con
     const int ni = t >> 2, mi = t & 3;
     if (mi == 0 && ni < 7)
       bf[(ni + 1) & 1] = read_frag(tb, pl.b_lo + (ni + 1) * 2048, pl.b_hi + (ni + 1) * 2048);
-    pp.part[t % kRing] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf[ni & 1], zero, 0, 0, 0, 0, 0, 0);
+    pp.part[t % kRing] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf[ni & 1], zero, kFa, kFb, 0, 0, 0, 0);
     if (t >= kLag) {
       promote(pp, pp.comb, t - kLag, acc);
     } else if (!first) {
@@ -241,13 +245,13 @@ __device__ __forceinline__ void drain(const Pipe& pp, v4f (&acc)[4][8]) {
 // wait for the copies (the only vector memory operations in flight), barrier.
 // The block index of the copy is clamped to the last block (the tail copy
 // lands in a stage nobody reads again).
-template <bool first>
+template <bool first, int kFa, int kFb>
 __device__ __forceinline__ void k_step(const Plan& pl, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                        __amdgpu_buffer_rsrc_t rs, int kb, int nk, const uint8_t* ca,
                                        const uint8_t* cb, const float* cs, uint8_t* na, uint8_t* nb,
                                        float* ns, float* sink, bool active, Pipe& pp, v4f (&acc)[4][8]) {
   issue(pl, ra, rb, rs, min(kb + 1, nk - 1), na, nb, ns, sink);
-  if (active) mma_block<first>(pl, ca, cb, cs, pp, acc);
+  if (active) mma_block<first, kFa, kFb>(pl, ca, cb, cs, pp, acc);
   wait_vm<0>();
   raw_barrier();
 }
@@ -256,6 +260,7 @@ __device__ __forceinline__ void k_step(const Plan& pl, __amdgpu_buffer_rsrc_t ra
 // stages' tiles and scale slots, the sink, and the arrays they read) is a
 // distinct non-aliasing parameter, so that the compiler can tell that reading
 // one stage does not depend on the copies in flight into the other.
+template <int kFa, int kFb>
 __device__ __forceinline__ void k_loop(const Plan& pl, const uint8_t* __restrict__ ga, uint32_t ga_bytes,
                                        const uint8_t* __restrict__ gb, uint32_t gb_bytes,
                                        const float* __restrict__ gs, uint32_t gs_bytes,
@@ -270,17 +275,17 @@ __device__ __forceinline__ void k_loop(const Plan& pl, const uint8_t* __restrict
   issue(pl, ra, rb, rs, 0, a0, b0, s0, sink);
   wait_vm<0>();
   raw_barrier();
-  k_step<true>(pl, ra, rb, rs, 0, nk, a0, b0, s0, a1, b1, s1, sink, active, pp, acc);
+  k_step<true, kFa, kFb>(pl, ra, rb, rs, 0, nk, a0, b0, s0, a1, b1, s1, sink, active, pp, acc);
   int kb = 1;
   for (; kb + 1 < nk; kb += 2) {
-    k_step<false>(pl, ra, rb, rs, kb, nk, a1, b1, s1, a0, b0, s0, sink, active, pp, acc);
-    k_step<false>(pl, ra, rb, rs, kb + 1, nk, a0, b0, s0, a1, b1, s1, sink, active, pp, acc);
+    k_step<false, kFa, kFb>(pl, ra, rb, rs, kb, nk, a1, b1, s1, a0, b0, s0, sink, active, pp, acc);
+    k_step<false, kFa, kFb>(pl, ra, rb, rs, kb + 1, nk, a0, b0, s0, a1, b1, s1, sink, active, pp, acc);
   }
-  if (kb < nk) k_step<false>(pl, ra, rb, rs, kb, nk, a1, b1, s1, a0, b0, s0, sink, active, pp, acc);
+  if (kb < nk) k_step<false, kFa, kFb>(pl, ra, rb, rs, kb, nk, a1, b1, s1, a0, b0, s0, sink, active, pp, acc);
   if (active) drain(pp, acc);
 }
 
-template <bool kBf16Out>
+template <bool kBf16Out, int kFa, int kFb>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
   // LDS: two stages of operand tiles and scales during the K loop; afterwards
   // the same memory stages the bf16 output for coalesced stores
@@ -378,7 +383,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
 #pragma unroll
     for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  k_loop(pl, p.a + (int64_t)m0 * p.lda, (uint32_t)(rows_a * (int)p.lda), p.b + (int64_t)n0 * p.ldb,
+  k_loop<kFa, kFb>(pl, p.a + (int64_t)m0 * p.lda, (uint32_t)(rows_a * (int)p.lda), p.b + (int64_t)n0 * p.ldb,
          (uint32_t)(rows_b * (int)p.ldb), gs, gs_bytes, ta0, ta1, tb0, tb1, ts0, ts1, sink, nk, active, acc);
 
   if (!active) return;
@@ -455,7 +460,7 @@ __device__ __forceinline__ v8i load_frag32(const uint8_t* p) {
   return f;
 }
 
-template <int MT, bool kBf16Out>
+template <int MT, bool kBf16Out, int kFa, int kFb>
 __global__ __launch_bounds__(kDecThreads) void k_gemm_fp8_decode(GemmParams p) {
   __shared__ float red[kDecSplit][4 * MT * 64 * 4];
 
@@ -511,7 +516,8 @@ __global__ __launch_bounds__(kDecThreads) void k_gemm_fp8_decode(GemmParams p) {
         const float comb = cur.sa[mt] * cur.sw;
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns) {
-          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur.w[ns], cur.a[mt], zero, 0, 0, 0, 0, 0, 0);
+          // weights are the first MFMA operand here
+          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur.w[ns], cur.a[mt], zero, kFb, kFa, 0, 0, 0, 0);
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[ns][mt][v] = __builtin_fmaf(part[v], comb, acc[ns][mt][v]);
         }
@@ -547,13 +553,27 @@ __global__ __launch_bounds__(kDecThreads) void k_gemm_fp8_decode(GemmParams p) {
   }
 }
 
-template <int MT>
+template <int MT, int kFa, int kFb>
 void launch_decode(const GemmParams& p, bool bf16, hipStream_t st) {
   const dim3 grid((unsigned)(p.N / kDecBN));
   if (bf16)
-    hipLaunchKernelGGL((k_gemm_fp8_decode<MT, true>), grid, dim3(kDecThreads), 0, st, p);
+    hipLaunchKernelGGL((k_gemm_fp8_decode<MT, true, kFa, kFb>), grid, dim3(kDecThreads), 0, st, p);
   else
-    hipLaunchKernelGGL((k_gemm_fp8_decode<MT, false>), grid, dim3(kDecThreads), 0, st, p);
+    hipLaunchKernelGGL((k_gemm_fp8_decode<MT, false, kFa, kFb>), grid, dim3(kDecThreads), 0, st, p);
+}
+
+// Kernel choice for one (format of A, format of B) pair: the decode kernel for
+// M <= 64, else the prefill kernel on a grid of n_full + 2 n_half workgroups.
+template <int kFa, int kFb>
+void launch_formats(const GemmParams& p, bool bf16, hipStream_t st) {
+  if (p.M <= 16) return launch_decode<1, kFa, kFb>(p, bf16, st);
+  if (p.M <= 32) return launch_decode<2, kFa, kFb>(p, bf16, st);
+  if (p.M <= 64) return launch_decode<4, kFa, kFb>(p, bf16, st);
+  const dim3 grid((unsigned)(p.n_full + 2 * p.n_half));
+  if (bf16)
+    hipLaunchKernelGGL((k_gemm_fp8_block<true, kFa, kFb>), grid, dim3(kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((k_gemm_fp8_block<false, kFa, kFb>), grid, dim3(kThreads), 0, st, p);
 }
 
 }  // namespace
@@ -592,21 +612,9 @@ hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t st) {
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
   const bool bf16 = g.c_dtype == DTYPE_BF16;
-  if (p.M <= 16) {
-    launch_decode<1>(p, bf16, st);
-    return hipGetLastError();
-  }
-  if (p.M <= 32) {
-    launch_decode<2>(p, bf16, st);
-    return hipGetLastError();
-  }
-  if (p.M <= 64) {
-    launch_decode<4>(p, bf16, st);
-    return hipGetLastError();
-  }
   // tail balancing (see GemmParams)
   const int tiles = p.tiles_m * p.tiles_n;
-  const int cus = device_cu_count();
+  const int cus = p.M > 64 ? device_cu_count() : 0;
   const int rem = cus > 0 ? tiles % cus : 0;
   p.n_full = tiles;
   p.n_half = 0;
@@ -614,11 +622,11 @@ hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t st) {
     p.n_full = tiles - rem;
     p.n_half = rem;
   }
-  const dim3 grid((unsigned)(p.n_full + 2 * p.n_half));
-  if (g.c_dtype == DTYPE_BF16)
-    hipLaunchKernelGGL(k_gemm_fp8_block<true>, grid, dim3(kThreads), 0, st, p);
-  else
-    hipLaunchKernelGGL(k_gemm_fp8_block<false>, grid, dim3(kThreads), 0, st, p);
+  const bool a5 = g.fmt_a == FMT_E5M2, b5 = g.fmt_b == FMT_E5M2;
+  if (!a5 && !b5) launch_formats<FMT_E4M3, FMT_E4M3>(p, bf16, st);
+  else if (!a5 && b5) launch_formats<FMT_E4M3, FMT_E5M2>(p, bf16, st);
+  else if (a5 && !b5) launch_formats<FMT_E5M2, FMT_E4M3>(p, bf16, st);
+  else launch_formats<FMT_E5M2, FMT_E5M2>(p, bf16, st);
   return hipGetLastError();
 }
 

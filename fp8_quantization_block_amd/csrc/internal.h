@@ -10,12 +10,16 @@ namespace fp8blk {
 
 enum Gran : int { GRAN_PER_TENSOR = 0, GRAN_GROUP_1x128 = 1, GRAN_BLOCK_128x128 = 2 };
 enum DType : int { DTYPE_BF16 = 0, DTYPE_F32 = 1 };
+// FP8 encodings; the values are also the operand-format selectors of the
+// gfx950 f8f6f4 MFMA (0 = E4M3, 1 = E5M2).
+enum Fmt : int { FMT_E4M3 = 0, FMT_E5M2 = 1 };
 
 struct QuantArgs {
   const void* x;
   int x_dtype;
   int64_t rows, cols, ld_x;
   int gran;
+  int fmt;
   uint8_t* q;
   int64_t ld_q;
   float* scales;
@@ -26,6 +30,7 @@ struct KvArgs {
   const void* kv;        // quantize input
   const uint8_t* q_in;   // dequantize input
   int64_t heads, tokens, head_dim, stride_head, stride_token, token_block;
+  int fmt;
   uint8_t* q;            // quantize output
   float* scales;         // quantize output / dequantize input
   const float* scales_in;
@@ -47,6 +52,7 @@ struct GemmArgs {
   void* c;
   int c_dtype;
   int64_t ldc;
+  int fmt_a, fmt_b;
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);

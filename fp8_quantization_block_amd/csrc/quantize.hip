@@ -2,12 +2,14 @@
 // (head x token block) groups, and the KV dequantizer.
 //
 // Method ([FP8] wangyu.me, "大语言模型量化技术（五）：FP8"): per group, amax = max|x|,
-// s = amax / 448, code = E4M3(x / s) rounded to nearest even and saturated
+// s = amax / max_fmt, code = FP8(x / s) rounded to nearest even and saturated
 // (section "什么是 FP8 量化"; section "权重量化：128×128 分块 FP8" for 128x128
 // blocks; section "激活动态量化" for per-token 1x128 groups). KV groups are one
 // head x 128 tokens x head_dim ([LONG] pwwt.cn Llama-3 FP8 notes, section 3).
 // Dequantization is x ~ q * s ([MIXED] charles2530.github.io, "量化：FP8 与混合精度推理",
-// section "E4M3 和 E5M2 是范围与格点的取舍").
+// section "E4M3 和 E5M2 是范围与格点的取舍"). Every kernel is instantiated for both
+// FP8 formats ([FP8] section "FP8 是什么", format table): E4M3 (max_fmt = 448)
+// and E5M2 (max_fmt = 57344; [LONG] section 1 stores the KV cache in E5M2).
 //
 // All passes are HBM-bound: 16-byte loads, a max reduction in registers / DPP
 // / LDS, then packed code stores.
@@ -61,10 +63,11 @@ struct Vec8<__hip_bfloat16> {
   }
   __device__ __forceinline__ void zero() { w = make_uint4(0, 0, 0, 0); }
   __device__ __forceinline__ uint32_t amax_bits() const { return amax_bf16x8(w); }
+  template <int kFmt>
   __device__ __forceinline__ uint2 cast(const GroupScale& g) const {
     uint2 r;
-    r.x = cast4_bf16(g, bf16_lo_to_f32(w.x), bf16_hi_to_f32(w.x), bf16_lo_to_f32(w.y), bf16_hi_to_f32(w.y));
-    r.y = cast4_bf16(g, bf16_lo_to_f32(w.z), bf16_hi_to_f32(w.z), bf16_lo_to_f32(w.w), bf16_hi_to_f32(w.w));
+    r.x = cast4_bf16<kFmt>(g, bf16_lo_to_f32(w.x), bf16_hi_to_f32(w.x), bf16_lo_to_f32(w.y), bf16_hi_to_f32(w.y));
+    r.y = cast4_bf16<kFmt>(g, bf16_lo_to_f32(w.z), bf16_hi_to_f32(w.z), bf16_lo_to_f32(w.w), bf16_hi_to_f32(w.w));
     return r;
   }
 };
@@ -96,10 +99,11 @@ struct Vec8<float> {
     m = amax_f32(b.x, m); m = amax_f32(b.y, m); m = amax_f32(b.z, m); m = amax_f32(b.w, m);
     return m;
   }
+  template <int kFmt>
   __device__ __forceinline__ uint2 cast(const GroupScale& g) const {
     uint2 r;
-    r.x = cast4_f32(g, a.x, a.y, a.z, a.w);
-    r.y = cast4_f32(g, b.x, b.y, b.z, b.w);
+    r.x = cast4_f32<kFmt>(g, a.x, a.y, a.z, a.w);
+    r.y = cast4_f32<kFmt>(g, b.x, b.y, b.z, b.w);
     return r;
   }
 };
@@ -136,7 +140,7 @@ __device__ __forceinline__ uint32_t block256_max(uint32_t m) {
 // kUnroll groups per lane with all loads issued before any arithmetic.
 // Group g of the flat (row, group) index space: row = g / ngroups.
 // ---------------------------------------------------------------------------
-template <typename T, int kUnroll>
+template <typename T, int kUnroll, int kFmt>
 __global__ __launch_bounds__(256) void k_quant_group_1x128(
     const T* __restrict__ x, int64_t ld_x, uint32_t cols, uint32_t ngroups, uint32_t total_groups,
     FastDiv div_groups, uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ sc,
@@ -166,10 +170,10 @@ __global__ __launch_bounds__(256) void k_quant_group_1x128(
   for (int u = 0; u < kUnroll; ++u) {
     const uint32_t a0 = v[u][0].amax_bits(), a1 = v[u][1].amax_bits();
     const uint32_t amax = row8_max(a0 > a1 ? a0 : a1);
-    const GroupScale gs = make_group_scale(amax);
+    const GroupScale gs = make_group_scale<kFmt>(amax);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint2 codes = v[u][h].cast(gs);
+      const uint2 codes = v[u][h].template cast<kFmt>(gs);
       const uint32_t col0 = grp[u] * 128u + h * 64u + lane8 * 8u;
       if (nv[u][h] > 0) store_codes8(q + (int64_t)row[u] * ld_q + col0, codes, nv[u][h]);
     }
@@ -192,7 +196,7 @@ struct TileGroup {
   uint32_t cols;       // valid columns in this group
 };
 
-template <typename T>
+template <typename T, int kFmt>
 __device__ __forceinline__ void quant_tile_group(const T* __restrict__ x, uint8_t* __restrict__ q,
                                                  float* __restrict__ sc, const TileGroup& tg) {
   const uint32_t cpr = (tg.cols + 7u) >> 3;   // chunks per row
@@ -216,16 +220,17 @@ __device__ __forceinline__ void quant_tile_group(const T* __restrict__ x, uint8_
     const uint32_t a = v[i].amax_bits();
     m = a > m ? a : m;
   }
-  const GroupScale gs = make_group_scale(block256_max(m));
+  const GroupScale gs = make_group_scale<kFmt>(block256_max(m));
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    if (nv[i] > 0) store_codes8(q + tg.out_off + (int64_t)r[i] * tg.out_ld + cc[i] * 8u, v[i].cast(gs), nv[i]);
+    if (nv[i] > 0)
+      store_codes8(q + tg.out_off + (int64_t)r[i] * tg.out_ld + cc[i] * 8u, v[i].template cast<kFmt>(gs), nv[i]);
   }
   if (threadIdx.x == 0) sc[tg.scale_off] = gs.s;
 }
 
 // 128x128 blocks of a [rows][cols] matrix; grid (ceil(cols/128), ceil(rows/128)).
-template <typename T>
+template <typename T, int kFmt>
 __global__ __launch_bounds__(256) void k_quant_block_128x128(
     const T* __restrict__ x, int64_t ld_x, uint32_t rows, uint32_t cols, uint8_t* __restrict__ q,
     int64_t ld_q, float* __restrict__ sc, int64_t ss_row, int64_t ss_col) {
@@ -238,10 +243,11 @@ __global__ __launch_bounds__(256) void k_quant_block_128x128(
   tg.scale_off = (int64_t)gy * ss_row + (int64_t)gx * ss_col;
   tg.rows = min(128u, rows - gy * 128u);
   tg.cols = min(128u, cols - gx * 128u);
-  quant_tile_group<T>(x, q, sc, tg);
+  quant_tile_group<T, kFmt>(x, q, sc, tg);
 }
 
 // KV groups; grid (ceil(tokens/token_block), heads).
+template <int kFmt>
 __global__ __launch_bounds__(256) void k_kv_quant(
     const __hip_bfloat16* __restrict__ kv, int64_t stride_head, int64_t stride_token,
     uint32_t tokens, uint32_t head_dim, uint32_t token_block, uint8_t* __restrict__ q,
@@ -256,11 +262,12 @@ __global__ __launch_bounds__(256) void k_kv_quant(
   tg.scale_off = (int64_t)h * nb + b;
   tg.rows = min(token_block, tokens - t0);
   tg.cols = head_dim;
-  quant_tile_group<__hip_bfloat16>(kv, q, sc, tg);
+  quant_tile_group<__hip_bfloat16, kFmt>(kv, q, sc, tg);
 }
 
 // KV dequantize: one workgroup per group, 8 codes per chunk (contiguous run
 // of rows * head_dim codes in the dense layout), up to 2048 chunks per group.
+template <int kFmt>
 __global__ __launch_bounds__(256) void k_kv_dequant(
     const uint8_t* __restrict__ q, const float* __restrict__ sc, uint32_t tokens,
     uint32_t head_dim, uint32_t token_block, __hip_bfloat16* __restrict__ out) {
@@ -286,8 +293,8 @@ __global__ __launch_bounds__(256) void k_kv_dequant(
     const uint32_t ws[2] = {w[i].x, w[i].y};
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[k], false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[k], true);
+      const auto lo = Fp8<kFmt>::template decode2<false>(ws[k]);
+      const auto hi = Fp8<kFmt>::template decode2<true>(ws[k]);
       const __hip_bfloat16 e0 = __float2bfloat16(lo[0] * s);
       const __hip_bfloat16 e1 = __float2bfloat16(lo[1] * s);
       const __hip_bfloat16 e2 = __float2bfloat16(hi[0] * s);
@@ -329,12 +336,12 @@ __global__ __launch_bounds__(256) void k_amax_tensor(const T* __restrict__ x, in
   if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(acc), m);
 }
 
-template <typename T>
+template <typename T, int kFmt>
 __global__ __launch_bounds__(256) void k_cast_tensor(const T* __restrict__ x, int64_t ld_x,
                                                      uint32_t cols, uint64_t nchunks,
                                                      const float* __restrict__ acc,
                                                      uint8_t* __restrict__ q, int64_t ld_q) {
-  const GroupScale gs = make_group_scale(*reinterpret_cast<const uint32_t*>(acc));
+  const GroupScale gs = make_group_scale<kFmt>(*reinterpret_cast<const uint32_t*>(acc));
   const uint32_t cpr = (cols + 7u) >> 3;
   for (uint64_t c = (uint64_t)blockIdx.x * 256u + threadIdx.x; c < nchunks;
        c += (uint64_t)gridDim.x * 256u) {
@@ -343,14 +350,15 @@ __global__ __launch_bounds__(256) void k_cast_tensor(const T* __restrict__ x, in
     const uint32_t nv = min(8u, cols - cc * 8u);
     Vec8<T> v;
     v.load(x + (int64_t)r * ld_x + cc * 8u, nv);
-    store_codes8(q + (int64_t)r * ld_q + cc * 8u, v.cast(gs), nv);
+    store_codes8(q + (int64_t)r * ld_q + cc * 8u, v.template cast<kFmt>(gs), nv);
   }
 }
 
+template <int kFmt>
 __global__ void k_finalize_tensor_scale(float* __restrict__ acc) {
   if (threadIdx.x == 0 && blockIdx.x == 0) {
     const uint32_t bits = *reinterpret_cast<const uint32_t*>(acc);
-    acc[0] = __uint_as_float(bits) / kE4M3Max;
+    acc[0] = __uint_as_float(bits) / Fp8<kFmt>::kMax;
   }
 }
 
@@ -370,7 +378,7 @@ FastDiv make_fastdiv(uint32_t d) {
   return f;
 }
 
-template <typename T>
+template <typename T, int kFmt>
 hipError_t quantize_typed(const QuantArgs& a, hipStream_t st) {
   const T* x = static_cast<const T*>(a.x);
   const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
@@ -381,9 +389,9 @@ hipError_t quantize_typed(const QuantArgs& a, hipStream_t st) {
     const uint64_t want = (nchunks + 255) / 256;
     const uint32_t grid = (uint32_t)(want < 4096 ? want : 4096);
     hipLaunchKernelGGL(k_amax_tensor<T>, dim3(grid), dim3(256), 0, st, x, a.ld_x, cols, nchunks, a.scales);
-    hipLaunchKernelGGL(k_cast_tensor<T>, dim3(grid), dim3(256), 0, st, x, a.ld_x, cols, nchunks,
+    hipLaunchKernelGGL((k_cast_tensor<T, kFmt>), dim3(grid), dim3(256), 0, st, x, a.ld_x, cols, nchunks,
                        a.scales, a.q, a.ld_q);
-    hipLaunchKernelGGL(k_finalize_tensor_scale, dim3(1), dim3(64), 0, st, a.scales);
+    hipLaunchKernelGGL(k_finalize_tensor_scale<kFmt>, dim3(1), dim3(64), 0, st, a.scales);
     return hipGetLastError();
   }
   if (rows == 0 || cols == 0) return hipSuccess;
@@ -392,28 +400,33 @@ hipError_t quantize_typed(const QuantArgs& a, hipStream_t st) {
     const uint32_t total = rows * ngroups;
     const uint32_t per_block = 32u * kGroupUnroll;
     const uint32_t grid = (total + per_block - 1) / per_block;
-    hipLaunchKernelGGL((k_quant_group_1x128<T, kGroupUnroll>), dim3(grid), dim3(256), 0, st, x,
+    hipLaunchKernelGGL((k_quant_group_1x128<T, kGroupUnroll, kFmt>), dim3(grid), dim3(256), 0, st, x,
                        a.ld_x, cols, ngroups, total, make_fastdiv(ngroups), a.q, a.ld_q, a.scales,
                        a.ss_row, a.ss_col);
     return hipGetLastError();
   }
   // 128x128 blocks
   const dim3 grid((cols + 127u) / 128u, (rows + 127u) / 128u);
-  hipLaunchKernelGGL(k_quant_block_128x128<T>, grid, dim3(256), 0, st, x, a.ld_x, rows, cols, a.q,
+  hipLaunchKernelGGL((k_quant_block_128x128<T, kFmt>), grid, dim3(256), 0, st, x, a.ld_x, rows, cols, a.q,
                      a.ld_q, a.scales, a.ss_row, a.ss_col);
   return hipGetLastError();
 }
 }  // namespace
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
-  if (a.x_dtype == DTYPE_BF16) return quantize_typed<__hip_bfloat16>(a, st);
-  return quantize_typed<float>(a, st);
+  if (a.fmt == FMT_E5M2) {
+    if (a.x_dtype == DTYPE_BF16) return quantize_typed<__hip_bfloat16, FMT_E5M2>(a, st);
+    return quantize_typed<float, FMT_E5M2>(a, st);
+  }
+  if (a.x_dtype == DTYPE_BF16) return quantize_typed<__hip_bfloat16, FMT_E4M3>(a, st);
+  return quantize_typed<float, FMT_E4M3>(a, st);
 }
 
 hipError_t launch_kv_quantize(const KvArgs& a, hipStream_t st) {
   if (a.heads == 0 || a.tokens == 0) return hipSuccess;
   const dim3 grid((uint32_t)((a.tokens + a.token_block - 1) / a.token_block), (uint32_t)a.heads);
-  hipLaunchKernelGGL(k_kv_quant, grid, dim3(256), 0, st,
+  auto kernel = a.fmt == FMT_E5M2 ? k_kv_quant<FMT_E5M2> : k_kv_quant<FMT_E4M3>;
+  hipLaunchKernelGGL(kernel, grid, dim3(256), 0, st,
                      static_cast<const __hip_bfloat16*>(a.kv), a.stride_head, a.stride_token,
                      (uint32_t)a.tokens, (uint32_t)a.head_dim, (uint32_t)a.token_block, a.q,
                      a.scales);
@@ -423,7 +436,8 @@ hipError_t launch_kv_quantize(const KvArgs& a, hipStream_t st) {
 hipError_t launch_kv_dequantize(const KvArgs& a, hipStream_t st) {
   if (a.heads == 0 || a.tokens == 0) return hipSuccess;
   const dim3 grid((uint32_t)((a.tokens + a.token_block - 1) / a.token_block), (uint32_t)a.heads);
-  hipLaunchKernelGGL(k_kv_dequant, grid, dim3(256), 0, st, a.q_in, a.scales_in, (uint32_t)a.tokens,
+  auto kernel = a.fmt == FMT_E5M2 ? k_kv_dequant<FMT_E5M2> : k_kv_dequant<FMT_E4M3>;
+  hipLaunchKernelGGL(kernel, grid, dim3(256), 0, st, a.q_in, a.scales_in, (uint32_t)a.tokens,
                      (uint32_t)a.head_dim, (uint32_t)a.token_block,
                      static_cast<__hip_bfloat16*>(a.out));
   return hipGetLastError();

@@ -11,15 +11,18 @@
  *   [LONG]  pwwt.cn, Llama-3 FP8 and long-context practice notes
  *
  * Numerics shared by every entry point:
- *   - FP8 format: OCP E4M3 (bias 7, subnormals, no infinity, S.1111.111 = NaN),
- *     largest finite value 448 ([FP8] section "FP8 是什么", format table).
- *   - Scale of a group: s = fl32(amax / 448), an IEEE fp32 correctly rounded
+ *   - FP8 formats ([FP8] section "FP8 是什么", format table): OCP E4M3 (bias 7,
+ *     subnormals, no infinity, S.1111.111 = NaN), largest finite value
+ *     MAX = 448; and OCP E5M2 (bias 15, subnormals, S.11111.00 = infinity,
+ *     S.11111.{01,10,11} = NaN), largest finite value MAX = 57344.
+ *   - Scale of a group: s = fl32(amax / MAX), an IEEE fp32 correctly rounded
  *     division; the stored scale is the dequantization multiplier, x ~ q * s
  *     ([FP8] section "什么是 FP8 量化"; section "权重量化：128×128 分块 FP8").
- *   - Code of an element: the E4M3 value nearest to fl32(x / s) (the IEEE fp32
- *     correctly rounded quotient), ties to even, magnitudes >= 448 saturate to
- *     +-448, the sign of a zero result is the sign of x. A group with s == 0
- *     gets sign-only zero codes.
+ *   - Code of an element: the value of the format nearest to fl32(x / s) (the
+ *     IEEE fp32 correctly rounded quotient), ties to even, magnitudes >= MAX
+ *     saturate to +-MAX (no infinity or NaN code is ever written), the sign of
+ *     a zero result is the sign of x. A group with s == 0 gets sign-only zero
+ *     codes.
  *   - Denormals are honoured, never flushed.
  *   - Inputs must be finite; non-finite inputs give unspecified codes but never
  *     out-of-bounds accesses.
@@ -45,12 +48,13 @@ typedef enum fp8blk_status {
   FP8BLK_OK = 0,
   FP8BLK_EINVAL = 1,       /* null pointer, negative size, ld < cols, bad enum, aliasing */
   FP8BLK_EALIGN = 2,       /* base pointer or leading dimension not 16-byte aligned */
-  FP8BLK_EUNSUPPORTED = 3, /* valid request this version does not implement (e.g. E5M2) */
+  FP8BLK_EUNSUPPORTED = 3, /* valid request this version does not implement (e.g. N % 128 != 0) */
   FP8BLK_EHIP = 4          /* the HIP runtime rejected a launch */
 } fp8blk_status;
 
-/* FP8 encodings ([FP8] section "FP8 是什么"). Only E4M3 is implemented; E5M2
- * is reserved and returns FP8BLK_EUNSUPPORTED. */
+/* FP8 encodings ([FP8] section "FP8 是什么", format table; [LONG] section 1 keeps
+ * weights and activations in E4M3 and the KV cache in E5M2). Every entry point
+ * takes either; the GEMM takes each operand in its own format. */
 typedef enum fp8blk_format { FP8BLK_E4M3 = 0, FP8BLK_E5M2 = 1 } fp8blk_format;
 
 /* Scale granularity ([MIXED] section "scale 是控制面"; [FP8] sections
@@ -64,7 +68,7 @@ typedef enum fp8blk_granularity {
 typedef enum fp8blk_dtype { FP8BLK_BF16 = 0, FP8BLK_F32 = 1 } fp8blk_dtype;
 
 /*
- * fp8_quantize -- dynamic quantization of a 2-D tensor to E4M3 codes plus fp32 scales.
+ * fp8_quantize -- dynamic quantization of a 2-D tensor to FP8 codes (fmt) plus fp32 scales.
  *
  * Defined by [FP8] section "什么是 FP8 量化" (scale max|x|/448, divide, round to
  * nearest, saturate, keep codes and scale), section "权重量化：128×128 分块 FP8"
@@ -73,7 +77,7 @@ typedef enum fp8blk_dtype { FP8BLK_BF16 = 0, FP8BLK_F32 = 1 } fp8blk_dtype;
  * group, computed at run time).
  *
  *   x       device, [rows][cols] of x_dtype (bf16 or fp32), row stride ld_x elements.
- *   q       device, uint8 E4M3 codes [rows][cols], row stride ld_q bytes.
+ *   q       device, uint8 codes of format fmt [rows][cols], row stride ld_q bytes.
  *   scales  device, fp32 scale grid; element (i, j) of the grid lives at
  *           scales[i * scale_stride_row + j * scale_stride_col] (strides in
  *           elements; ignored for PER_TENSOR, whose single scale is scales[0]).
@@ -93,7 +97,7 @@ fp8blk_status fp8_quantize(const void* x, fp8blk_dtype x_dtype, int64_t rows, in
                            int64_t scale_stride_col, void* stream);
 
 /*
- * fp8_block_gemm -- C[M][N] = A[M][K] . B[N][K]^T from E4M3 codes and their scales.
+ * fp8_block_gemm -- C[M][N] = A[M][K] . B[N][K]^T from FP8 codes and their scales.
  *
  * Defined by [FP8] section "激活动态量化" (the product is a sum over 128-wide K
  * blocks j of activation scale x weight-block scale x FP8 block product, the
@@ -106,10 +110,10 @@ fp8blk_status fp8_quantize(const void* x, fp8blk_dtype x_dtype, int64_t rows, in
  * with every P_j summed in fp32 from zero and promoted into an fp32 accumulator
  * with one fused multiply-add per K block; the result is rounded once to c_dtype.
  *
- *   a       device, uint8 codes [M][K], row stride lda bytes (activations).
+ *   a       device, uint8 codes [M][K] of format fmt_a, row stride lda bytes (activations).
  *   scale_a device, fp32. gran_a = PER_TENSOR: scale_a[0]. gran_a = GROUP_1x128:
  *           s_a(m, j) = scale_a[m * sa_stride_m + j * sa_stride_k].
- *   b       device, uint8 codes [N][K], row stride ldb bytes (weights W in R^{N x K}).
+ *   b       device, uint8 codes [N][K] of format fmt_b, row stride ldb bytes (weights W in R^{N x K}).
  *   scale_b device, fp32. gran_b = PER_TENSOR: scale_b[0]. gran_b = BLOCK_128x128:
  *           s_b(nb, j) = scale_b[nb * sb_stride_n + j * sb_stride_k]
  *           (the ceil(N/128) x ceil(K/128) weight_scale_inv grid).
@@ -121,7 +125,9 @@ fp8blk_status fp8_quantize(const void* x, fp8blk_dtype x_dtype, int64_t rows, in
  * below 2^23 (else FP8BLK_EUNSUPPORTED);
  * ldc >= N; a, b, c 16-byte aligned and lda, ldb, ldc * sizeof(c_dtype)
  * multiples of 16; gran_a in {PER_TENSOR, GROUP_1x128}; gran_b in {PER_TENSOR,
- * BLOCK_128x128}; fmt_a = fmt_b = E4M3; c must not overlap the inputs.
+ * BLOCK_128x128}; fmt_a, fmt_b in {E4M3, E5M2} (independently); codes must be
+ * finite (E4M3: not S.1111.111; E5M2: exponent field not 11111), as every
+ * code fp8_quantize writes is; c must not overlap the inputs.
  */
 fp8blk_status fp8_block_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
                              const float* scale_a, fp8blk_granularity gran_a, int64_t sa_stride_m,
@@ -136,13 +142,14 @@ fp8blk_status fp8_block_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, 
  * Defined by [LONG] section 1 (K and V quantized to FP8 with separate scales)
  * and section 3 (finer KV granularity: per head and per 128-token block, so
  * that small late-position keys keep their precision); [MIXED] section
- * "scale 是控制面" (per-head scales). Same per-group arithmetic as fp8_quantize.
- * Call once for K and once for V.
+ * "scale 是控制面" (per-head scales). Same per-group arithmetic as fp8_quantize,
+ * in format fmt (E5M2 is the KV format of [LONG] section 1). Call once for K
+ * and once for V.
  *
  *   kv      device, bf16 [heads][tokens][head_dim]; element (h, t, d) at
  *           kv[h * stride_head + t * stride_token + d] (strides in elements,
  *           head_dim contiguous).
- *   q       device, dense uint8 codes [heads][tokens][head_dim].
+ *   q       device, dense uint8 codes of format fmt [heads][tokens][head_dim].
  *   scales  device, dense fp32 [heads][ceil(tokens / token_block)].
  *   A group is one head, token_block consecutive tokens (fewer in the ragged
  *   last block) and all of head_dim.
@@ -162,8 +169,8 @@ fp8blk_status fp8_kv_quantize(const void* kv, int64_t heads, int64_t tokens, int
  *
  * Defined by [MIXED] section "E4M3 和 E5M2 是范围与格点的取舍" (dequantization
  * multiplies the FP8 value by its scale) and [FP8] section "什么是 FP8 量化"
- * (x ~ q * s). Layouts are those fp8_kv_quantize writes; out is dense bf16
- * [heads][tokens][head_dim].
+ * (x ~ q * s). Layouts are those fp8_kv_quantize writes; fmt must be the
+ * format the codes were written in; out is dense bf16 [heads][tokens][head_dim].
  *
  * Requirements as fp8_kv_quantize; out must not overlap q or scales.
  */

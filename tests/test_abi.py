@@ -72,7 +72,8 @@ def q(lib, x=PA, dt=BF16, rows=4, cols=256, ldx=256, gran=GROUP, fmt=E4M3, qp=PB
     (dict(dt=7), EINVAL),
     (dict(gran=9), EINVAL),
     (dict(fmt=5), EINVAL),
-    (dict(fmt=E5M2), EUNSUPPORTED),
+    (dict(fmt=2), EINVAL),
+    (dict(fmt=E5M2, ldx=100), EINVAL),     # E5M2 passes the format check
     (dict(x=PA + 2), EALIGN),
     (dict(qp=PB + 8), EALIGN),
     (dict(ldx=260, cols=256), EALIGN),
@@ -108,7 +109,8 @@ def g(lib, M=256, N=256, K=256, a=PA, lda=256, sa=PB, ga=GROUP, sam=2, sak=1, b=
     (dict(ga=BLOCK), EINVAL),
     (dict(gb=GROUP), EINVAL),
     (dict(cdt=3), EINVAL),
-    (dict(fa=E5M2), EUNSUPPORTED),
+    (dict(fa=2), EINVAL),
+    (dict(fa=E5M2, fb=E5M2, lda=128), EINVAL),   # E5M2 operands pass the format check
     (dict(fb=4), EINVAL),
     (dict(M=-1), EINVAL),
     (dict(N=0), EINVAL),
@@ -143,7 +145,8 @@ def kvq(lib, kv=PA, h=2, t=300, d=128, sh=300 * 128, st=128, tb=128, fmt=E4M3, q
     (dict(d=100, st=104, sh=300 * 104), EUNSUPPORTED),
     (dict(d=256, st=256, sh=300 * 256), EUNSUPPORTED),   # 128 x 256 > 16384 per group
     (dict(st=64), EINVAL),
-    (dict(fmt=E5M2), EUNSUPPORTED),
+    (dict(fmt=3), EINVAL),
+    (dict(fmt=E5M2, st=64), EINVAL),      # E5M2 passes the format check
     (dict(kv=PA + 8), EALIGN),
     (dict(st=132), EALIGN),
     (dict(qp=PA + 4096), EINVAL),          # codes overlap the input
@@ -159,7 +162,8 @@ def test_kv_empty_is_a_noop(lib):
 
 @pytest.mark.parametrize("args,status", [
     ((0, PC, 2, 300, 128, 128, E4M3, PD), EINVAL),
-    ((PB, PC, 2, 300, 128, 128, E5M2, PD), EUNSUPPORTED),
+    ((PB, PC, 2, 300, 128, 128, 2, PD), EINVAL),
+    ((PB, PC, 2, 300, 128, 128, E5M2, PD + 2), EALIGN),
     ((PB, PC, 2, 300, 100, 128, E4M3, PD), EUNSUPPORTED),
     ((PB, PC, 2, 300, 128, 128, E4M3, PD + 2), EALIGN),
     ((PB, PC, 2, 300, 128, 128, E4M3, PB + 64), EINVAL),   # out overlaps the codes
