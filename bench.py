@@ -196,6 +196,20 @@ def main():
         t_gemm = timer.run(gemm, max(args.steps, 10), warmup=args.warmup, name="gemm")
         passes["gemm"] = {"us": t_gemm * 1e6, "TFLOP/s": flops / t_gemm / 1e12,
                           "frac_fp8_peak": flops / t_gemm / 1e12 / PEAK_FP8_TFLOPS}
+    if args.only is None and not args.no_secondary:
+        # E5M2 activations (1x128) against the E4M3 weights: the same GEMM
+        # kernel with the MFMA's A operand decoded as E5M2
+        qa5 = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        sa5 = torch.empty((K // 128, M), dtype=torch.float32, device=dev).t()
+        fp8.fp8_quantize(a_sets[0], "group_1x128", fmt="e5m2", out=qa5, scales=sa5)
+
+        def gemm5(i):
+            fp8.fp8_block_gemm(qa5, sa5, "group_1x128", qw, sw, "block_128x128", out=out, fmt_a="e5m2")
+
+        t5 = timer.run(gemm5, max(args.steps, 10), warmup=args.warmup, name="gemm_e5m2_act")
+        passes["gemm_e5m2_act"] = {"us": t5 * 1e6, "TFLOP/s": flops / t5 / 1e12,
+                                   "frac_fp8_peak": flops / t5 / 1e12 / PEAK_FP8_TFLOPS}
+        del qa5, sa5
     if args.only in (None, "quant"):
         t_qa = timer.run(quant_a, max(args.steps, 22), warmup=args.warmup, name="act_quant_1x128")
         bytes_qa = M * K * 2 + M * K + M * (K // 128) * 4
@@ -242,22 +256,25 @@ def main():
         lib = fp8.load_library()
         stream = torch.cuda.current_stream().cuda_stream
 
-        def kvq(i):
-            fp8._check(lib.fp8_kv_quantize(kd.data_ptr(), H, T, D, T * D, D, 128, 0, qk.data_ptr(), sk.data_ptr(), stream))
-            fp8._check(lib.fp8_kv_quantize(vd.data_ptr(), H, T, D, T * D, D, 128, 0, qv.data_ptr(), sv.data_ptr(), stream))
-
-        def kvd(i):
-            fp8._check(lib.fp8_kv_dequantize(qk.data_ptr(), sk.data_ptr(), H, T, D, 128, 0, ok.data_ptr(), stream))
-            fp8._check(lib.fp8_kv_dequantize(qv.data_ptr(), sv.data_ptr(), H, T, D, 128, 0, ov.data_ptr(), stream))
-
         n = 2 * H * T * D
         kv_bytes = n * 2 + n + 2 * H * (T // 128) * 4
-        t_kvq = timer.run(kvq, 20, warmup=3, name="kv_quant_K+V")
-        t_kvd = timer.run(kvd, 20, warmup=3, name="kv_dequant_K+V")
-        passes["kv_quant_K+V"] = {"us": t_kvq * 1e6, "GB/s": kv_bytes / t_kvq / 1e9,
-                                  "frac_hbm": kv_bytes / t_kvq / 1e9 / PEAK_HBM_GBPS}
-        passes["kv_dequant_K+V"] = {"us": t_kvd * 1e6, "GB/s": kv_bytes / t_kvd / 1e9,
-                                    "frac_hbm": kv_bytes / t_kvd / 1e9 / PEAK_HBM_GBPS}
+        # E4M3 (the default KV format) and E5M2 (the KV format of the serving
+        # recipe on the pages); same bytes, same kernels up to the conversion
+        for fmt, tag in ((fp8.E4M3, ""), (fp8.E5M2, "_e5m2")):
+            def kvq(i, fmt=fmt):
+                fp8._check(lib.fp8_kv_quantize(kd.data_ptr(), H, T, D, T * D, D, 128, fmt, qk.data_ptr(), sk.data_ptr(), stream))
+                fp8._check(lib.fp8_kv_quantize(vd.data_ptr(), H, T, D, T * D, D, 128, fmt, qv.data_ptr(), sv.data_ptr(), stream))
+
+            def kvd(i, fmt=fmt):
+                fp8._check(lib.fp8_kv_dequantize(qk.data_ptr(), sk.data_ptr(), H, T, D, 128, fmt, ok.data_ptr(), stream))
+                fp8._check(lib.fp8_kv_dequantize(qv.data_ptr(), sv.data_ptr(), H, T, D, 128, fmt, ov.data_ptr(), stream))
+
+            t_kvq = timer.run(kvq, 20, warmup=3, name="kv_quant_K+V" + tag)
+            t_kvd = timer.run(kvd, 20, warmup=3, name="kv_dequant_K+V" + tag)
+            passes["kv_quant_K+V" + tag] = {"us": t_kvq * 1e6, "GB/s": kv_bytes / t_kvq / 1e9,
+                                            "frac_hbm": kv_bytes / t_kvq / 1e9 / PEAK_HBM_GBPS}
+            passes["kv_dequant_K+V" + tag] = {"us": t_kvd * 1e6, "GB/s": kv_bytes / t_kvd / 1e9,
+                                              "frac_hbm": kv_bytes / t_kvd / 1e9 / PEAK_HBM_GBPS}
         del kd, vd, qk, qv, ok, ov
     if not args.no_secondary and args.only in (None, "decode"):
         c3 = syn.CONFIGS[3]
