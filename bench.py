@@ -197,6 +197,28 @@ def main():
         passes["gemm"] = {"us": t_gemm * 1e6, "TFLOP/s": flops / t_gemm / 1e12,
                           "frac_fp8_peak": flops / t_gemm / 1e12 / PEAK_FP8_TFLOPS}
     if args.only is None and not args.no_secondary:
+        # The GEMM's output quantized for the next layer (1 x 128 groups along
+        # N): fused into the GEMM epilogue, against the GEMM's bf16 output
+        # followed by the stand-alone quantizer over it.
+        qc = torch.empty((M, N), dtype=torch.uint8, device=dev)
+        scq = torch.empty((N // 128, M), dtype=torch.float32, device=dev).t()
+
+        def fused(i):
+            j = i % nsets
+            fp8.fp8_block_gemm_quant(qa_sets[j], sa_sets[j], "group_1x128", qw, sw, "block_128x128",
+                                     out=qc, scales=scq)
+
+        def unfused(i):
+            gemm(i)
+            fp8.fp8_quantize(out, "group_1x128", out=qc, scales=scq)
+
+        t_f = timer.run(fused, max(args.steps, 10), warmup=args.warmup, name="gemm_fused_quant_out")
+        t_u = timer.run(unfused, max(args.steps, 10), warmup=args.warmup, name="gemm_then_quantize_out")
+        passes["gemm_fused_quant_out"] = {"us": t_f * 1e6, "TFLOP/s": flops / t_f / 1e12,
+                                          "frac_fp8_peak": flops / t_f / 1e12 / PEAK_FP8_TFLOPS}
+        passes["gemm_then_quantize_out"] = {"us": t_u * 1e6, "TFLOP/s": flops / t_u / 1e12}
+        del qc, scq
+    if args.only is None and not args.no_secondary:
         # E5M2 activations (1x128) against the E4M3 weights: the same GEMM
         # kernel with the MFMA's A operand decoded as E5M2
         qa5 = torch.empty((M, K), dtype=torch.uint8, device=dev)

@@ -10,6 +10,7 @@ Entry points (same names as the C ABI):
 
 * ``fp8_quantize(x, granularity, fmt="e4m3", scale_layout="row")`` -> (codes uint8, scales fp32)
 * ``fp8_block_gemm(qa, sa, gran_a, qw, sw, gran_w, out_dtype=torch.bfloat16, fmt_a="e4m3", fmt_w="e4m3")``
+* ``fp8_block_gemm_quant(qa, sa, gran_a, qw, sw, gran_w, fmt_c="e4m3", ...)`` -> (codes uint8, scales fp32)
 * ``fp8_kv_quantize(kv, token_block=128, fmt="e4m3")`` -> (codes uint8, scales fp32)
 * ``fp8_kv_dequantize(q, scales, token_block=128, fmt="e4m3")`` -> bf16
 
@@ -54,6 +55,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp8_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, vp, i64, vp, i64, i64, vp]
     lib.fp8_block_gemm.argtypes = [i64, i64, i64, vp, i64, vp, i32, i64, i64, vp, i64, vp, i32,
                                    i64, i64, i32, i32, vp, i32, i64, vp]
+    lib.fp8_block_gemm_quant.argtypes = [i64, i64, i64, vp, i64, vp, i32, i64, i64, vp, i64, vp, i32,
+                                         i64, i64, i32, i32, i32, vp, i64, vp, i64, i64, vp]
+    lib.fp8_block_gemm_quant.restype = i32
     lib.fp8_kv_quantize.argtypes = [vp, i64, i64, i64, i64, i64, i64, i32, vp, vp, vp]
     lib.fp8_kv_dequantize.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp, vp]
     for f in ("fp8_quantize", "fp8_block_gemm", "fp8_kv_quantize", "fp8_kv_dequantize"):
@@ -156,6 +160,40 @@ def fp8_block_gemm(qa: torch.Tensor, sa: torch.Tensor, gran_a: str, qw: torch.Te
                               _ptr(qw), qw.stride(0), _ptr(sw), gw, swn, swk, _FMT[fmt_a], _FMT[fmt_w],
                               _ptr(out), cdt, out.stride(0), _stream(qa)))
     return out
+
+
+def fp8_block_gemm_quant(qa: torch.Tensor, sa: torch.Tensor, gran_a: str, qw: torch.Tensor, sw: torch.Tensor,
+                         gran_w: str, fmt_c: str = "e4m3", fmt_a: str = "e4m3", fmt_w: str = "e4m3",
+                         scale_layout: str = "kmajor", out: torch.Tensor = None, scales: torch.Tensor = None):
+    """C = A . W^T quantized in the GEMM's epilogue: returns (codes uint8 [M, N]
+    of format fmt_c, scales fp32 [M, N/128]), equal to fp8_quantize(C32,
+    "group_1x128") of the fp32 product. scale_layout "kmajor" stores the grid as
+    [N/128, M] in memory (the layout the next GEMM reads fastest) and returns
+    it as a strided [M, N/128] view."""
+    lib = load_library()
+    _require_cuda(qa, sa, qw, sw)
+    M, K = qa.shape
+    N, K2 = qw.shape
+    if K != K2:
+        raise ValueError("fp8_block_gemm_quant: K mismatch")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.uint8, device=qa.device)
+    if scales is None:
+        g = N // 128
+        if scale_layout == "kmajor":
+            scales = torch.empty((g, M), dtype=torch.float32, device=qa.device).t()
+        else:
+            scales = torch.empty((M, g), dtype=torch.float32, device=qa.device)
+    ga, gw = _GRAN[gran_a], _GRAN[gran_w]
+    sam = sa.stride(0) if sa.dim() == 2 else 0
+    sak = sa.stride(1) if sa.dim() == 2 else 0
+    swn = sw.stride(0) if sw.dim() == 2 else 0
+    swk = sw.stride(1) if sw.dim() == 2 else 0
+    _check(lib.fp8_block_gemm_quant(M, N, K, _ptr(qa), qa.stride(0), _ptr(sa), ga, sam, sak,
+                                    _ptr(qw), qw.stride(0), _ptr(sw), gw, swn, swk, _FMT[fmt_a], _FMT[fmt_w],
+                                    _FMT[fmt_c], _ptr(out), out.stride(0), _ptr(scales), scales.stride(0),
+                                    scales.stride(1), _stream(qa)))
+    return out, scales
 
 
 def fp8_kv_quantize(kv: torch.Tensor, token_block: int = 128, fmt: str = "e4m3"):

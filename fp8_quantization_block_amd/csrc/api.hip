@@ -138,20 +138,23 @@ fp8blk_status fp8_quantize(const void* x, fp8blk_dtype x_dtype, int64_t rows, in
   return hip_status(fp8blk::launch_quantize(a, static_cast<hipStream_t>(stream)), fn);
 }
 
-fp8blk_status fp8_block_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
-                             const float* scale_a, fp8blk_granularity gran_a, int64_t sa_stride_m,
-                             int64_t sa_stride_k, const uint8_t* b, int64_t ldb,
-                             const float* scale_b, fp8blk_granularity gran_b, int64_t sb_stride_n,
-                             int64_t sb_stride_k, fp8blk_format fmt_a, fp8blk_format fmt_b,
-                             void* c, fp8blk_dtype c_dtype, int64_t ldc, void* stream) {
-  const char* fn = "fp8_block_gemm";
-  if (!a || !b || !scale_a || !scale_b || !c) return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
+}  // extern "C"
+
+namespace {
+
+// Validation shared by both GEMM entry points: everything about the inputs.
+// Fills `g` with the inputs and the byte ranges of the four input arrays.
+fp8blk_status check_gemm_inputs(const char* fn, int64_t M, int64_t N, int64_t K, const uint8_t* a,
+                                int64_t lda, const float* scale_a, fp8blk_granularity gran_a,
+                                int64_t sa_stride_m, int64_t sa_stride_k, const uint8_t* b, int64_t ldb,
+                                const float* scale_b, fp8blk_granularity gran_b, int64_t sb_stride_n,
+                                int64_t sb_stride_k, fp8blk_format fmt_a, fp8blk_format fmt_b,
+                                fp8blk::GemmArgs& g, Range (&in)[4]) {
+  if (!a || !b || !scale_a || !scale_b) return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
   if (gran_a != FP8BLK_PER_TENSOR && gran_a != FP8BLK_GROUP_1x128)
     return fail(FP8BLK_EINVAL, "%s: gran_a must be PER_TENSOR or GROUP_1x128", fn);
   if (gran_b != FP8BLK_PER_TENSOR && gran_b != FP8BLK_BLOCK_128x128)
     return fail(FP8BLK_EINVAL, "%s: gran_b must be PER_TENSOR or BLOCK_128x128", fn);
-  if (c_dtype != FP8BLK_BF16 && c_dtype != FP8BLK_F32)
-    return fail(FP8BLK_EINVAL, "%s: unknown output dtype %d", fn, (int)c_dtype);
   if (fp8blk_status st = check_format(fmt_a, fn)) return st;
   if (fp8blk_status st = check_format(fmt_b, fn)) return st;
   if (M < 0 || N <= 0 || K <= 0) return fail(FP8BLK_EINVAL, "%s: need M >= 0, N > 0, K > 0", fn);
@@ -159,27 +162,22 @@ fp8blk_status fp8_block_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, 
     return fail(FP8BLK_EUNSUPPORTED, "%s: dimension above 2^31", fn);
   if (N % 128 != 0 || K % 128 != 0)
     return fail(FP8BLK_EUNSUPPORTED, "%s: N and K must be multiples of 128", fn);
-  if (lda < K || ldb < K || ldc < N) return fail(FP8BLK_EINVAL, "%s: leading dimension too small", fn);
+  if (lda < K || ldb < K) return fail(FP8BLK_EINVAL, "%s: leading dimension too small", fn);
   if (lda >= kMaxLdCodes || ldb >= kMaxLdCodes)
     return fail(FP8BLK_EUNSUPPORTED, "%s: lda and ldb must be below 2^23", fn);
   if (sa_stride_m < 0 || sa_stride_k < 0 || sb_stride_n < 0 || sb_stride_k < 0)
     return fail(FP8BLK_EINVAL, "%s: negative scale stride", fn);
-  const int64_t csz = c_dtype == FP8BLK_BF16 ? 2 : 4;
-  if (!aligned16(a) || !aligned16(b) || !aligned16(c))
-    return fail(FP8BLK_EALIGN, "%s: a, b and c must be 16-byte aligned", fn);
-  if (lda % 16 != 0 || ldb % 16 != 0 || (ldc * csz) % 16 != 0)
-    return fail(FP8BLK_EALIGN, "%s: lda, ldb and ldc * elem_size must be multiples of 16 bytes", fn);
-  if (M == 0) return ok();
-  const Range rc = range2d(c, M, N, ldc, csz);
-  const Range ra = range2d(a, M, K, lda, 1);
-  const Range rb = range2d(b, N, K, ldb, 1);
-  const Range rsa = gran_a == FP8BLK_PER_TENSOR ? range_grid(scale_a, 1, 1, 0, 0)
-                                                : range_grid(scale_a, M, K / 128, sa_stride_m, sa_stride_k);
-  const Range rsb = gran_b == FP8BLK_PER_TENSOR ? range_grid(scale_b, 1, 1, 0, 0)
-                                                : range_grid(scale_b, N / 128, K / 128, sb_stride_n, sb_stride_k);
-  if (overlap(rc, ra) || overlap(rc, rb) || overlap(rc, rsa) || overlap(rc, rsb))
-    return fail(FP8BLK_EINVAL, "%s: c must not overlap the inputs", fn);
-  fp8blk::GemmArgs g;
+  if (!aligned16(a) || !aligned16(b)) return fail(FP8BLK_EALIGN, "%s: a and b must be 16-byte aligned", fn);
+  if (lda % 16 != 0 || ldb % 16 != 0) return fail(FP8BLK_EALIGN, "%s: lda and ldb must be multiples of 16 bytes", fn);
+  if (M > 0) {
+    in[0] = range2d(a, M, K, lda, 1);
+    in[1] = range2d(b, N, K, ldb, 1);
+    in[2] = gran_a == FP8BLK_PER_TENSOR ? range_grid(scale_a, 1, 1, 0, 0)
+                                        : range_grid(scale_a, M, K / 128, sa_stride_m, sa_stride_k);
+    in[3] = gran_b == FP8BLK_PER_TENSOR ? range_grid(scale_b, 1, 1, 0, 0)
+                                        : range_grid(scale_b, N / 128, K / 128, sb_stride_n, sb_stride_k);
+  }
+  g = fp8blk::GemmArgs{};
   g.M = M;
   g.N = N;
   g.K = K;
@@ -195,11 +193,85 @@ fp8blk_status fp8_block_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, 
   g.gran_b = (int)gran_b;
   g.sb_n = sb_stride_n;
   g.sb_k = sb_stride_k;
+  g.fmt_a = (int)fmt_a;
+  g.fmt_b = (int)fmt_b;
+  return FP8BLK_OK;
+}
+
+bool overlaps_any(Range r, const Range (&in)[4]) {
+  for (const Range& x : in)
+    if (overlap(r, x)) return true;
+  return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8blk_status fp8_block_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                             const float* scale_a, fp8blk_granularity gran_a, int64_t sa_stride_m,
+                             int64_t sa_stride_k, const uint8_t* b, int64_t ldb,
+                             const float* scale_b, fp8blk_granularity gran_b, int64_t sb_stride_n,
+                             int64_t sb_stride_k, fp8blk_format fmt_a, fp8blk_format fmt_b,
+                             void* c, fp8blk_dtype c_dtype, int64_t ldc, void* stream) {
+  const char* fn = "fp8_block_gemm";
+  fp8blk::GemmArgs g;
+  Range in[4] = {};
+  if (fp8blk_status st = check_gemm_inputs(fn, M, N, K, a, lda, scale_a, gran_a, sa_stride_m, sa_stride_k, b,
+                                           ldb, scale_b, gran_b, sb_stride_n, sb_stride_k, fmt_a, fmt_b, g, in))
+    return st;
+  if (!c) return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
+  if (c_dtype != FP8BLK_BF16 && c_dtype != FP8BLK_F32)
+    return fail(FP8BLK_EINVAL, "%s: unknown output dtype %d", fn, (int)c_dtype);
+  if (ldc < N) return fail(FP8BLK_EINVAL, "%s: leading dimension too small", fn);
+  const int64_t csz = c_dtype == FP8BLK_BF16 ? 2 : 4;
+  if (!aligned16(c)) return fail(FP8BLK_EALIGN, "%s: c must be 16-byte aligned", fn);
+  if ((ldc * csz) % 16 != 0) return fail(FP8BLK_EALIGN, "%s: ldc * elem_size must be a multiple of 16 bytes", fn);
+  if (M == 0) return ok();
+  if (overlaps_any(range2d(c, M, N, ldc, csz), in)) return fail(FP8BLK_EINVAL, "%s: c must not overlap the inputs", fn);
   g.c = c;
   g.c_dtype = (int)c_dtype;
   g.ldc = ldc;
-  g.fmt_a = (int)fmt_a;
-  g.fmt_b = (int)fmt_b;
+  g.quant_out = 0;
+  return hip_status(fp8blk::launch_block_gemm(g, static_cast<hipStream_t>(stream)), fn);
+}
+
+fp8blk_status fp8_block_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                                   const float* scale_a, fp8blk_granularity gran_a, int64_t sa_stride_m,
+                                   int64_t sa_stride_k, const uint8_t* b, int64_t ldb,
+                                   const float* scale_b, fp8blk_granularity gran_b, int64_t sb_stride_n,
+                                   int64_t sb_stride_k, fp8blk_format fmt_a, fp8blk_format fmt_b,
+                                   fp8blk_format fmt_c, uint8_t* qc, int64_t ldqc, float* scale_c,
+                                   int64_t sc_stride_m, int64_t sc_stride_n, void* stream) {
+  const char* fn = "fp8_block_gemm_quant";
+  fp8blk::GemmArgs g;
+  Range in[4] = {};
+  if (fp8blk_status st = check_gemm_inputs(fn, M, N, K, a, lda, scale_a, gran_a, sa_stride_m, sa_stride_k, b,
+                                           ldb, scale_b, gran_b, sb_stride_n, sb_stride_k, fmt_a, fmt_b, g, in))
+    return st;
+  if (!qc || !scale_c) return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
+  if (fp8blk_status st = check_format(fmt_c, fn)) return st;
+  if (ldqc < N) return fail(FP8BLK_EINVAL, "%s: leading dimension too small", fn);
+  if (sc_stride_m < 0 || sc_stride_n < 0) return fail(FP8BLK_EINVAL, "%s: negative scale stride", fn);
+  if (!aligned16(qc) || ldqc % 16 != 0)
+    return fail(FP8BLK_EALIGN, "%s: qc must be 16-byte aligned and ldqc a multiple of 16", fn);
+  if (M == 0) return ok();
+  const int64_t groups = N / 128;
+  if ((M > 1 && sc_stride_m == 0) || (groups > 1 && sc_stride_n == 0))
+    return fail(FP8BLK_EINVAL, "%s: zero scale stride on a grid axis longer than 1", fn);
+  const Range rq = range2d(qc, M, N, ldqc, 1);
+  const Range rs = range_grid(scale_c, M, groups, sc_stride_m, sc_stride_n);
+  if (overlaps_any(rq, in) || overlaps_any(rs, in) || overlap(rq, rs))
+    return fail(FP8BLK_EINVAL, "%s: qc and scale_c must not overlap each other or the inputs", fn);
+  g.c = nullptr;
+  g.c_dtype = (int)FP8BLK_F32;
+  g.ldc = ldqc;
+  g.quant_out = 1;
+  g.fmt_c = (int)fmt_c;
+  g.qc = qc;
+  g.sc = scale_c;
+  g.sc_m = sc_stride_m;
+  g.sc_n = sc_stride_n;
   return hip_status(fp8blk::launch_block_gemm(g, static_cast<hipStream_t>(stream)), fn);
 }
 

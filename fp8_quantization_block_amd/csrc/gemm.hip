@@ -34,9 +34,17 @@
 //   chunk c ^ swz(r), so the operand reads are free of bank conflicts.
 // * Workgroup ids are remapped so that neighbouring tiles (which share A rows
 //   or B columns) run on the same XCD and share its L2.
+// * Output: bf16, fp32, or (fused quantization) FP8 codes with one scale per
+//   row and 128-column group. A wave owns 64 rows x 128 columns, i.e. exactly
+//   one 1 x 128 group of each of its rows, so the group amax is a max over the
+//   wave's own registers and one 16-lane DPP reduction: the next GEMM's
+//   activation quantization ([FP8] section "激活动态量化": one scale per token
+//   and 128-channel group, computed at run time) runs in this epilogue instead
+//   of as a separate pass over the bf16 output.
 #include <hip/hip_bf16.h>
 #include <hip/hip_runtime.h>
 
+#include "device_common.h"
 #include "internal.h"
 
 namespace fp8blk {
@@ -70,6 +78,9 @@ struct GemmParams {
   void* c;
   int64_t lda, ldb, ldc;
   int64_t sa_m, sa_k, sb_n, sb_k;
+  uint8_t* qc;          // fused quantization: codes (row stride ldc bytes) ...
+  float* sc;            // ... and scales, sc[row * sc_m + group * sc_n]
+  int64_t sc_m, sc_n;
   int M, N, K;
   int tiles_m, tiles_n;
   // Tail balancing: the last n_half tiles (in tile order) are computed as two
@@ -285,7 +296,13 @@ __device__ __forceinline__ void k_loop(const Plan& pl, const uint8_t* __restrict
   if (active) drain(pp, acc);
 }
 
-template <bool kBf16Out, int kFa, int kFb>
+// Output modes of the prefill kernel.
+enum OutMode : int { OUT_BF16 = 0, OUT_F32 = 1, OUT_Q_E4M3 = 2, OUT_Q_E5M2 = 3 };
+// quantized output staging: per wave 64 rows of 128 codes, 144-byte pitch
+constexpr int kQPitch = 144;
+static_assert(8 * 64 * kQPitch <= kSmemBytes, "quantized output staging exceeds the LDS");
+
+template <int kOut, int kFa, int kFb>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
   // LDS: two stages of operand tiles and scales during the K loop; afterwards
   // the same memory stages the bf16 output for coalesced stores
@@ -389,7 +406,45 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
   if (!active) return;
   // ---- epilogue: lane holds rows 4 * (lane / 16) + v, column lane % 16 ----
   const int q = lane >> 4, c16 = lane & 15;
-  if (kBf16Out) {
+  if constexpr (kOut == OUT_Q_E4M3 || kOut == OUT_Q_E5M2) {
+    // Row (mi, v) of this lane has its 128-column group in the 16 lanes of the
+    // lane's DPP row (8 values each): group amax, scale, codes as the
+    // stand-alone 1 x 128 quantizer computes them for fp32 inputs; codes are
+    // staged in the idle LDS and stored row by row, 16 bytes per lane.
+    constexpr int kFc = kOut == OUT_Q_E4M3 ? FMT_E4M3 : FMT_E5M2;
+    uint8_t* const ep = smem + wave * (64 * kQPitch);
+    const int64_t grp = (n0 + wn * 128) >> 7;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni) m = amax_f32(acc[mi][ni][v], m);
+        const GroupScale gs = make_group_scale<kFc>(row16_max(m));
+        const uint32_t w0 = cast4_f32<kFc>(gs, acc[mi][0][v], acc[mi][1][v], acc[mi][2][v], acc[mi][3][v]);
+        const uint32_t w1 = cast4_f32<kFc>(gs, acc[mi][4][v], acc[mi][5][v], acc[mi][6][v], acc[mi][7][v]);
+        const int r = mi * 16 + 4 * q + v;
+        uint8_t* const rowp = ep + r * kQPitch + c16;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          rowp[ni * 16] = (uint8_t)(w0 >> (8 * ni));
+          rowp[(ni + 4) * 16] = (uint8_t)(w1 >> (8 * ni));
+        }
+        const int row = m0 + wm * 64 + r;
+        if (c16 == 0 && row < p.M) p.sc[(int64_t)row * p.sc_m + grp * p.sc_n] = gs.s;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = i * 64 + lane;
+      const int r = idx >> 3, ch = idx & 7;
+      const v4i val = *reinterpret_cast<const v4i*>(ep + r * kQPitch + ch * 16);
+      const int row = m0 + wm * 64 + r;
+      if (row < p.M)
+        __builtin_nontemporal_store(val, reinterpret_cast<v4i*>(p.qc + (int64_t)row * p.ldc + n0 + wn * 128 + ch * 16));
+    }
+  } else if constexpr (kOut == OUT_BF16) {
     // Every wave is past the loop's last barrier and no copy is in flight, so
     // the LDS is free: stage the wave's 64 x 128 block as bf16, then store it
     // row by row, 16 bytes per lane (16 lanes per 256-byte row).
@@ -563,17 +618,24 @@ void launch_decode(const GemmParams& p, bool bf16, hipStream_t st) {
 }
 
 // Kernel choice for one (format of A, format of B) pair: the decode kernel for
-// M <= 64, else the prefill kernel on a grid of n_full + 2 n_half workgroups.
+// M <= 64 (bf16 / fp32 output), else the prefill kernel on a grid of
+// n_full + 2 n_half workgroups. The fused quantized output always takes the
+// prefill kernel (its epilogue needs a wave's whole 128-column group).
 template <int kFa, int kFb>
-void launch_formats(const GemmParams& p, bool bf16, hipStream_t st) {
-  if (p.M <= 16) return launch_decode<1, kFa, kFb>(p, bf16, st);
-  if (p.M <= 32) return launch_decode<2, kFa, kFb>(p, bf16, st);
-  if (p.M <= 64) return launch_decode<4, kFa, kFb>(p, bf16, st);
+void launch_formats(const GemmParams& p, int out, hipStream_t st) {
+  if (out == OUT_BF16 || out == OUT_F32) {
+    const bool bf16 = out == OUT_BF16;
+    if (p.M <= 16) return launch_decode<1, kFa, kFb>(p, bf16, st);
+    if (p.M <= 32) return launch_decode<2, kFa, kFb>(p, bf16, st);
+    if (p.M <= 64) return launch_decode<4, kFa, kFb>(p, bf16, st);
+  }
   const dim3 grid((unsigned)(p.n_full + 2 * p.n_half));
-  if (bf16)
-    hipLaunchKernelGGL((k_gemm_fp8_block<true, kFa, kFb>), grid, dim3(kThreads), 0, st, p);
-  else
-    hipLaunchKernelGGL((k_gemm_fp8_block<false, kFa, kFb>), grid, dim3(kThreads), 0, st, p);
+  switch (out) {
+    case OUT_BF16: hipLaunchKernelGGL((k_gemm_fp8_block<OUT_BF16, kFa, kFb>), grid, dim3(kThreads), 0, st, p); break;
+    case OUT_F32: hipLaunchKernelGGL((k_gemm_fp8_block<OUT_F32, kFa, kFb>), grid, dim3(kThreads), 0, st, p); break;
+    case OUT_Q_E4M3: hipLaunchKernelGGL((k_gemm_fp8_block<OUT_Q_E4M3, kFa, kFb>), grid, dim3(kThreads), 0, st, p); break;
+    default: hipLaunchKernelGGL((k_gemm_fp8_block<OUT_Q_E5M2, kFa, kFb>), grid, dim3(kThreads), 0, st, p); break;
+  }
 }
 
 }  // namespace
@@ -599,6 +661,10 @@ hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t st) {
   p.sa = g.sa;
   p.sb = g.sb;
   p.c = g.c;
+  p.qc = g.qc;
+  p.sc = g.sc;
+  p.sc_m = g.sc_m;
+  p.sc_n = g.sc_n;
   p.lda = g.lda;
   p.ldb = g.ldb;
   p.ldc = g.ldc;
@@ -611,10 +677,11 @@ hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t st) {
   p.K = (int)g.K;
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
-  const bool bf16 = g.c_dtype == DTYPE_BF16;
+  const int out = g.quant_out ? (g.fmt_c == FMT_E5M2 ? OUT_Q_E5M2 : OUT_Q_E4M3)
+                              : (g.c_dtype == DTYPE_BF16 ? OUT_BF16 : OUT_F32);
   // tail balancing (see GemmParams)
   const int tiles = p.tiles_m * p.tiles_n;
-  const int cus = p.M > 64 ? device_cu_count() : 0;
+  const int cus = (p.M > 64 || g.quant_out) ? device_cu_count() : 0;
   const int rem = cus > 0 ? tiles % cus : 0;
   p.n_full = tiles;
   p.n_half = 0;
@@ -623,10 +690,10 @@ hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t st) {
     p.n_half = rem;
   }
   const bool a5 = g.fmt_a == FMT_E5M2, b5 = g.fmt_b == FMT_E5M2;
-  if (!a5 && !b5) launch_formats<FMT_E4M3, FMT_E4M3>(p, bf16, st);
-  else if (!a5 && b5) launch_formats<FMT_E4M3, FMT_E5M2>(p, bf16, st);
-  else if (a5 && !b5) launch_formats<FMT_E5M2, FMT_E4M3>(p, bf16, st);
-  else launch_formats<FMT_E5M2, FMT_E5M2>(p, bf16, st);
+  if (!a5 && !b5) launch_formats<FMT_E4M3, FMT_E4M3>(p, out, st);
+  else if (!a5 && b5) launch_formats<FMT_E4M3, FMT_E5M2>(p, out, st);
+  else if (a5 && !b5) launch_formats<FMT_E5M2, FMT_E4M3>(p, out, st);
+  else launch_formats<FMT_E5M2, FMT_E5M2>(p, out, st);
   return hipGetLastError();
 }
 

@@ -51,8 +51,16 @@ struct GemmArgs {
   int64_t sb_n, sb_k;
   void* c;
   int c_dtype;
-  int64_t ldc;
+  int64_t ldc;          // row stride of c, or of qc (bytes) when quant_out
   int fmt_a, fmt_b;
+  // quant_out: instead of c, write the output as FP8 codes of format fmt_c
+  // (qc) with one fp32 scale per row and 128-column group at
+  // sc[row * sc_m + group * sc_n]
+  int quant_out;
+  int fmt_c;
+  uint8_t* qc;
+  float* sc;
+  int64_t sc_m, sc_n;
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);

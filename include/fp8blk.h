@@ -137,6 +137,43 @@ fp8blk_status fp8_block_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, 
                              void* c, fp8blk_dtype c_dtype, int64_t ldc, void* stream);
 
 /*
+ * fp8_block_gemm_quant -- fp8_block_gemm whose output is quantized in the same
+ * kernel: C = A . B^T computed exactly as fp8_block_gemm computes its fp32
+ * output, then written as FP8 codes of format fmt_c with one fp32 scale per
+ * row and 128-column group, i.e. the 1 x 128 activation quantization of
+ * fp8_quantize (GROUP_1x128) applied to that fp32 C.
+ *
+ * Defined by [FP8] section "激活动态量化" (activations of the next matrix
+ * multiply get one scale per token and 128-channel group, computed at run
+ * time) on top of the product fp8_block_gemm defines; the output of one layer
+ * is the activation of the next, so quantizing it where it is produced
+ * replaces a separate pass over a bf16 copy of it.
+ *
+ *   Inputs, their layouts and requirements: as fp8_block_gemm.
+ *   qc      device, uint8 codes [M][N] of format fmt_c, row stride ldqc bytes.
+ *   scale_c device, fp32 grid [M][N / 128]; element (m, g) at
+ *           scale_c[m * sc_stride_m + g * sc_stride_n]. sc_stride_m = 1 and
+ *           sc_stride_n = M give the K-block-major layout fp8_block_gemm reads
+ *           fastest when qc is the next GEMM's A.
+ *
+ * Requirements: as fp8_block_gemm for the inputs; qc and scale_c non-null; qc
+ * 16-byte aligned, ldqc >= N and a multiple of 16; strides >= 0, nonzero on a
+ * grid axis longer than 1; qc and scale_c must not overlap each other or the
+ * inputs. For M > 64 the results are bit-identical to fp8_quantize(GROUP_1x128)
+ * of the fp32 output of fp8_block_gemm on the same inputs (the same kernel
+ * and summation order). For M <= 64 this entry point still runs that kernel,
+ * while fp8_block_gemm takes a split-K kernel whose fp32 sums may differ in
+ * the last bits; both meet the same tolerance.
+ */
+fp8blk_status fp8_block_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                                   const float* scale_a, fp8blk_granularity gran_a, int64_t sa_stride_m,
+                                   int64_t sa_stride_k, const uint8_t* b, int64_t ldb,
+                                   const float* scale_b, fp8blk_granularity gran_b, int64_t sb_stride_n,
+                                   int64_t sb_stride_k, fp8blk_format fmt_a, fp8blk_format fmt_b,
+                                   fp8blk_format fmt_c, uint8_t* qc, int64_t ldqc, float* scale_c,
+                                   int64_t sc_stride_m, int64_t sc_stride_n, void* stream);
+
+/*
  * fp8_kv_quantize -- FP8 KV-cache quantization with one scale per (head, token block).
  *
  * Defined by [LONG] section 1 (K and V quantized to FP8 with separate scales)

@@ -40,7 +40,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("fp8_quantize", "fp8_block_gemm", "fp8_kv_quantize", "fp8_kv_dequantize",
+    for n in ("fp8_quantize", "fp8_block_gemm", "fp8_block_gemm_quant", "fp8_kv_quantize", "fp8_kv_dequantize",
               "fp8blk_status_string", "fp8blk_last_error", "fp8blk_abi_version"):
         assert n in names
 
@@ -127,6 +127,37 @@ def g(lib, M=256, N=256, K=256, a=PA, lda=256, sa=PB, ga=GROUP, sam=2, sak=1, b=
 def test_gemm_rejects(lib, kw, status):
     assert g(lib, **kw) == status
     assert lib.fp8blk_last_error().decode().startswith("fp8_block_gemm")
+
+
+def gq(lib, M=256, N=256, K=256, a=PA, lda=256, sa=PB, ga=GROUP, sam=2, sak=1, b=PC, ldb=256,
+       sb=PB + 65536, gb=BLOCK, sbn=2, sbk=1, fa=E4M3, fb=E4M3, fc=E4M3, qc=PD, ldqc=256,
+       sc=PD + (1 << 20), scm=1, scn=256):
+    return lib.fp8_block_gemm_quant(M, N, K, a, lda, sa, ga, sam, sak, b, ldb, sb, gb, sbn, sbk, fa, fb, fc,
+                                    qc, ldqc, sc, scm, scn, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a=0), EINVAL),
+    (dict(qc=0), EINVAL),
+    (dict(sc=0), EINVAL),
+    (dict(fc=2), EINVAL),
+    (dict(fc=E5M2, ldqc=128), EINVAL),       # E5M2 output passes the format check
+    (dict(N=200), EUNSUPPORTED),
+    (dict(qc=PD + 4), EALIGN),
+    (dict(ldqc=264), EALIGN),
+    (dict(scm=-1), EINVAL),
+    (dict(scm=0), EINVAL),                   # rows collapse onto one scale
+    (dict(scn=0), EINVAL),                   # groups collapse onto one scale
+    (dict(qc=PA + 1024), EINVAL),            # codes overlap a
+    (dict(sc=PD + 4096), EINVAL),            # scales overlap the codes
+])
+def test_gemm_quant_rejects(lib, kw, status):
+    assert gq(lib, **kw) == status
+    assert lib.fp8blk_last_error().decode().startswith("fp8_block_gemm_quant")
+
+
+def test_gemm_quant_empty_m_is_a_noop(lib):
+    assert gq(lib, M=0) == OK
 
 
 def test_gemm_empty_m_is_a_noop(lib):
