@@ -297,6 +297,23 @@ def main():
                                             "frac_hbm": kv_bytes / t_kvq / 1e9 / PEAK_HBM_GBPS}
             passes["kv_dequant_K+V" + tag] = {"us": t_kvd * 1e6, "GB/s": kv_bytes / t_kvd / 1e9,
                                               "frac_hbm": kv_bytes / t_kvd / 1e9 / PEAK_HBM_GBPS}
+            # decode attention of 64 query heads (8 per kv head) over the codes
+            # just written: algorithmic bytes = both code tensors, their
+            # scales, the bf16 query and output
+            hq = c5["heads_q"]
+            qd = syn.decode_queries(heads_q=hq).to(dev)
+            od = torch.empty((hq, D), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(lib.fp8_kv_decode_attention_workspace_size(hq, T), dtype=torch.uint8, device=dev)
+            fname = "e5m2" if fmt == fp8.E5M2 else "e4m3"
+
+            def att(i, fname=fname):
+                fp8.fp8_kv_decode_attention(qd, qk, sk, qv, sv, 1.0 / 128 ** 0.5, fmt=fname, out=od, workspace=ws)
+
+            att_bytes = n + 2 * H * (T // 128) * 4 + 2 * hq * D * 2
+            t_att = timer.run(att, 20, warmup=3, name="kv_decode_attention" + tag)
+            passes["kv_decode_attention" + tag] = {"us": t_att * 1e6, "GB/s": att_bytes / t_att / 1e9,
+                                                   "frac_hbm": att_bytes / t_att / 1e9 / PEAK_HBM_GBPS}
+            del qd, od, ws
         del kd, vd, qk, qv, ok, ov
     if not args.no_secondary and args.only in (None, "decode"):
         c3 = syn.CONFIGS[3]

@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
 * ``fp8_block_gemm_quant(qa, sa, gran_a, qw, sw, gran_w, fmt_c="e4m3", ...)`` -> (codes uint8, scales fp32)
 * ``fp8_kv_quantize(kv, token_block=128, fmt="e4m3")`` -> (codes uint8, scales fp32)
 * ``fp8_kv_dequantize(q, scales, token_block=128, fmt="e4m3")`` -> bf16
+* ``fp8_kv_decode_attention(q, k_codes, k_scales, v_codes, v_scales, softmax_scale, fmt="e4m3")`` -> [heads_q, 128]
 
 ``fmt`` is "e4m3" (largest value 448) or "e5m2" (largest value 57344).
 """
@@ -58,6 +59,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp8_block_gemm_quant.argtypes = [i64, i64, i64, vp, i64, vp, i32, i64, i64, vp, i64, vp, i32,
                                          i64, i64, i32, i32, i32, vp, i64, vp, i64, i64, vp]
     lib.fp8_block_gemm_quant.restype = i32
+    lib.fp8_kv_decode_attention_workspace_size.argtypes = [i64, i64]
+    lib.fp8_kv_decode_attention_workspace_size.restype = ctypes.c_size_t
+    lib.fp8_kv_decode_attention.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, i64, i32, ctypes.c_float,
+                                            vp, i32, i64, vp, ctypes.c_size_t, vp]
+    lib.fp8_kv_decode_attention.restype = i32
     lib.fp8_kv_quantize.argtypes = [vp, i64, i64, i64, i64, i64, i64, i32, vp, vp, vp]
     lib.fp8_kv_dequantize.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp, vp]
     for f in ("fp8_quantize", "fp8_block_gemm", "fp8_kv_quantize", "fp8_kv_dequantize"):
@@ -209,6 +215,36 @@ def fp8_kv_quantize(kv: torch.Tensor, token_block: int = 128, fmt: str = "e4m3")
     _check(lib.fp8_kv_quantize(_ptr(kv), h, t, d, kv.stride(0), kv.stride(1), token_block, _FMT[fmt],
                                _ptr(q), _ptr(s), _stream(kv)))
     return q, s
+
+
+def fp8_kv_decode_attention(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, v_codes: torch.Tensor,
+                            v_scales: torch.Tensor, softmax_scale: float, fmt: str = "e4m3",
+                            out_dtype=torch.bfloat16, out: torch.Tensor = None, workspace: torch.Tensor = None):
+    """One decode step of attention over an FP8 KV cache: q bf16 [heads_q, 128];
+    k_codes / v_codes uint8 [heads_kv, tokens, 128] with fp32 scales
+    [heads_kv, ceil(tokens/128)] (as fp8_kv_quantize writes them). Returns
+    [heads_q, 128] in out_dtype. The workspace is allocated here unless given."""
+    lib = load_library()
+    _require_cuda(q, k_codes, k_scales, v_codes, v_scales)
+    if q.dtype != torch.bfloat16 or q.dim() != 2 or q.stride(1) != 1:
+        raise ValueError("fp8_kv_decode_attention: q must be bf16 [heads_q, head_dim] with contiguous rows")
+    hq, d = q.shape
+    hkv, t, d2 = k_codes.shape
+    if d2 != d or tuple(v_codes.shape) != (hkv, t, d):
+        raise ValueError("fp8_kv_decode_attention: shape mismatch")
+    k_codes, v_codes = k_codes.contiguous(), v_codes.contiguous()
+    k_scales, v_scales = k_scales.contiguous(), v_scales.contiguous()
+    if out is None:
+        out = torch.empty((hq, d), dtype=out_dtype, device=q.device)
+    need = lib.fp8_kv_decode_attention_workspace_size(hq, t)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    odt = BF16 if out.dtype == torch.bfloat16 else F32
+    _check(lib.fp8_kv_decode_attention(_ptr(q), q.stride(0), hq, hkv, t, d, _ptr(k_codes), _ptr(k_scales),
+                                       _ptr(v_codes), _ptr(v_scales), 128, _FMT[fmt], float(softmax_scale),
+                                       _ptr(out), odt, out.stride(0), _ptr(workspace), workspace.numel(),
+                                       _stream(q)))
+    return out
 
 
 def fp8_kv_dequantize(q: torch.Tensor, scales: torch.Tensor, token_block: int = 128, fmt: str = "e4m3"):

@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfp8blk.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "attention.hip"]
 # measurement-only kernels, loaded by bench.py alone (kept out of the product library)
 BENCH_LIB = os.path.join(PKG, "libfp8blk_bench.so")
 BENCH_SOURCES = ["bench_ceiling.hip"]

@@ -275,6 +275,72 @@ fp8blk_status fp8_block_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_
   return hip_status(fp8blk::launch_block_gemm(g, static_cast<hipStream_t>(stream)), fn);
 }
 
+size_t fp8_kv_decode_attention_workspace_size(int64_t heads_q, int64_t tokens) {
+  if (heads_q <= 0 || tokens <= 0) return 0;
+  return (size_t)heads_q * (size_t)fp8blk::attention_splits(tokens) * (size_t)fp8blk::attention_partial_floats() *
+         sizeof(float);
+}
+
+fp8blk_status fp8_kv_decode_attention(const void* q, int64_t ld_q, int64_t heads_q, int64_t heads_kv,
+                                      int64_t tokens, int64_t head_dim, const uint8_t* k_codes,
+                                      const float* k_scales, const uint8_t* v_codes, const float* v_scales,
+                                      int64_t token_block, fp8blk_format fmt, float softmax_scale, void* out,
+                                      fp8blk_dtype out_dtype, int64_t ld_o, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  const char* fn = "fp8_kv_decode_attention";
+  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !out || !workspace)
+    return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
+  if (fp8blk_status st = check_format(fmt, fn)) return st;
+  if (out_dtype != FP8BLK_BF16 && out_dtype != FP8BLK_F32)
+    return fail(FP8BLK_EINVAL, "%s: unknown output dtype %d", fn, (int)out_dtype);
+  if (heads_q <= 0 || heads_kv <= 0 || tokens <= 0)
+    return fail(FP8BLK_EINVAL, "%s: heads_q, heads_kv and tokens must be positive", fn);
+  if (heads_q % heads_kv != 0) return fail(FP8BLK_EINVAL, "%s: heads_q must be a multiple of heads_kv", fn);
+  if (heads_q / heads_kv > 16) return fail(FP8BLK_EUNSUPPORTED, "%s: more than 16 query heads per kv head", fn);
+  if (head_dim != 128) return fail(FP8BLK_EUNSUPPORTED, "%s: head_dim must be 128", fn);
+  if (token_block != 128) return fail(FP8BLK_EUNSUPPORTED, "%s: token_block must be 128", fn);
+  if (heads_kv >= 65536 || heads_q >= kMaxDim || tokens * 128 >= ((int64_t)1 << 32))
+    return fail(FP8BLK_EUNSUPPORTED, "%s: tensor too large", fn);
+  if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
+    return fail(FP8BLK_EINVAL, "%s: softmax_scale must be finite", fn);
+  if (ld_q < head_dim || ld_o < head_dim) return fail(FP8BLK_EINVAL, "%s: leading dimension too small", fn);
+  if (!aligned16(q) || ld_q % 8 != 0)
+    return fail(FP8BLK_EALIGN, "%s: q must be 16-byte aligned and ld_q a multiple of 8", fn);
+  if ((reinterpret_cast<uintptr_t>(out) & 3u) != 0 || (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(k_scales) & 3u) != 0 || (reinterpret_cast<uintptr_t>(v_scales) & 3u) != 0)
+    return fail(FP8BLK_EALIGN, "%s: out, workspace and scales must be 4-byte aligned", fn);
+  const size_t need = fp8_kv_decode_attention_workspace_size(heads_q, tokens);
+  if (workspace_bytes < need) return fail(FP8BLK_EINVAL, "%s: workspace smaller than %zu bytes", fn, need);
+  const int64_t nb = (tokens + 127) / 128;
+  const int64_t osz = out_dtype == FP8BLK_BF16 ? 2 : 4;
+  const Range in[5] = {range2d(q, heads_q, head_dim, ld_q, 2),
+                       {reinterpret_cast<uintptr_t>(k_codes), reinterpret_cast<uintptr_t>(k_codes) + (uintptr_t)(heads_kv * tokens * head_dim)},
+                       {reinterpret_cast<uintptr_t>(v_codes), reinterpret_cast<uintptr_t>(v_codes) + (uintptr_t)(heads_kv * tokens * head_dim)},
+                       range_grid(k_scales, heads_kv, nb, nb, 1), range_grid(v_scales, heads_kv, nb, nb, 1)};
+  const Range ro = range2d(out, heads_q, head_dim, ld_o, osz);
+  const Range rw = {reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+  for (const Range& r : in)
+    if (overlap(r, ro) || overlap(r, rw)) return fail(FP8BLK_EINVAL, "%s: out and workspace must not overlap the inputs", fn);
+  if (overlap(ro, rw)) return fail(FP8BLK_EINVAL, "%s: out must not overlap the workspace", fn);
+  fp8blk::AttnArgs a;
+  a.q = q;
+  a.ld_q = ld_q;
+  a.heads_q = heads_q;
+  a.heads_kv = heads_kv;
+  a.tokens = tokens;
+  a.k = k_codes;
+  a.v = v_codes;
+  a.sk = k_scales;
+  a.sv = v_scales;
+  a.fmt = (int)fmt;
+  a.softmax_scale = softmax_scale;
+  a.ws = static_cast<float*>(workspace);
+  a.out = out;
+  a.out_dtype = (int)out_dtype;
+  a.ld_o = ld_o;
+  return hip_status(fp8blk::launch_kv_decode_attention(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 static fp8blk_status check_kv_common(const char* fn, int64_t heads, int64_t tokens, int64_t head_dim,
                                      int64_t token_block, fp8blk_format fmt) {
   if (fp8blk_status st = check_format(fmt, fn)) return st;

@@ -1,0 +1,397 @@
+// Decode attention over an FP8 KV cache (one query token per head).
+//
+// o[g] = sum_t softmax_t(c * q[g] . k_hat[h, t]) v_hat[h, t], h = g / G, with
+// k_hat = dec(k codes) * s_k(h, t / 128) and v_hat likewise: the consumer of
+// the KV cache that fp8_kv_quantize writes. [LONG] pwwt.cn Llama-3 FP8 notes,
+// section 1 (K and V stored in FP8 with their own scales, dequantized when
+// attention reads them) and section 3 (per head and per 128-token scales);
+// [MIXED] charles2530.github.io, "量化：FP8 与混合精度推理", section "scale 是控制面"
+// (KV-cache scales per head, read by the attention backend).
+//
+// Design (gfx950), one workgroup of 4 waves per (kv head, 2048-token split):
+// * Each wave streams its 512 tokens in 64-token units, double buffered: the
+//   K and V codes of the next unit go into the wave's own LDS buffers by
+//   direct global -> LDS copies while the current unit is computed. Rows are
+//   128 bytes; logical 16-byte chunk c of row r is stored at c ^ (r % 8), so
+//   that 16 lanes reading one chunk of 16 consecutive rows hit distinct banks.
+//   The kernel is bound by reading the codes from HBM.
+// * Scores S^T = K Q^T on the bf16 MFMA (16 x 16 x 32): FP8 codes convert to
+//   bf16 exactly and the query is bf16; the 16 MFMA columns are the G query
+//   heads that share the kv head (G <= 16). Head_dim is permuted the same way
+//   in both operands, so that a lane reads 32 contiguous bytes of a key.
+// * Softmax in fp32, base 2 (scores multiplied by c * s_k * log2 e), online
+//   over units: running max m, running sum l, rescaled output.
+// * O^T += V^T P^T on the bf16 MFMA: V codes are read transposed from LDS by
+//   ds_read_b64_tr_b8 (in each 16-lane group, lane j receives byte j % 8 of
+//   the 8-byte rows addressed by lanes 2 i + j / 8, i = 0..7); P' = P * s_v is
+//   split into two bf16 terms (hi + lo: 16 significant bits), so that the
+//   products carry the fp32 softmax weights to within 2^-16 relative.
+// * The 4 waves' (m, l, O) are merged through LDS into one partial per
+//   workgroup; a second kernel merges the splits of each query head.
+#include <hip/hip_bf16.h>
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace fp8blk {
+
+namespace {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+
+constexpr int kD = 128;                    // head_dim
+constexpr int kWaves = 4;
+constexpr int kThreadsA = kWaves * 64;
+constexpr int kUnit = 64;                  // tokens per unit
+constexpr int kUnitsPerWave = 8;           // 512 tokens per wave
+constexpr int kSplitTokens = kWaves * kUnitsPerWave * kUnit;   // 2048
+constexpr int kUnitBytes = kUnit * kD;     // 8 KB of codes
+constexpr int kPartial = kD + 2;           // floats per (query head, split): O[128], m, l
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;        // running max before any token (finite)
+
+struct AttnParams {
+  const __hip_bfloat16* q;   // [Hq][ld_q]
+  const uint8_t* k;          // [Hkv][T][128]
+  const uint8_t* v;
+  const float* sk;           // [Hkv][nb]
+  const float* sv;
+  float* ws;                 // [Hq][splits][kPartial]
+  void* out;                 // [Hq][ld_o]
+  int64_t ld_q, ld_o;
+  int T, nb, G, splits;
+  float c_log2;              // softmax scale * log2 e
+};
+
+// 8 codes (two words) -> 8 bf16, exact (an FP8 value has at most 4
+// significant bits and an exponent inside bf16's range): decode to fp32 and
+// keep the upper halves.
+template <int kFmt>
+__device__ __forceinline__ v8bf codes_to_bf16(uint32_t w0, uint32_t w1) {
+  const auto a = Fp8<kFmt>::template decode2<false>(w0);
+  const auto b = Fp8<kFmt>::template decode2<true>(w0);
+  const auto c = Fp8<kFmt>::template decode2<false>(w1);
+  const auto d = Fp8<kFmt>::template decode2<true>(w1);
+  v4u r;
+  r[0] = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+  r[1] = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+  r[2] = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
+  r[3] = __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), 0x07060302u);
+  return __builtin_bit_cast(v8bf, r);
+}
+
+// Upper halves of two fp32 values as two bf16 (exact when the low halves are
+// zero; otherwise truncation).
+__device__ __forceinline__ uint32_t hi2(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// Codes of one unit (64 token rows of 128 bytes) into an LDS buffer: 8
+// copies of 1 KB. Lane l of copy i fills row 8 i + l / 8, physical chunk l % 8,
+// i.e. logical chunk (l % 8) ^ (row % 8). Every offset is in the VGPR offset,
+// which the buffer's range check covers (rows past T read zero).
+__device__ __forceinline__ void load_unit(__amdgpu_buffer_rsrc_t r, uint32_t unit_off, uint32_t lane_voff,
+                                          uint8_t* buf) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dma16(r, unit_off + (uint32_t)(i * 1024) + lane_voff, 0u, buf + i * 1024);
+}
+
+// Byte offset of logical byte `b` of row `row` in a swizzled buffer.
+__device__ __forceinline__ int swz_off(int row, int b) {
+  return row * kD + ((((b >> 4) ^ (row & 7))) << 4) + (b & 15);
+}
+
+// Running state of one wave for its query columns (lane % 16).
+struct Run {
+  float m;        // running max (base-2 scores), same in the 4 lane groups
+  float l;        // this lane's share of the running sum (its own tokens)
+  v4f o[8];       // O^T, dims 16 j + 4 g + v, query column lane % 16
+};
+
+// One unit: scores, softmax update, P V. `kr` holds the unit's K codes, `vb`
+// its V codes in LDS. unit_t0: first token of the unit; s_scale: c * s_k *
+// log2 e of the unit's token block; s_v: its V scale.
+template <int kFmt>
+__device__ __forceinline__ void unit_step(const uint8_t* kb, const uint8_t* vb, const v8bf (&qb)[4], Run& st,
+                                          int unit_t0, int T, float s_scale, float s_v, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  // ---- scores: S^T[token 16 i + 4 g + v][query c]; the lane's A operand is
+  // token 16 i + c, dims 32 g .. 32 g + 31 (two 16-byte chunks)
+  v4f s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * i + c;
+    const v4u w0 = *reinterpret_cast<const v4u*>(kb + swz_off(row, 32 * g));
+    const v4u w1 = *reinterpret_cast<const v4u*>(kb + swz_off(row, 32 * g + 16));
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      const v4u& w = sl < 2 ? w0 : w1;
+      const v8bf a = codes_to_bf16<kFmt>(w[(sl & 1) * 2], w[(sl & 1) * 2 + 1]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[sl], acc, 0, 0, 0);
+    }
+    s[i] = acc;
+  }
+  // ---- softmax update (base 2)
+  float mx = kNegBig;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = unit_t0 + 16 * i + 4 * g + v;
+      s[i][v] = t < T ? s[i][v] * s_scale : -__builtin_inff();
+      mx = fmaxf(mx, s[i][v]);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(st.m, mx);
+  const float corr = __builtin_amdgcn_exp2f(st.m - m_new);
+  st.m = m_new;
+  float psum = 0.f;
+  float p[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      p[i][v] = __builtin_amdgcn_exp2f(s[i][v] - m_new);
+      psum += p[i][v];
+    }
+  st.l = st.l * corr + psum;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.o[j] *= corr;
+  // ---- O^T += V^T P'^T over two 32-token steps; k element e of lane group
+  // g is token 4 g + e (e < 4) or 16 + 4 g + e - 4 of the step
+#pragma unroll
+  for (int st32 = 0; st32 < 2; ++st32) {
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      // elements 2 e2, 2 e2 + 1
+      const int e0 = 2 * e2, e1 = 2 * e2 + 1;
+      const float p0 = (e0 < 4 ? p[2 * st32][e0] : p[2 * st32 + 1][e0 - 4]) * s_v;
+      const float p1 = (e1 < 4 ? p[2 * st32][e1] : p[2 * st32 + 1][e1 - 4]) * s_v;
+      const uint32_t b0 = __float_as_uint(p0) & 0xffff0000u, b1 = __float_as_uint(p1) & 0xffff0000u;
+      hw[e2] = hi2(b0, b1);
+      lw[e2] = hi2(__float_as_uint(p0 - __uint_as_float(b0)), __float_as_uint(p1 - __uint_as_float(b1)));
+    }
+    const v8bf ph = __builtin_bit_cast(v8bf, v4u{hw[0], hw[1], hw[2], hw[3]});
+    const v8bf pl = __builtin_bit_cast(v8bf, v4u{lw[0], lw[1], lw[2], lw[3]});
+    // transposed read: lane r of the 16-lane group addresses token
+    // index r / 2 (mapped as above) and dims 8 (r % 2) .. +7 of the subtile
+    const int r = c;
+    const int ti = r >> 1;
+    const int tok = 32 * st32 + (ti < 4 ? 4 * g + ti : 16 + 4 * g + ti - 4);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const v2i w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb + swz_off(tok, 16 * j + 8 * (r & 1))));
+      const v8bf a = codes_to_bf16<kFmt>((uint32_t)w[0], (uint32_t)w[1]);
+      st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph, st.o[j], 0, 0, 0);
+      st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl, st.o[j], 0, 0, 0);
+    }
+  }
+}
+
+// The wave's loop over its units, double buffered (two LDS stages of K and
+// V codes). Every step copies the next unit unconditionally (its index
+// clamped to the wave's last unit, so the tail copy repeats one nobody reads
+// again), waits for the current unit's 16 copies, then computes it. Distinct
+// __restrict__ stages and arrays, and resources built here, let the compiler
+// see that reading one stage does not wait for the copies into the other.
+template <int kFmt>
+__device__ __forceinline__ void wave_loop(const AttnParams& p, const uint8_t* __restrict__ kh,
+                                          const uint8_t* __restrict__ vh, uint32_t head_bytes,
+                                          uint8_t* __restrict__ k0, uint8_t* __restrict__ v0,
+                                          uint8_t* __restrict__ k1, uint8_t* __restrict__ v1, const v8bf (&qb)[4],
+                                          Run& st, int h, int t_begin, int nunits, int lane) {
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh, head_bytes);
+  const int crow = lane >> 3;
+  const uint32_t lane_voff = (uint32_t)(crow * kD + (((lane & 7) ^ (crow & 7)) << 4));
+  // per-token-block scales, read through the constant address space (scalar
+  // loads: they are inputs the kernel never writes)
+  typedef const __attribute__((address_space(4))) float* cf_ptr;
+  const cf_ptr skh = (cf_ptr)(p.sk + (int64_t)h * p.nb);
+  const cf_ptr svh = (cf_ptr)(p.sv + (int64_t)h * p.nb);
+  const int last = nunits - 1;
+  auto unit_off = [&](int u) { return (uint32_t)(t_begin + min(u, last) * kUnit) * kD; };
+  load_unit(rk, unit_off(0), lane_voff, k0);
+  load_unit(rv, unit_off(0), lane_voff, v0);
+  for (int u = 0; u < nunits; u += 2) {
+    // one 128-token scale block per pair of units (t_begin is a multiple of 512)
+    const int blk = (t_begin + u * kUnit) >> 7;
+    const float s_scale = skh[blk] * p.c_log2, s_v = svh[blk];
+    load_unit(rk, unit_off(u + 1), lane_voff, k1);
+    load_unit(rv, unit_off(u + 1), lane_voff, v1);
+    wait_vm<16>();
+    asm volatile("" ::: "memory");
+    unit_step<kFmt>(k0, v0, qb, st, t_begin + u * kUnit, p.T, s_scale, s_v, lane);
+    if (u + 1 >= nunits) break;
+    load_unit(rk, unit_off(u + 2), lane_voff, k0);
+    load_unit(rv, unit_off(u + 2), lane_voff, v0);
+    wait_vm<16>();
+    asm volatile("" ::: "memory");
+    unit_step<kFmt>(k1, v1, qb, st, t_begin + (u + 1) * kUnit, p.T, s_scale, s_v, lane);
+  }
+  wait_vm<0>();
+}
+
+// grid (splits, Hkv), 256 threads.
+template <int kFmt>
+__global__ __launch_bounds__(kThreadsA) void k_fp8kv_decode_attn(AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kWaves * 4 * kUnitBytes];   // 128 KB
+  const int split = blockIdx.x, h = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+
+  // query fragments (B operand): column c = query head h G + c, dims
+  // 32 g + 8 sl .. +7 for slab sl; zero columns past G
+  v8bf qb[4];
+  {
+    const bool live = c < p.G;
+    const __hip_bfloat16* qrow = p.q + (int64_t)(h * p.G + (live ? c : 0)) * p.ld_q + 32 * g;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      const v4u w = live ? *reinterpret_cast<const v4u*>(qrow + 8 * sl) : v4u{0u, 0u, 0u, 0u};
+      qb[sl] = __builtin_bit_cast(v8bf, w);
+    }
+  }
+  Run st;
+  st.m = kNegBig;
+  st.l = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.o[j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int t_begin = split * kSplitTokens + wave * (kUnitsPerWave * kUnit);
+  const int left = p.T - t_begin;
+  const int nunits = left <= 0 ? 0 : min(kUnitsPerWave, (left + kUnit - 1) / kUnit);
+  const uint32_t head_bytes = (uint32_t)p.T * kD;
+  uint8_t* const b = smem + wave * 4 * kUnitBytes;
+  if (nunits > 0)
+    wave_loop<kFmt>(p, p.k + (int64_t)h * p.T * kD, p.v + (int64_t)h * p.T * kD, head_bytes, b, b + kUnitBytes,
+                    b + 2 * kUnitBytes, b + 3 * kUnitBytes, qb, st, h, t_begin, nunits, lane);
+
+  // ---- merge the 4 waves through LDS (the stages are free: every wave
+  // has waited for its last copies and passes this barrier first)
+  float lsum = st.l;
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  raw_barrier();
+  float* const red = reinterpret_cast<float*>(smem);      // [wave][16 q][kPartial]
+  float* const mine = red + wave * 16 * kPartial;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) mine[c * kPartial + 16 * j + 4 * g + v] = st.o[j][v];
+  if (g == 0) {
+    mine[c * kPartial + kD] = st.m;
+    mine[c * kPartial + kD + 1] = lsum;
+  }
+  raw_barrier();
+  // thread t: query column t / 16, dims (t % 16) * 8 .. +7
+  const int qc = threadIdx.x >> 4, d0 = (threadIdx.x & 15) * 8;
+  if (qc < p.G) {
+    float mw[kWaves], M = kNegBig;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      mw[w] = red[(w * 16 + qc) * kPartial + kD];
+      M = fmaxf(M, mw[w]);
+    }
+    float L = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = __builtin_amdgcn_exp2f(mw[w] - M);
+      L += red[(w * 16 + qc) * kPartial + kD + 1] * f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += red[(w * 16 + qc) * kPartial + d0 + e] * f;
+    }
+    float* const dst = p.ws + ((int64_t)(h * p.G + qc) * p.splits + split) * kPartial;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[d0 + e] = o[e];
+    if (d0 == 0) {
+      dst[kD] = M;
+      dst[kD + 1] = L;
+    }
+  }
+}
+
+// Merge of the splits of each query head; grid (Hq), 512 threads: thread t
+// takes dim t % 128 over the splits s = t / 128 (mod 4), so that four
+// independent streams of loads are in flight per dim; the global max comes
+// first from a block reduction.
+constexpr int kCombThreads = 512;
+
+template <bool kBf16Out>
+__global__ __launch_bounds__(kCombThreads) void k_fp8kv_attn_combine(AttnParams p) {
+  __shared__ float red[kCombThreads];
+  __shared__ float po[4][kD], pl[4][kD];
+  const int hq = blockIdx.x, t = threadIdx.x, d = t & (kD - 1), part = t >> 7;
+  const float* base = p.ws + (int64_t)hq * p.splits * kPartial;
+  float m = kNegBig;
+  for (int s = t; s < p.splits; s += kCombThreads) m = fmaxf(m, base[(int64_t)s * kPartial + kD]);
+  red[t] = m;
+  __syncthreads();
+  for (int w = kCombThreads / 2; w > 0; w >>= 1) {
+    if (t < w) red[t] = fmaxf(red[t], red[t + w]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  float o = 0.f, L = 0.f;
+#pragma unroll 4
+  for (int s = part; s < p.splits; s += 4) {
+    const float* ps = base + (int64_t)s * kPartial;
+    const float w = __builtin_amdgcn_exp2f(ps[kD] - M);
+    o += ps[d] * w;
+    L += ps[kD + 1] * w;
+  }
+  po[part][d] = o;
+  pl[part][d] = L;
+  __syncthreads();
+  if (part == 0) {
+    const float r = (po[0][d] + po[1][d] + po[2][d] + po[3][d]) / (pl[0][d] + pl[1][d] + pl[2][d] + pl[3][d]);
+    if (kBf16Out)
+      static_cast<__hip_bfloat16*>(p.out)[(int64_t)hq * p.ld_o + d] = __float2bfloat16(r);
+    else
+      static_cast<float*>(p.out)[(int64_t)hq * p.ld_o + d] = r;
+  }
+}
+
+}  // namespace
+
+int attention_splits(int64_t tokens) { return (int)((tokens + kSplitTokens - 1) / kSplitTokens); }
+int64_t attention_partial_floats() { return kPartial; }
+
+hipError_t launch_kv_decode_attention(const AttnArgs& a, hipStream_t st) {
+  AttnParams p;
+  p.q = static_cast<const __hip_bfloat16*>(a.q);
+  p.k = a.k;
+  p.v = a.v;
+  p.sk = a.sk;
+  p.sv = a.sv;
+  p.ws = a.ws;
+  p.out = a.out;
+  p.ld_q = a.ld_q;
+  p.ld_o = a.ld_o;
+  p.T = (int)a.tokens;
+  p.nb = (int)((a.tokens + 127) / 128);
+  p.G = (int)(a.heads_q / a.heads_kv);
+  p.splits = attention_splits(a.tokens);
+  p.c_log2 = a.softmax_scale * kLog2e;
+  const dim3 grid((unsigned)p.splits, (unsigned)a.heads_kv);
+  if (a.fmt == FMT_E5M2)
+    hipLaunchKernelGGL(k_fp8kv_decode_attn<FMT_E5M2>, grid, dim3(kThreadsA), 0, st, p);
+  else
+    hipLaunchKernelGGL(k_fp8kv_decode_attn<FMT_E4M3>, grid, dim3(kThreadsA), 0, st, p);
+  if (a.out_dtype == DTYPE_BF16)
+    hipLaunchKernelGGL(k_fp8kv_attn_combine<true>, dim3((unsigned)a.heads_q), dim3(kCombThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL(k_fp8kv_attn_combine<false>, dim3((unsigned)a.heads_q), dim3(kCombThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace fp8blk

@@ -25,6 +25,42 @@ __device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_f
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // ---------------------------------------------------------------------------
+// Buffer resources, direct global -> LDS copies, waits and barriers.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Buffer resource over `bytes` bytes from `base` (raw loads; reads at or past
+// `bytes` return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Direct global -> LDS copy through a buffer resource: lane l writes `size`
+// bytes at lds + size * l (lds must be wave-uniform); reads past the
+// resource's end write zeros.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
+}
+
+// s_waitcnt with vmcnt(n) only (expcnt and lgkmcnt left at their maxima).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(((n >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (n & 15));
+}
+
+// Workgroup barrier; the empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
 // Max reductions over non-negative fp32 bit patterns (which order like uints).
 // ---------------------------------------------------------------------------
 template <int kCtrl>

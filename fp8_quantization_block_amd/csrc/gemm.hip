@@ -52,7 +52,6 @@ namespace fp8blk {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 namespace {
 
@@ -97,22 +96,6 @@ struct GemmParams {
 // read; the swizzle (r % 8) ^ (r / 8 % 2) measured 2-way conflicted).
 __device__ __forceinline__ int swz(int row) { return row & 7; }
 
-// Buffer resource over `bytes` bytes from `base` (raw loads; reads at or past
-// `bytes` return zero).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Direct global -> LDS copy through a buffer resource: lane l writes `size`
-// bytes at lds + size * l (lds must be wave-uniform); reads past the
-// resource's end write zeros.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
-}
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
-}
-
 __device__ __forceinline__ v8i pack_frag(uint4 lo, uint4 hi) {
   v8i f;
   f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
@@ -127,21 +110,6 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* tile, uint32_t lo_off, u
   const uint4 lo = *reinterpret_cast<const uint4*>(tile + lo_off);
   const uint4 hi = *reinterpret_cast<const uint4*>(tile + hi_off);
   return pack_frag(lo, hi);
-}
-
-// s_waitcnt with vmcnt(n) only (expcnt and lgkmcnt left at their maxima).
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt(((n >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (n & 15));
-}
-
-// Workgroup barrier; the empty asm statements keep the compiler from moving
-// memory accesses across it.
-__device__ __forceinline__ void raw_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 // Per-thread copy and read plan.

@@ -63,7 +63,29 @@ struct GemmArgs {
   int64_t sc_m, sc_n;
 };
 
+struct AttnArgs {
+  const void* q;          // bf16 [heads_q][ld_q]
+  int64_t ld_q;
+  int64_t heads_q, heads_kv, tokens;
+  const uint8_t* k;       // codes [heads_kv][tokens][128]
+  const uint8_t* v;
+  const float* sk;        // [heads_kv][ceil(tokens / 128)]
+  const float* sv;
+  int fmt;
+  float softmax_scale;
+  float* ws;              // attention_splits(tokens) * heads_q * attention_partial_floats() floats
+  void* out;              // [heads_q][ld_o] of out_dtype
+  int out_dtype;
+  int64_t ld_o;
+};
+
+// Token splits of the decode attention and the workspace floats per (query
+// head, split).
+int attention_splits(int64_t tokens);
+int64_t attention_partial_floats();
+
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
+hipError_t launch_kv_decode_attention(const AttnArgs& a, hipStream_t st);
 hipError_t launch_kv_quantize(const KvArgs& a, hipStream_t st);
 hipError_t launch_kv_dequantize(const KvArgs& a, hipStream_t st);
 hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t st);

@@ -36,6 +36,7 @@
 #ifndef FP8BLK_H
 #define FP8BLK_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -214,6 +215,48 @@ fp8blk_status fp8_kv_quantize(const void* kv, int64_t heads, int64_t tokens, int
 fp8blk_status fp8_kv_dequantize(const uint8_t* q, const float* scales, int64_t heads,
                                 int64_t tokens, int64_t head_dim, int64_t token_block,
                                 fp8blk_format fmt, void* out_bf16, void* stream);
+
+/*
+ * fp8_kv_decode_attention -- one decode step of attention over the FP8 KV cache
+ * that fp8_kv_quantize writes (grouped-query attention, one query token).
+ *
+ * Defined by [LONG] section 1 (K and V kept in FP8, each with its own scales,
+ * and dequantized where attention reads them) and section 3 (per head and
+ * per 128-token scales); [MIXED] section "scale 是控制面" (per-head KV scales
+ * read by the attention backend). For query head g (kv head h = g / G,
+ * G = heads_q / heads_kv):
+ *   s_t  = softmax_scale * sum_d q[g][d] * dec(k[h][t][d]) * k_scales[h][t / 128]
+ *   p_t  = exp(s_t - max_t s_t) / sum_t exp(s_t - max_t s_t)
+ *   o[g][d] = sum_t p_t * dec(v[h][t][d]) * v_scales[h][t / 128]
+ * computed in fp32 (scores, softmax, accumulation) from exactly converted
+ * codes; each output is within 1e-3 * sum_t p_t |dec(v[h][t][d]) * v_scale|
+ * of the exact value (plus half a bf16 ulp for bf16 output).
+ *
+ *   q          device, bf16 [heads_q][ld_q] (head_dim contiguous).
+ *   k_codes, v_codes
+ *              device, dense uint8 codes [heads_kv][tokens][head_dim] of format fmt.
+ *   k_scales, v_scales
+ *              device, dense fp32 [heads_kv][ceil(tokens / token_block)].
+ *   out        device, [heads_q][ld_o] of out_dtype (BF16 or F32).
+ *   workspace  device, caller-owned scratch of at least
+ *              fp8_kv_decode_attention_workspace_size(heads_q, tokens) bytes;
+ *              its contents on entry do not matter and on return are unspecified.
+ *
+ * Requirements: pointers non-null; heads_q, heads_kv, tokens > 0; heads_q a
+ * multiple of heads_kv with at most 16 query heads per kv head; head_dim == 128
+ * and token_block == 128 (else FP8BLK_EUNSUPPORTED); softmax_scale finite;
+ * q 16-byte aligned, ld_q >= 128 and a multiple of 8; out, scales and
+ * workspace 4-byte aligned; ld_o >= 128; out and workspace must not overlap
+ * the inputs or each other. Calls that share a workspace must not overlap in
+ * time.
+ */
+size_t fp8_kv_decode_attention_workspace_size(int64_t heads_q, int64_t tokens);
+fp8blk_status fp8_kv_decode_attention(const void* q, int64_t ld_q, int64_t heads_q, int64_t heads_kv,
+                                      int64_t tokens, int64_t head_dim, const uint8_t* k_codes,
+                                      const float* k_scales, const uint8_t* v_codes, const float* v_scales,
+                                      int64_t token_block, fp8blk_format fmt, float softmax_scale, void* out,
+                                      fp8blk_dtype out_dtype, int64_t ld_o, void* workspace,
+                                      size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* fp8blk_status_string(fp8blk_status s);

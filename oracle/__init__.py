@@ -13,7 +13,9 @@ It is a plain, slow, NumPy implementation written straight from the pages:
 * ``quant`` -- the amax / scale / cast quantizer for every group shape the path
   uses (per tensor, 1x128, 128x128, KV head x 128 tokens) and the KV dequantizer;
 * ``gemm``  -- the block-scaled GEMM as dequantize-to-fp64 followed by a plain
-  fp64 matmul, plus the tolerance base |A|.|W|^T.
+  fp64 matmul, plus the tolerance base |A|.|W|^T;
+* ``attention`` -- decode attention over the FP8 KV cache, dequantized to fp64,
+  plus the tolerance base sum_t p_t |v_hat_t|.
 
 Every function cites the page and section it follows. Pages are cited as
 
@@ -26,4 +28,4 @@ Parity status: every function here is pinned by tests under ``tests/``
 invariants and brute force; none is "parity unpinned".
 """
 
-from . import e4m3, e5m2, quant, gemm  # noqa: F401
+from . import e4m3, e5m2, quant, gemm, attention  # noqa: F401

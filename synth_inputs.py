@@ -19,16 +19,18 @@ stand in for them:
 * Weights are N(0, 0.02).
 * Keys shrink toward the end of the sequence ([LONG] section 3): K = N(0, 1) *
   2^(-12 t / T); values are more spread: V = N(0, 2).
+* Decode-step queries for attention over the KV cache: 64 query heads
+  (Llama-3-70B, 8 per kv head) x 128, N(0, 2).
 
 Seeds are 1000 * config + role, roles 0 = activations, 1 = outlier positions,
-2 = weights, 3 = K, 4 = V. fp32 draws are rounded to bf16 with
+2 = weights, 3 = K, 4 = V, 5 = queries. fp32 draws are rounded to bf16 with
 round-to-nearest-even (torch's CPU conversion).
 """
 
 import numpy as np
 import torch
 
-ROLE_A, ROLE_OUTLIER, ROLE_W, ROLE_K, ROLE_V = 0, 1, 2, 3, 4
+ROLE_A, ROLE_OUTLIER, ROLE_W, ROLE_K, ROLE_V, ROLE_Q = 0, 1, 2, 3, 4, 5
 
 CONFIGS = {
     1: dict(workload="per_tensor_e4m3_gemm_64x512x512", M=64, N=512, K=512,
@@ -39,7 +41,7 @@ CONFIGS = {
             gran_a="group_1x128", gran_w="block_128x128"),
     4: dict(workload="llama3_70b_qkv_prefill_8192x10240x8192", M=8192, N=10240, K=8192,
             gran_a="group_1x128", gran_w="block_128x128"),
-    5: dict(workload="kv_cache_8x131072x128", heads=8, tokens=131072, head_dim=128),
+    5: dict(workload="kv_cache_8x131072x128", heads=8, tokens=131072, head_dim=128, heads_q=64),
 }
 
 
@@ -96,6 +98,12 @@ def kv_pair(config: int = 5, heads: int = None, tokens: int = None, head_dim: in
     rv = np.random.default_rng(seed_of(config, ROLE_V, variant))
     v = rv.standard_normal((heads, tokens, head_dim), dtype=np.float32) * np.float32(2.0)
     return to_bf16(k), to_bf16(v)
+
+
+def decode_queries(heads_q: int = 64, head_dim: int = 128, variant: int = 0) -> torch.Tensor:
+    """bf16 [heads_q, head_dim] decode-step queries, N(0, 2)."""
+    rq = np.random.default_rng(seed_of(5, ROLE_Q, variant))
+    return to_bf16(rq.standard_normal((heads_q, head_dim), dtype=np.float32) * np.float32(2.0))
 
 
 def bf16_to_f32_numpy(t: torch.Tensor) -> np.ndarray:

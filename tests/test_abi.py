@@ -41,6 +41,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fp8_quantize", "fp8_block_gemm", "fp8_block_gemm_quant", "fp8_kv_quantize", "fp8_kv_dequantize",
+              "fp8_kv_decode_attention", "fp8_kv_decode_attention_workspace_size",
               "fp8blk_status_string", "fp8blk_last_error", "fp8blk_abi_version"):
         assert n in names
 
@@ -154,6 +155,44 @@ def gq(lib, M=256, N=256, K=256, a=PA, lda=256, sa=PB, ga=GROUP, sam=2, sak=1, b
 def test_gemm_quant_rejects(lib, kw, status):
     assert gq(lib, **kw) == status
     assert lib.fp8blk_last_error().decode().startswith("fp8_block_gemm_quant")
+
+
+def att(lib, q=PA, ldq=128, hq=64, hkv=8, t=300, d=128, kc=PB, ks=PC, vc=PB + (1 << 24), vs=PC + 4096, tb=128,
+        fmt=E4M3, scale=0.088, out=PD, odt=BF16, ldo=128, ws=PD + (1 << 20), wsb=1 << 20):
+    return lib.fp8_kv_decode_attention(q, ldq, hq, hkv, t, d, kc, ks, vc, vs, tb, fmt, scale, out, odt, ldo, ws,
+                                       wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), EINVAL),
+    (dict(ws=0), EINVAL),
+    (dict(hq=60), EINVAL),                   # not a multiple of heads_kv
+    (dict(hq=136), EUNSUPPORTED),            # 17 query heads per kv head
+    (dict(t=0), EINVAL),
+    (dict(d=64), EUNSUPPORTED),
+    (dict(tb=64), EUNSUPPORTED),
+    (dict(fmt=2), EINVAL),
+    (dict(odt=5), EINVAL),
+    (dict(scale=float("nan")), EINVAL),
+    (dict(q=PA + 8), EALIGN),
+    (dict(ldq=132), EALIGN),
+    (dict(out=PD + 2), EALIGN),
+    (dict(wsb=16), EINVAL),                  # workspace too small
+    (dict(out=PB + 64), EINVAL),             # out overlaps the K codes
+    (dict(ws=PA), EINVAL),                   # workspace overlaps q
+])
+def test_attention_rejects(lib, kw, status):
+    assert att(lib, **kw) == status
+    assert lib.fp8blk_last_error().decode().startswith("fp8_kv_decode_attention")
+
+
+def test_attention_workspace_size(lib):
+    lib.fp8_kv_decode_attention_workspace_size.restype = ctypes.c_size_t
+    # 64 query heads, 131072 tokens: 64 splits of 2048 tokens, 130 floats each
+    assert lib.fp8_kv_decode_attention_workspace_size(64, 131072) == 64 * 64 * 130 * 4
+    assert lib.fp8_kv_decode_attention_workspace_size(8, 1) == 8 * 1 * 130 * 4
+    assert lib.fp8_kv_decode_attention_workspace_size(8, 2049) == 8 * 2 * 130 * 4
+    assert lib.fp8_kv_decode_attention_workspace_size(0, 5) == 0
 
 
 def test_gemm_quant_empty_m_is_a_noop(lib):
