@@ -8,10 +8,11 @@
 // [MIXED] charles2530.github.io, "量化：FP8 与混合精度推理", section "scale 是控制面"
 // (KV-cache scales per head, read by the attention backend).
 //
-// Design (gfx950), one workgroup of 4 waves per (kv head, 2048-token split):
-// * Each wave streams its 512 tokens in 64-token units, double buffered: the
-//   K and V codes of the next unit go into the wave's own LDS buffers by
-//   direct global -> LDS copies while the current unit is computed. Rows are
+// Design (gfx950), one workgroup of 4 waves per (kv head, 4096-token split):
+// * Each wave streams its 1024 tokens in 32-token units through a ring of 4
+//   LDS stages: the K and V codes of the unit three ahead go into the wave's
+//   own stage by direct global -> LDS copies while the current unit is
+//   computed (24 KB in flight per wave). Rows are
 //   128 bytes; logical 16-byte chunk c of row r is stored at c ^ (r % 8), so
 //   that 16 lanes reading one chunk of 16 consecutive rows hit distinct banks.
 //   The kernel is bound by reading the codes from HBM.
@@ -47,10 +48,13 @@ typedef __attribute__((address_space(3))) v2i lds_v2i;
 constexpr int kD = 128;                    // head_dim
 constexpr int kWaves = 4;
 constexpr int kThreadsA = kWaves * 64;
-constexpr int kUnit = 64;                  // tokens per unit
-constexpr int kUnitsPerWave = 8;           // 512 tokens per wave
-constexpr int kSplitTokens = kWaves * kUnitsPerWave * kUnit;   // 2048
-constexpr int kUnitBytes = kUnit * kD;     // 8 KB of codes
+constexpr int kUnit = 32;                  // tokens per unit
+constexpr int kSub = kUnit / 16;           // 16-token subtiles per unit
+constexpr int kUnitsPerWave = 32;          // 1024 tokens per wave
+constexpr int kStages = 4;                 // LDS ring per wave (3 units in flight)
+constexpr int kSplitTokens = kWaves * kUnitsPerWave * kUnit;   // 4096
+constexpr int kUnitBytes = kUnit * kD;     // 4 KB of codes per tensor
+constexpr int kCopies = kUnitBytes / 1024; // 1 KB copies per tensor and unit
 constexpr int kPartial = kD + 2;           // floats per (query head, split): O[128], m, l
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;        // running max before any token (finite)
@@ -91,14 +95,14 @@ __device__ __forceinline__ uint32_t hi2(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
-// Codes of one unit (64 token rows of 128 bytes) into an LDS buffer: 8
+// Codes of one unit (32 token rows of 128 bytes) into an LDS buffer: 4
 // copies of 1 KB. Lane l of copy i fills row 8 i + l / 8, physical chunk l % 8,
 // i.e. logical chunk (l % 8) ^ (row % 8). Every offset is in the VGPR offset,
 // which the buffer's range check covers (rows past T read zero).
 __device__ __forceinline__ void load_unit(__amdgpu_buffer_rsrc_t r, uint32_t unit_off, uint32_t lane_voff,
                                           uint8_t* buf) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dma16(r, unit_off + (uint32_t)(i * 1024) + lane_voff, 0u, buf + i * 1024);
+  for (int i = 0; i < kCopies; ++i) dma16(r, unit_off + (uint32_t)(i * 1024) + lane_voff, 0u, buf + i * 1024);
 }
 
 // Byte offset of logical byte `b` of row `row` in a swizzled buffer.
@@ -122,9 +126,9 @@ __device__ __forceinline__ void unit_step(const uint8_t* kb, const uint8_t* vb, 
   const int g = lane >> 4, c = lane & 15;
   // ---- scores: S^T[token 16 i + 4 g + v][query c]; the lane's A operand is
   // token 16 i + c, dims 32 g .. 32 g + 31 (two 16-byte chunks)
-  v4f s[4];
+  v4f s[kSub];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kSub; ++i) {
     const int row = 16 * i + c;
     const v4u w0 = *reinterpret_cast<const v4u*>(kb + swz_off(row, 32 * g));
     const v4u w1 = *reinterpret_cast<const v4u*>(kb + swz_off(row, 32 * g + 16));
@@ -140,7 +144,7 @@ __device__ __forceinline__ void unit_step(const uint8_t* kb, const uint8_t* vb, 
   // ---- softmax update (base 2)
   float mx = kNegBig;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kSub; ++i)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int t = unit_t0 + 16 * i + 4 * g + v;
@@ -153,9 +157,9 @@ __device__ __forceinline__ void unit_step(const uint8_t* kb, const uint8_t* vb, 
   const float corr = __builtin_amdgcn_exp2f(st.m - m_new);
   st.m = m_new;
   float psum = 0.f;
-  float p[4][4];
+  float p[kSub][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kSub; ++i)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       p[i][v] = __builtin_amdgcn_exp2f(s[i][v] - m_new);
@@ -164,10 +168,10 @@ __device__ __forceinline__ void unit_step(const uint8_t* kb, const uint8_t* vb, 
   st.l = st.l * corr + psum;
 #pragma unroll
   for (int j = 0; j < 8; ++j) st.o[j] *= corr;
-  // ---- O^T += V^T P'^T over two 32-token steps; k element e of lane group
-  // g is token 4 g + e (e < 4) or 16 + 4 g + e - 4 of the step
+  // ---- O^T += V^T P'^T over the unit's 32-token steps; k element e of lane
+  // group g is token 4 g + e (e < 4) or 16 + 4 g + e - 4 of the step
 #pragma unroll
-  for (int st32 = 0; st32 < 2; ++st32) {
+  for (int st32 = 0; st32 < kUnit / 32; ++st32) {
     uint32_t hw[4], lw[4];
 #pragma unroll
     for (int e2 = 0; e2 < 4; ++e2) {
@@ -196,17 +200,20 @@ __device__ __forceinline__ void unit_step(const uint8_t* kb, const uint8_t* vb, 
   }
 }
 
-// The wave's loop over its units, double buffered (two LDS stages of K and
-// V codes). Every step copies the next unit unconditionally (its index
-// clamped to the wave's last unit, so the tail copy repeats one nobody reads
-// again), waits for the current unit's 16 copies, then computes it. Distinct
-// __restrict__ stages and arrays, and resources built here, let the compiler
-// see that reading one stage does not wait for the copies into the other.
+// The wave's loop over its units through a ring of 4 LDS stages (K and V
+// codes). Every step copies the unit three ahead unconditionally (its index
+// clamped to the wave's last unit, so tail copies repeat one nobody reads
+// again; a stage is refilled only after its unit has been computed), waits
+// for the current unit's copies, then computes it. Distinct __restrict__
+// stages and arrays, and resources built here, let the compiler see that
+// reading one stage does not wait for the copies into the others.
 template <int kFmt>
 __device__ __forceinline__ void wave_loop(const AttnParams& p, const uint8_t* __restrict__ kh,
                                           const uint8_t* __restrict__ vh, uint32_t head_bytes,
                                           uint8_t* __restrict__ k0, uint8_t* __restrict__ v0,
-                                          uint8_t* __restrict__ k1, uint8_t* __restrict__ v1, const v8bf (&qb)[4],
+                                          uint8_t* __restrict__ k1, uint8_t* __restrict__ v1,
+                                          uint8_t* __restrict__ k2, uint8_t* __restrict__ v2,
+                                          uint8_t* __restrict__ k3, uint8_t* __restrict__ v3, const v8bf (&qb)[4],
                                           Run& st, int h, int t_begin, int nunits, int lane) {
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh, head_bytes);
@@ -219,23 +226,39 @@ __device__ __forceinline__ void wave_loop(const AttnParams& p, const uint8_t* __
   const cf_ptr svh = (cf_ptr)(p.sv + (int64_t)h * p.nb);
   const int last = nunits - 1;
   auto unit_off = [&](int u) { return (uint32_t)(t_begin + min(u, last) * kUnit) * kD; };
-  load_unit(rk, unit_off(0), lane_voff, k0);
-  load_unit(rv, unit_off(0), lane_voff, v0);
-  for (int u = 0; u < nunits; u += 2) {
-    // one 128-token scale block per pair of units (t_begin is a multiple of 512)
-    const int blk = (t_begin + u * kUnit) >> 7;
-    const float s_scale = skh[blk] * p.c_log2, s_v = svh[blk];
-    load_unit(rk, unit_off(u + 1), lane_voff, k1);
-    load_unit(rv, unit_off(u + 1), lane_voff, v1);
-    wait_vm<16>();
+  auto copy = [&](int u, uint8_t* kb, uint8_t* vb) {
+    load_unit(rk, unit_off(u), lane_voff, kb);
+    load_unit(rv, unit_off(u), lane_voff, vb);
+  };
+  auto step = [&](int u, const uint8_t* kb, const uint8_t* vb) {
+    const int t0 = t_begin + u * kUnit;
+    const int blk = t0 >> 7;
+    unit_step<kFmt>(kb, vb, qb, st, t0, p.T, skh[blk] * p.c_log2, svh[blk], lane);
+  };
+  constexpr int kAhead = (kStages - 1) * 2 * kCopies;   // copies in flight beyond the current unit
+  copy(0, k0, v0);
+  copy(1, k1, v1);
+  copy(2, k2, v2);
+  for (int u = 0; u < nunits; u += 4) {
+    copy(u + 3, k3, v3);
+    wait_vm<kAhead>();
     asm volatile("" ::: "memory");
-    unit_step<kFmt>(k0, v0, qb, st, t_begin + u * kUnit, p.T, s_scale, s_v, lane);
+    step(u, k0, v0);
     if (u + 1 >= nunits) break;
-    load_unit(rk, unit_off(u + 2), lane_voff, k0);
-    load_unit(rv, unit_off(u + 2), lane_voff, v0);
-    wait_vm<16>();
+    copy(u + 4, k0, v0);
+    wait_vm<kAhead>();
     asm volatile("" ::: "memory");
-    unit_step<kFmt>(k1, v1, qb, st, t_begin + (u + 1) * kUnit, p.T, s_scale, s_v, lane);
+    step(u + 1, k1, v1);
+    if (u + 2 >= nunits) break;
+    copy(u + 5, k1, v1);
+    wait_vm<kAhead>();
+    asm volatile("" ::: "memory");
+    step(u + 2, k2, v2);
+    if (u + 3 >= nunits) break;
+    copy(u + 6, k2, v2);
+    wait_vm<kAhead>();
+    asm volatile("" ::: "memory");
+    step(u + 3, k3, v3);
   }
   wait_vm<0>();
 }
@@ -243,7 +266,7 @@ __device__ __forceinline__ void wave_loop(const AttnParams& p, const uint8_t* __
 // grid (splits, Hkv), 256 threads.
 template <int kFmt>
 __global__ __launch_bounds__(kThreadsA) void k_fp8kv_decode_attn(AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kWaves * 4 * kUnitBytes];   // 128 KB
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kWaves * kStages * 2 * kUnitBytes];   // 128 KB
   const int split = blockIdx.x, h = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -271,10 +294,11 @@ __global__ __launch_bounds__(kThreadsA) void k_fp8kv_decode_attn(AttnParams p) {
   const int left = p.T - t_begin;
   const int nunits = left <= 0 ? 0 : min(kUnitsPerWave, (left + kUnit - 1) / kUnit);
   const uint32_t head_bytes = (uint32_t)p.T * kD;
-  uint8_t* const b = smem + wave * 4 * kUnitBytes;
+  uint8_t* const b = smem + wave * kStages * 2 * kUnitBytes;
   if (nunits > 0)
     wave_loop<kFmt>(p, p.k + (int64_t)h * p.T * kD, p.v + (int64_t)h * p.T * kD, head_bytes, b, b + kUnitBytes,
-                    b + 2 * kUnitBytes, b + 3 * kUnitBytes, qb, st, h, t_begin, nunits, lane);
+                    b + 2 * kUnitBytes, b + 3 * kUnitBytes, b + 4 * kUnitBytes, b + 5 * kUnitBytes,
+                    b + 6 * kUnitBytes, b + 7 * kUnitBytes, qb, st, h, t_begin, nunits, lane);
 
   // ---- merge the 4 waves through LDS (the stages are free: every wave
   // has waited for its last copies and passes this barrier first)
@@ -320,17 +344,20 @@ __global__ __launch_bounds__(kThreadsA) void k_fp8kv_decode_attn(AttnParams p) {
   }
 }
 
-// Merge of the splits of each query head; grid (Hq), 512 threads: thread t
-// takes dim t % 128 over the splits s = t / 128 (mod 4), so that four
-// independent streams of loads are in flight per dim; the global max comes
-// first from a block reduction.
+// Merge of the splits of each query head; grid (Hq, 4), 512 threads: a
+// workgroup takes 32 dims of one query head, thread t dim t % 32 over the
+// splits s = t / 32 (mod 16), so that 16 independent streams of loads are in
+// flight per dim; the global max comes first from a block reduction.
 constexpr int kCombThreads = 512;
+constexpr int kCombDims = 32;
+constexpr int kCombParts = kCombThreads / kCombDims;
 
 template <bool kBf16Out>
 __global__ __launch_bounds__(kCombThreads) void k_fp8kv_attn_combine(AttnParams p) {
   __shared__ float red[kCombThreads];
-  __shared__ float po[4][kD], pl[4][kD];
-  const int hq = blockIdx.x, t = threadIdx.x, d = t & (kD - 1), part = t >> 7;
+  __shared__ float po[kCombParts][kCombDims], pl[kCombParts][kCombDims];
+  const int hq = blockIdx.x, t = threadIdx.x;
+  const int dl = t % kCombDims, part = t / kCombDims, d = blockIdx.y * kCombDims + dl;
   const float* base = p.ws + (int64_t)hq * p.splits * kPartial;
   float m = kNegBig;
   for (int s = t; s < p.splits; s += kCombThreads) m = fmaxf(m, base[(int64_t)s * kPartial + kD]);
@@ -342,18 +369,24 @@ __global__ __launch_bounds__(kCombThreads) void k_fp8kv_attn_combine(AttnParams 
   }
   const float M = red[0];
   float o = 0.f, L = 0.f;
-#pragma unroll 4
-  for (int s = part; s < p.splits; s += 4) {
+#pragma unroll 2
+  for (int s = part; s < p.splits; s += kCombParts) {
     const float* ps = base + (int64_t)s * kPartial;
     const float w = __builtin_amdgcn_exp2f(ps[kD] - M);
     o += ps[d] * w;
     L += ps[kD + 1] * w;
   }
-  po[part][d] = o;
-  pl[part][d] = L;
+  po[part][dl] = o;
+  pl[part][dl] = L;
   __syncthreads();
   if (part == 0) {
-    const float r = (po[0][d] + po[1][d] + po[2][d] + po[3][d]) / (pl[0][d] + pl[1][d] + pl[2][d] + pl[3][d]);
+    float os = 0.f, ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < kCombParts; ++i) {
+      os += po[i][dl];
+      ls += pl[i][dl];
+    }
+    const float r = os / ls;
     if (kBf16Out)
       static_cast<__hip_bfloat16*>(p.out)[(int64_t)hq * p.ld_o + d] = __float2bfloat16(r);
     else
@@ -388,9 +421,11 @@ hipError_t launch_kv_decode_attention(const AttnArgs& a, hipStream_t st) {
   else
     hipLaunchKernelGGL(k_fp8kv_decode_attn<FMT_E4M3>, grid, dim3(kThreadsA), 0, st, p);
   if (a.out_dtype == DTYPE_BF16)
-    hipLaunchKernelGGL(k_fp8kv_attn_combine<true>, dim3((unsigned)a.heads_q), dim3(kCombThreads), 0, st, p);
+    hipLaunchKernelGGL(k_fp8kv_attn_combine<true>, dim3((unsigned)a.heads_q, kD / kCombDims), dim3(kCombThreads), 0,
+                       st, p);
   else
-    hipLaunchKernelGGL(k_fp8kv_attn_combine<false>, dim3((unsigned)a.heads_q), dim3(kCombThreads), 0, st, p);
+    hipLaunchKernelGGL(k_fp8kv_attn_combine<false>, dim3((unsigned)a.heads_q, kD / kCombDims), dim3(kCombThreads), 0,
+                       st, p);
   return hipGetLastError();
 }
 

@@ -188,10 +188,10 @@ def test_attention_rejects(lib, kw, status):
 
 def test_attention_workspace_size(lib):
     lib.fp8_kv_decode_attention_workspace_size.restype = ctypes.c_size_t
-    # 64 query heads, 131072 tokens: 64 splits of 2048 tokens, 130 floats each
-    assert lib.fp8_kv_decode_attention_workspace_size(64, 131072) == 64 * 64 * 130 * 4
+    # 64 query heads, 131072 tokens: 32 splits of 4096 tokens, 130 floats each
+    assert lib.fp8_kv_decode_attention_workspace_size(64, 131072) == 64 * 32 * 130 * 4
     assert lib.fp8_kv_decode_attention_workspace_size(8, 1) == 8 * 1 * 130 * 4
-    assert lib.fp8_kv_decode_attention_workspace_size(8, 2049) == 8 * 2 * 130 * 4
+    assert lib.fp8_kv_decode_attention_workspace_size(8, 4097) == 8 * 2 * 130 * 4
     assert lib.fp8_kv_decode_attention_workspace_size(0, 5) == 0
 
 
