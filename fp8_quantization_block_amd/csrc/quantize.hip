@@ -9,7 +9,8 @@
 // Dequantization is x ~ q * s ([MIXED] charles2530.github.io, "量化：FP8 与混合精度推理",
 // section "E4M3 和 E5M2 是范围与格点的取舍"). Every kernel is instantiated for both
 // FP8 formats ([FP8] section "FP8 是什么", format table): E4M3 (max_fmt = 448)
-// and E5M2 (max_fmt = 57344; [LONG] section 1 stores the KV cache in E5M2).
+// and E5M2 (max_fmt = 57344; [VS] api.makesence.top, "LLM推理量化：FP8 versus INT8",
+// section 2, serves a W8A8 E4M3 model with an E5M2 KV cache).
 //
 // All passes are HBM-bound: 16-byte loads, a max reduction in registers / DPP
 // / LDS, then packed code stores.

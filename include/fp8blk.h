@@ -9,6 +9,7 @@
  *   [FP8]   wangyu.me, "大语言模型量化技术（五）：FP8" (LLM quantization part 5: FP8)
  *   [MIXED] charles2530.github.io, "量化：FP8 与混合精度推理：它不是一个 dtype 开关"
  *   [LONG]  pwwt.cn, Llama-3 FP8 and long-context practice notes
+ *   [VS]    api.makesence.top, "LLM推理量化：FP8 versus INT8"
  *
  * Numerics shared by every entry point:
  *   - FP8 formats ([FP8] section "FP8 是什么", format table): OCP E4M3 (bias 7,
@@ -53,7 +54,7 @@ typedef enum fp8blk_status {
   FP8BLK_EHIP = 4          /* the HIP runtime rejected a launch */
 } fp8blk_status;
 
-/* FP8 encodings ([FP8] section "FP8 是什么", format table; [LONG] section 1 keeps
+/* FP8 encodings ([FP8] section "FP8 是什么", format table; [VS] section 2 keeps
  * weights and activations in E4M3 and the KV cache in E5M2). Every entry point
  * takes either; the GEMM takes each operand in its own format. */
 typedef enum fp8blk_format { FP8BLK_E4M3 = 0, FP8BLK_E5M2 = 1 } fp8blk_format;
@@ -181,7 +182,7 @@ fp8blk_status fp8_block_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_
  * and section 3 (finer KV granularity: per head and per 128-token block, so
  * that small late-position keys keep their precision); [MIXED] section
  * "scale 是控制面" (per-head scales). Same per-group arithmetic as fp8_quantize,
- * in format fmt (E5M2 is the KV format of [LONG] section 1). Call once for K
+ * in format fmt (E5M2 is the KV format of [VS] section 2). Call once for K
  * and once for V.
  *
  *   kv      device, bf16 [heads][tokens][head_dim]; element (h, t, d) at

@@ -36,7 +36,7 @@ Readings taken where the pages are silent:
   with round-to-nearest-even.
 
 Formats: every function takes ``fmt`` = "e4m3" (default) or "e5m2". E5M2 ([FP8]
-section "FP8 是什么", format table; [LONG] section 1, E5M2 KV cache) runs the same
+section "FP8 是什么", format table; [VS] section 2, E5M2 KV cache) runs the same
 steps with its own largest value: s = a / 57344 and codes from the E5M2 grid.
 """
 

@@ -1,8 +1,8 @@
 """GPU parity of the E5M2 format through every entry point, against the CPU oracle.
 
-E5M2 ([FP8] section "FP8 是什么", format table: largest value 57344; [LONG]
-section 1: the KV cache in E5M2) runs the same per-group method with
-s = amax / 57344. Codes, scales and dequantized values are compared bit for
+E5M2 ([FP8] section "FP8 是什么", format table: largest value 57344; [VS]
+api.makesence.top section 2: the KV cache in E5M2) runs the same per-group
+method with s = amax / 57344. Codes, scales and dequantized values are compared bit for
 bit; the GEMM with E5M2 operands (alone or mixed with E4M3) is held to the same
 tolerance as the E4M3 GEMM.
 

@@ -3,8 +3,8 @@
 Sources: wangyu.me "大语言模型量化技术（五）：FP8", section "FP8 是什么" (format table
 row E5M2: 1-5-2 bits, largest value 57344, smallest normal 2^-14, smallest
 subnormal 2^-16) and section "什么是 FP8 量化" (round to the nearest
-representable value, ties to even, saturate); pwwt.cn Llama-3 FP8 notes,
-section 1 (E5M2 range +-57344, used for the KV cache).
+representable value, ties to even, saturate); api.makesence.top "LLM推理量化：FP8
+versus INT8", section 1 (E5M2 range +-57344) and section 2 (E5M2 KV cache).
 
 Independent checks: E5M2 shares sign, exponent width and bias with IEEE
 binary16, so every code is the upper byte of a binary16 value (NumPy's float16
