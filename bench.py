@@ -219,6 +219,31 @@ def main():
         passes["gemm_then_quantize_out"] = {"us": t_u * 1e6, "TFLOP/s": flops / t_u / 1e12}
         del qc, scq
     if args.only is None and not args.no_secondary:
+        # MX operands (E4M3 codes, one power-of-two scale per 32 K elements):
+        # the same step shape, the scales applied inside the scaled MFMA
+        qamx = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(nsets)]
+        samx = [torch.empty((M, K // 32), dtype=torch.uint8, device=dev) for _ in range(nsets)]
+        qwmx, swmx = fp8.fp8_quantize_mx(w)
+
+        def quant_mx(i):
+            j = i % nsets
+            fp8.fp8_quantize_mx(a_sets[j], out=qamx[j], scales=samx[j])
+
+        def gemm_mx(i):
+            j = i % nsets
+            fp8.fp8_mx_gemm(qamx[j], samx[j], qwmx, swmx, out=out)
+
+        for i in range(nsets):
+            quant_mx(i)
+        t_qmx = timer.run(quant_mx, max(args.steps, 22), warmup=args.warmup, name="act_quant_mx32")
+        t_gmx = timer.run(gemm_mx, max(args.steps, 10), warmup=args.warmup, name="gemm_mx32")
+        bytes_qmx = M * K * 2 + M * K + M * (K // 32)
+        passes["act_quant_mx32"] = {"us": t_qmx * 1e6, "GB/s": bytes_qmx / t_qmx / 1e9,
+                                    "frac_hbm": bytes_qmx / t_qmx / 1e9 / PEAK_HBM_GBPS}
+        passes["gemm_mx32"] = {"us": t_gmx * 1e6, "TFLOP/s": flops / t_gmx / 1e12,
+                               "frac_fp8_peak": flops / t_gmx / 1e12 / PEAK_FP8_TFLOPS}
+        del qamx, samx, qwmx, swmx
+    if args.only is None and not args.no_secondary:
         # E5M2 activations (1x128) against the E4M3 weights: the same GEMM
         # kernel with the MFMA's A operand decoded as E5M2
         qa5 = torch.empty((M, K), dtype=torch.uint8, device=dev)

@@ -14,6 +14,8 @@ Entry points (same names as the C ABI):
 * ``fp8_kv_quantize(kv, token_block=128, fmt="e4m3")`` -> (codes uint8, scales fp32)
 * ``fp8_kv_dequantize(q, scales, token_block=128, fmt="e4m3")`` -> bf16
 * ``fp8_kv_decode_attention(q, k_codes, k_scales, v_codes, v_scales, softmax_scale, fmt="e4m3")`` -> [heads_q, 128]
+* ``fp8_quantize_mx(x, fmt="e4m3")`` -> (codes uint8, E8M0 scale bytes uint8 [rows, cols/32])
+* ``fp8_mx_gemm(qa, sa, qw, sw, out_dtype=torch.bfloat16)`` -> C
 
 ``fmt`` is "e4m3" (largest value 448) or "e5m2" (largest value 57344).
 """
@@ -59,6 +61,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp8_block_gemm_quant.argtypes = [i64, i64, i64, vp, i64, vp, i32, i64, i64, vp, i64, vp, i32,
                                          i64, i64, i32, i32, i32, vp, i64, vp, i64, i64, vp]
     lib.fp8_block_gemm_quant.restype = i32
+    lib.fp8_quantize_mx.argtypes = [vp, i32, i64, i64, i64, i32, vp, i64, vp, i64, vp]
+    lib.fp8_quantize_mx.restype = i32
+    lib.fp8_mx_gemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, i32, i32, vp, i32, i64, vp]
+    lib.fp8_mx_gemm.restype = i32
     lib.fp8_kv_decode_attention_workspace_size.argtypes = [i64, i64]
     lib.fp8_kv_decode_attention_workspace_size.restype = ctypes.c_size_t
     lib.fp8_kv_decode_attention.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, i64, i32, ctypes.c_float,
@@ -200,6 +206,53 @@ def fp8_block_gemm_quant(qa: torch.Tensor, sa: torch.Tensor, gran_a: str, qw: to
                                     _FMT[fmt_c], _ptr(out), out.stride(0), _ptr(scales), scales.stride(0),
                                     scales.stride(1), _stream(qa)))
     return out, scales
+
+
+def fp8_quantize_mx(x: torch.Tensor, fmt: str = "e4m3", out: torch.Tensor = None, scales: torch.Tensor = None):
+    """MX quantization of a 2-D bf16/fp32 tensor: (codes uint8 [rows, cols],
+    E8M0 scale bytes uint8 [rows, ceil(cols/32)], one per 32 elements of a row)."""
+    lib = load_library()
+    _require_cuda(x)
+    if x.dim() != 2:
+        raise ValueError("fp8_quantize_mx expects a 2-D tensor")
+    if x.dtype == torch.bfloat16:
+        dt = BF16
+    elif x.dtype == torch.float32:
+        dt = F32
+    else:
+        raise ValueError("fp8_quantize_mx: x must be bf16 or fp32")
+    if x.stride(1) != 1:
+        x = x.contiguous()
+    rows, cols = x.shape
+    nb = (cols + 31) // 32
+    if out is None:
+        ldq = ((cols + 15) // 16) * 16
+        out = torch.empty((rows, ldq), dtype=torch.uint8, device=x.device)[:, :cols]
+    if scales is None:
+        lds = ((nb + 3) // 4) * 4
+        scales = torch.empty((rows, lds), dtype=torch.uint8, device=x.device)[:, :nb]
+    _check(lib.fp8_quantize_mx(_ptr(x), dt, rows, cols, x.stride(0), _FMT[fmt], _ptr(out), out.stride(0),
+                               _ptr(scales), scales.stride(0), _stream(x)))
+    return out, scales
+
+
+def fp8_mx_gemm(qa: torch.Tensor, sa: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor, out_dtype=torch.bfloat16,
+                out: torch.Tensor = None, fmt_a: str = "e4m3", fmt_w: str = "e4m3"):
+    """C = A . W^T from MX operands: qa [M, K] codes with E8M0 scale bytes sa
+    [M, K/32], qw [N, K] codes with sw [N, K/32]; returns C [M, N]."""
+    lib = load_library()
+    _require_cuda(qa, sa, qw, sw)
+    M, K = qa.shape
+    N, K2 = qw.shape
+    if K != K2:
+        raise ValueError("fp8_mx_gemm: K mismatch")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=qa.device)
+    cdt = BF16 if out.dtype == torch.bfloat16 else F32
+    _check(lib.fp8_mx_gemm(M, N, K, _ptr(qa), qa.stride(0), _ptr(sa), sa.stride(0), _ptr(qw), qw.stride(0),
+                           _ptr(sw), sw.stride(0), _FMT[fmt_a], _FMT[fmt_w], _ptr(out), cdt, out.stride(0),
+                           _stream(qa)))
+    return out
 
 
 def fp8_kv_quantize(kv: torch.Tensor, token_block: int = 128, fmt: str = "e4m3"):

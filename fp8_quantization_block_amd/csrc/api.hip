@@ -233,6 +233,7 @@ fp8blk_status fp8_block_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, 
   g.c_dtype = (int)c_dtype;
   g.ldc = ldc;
   g.quant_out = 0;
+  g.mx = 0;
   return hip_status(fp8blk::launch_block_gemm(g, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -267,11 +268,104 @@ fp8blk_status fp8_block_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_
   g.c_dtype = (int)FP8BLK_F32;
   g.ldc = ldqc;
   g.quant_out = 1;
+  g.mx = 0;
   g.fmt_c = (int)fmt_c;
   g.qc = qc;
   g.sc = scale_c;
   g.sc_m = sc_stride_m;
   g.sc_n = sc_stride_n;
+  return hip_status(fp8blk::launch_block_gemm(g, static_cast<hipStream_t>(stream)), fn);
+}
+
+fp8blk_status fp8_quantize_mx(const void* x, fp8blk_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                              fp8blk_format fmt, uint8_t* q, int64_t ld_q, uint8_t* scales, int64_t ld_s,
+                              void* stream) {
+  const char* fn = "fp8_quantize_mx";
+  if (!x || !q || !scales) return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
+  if (x_dtype != FP8BLK_BF16 && x_dtype != FP8BLK_F32)
+    return fail(FP8BLK_EINVAL, "%s: unknown input dtype %d", fn, (int)x_dtype);
+  if (fp8blk_status st = check_format(fmt, fn)) return st;
+  if (rows < 0 || cols < 0) return fail(FP8BLK_EINVAL, "%s: negative size", fn);
+  if (rows >= kMaxDim || cols >= kMaxDim || ld_x >= kMaxDim || ld_q >= kMaxDim || ld_s >= kMaxDim)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: dimension above 2^31", fn);
+  const int64_t nblk = (cols + 31) / 32;
+  if (ld_x < cols || ld_q < cols || ld_s < nblk) return fail(FP8BLK_EINVAL, "%s: leading dimension too small", fn);
+  if (rows * nblk >= kMaxDim) return fail(FP8BLK_EUNSUPPORTED, "%s: more than 2^31 blocks", fn);
+  const int64_t esz = x_dtype == FP8BLK_BF16 ? 2 : 4;
+  if (!aligned16(x) || !aligned16(q)) return fail(FP8BLK_EALIGN, "%s: x and q must be 16-byte aligned", fn);
+  if ((ld_x * esz) % 16 != 0 || ld_q % 16 != 0)
+    return fail(FP8BLK_EALIGN, "%s: ld_x * elem_size and ld_q must be multiples of 16 bytes", fn);
+  if (rows == 0 || cols == 0) return ok();
+  const Range rx = range2d(x, rows, cols, ld_x, esz);
+  const Range rq = range2d(q, rows, cols, ld_q, 1);
+  const Range rs = range2d(scales, rows, nblk, ld_s, 1);
+  if (overlap(rx, rq) || overlap(rx, rs) || overlap(rq, rs))
+    return fail(FP8BLK_EINVAL, "%s: x, q and scales must not overlap", fn);
+  fp8blk::QuantArgs a = {};
+  a.x = x;
+  a.x_dtype = (int)x_dtype;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld_x = ld_x;
+  a.fmt = (int)fmt;
+  a.q = q;
+  a.ld_q = ld_q;
+  a.scales = reinterpret_cast<float*>(scales);
+  a.ss_row = ld_s;
+  return hip_status(fp8blk::launch_quantize_mx(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+fp8blk_status fp8_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* scale_a,
+                          int64_t ld_sa, const uint8_t* b, int64_t ldb, const uint8_t* scale_b, int64_t ld_sb,
+                          fp8blk_format fmt_a, fp8blk_format fmt_b, void* c, fp8blk_dtype c_dtype, int64_t ldc,
+                          void* stream) {
+  const char* fn = "fp8_mx_gemm";
+  if (!a || !b || !scale_a || !scale_b || !c) return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
+  if (fp8blk_status st = check_format(fmt_a, fn)) return st;
+  if (fp8blk_status st = check_format(fmt_b, fn)) return st;
+  if (c_dtype != FP8BLK_BF16 && c_dtype != FP8BLK_F32)
+    return fail(FP8BLK_EINVAL, "%s: unknown output dtype %d", fn, (int)c_dtype);
+  if (M < 0 || N <= 0 || K <= 0) return fail(FP8BLK_EINVAL, "%s: need M >= 0, N > 0, K > 0", fn);
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: dimension above 2^31", fn);
+  if (N % 128 != 0 || K % 128 != 0)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: N and K must be multiples of 128", fn);
+  if (lda < K || ldb < K || ldc < N || ld_sa < K / 32 || ld_sb < K / 32)
+    return fail(FP8BLK_EINVAL, "%s: leading dimension too small", fn);
+  if (lda >= kMaxLdCodes || ldb >= kMaxLdCodes || ld_sa >= kMaxLdCodes || ld_sb >= kMaxLdCodes)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: leading dimensions must be below 2^23", fn);
+  const int64_t csz = c_dtype == FP8BLK_BF16 ? 2 : 4;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c))
+    return fail(FP8BLK_EALIGN, "%s: a, b and c must be 16-byte aligned", fn);
+  if (lda % 16 != 0 || ldb % 16 != 0 || (ldc * csz) % 16 != 0)
+    return fail(FP8BLK_EALIGN, "%s: lda, ldb and ldc * elem_size must be multiples of 16 bytes", fn);
+  if ((reinterpret_cast<uintptr_t>(scale_a) & 3u) != 0 || (reinterpret_cast<uintptr_t>(scale_b) & 3u) != 0 ||
+      ld_sa % 4 != 0 || ld_sb % 4 != 0)
+    return fail(FP8BLK_EALIGN, "%s: scale arrays and their row strides must be 4-byte aligned", fn);
+  if (M == 0) return ok();
+  const Range in[4] = {range2d(a, M, K, lda, 1), range2d(b, N, K, ldb, 1), range2d(scale_a, M, K / 32, ld_sa, 1),
+                       range2d(scale_b, N, K / 32, ld_sb, 1)};
+  if (overlaps_any(range2d(c, M, N, ldc, csz), in)) return fail(FP8BLK_EINVAL, "%s: c must not overlap the inputs", fn);
+  fp8blk::GemmArgs g = {};
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.a = a;
+  g.lda = lda;
+  g.b = b;
+  g.ldb = ldb;
+  g.gran_a = (int)FP8BLK_PER_TENSOR;
+  g.gran_b = (int)FP8BLK_PER_TENSOR;
+  g.fmt_a = (int)fmt_a;
+  g.fmt_b = (int)fmt_b;
+  g.c = c;
+  g.c_dtype = (int)c_dtype;
+  g.ldc = ldc;
+  g.mx = 1;
+  g.sa8 = scale_a;
+  g.sb8 = scale_b;
+  g.ld_sa8 = ld_sa;
+  g.ld_sb8 = ld_sb;
   return hip_status(fp8blk::launch_block_gemm(g, static_cast<hipStream_t>(stream)), fn);
 }
 

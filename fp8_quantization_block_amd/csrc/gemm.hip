@@ -66,8 +66,13 @@ constexpr int kScaleSlots = BM + 64;   // 256 activation scales, then 64 weight-
 // LDS read)
 constexpr int kOutPitch = 256;
 constexpr int kLoopSmem = 4 * kTileBytes + (2 * kScaleSlots + 64) * 4;
+// MX operands: per stage 1 KB of activation scale bytes (4 per row), then 1 KB
+// of weight scale bytes
+constexpr int kMxScaleStage = 2048;
+constexpr int kLoopSmemMx = 4 * kTileBytes + 2 * kMxScaleStage;
 constexpr int kOutSmem = 8 * 64 * kOutPitch;
-constexpr int kSmemBytes = kLoopSmem > kOutSmem ? kLoopSmem : kOutSmem;
+constexpr int kSmemA = kLoopSmem > kOutSmem ? kLoopSmem : kOutSmem;
+constexpr int kSmemBytes = kSmemA > kLoopSmemMx ? kSmemA : kLoopSmemMx;
 
 struct GemmParams {
   const uint8_t* a;
@@ -77,6 +82,9 @@ struct GemmParams {
   void* c;
   int64_t lda, ldb, ldc;
   int64_t sa_m, sa_k, sb_n, sb_k;
+  const uint8_t* sa8;   // MX operands: E8M0 scale bytes [M][ld_sa8] ...
+  const uint8_t* sb8;   // ... and [N][ld_sb8], one per 32 K elements
+  int64_t ld_sa8, ld_sb8;
   uint8_t* qc;          // fused quantization: codes (row stride ldc bytes) ...
   float* sc;            // ... and scales, sc[row * sc_m + group * sc_n]
   int64_t sc_m, sc_n;
@@ -264,13 +272,106 @@ __device__ __forceinline__ void k_loop(const Plan& pl, const uint8_t* __restrict
   if (active) drain(pp, acc);
 }
 
+// ---------------------------------------------------------------------------
+// MX operands ([VS] api.makesence.top, "LLM推理量化：FP8 versus INT8", section 3:
+// one power-of-two scale per 32 elements of a row, applied by block-scaled
+// hardware). gfx950's v_mfma_scale_f32_16x16x128_f8f6f4 takes one E8M0 byte
+// per lane for each operand: lane group g = lane / 16 supplies the scale of
+// the lane's row (A) or column (B) for the 32-element K block g of the
+// instruction's 128; with the fragment K order above (lane group g holds K
+// bytes 16 g .. and 64 + 16 g ..) that block is K [32 g, 32 g + 32). Both
+// established on the device. The scaled products accumulate in the MFMA
+// itself: no promotion FMAs.
+// ---------------------------------------------------------------------------
+// Copies of K block kb: the operand tiles as issue(), and the scale dwords
+// (4 bytes = the block's 4 scales) of 64 rows per wave: waves 0..3 activation
+// rows 64 w .., waves 4..7 weight rows 64 (w - 4) .., landing at stage bytes
+// 256 w (activation rows at 4 r, weight rows at 1024 + 4 r). Row offsets and
+// the K step are in the VGPR offset (rows past the tile read zero).
+__device__ __forceinline__ void issue_mx(const Plan& pl, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                         __amdgpu_buffer_rsrc_t rs, int kb, uint8_t* ta, uint8_t* tb, uint8_t* ts) {
+  const uint32_t soff = (uint32_t)kb * BK;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    dma16(ra, pl.a_voff[i], soff, ta + (pl.wave * 4 + i) * 1024);
+    dma16(rb, pl.b_voff, soff + (uint32_t)i * pl.b_istep, tb + (pl.wave * 4 + i) * 1024);
+  }
+  dma4(rs, pl.s_voff + (uint32_t)kb * 4u, 0u, ts + pl.wave * 256);
+}
+
+// One K block of a wave, MX operands: 32 scaled MFMAs accumulating in place.
+// pl.s_rd / pl.w_rd: byte offsets of this lane's activation / weight scale
+// (subtile 0) in the stage. Weight fragments are read two subtiles ahead
+// (three-deep ring) and the program order is pinned per step: with no
+// promotion work between the MFMAs, a one-subtile lead left them waiting on
+// the LDS reads.
+template <int kFa, int kFb>
+__device__ __forceinline__ void mma_block_mx(const Plan& pl, const uint8_t* ta, const uint8_t* tb, const uint8_t* ts,
+                                             v4f (&acc)[4][8]) {
+  v8i af[4], bf[3];
+  af[0] = read_frag(ta, pl.a_lo, pl.a_hi);
+  bf[0] = read_frag(tb, pl.b_lo, pl.b_hi);
+#pragma unroll
+  for (int mi = 1; mi < 4; ++mi) af[mi] = read_frag(ta, pl.a_lo + mi * 2048, pl.a_hi + mi * 2048);
+  bf[1] = read_frag(tb, pl.b_lo + 2048, pl.b_hi + 2048);
+  int sa[4], sb[8];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) sa[mi] = ts[pl.s_rd + mi * 64];
+#pragma unroll
+  for (int ni = 0; ni < 8; ++ni) sb[ni] = ts[pl.w_rd + ni * 64];
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    const int ni = t >> 2, mi = t & 3;
+    if (mi == 0 && ni < 6)
+      bf[(ni + 2) % 3] = read_frag(tb, pl.b_lo + (ni + 2) * 2048, pl.b_hi + (ni + 2) * 2048);
+    acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf[ni % 3], acc[mi][ni], kFa, kFb, 0,
+                                                                  sa[mi], 0, sb[ni]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int kFa, int kFb>
+__device__ __forceinline__ void k_step_mx(const Plan& pl, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                          __amdgpu_buffer_rsrc_t rs, int kb, int nk, const uint8_t* ca,
+                                          const uint8_t* cb, const uint8_t* cs, uint8_t* na, uint8_t* nb, uint8_t* ns,
+                                          bool active, v4f (&acc)[4][8]) {
+  issue_mx(pl, ra, rb, rs, min(kb + 1, nk - 1), na, nb, ns);
+  if (active) mma_block_mx<kFa, kFb>(pl, ca, cb, cs, acc);
+  wait_vm<0>();
+  raw_barrier();
+}
+
+// The MX K loop over two stages (distinct __restrict__ stages and arrays, as
+// k_loop).
+template <int kFa, int kFb>
+__device__ __forceinline__ void k_loop_mx(const Plan& pl, const uint8_t* __restrict__ ga, uint32_t ga_bytes,
+                                          const uint8_t* __restrict__ gb, uint32_t gb_bytes,
+                                          const uint8_t* __restrict__ gs, uint32_t gs_bytes,
+                                          uint8_t* __restrict__ a0, uint8_t* __restrict__ a1,
+                                          uint8_t* __restrict__ b0, uint8_t* __restrict__ b1,
+                                          uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, int nk, bool active,
+                                          v4f (&acc)[4][8]) {
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(ga, ga_bytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(gb, gb_bytes);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(gs, gs_bytes);
+  issue_mx(pl, ra, rb, rs, 0, a0, b0, s0);
+  wait_vm<0>();
+  raw_barrier();
+  int kb = 0;
+  for (; kb + 1 < nk; kb += 2) {
+    k_step_mx<kFa, kFb>(pl, ra, rb, rs, kb, nk, a0, b0, s0, a1, b1, s1, active, acc);
+    k_step_mx<kFa, kFb>(pl, ra, rb, rs, kb + 1, nk, a1, b1, s1, a0, b0, s0, active, acc);
+  }
+  if (kb < nk) k_step_mx<kFa, kFb>(pl, ra, rb, rs, kb, nk, a0, b0, s0, a1, b1, s1, active, acc);
+}
+
 // Output modes of the prefill kernel.
 enum OutMode : int { OUT_BF16 = 0, OUT_F32 = 1, OUT_Q_E4M3 = 2, OUT_Q_E5M2 = 3 };
 // quantized output staging: per wave 64 rows of 128 codes, 144-byte pitch
 constexpr int kQPitch = 144;
 static_assert(8 * 64 * kQPitch <= kSmemBytes, "quantized output staging exceeds the LDS");
 
-template <int kOut, int kFa, int kFb>
+template <int kOut, int kFa, int kFb, bool kMx = false>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
   // LDS: two stages of operand tiles and scales during the K loop; afterwards
   // the same memory stages the bf16 output for coalesced stores
@@ -344,6 +445,36 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
     pl.s_rd = (uint32_t)(wm * 64 + 4 * q);
     pl.w_rd = (uint32_t)(BM + wn);
   }
+  v4f acc[4][8];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  if constexpr (kMx) {
+    // scale copy plan: waves 0..3 activation rows 64 w + lane, waves 4..7
+    // weight rows 64 (w - 4) + lane of the tile; reads: this lane's row of
+    // subtile 0 (r = lane % 16) and scale byte g = lane / 16
+    const int rl = (wave & 3) * 64 + lane;
+    const uint8_t* gs8;
+    uint32_t gs8_bytes;
+    if (wave < 4) {
+      gs8 = p.sa8 + (int64_t)m0 * p.ld_sa8;
+      gs8_bytes = (uint32_t)(rows_a * p.ld_sa8);
+      pl.s_voff = (uint32_t)(rl * p.ld_sa8);
+    } else {
+      gs8 = p.sb8 + (int64_t)n0 * p.ld_sb8;
+      gs8_bytes = (uint32_t)(rows_b * p.ld_sb8);
+      pl.s_voff = (uint32_t)(rl * p.ld_sb8);
+    }
+    const int rrow = lane & 15, q = lane >> 4;
+    pl.s_rd = (uint32_t)((wm * 64 + rrow) * 4 + q);
+    pl.w_rd = (uint32_t)(1024 + (wn * 128 + rrow) * 4 + q);
+    uint8_t* const s0 = smem + 4 * kTileBytes;
+    k_loop_mx<kFa, kFb>(pl, p.a + (int64_t)m0 * p.lda, (uint32_t)(rows_a * (int)p.lda), p.b + (int64_t)n0 * p.ldb,
+                        (uint32_t)(rows_b * (int)p.ldb), gs8, gs8_bytes, ta0, ta1, tb0, tb1, s0,
+                        s0 + kMxScaleStage, nk, active, acc);
+  } else {
   // scale copy plan: waves 0..3 activation scales, waves 4..7 weight-block scales
   const float* gs;
   uint32_t gs_bytes;
@@ -362,14 +493,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_fp8_block(GemmParams p) {
     pl.s_kstep = (uint32_t)(p.sb_k * 4);
   }
 
-  v4f acc[4][8];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
-
   k_loop<kFa, kFb>(pl, p.a + (int64_t)m0 * p.lda, (uint32_t)(rows_a * (int)p.lda), p.b + (int64_t)n0 * p.ldb,
          (uint32_t)(rows_b * (int)p.ldb), gs, gs_bytes, ta0, ta1, tb0, tb1, ts0, ts1, sink, nk, active, acc);
+  }
 
   if (!active) return;
   // ---- epilogue: lane holds rows 4 * (lane / 16) + v, column lane % 16 ----
@@ -608,6 +734,16 @@ void launch_formats(const GemmParams& p, int out, hipStream_t st) {
 
 }  // namespace
 
+// MX operands: always the prefill kernel (bf16 or fp32 output).
+template <int kFa, int kFb>
+void launch_mx(const GemmParams& p, int out, hipStream_t st) {
+  const dim3 grid((unsigned)(p.n_full + 2 * p.n_half));
+  if (out == OUT_BF16)
+    hipLaunchKernelGGL((k_gemm_fp8_block<OUT_BF16, kFa, kFb, true>), grid, dim3(kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((k_gemm_fp8_block<OUT_F32, kFa, kFb, true>), grid, dim3(kThreads), 0, st, p);
+}
+
 // Compute units of the current device (cached per device; 0 if unknown).
 int device_cu_count() {
   static int cached[64] = {0};
@@ -629,6 +765,10 @@ hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t st) {
   p.sa = g.sa;
   p.sb = g.sb;
   p.c = g.c;
+  p.sa8 = g.sa8;
+  p.sb8 = g.sb8;
+  p.ld_sa8 = g.ld_sa8;
+  p.ld_sb8 = g.ld_sb8;
   p.qc = g.qc;
   p.sc = g.sc;
   p.sc_m = g.sc_m;
@@ -649,7 +789,7 @@ hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t st) {
                               : (g.c_dtype == DTYPE_BF16 ? OUT_BF16 : OUT_F32);
   // tail balancing (see GemmParams)
   const int tiles = p.tiles_m * p.tiles_n;
-  const int cus = (p.M > 64 || g.quant_out) ? device_cu_count() : 0;
+  const int cus = (p.M > 64 || g.quant_out || g.mx) ? device_cu_count() : 0;
   const int rem = cus > 0 ? tiles % cus : 0;
   p.n_full = tiles;
   p.n_half = 0;
@@ -658,6 +798,13 @@ hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t st) {
     p.n_half = rem;
   }
   const bool a5 = g.fmt_a == FMT_E5M2, b5 = g.fmt_b == FMT_E5M2;
+  if (g.mx) {
+    if (!a5 && !b5) launch_mx<FMT_E4M3, FMT_E4M3>(p, out, st);
+    else if (!a5 && b5) launch_mx<FMT_E4M3, FMT_E5M2>(p, out, st);
+    else if (a5 && !b5) launch_mx<FMT_E5M2, FMT_E4M3>(p, out, st);
+    else launch_mx<FMT_E5M2, FMT_E5M2>(p, out, st);
+    return hipGetLastError();
+  }
   if (!a5 && !b5) launch_formats<FMT_E4M3, FMT_E4M3>(p, out, st);
   else if (!a5 && b5) launch_formats<FMT_E4M3, FMT_E5M2>(p, out, st);
   else if (a5 && !b5) launch_formats<FMT_E5M2, FMT_E4M3>(p, out, st);

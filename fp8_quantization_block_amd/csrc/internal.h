@@ -56,6 +56,12 @@ struct GemmArgs {
   // quant_out: instead of c, write the output as FP8 codes of format fmt_c
   // (qc) with one fp32 scale per row and 128-column group at
   // sc[row * sc_m + group * sc_n]
+  // mx: operands carry E8M0 scale bytes (one per 32 K elements) in sa8 / sb8
+  // with row strides ld_sa8 / ld_sb8 bytes; sa, sb, gran_a, gran_b unused
+  int mx;
+  const uint8_t* sa8;
+  const uint8_t* sb8;
+  int64_t ld_sa8, ld_sb8;
   int quant_out;
   int fmt_c;
   uint8_t* qc;
@@ -85,6 +91,9 @@ int attention_splits(int64_t tokens);
 int64_t attention_partial_floats();
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
+// MX blocks of 32 along the rows: a.scales points at uint8 E8M0 bytes, a.ss_row
+// is the byte stride between their rows.
+hipError_t launch_quantize_mx(const QuantArgs& a, hipStream_t st);
 hipError_t launch_kv_decode_attention(const AttnArgs& a, hipStream_t st);
 hipError_t launch_kv_quantize(const KvArgs& a, hipStream_t st);
 hipError_t launch_kv_dequantize(const KvArgs& a, hipStream_t st);

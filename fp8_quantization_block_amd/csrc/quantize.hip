@@ -71,6 +71,16 @@ struct Vec8<__hip_bfloat16> {
     r.y = cast4_bf16<kFmt>(g, bf16_lo_to_f32(w.z), bf16_hi_to_f32(w.z), bf16_lo_to_f32(w.w), bf16_hi_to_f32(w.w));
     return r;
   }
+  // codes of x * 2^e (exact scaling), saturating
+  template <int kFmt>
+  __device__ __forceinline__ uint2 cast_pow2(int e) const {
+    uint2 r;
+    r.x = pack4_sat<kFmt>(__builtin_amdgcn_ldexpf(bf16_lo_to_f32(w.x), e), __builtin_amdgcn_ldexpf(bf16_hi_to_f32(w.x), e),
+                          __builtin_amdgcn_ldexpf(bf16_lo_to_f32(w.y), e), __builtin_amdgcn_ldexpf(bf16_hi_to_f32(w.y), e));
+    r.y = pack4_sat<kFmt>(__builtin_amdgcn_ldexpf(bf16_lo_to_f32(w.z), e), __builtin_amdgcn_ldexpf(bf16_hi_to_f32(w.z), e),
+                          __builtin_amdgcn_ldexpf(bf16_lo_to_f32(w.w), e), __builtin_amdgcn_ldexpf(bf16_hi_to_f32(w.w), e));
+    return r;
+  }
 };
 
 template <>
@@ -105,6 +115,15 @@ struct Vec8<float> {
     uint2 r;
     r.x = cast4_f32<kFmt>(g, a.x, a.y, a.z, a.w);
     r.y = cast4_f32<kFmt>(g, b.x, b.y, b.z, b.w);
+    return r;
+  }
+  template <int kFmt>
+  __device__ __forceinline__ uint2 cast_pow2(int e) const {
+    uint2 r;
+    r.x = pack4_sat<kFmt>(__builtin_amdgcn_ldexpf(a.x, e), __builtin_amdgcn_ldexpf(a.y, e),
+                          __builtin_amdgcn_ldexpf(a.z, e), __builtin_amdgcn_ldexpf(a.w, e));
+    r.y = pack4_sat<kFmt>(__builtin_amdgcn_ldexpf(b.x, e), __builtin_amdgcn_ldexpf(b.y, e),
+                          __builtin_amdgcn_ldexpf(b.z, e), __builtin_amdgcn_ldexpf(b.w, e));
     return r;
   }
 };
@@ -364,6 +383,56 @@ __global__ void k_finalize_tensor_scale(float* __restrict__ acc) {
 }
 
 // ---------------------------------------------------------------------------
+// MX blocks: 32 consecutive elements of a row share one power-of-two scale
+// X = 2^k, stored as the byte k + 127 (E8M0), with k the smallest integer such
+// that amax <= MAX * 2^k ([VS] api.makesence.top, "LLM推理量化：FP8 versus INT8",
+// section 3: Microscaling with block size 32; the pages' s = amax / MAX rounded
+// up to a power of two, so that the block max never saturates). With
+// MAX = 0.875 * 2^E and amax = m * 2^e (m in [0.5, 1), frexp), k = e - E +
+// (m > 0.875); an all-zero block takes k = -127; k is clamped to [-127, 127].
+// The codes are FP8(x * 2^-k), the scaling exact, so only the encoder rounds.
+// Four lanes (a DPP quad) per block, 8 elements each; one block per quad.
+// ---------------------------------------------------------------------------
+template <int kFmt>
+__device__ __forceinline__ int mx_exponent(uint32_t amax_bits) {
+  if (amax_bits == 0) return -127;
+  const float a = __uint_as_float(amax_bits);
+  const int e = __builtin_amdgcn_frexp_expf(a);
+  const float m = __builtin_amdgcn_frexp_mantf(a);
+  constexpr int kE = kFmt == FMT_E4M3 ? 9 : 16;   // MAX = 0.875 * 2^kE
+  const int k = e - kE + (m > 0.875f ? 1 : 0);
+  return k < -127 ? -127 : (k > 127 ? 127 : k);
+}
+
+template <typename T, int kFmt>
+__global__ __launch_bounds__(256) void k_quant_mx(const T* __restrict__ x, int64_t ld_x, uint32_t cols,
+                                                   uint32_t nblk, uint32_t total_blocks, FastDiv div_nblk,
+                                                   uint8_t* __restrict__ q, int64_t ld_q,
+                                                   uint8_t* __restrict__ sc, int64_t ld_s) {
+  const uint32_t sub = threadIdx.x & 3u;
+  const uint32_t b = blockIdx.x * 64u + (threadIdx.x >> 2);
+  const bool live = b < total_blocks;
+  const uint32_t row = live ? fastdiv(b, div_nblk) : 0u;
+  const uint32_t blk = b - row * nblk;
+  const uint32_t col0 = blk * 32u + sub * 8u;
+  const uint32_t nv = (live && col0 < cols) ? min(8u, cols - col0) : 0u;
+  Vec8<T> v;
+  if (nv > 0)
+    v.load(x + (int64_t)row * ld_x + col0, nv);
+  else
+    v.zero();
+  uint32_t m = v.amax_bits();
+  m = dpp_max_step<0xB1>(m);   // quad_perm [1,0,3,2]
+  m = dpp_max_step<0x4E>(m);   // quad_perm [2,3,0,1]
+  const int k = mx_exponent<kFmt>(m);
+  if (nv > 0) {
+    const uint2 codes = v.template cast_pow2<kFmt>(-k);
+    store_codes8(q + (int64_t)row * ld_q + col0, codes, nv);
+  }
+  if (live && sub == 0) sc[(int64_t)row * ld_s + blk] = (uint8_t)(k + 127);
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers (arguments already validated by the API layer).
 // ---------------------------------------------------------------------------
 namespace {
@@ -421,6 +490,30 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
   }
   if (a.x_dtype == DTYPE_BF16) return quantize_typed<__hip_bfloat16, FMT_E4M3>(a, st);
   return quantize_typed<float, FMT_E4M3>(a, st);
+}
+
+hipError_t launch_quantize_mx(const QuantArgs& a, hipStream_t st) {
+  const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const uint32_t nblk = (cols + 31u) / 32u;
+  const uint32_t total = rows * nblk;
+  const dim3 grid((total + 63u) / 64u);
+  uint8_t* const sc = reinterpret_cast<uint8_t*>(a.scales);
+  const FastDiv fd = make_fastdiv(nblk);
+  if (a.x_dtype == DTYPE_BF16) {
+    const __hip_bfloat16* x = static_cast<const __hip_bfloat16*>(a.x);
+    if (a.fmt == FMT_E5M2)
+      hipLaunchKernelGGL((k_quant_mx<__hip_bfloat16, FMT_E5M2>), grid, dim3(256), 0, st, x, a.ld_x, cols, nblk, total, fd, a.q, a.ld_q, sc, a.ss_row);
+    else
+      hipLaunchKernelGGL((k_quant_mx<__hip_bfloat16, FMT_E4M3>), grid, dim3(256), 0, st, x, a.ld_x, cols, nblk, total, fd, a.q, a.ld_q, sc, a.ss_row);
+  } else {
+    const float* x = static_cast<const float*>(a.x);
+    if (a.fmt == FMT_E5M2)
+      hipLaunchKernelGGL((k_quant_mx<float, FMT_E5M2>), grid, dim3(256), 0, st, x, a.ld_x, cols, nblk, total, fd, a.q, a.ld_q, sc, a.ss_row);
+    else
+      hipLaunchKernelGGL((k_quant_mx<float, FMT_E4M3>), grid, dim3(256), 0, st, x, a.ld_x, cols, nblk, total, fd, a.q, a.ld_q, sc, a.ss_row);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_kv_quantize(const KvArgs& a, hipStream_t st) {

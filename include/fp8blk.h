@@ -218,6 +218,61 @@ fp8blk_status fp8_kv_dequantize(const uint8_t* q, const float* scales, int64_t h
                                 fp8blk_format fmt, void* out_bf16, void* stream);
 
 /*
+ * fp8_quantize_mx -- MX quantization: FP8 codes with one power-of-two scale per
+ * 32 consecutive elements of a row.
+ *
+ * Defined by [VS] section 3 (Microscaling formats: blocks of 32 elements share
+ * one scale; block-scaled hardware runs them natively) and [FP8] section
+ * "什么是 FP8 量化" (map into the format's range, round to nearest even,
+ * saturate). The scale of a block is X = 2^k with k the smallest integer such
+ * that max|x| <= MAX * 2^k over the block (MAX = 448 for E4M3, 57344 for
+ * E5M2), clamped to [-127, 127] (an all-zero block gets k = -127); it is stored
+ * as the E8M0 byte k + 127. Codes are FP8(x * 2^-k): the scaling is exact, so
+ * the encoder's rounding (nearest, ties to even) is the only one.
+ *
+ *   x       device, [rows][cols] of x_dtype, row stride ld_x elements.
+ *   q       device, uint8 codes of format fmt [rows][cols], row stride ld_q bytes.
+ *   scales  device, uint8 E8M0 bytes [rows][ceil(cols / 32)], row stride ld_s bytes
+ *           (the ragged last block of a row uses its valid elements).
+ *
+ * Requirements: pointers non-null; rows, cols >= 0 (0 is a no-op); ld_x, ld_q
+ * >= cols and ld_s >= ceil(cols / 32); x and q 16-byte aligned with
+ * ld_x * sizeof(x_dtype) and ld_q multiples of 16; x, q and scales must not
+ * overlap.
+ */
+fp8blk_status fp8_quantize_mx(const void* x, fp8blk_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                              fp8blk_format fmt, uint8_t* q, int64_t ld_q, uint8_t* scales, int64_t ld_s,
+                              void* stream);
+
+/*
+ * fp8_mx_gemm -- C[M][N] = A[M][K] . B[N][K]^T from MX operands: each operand's
+ * codes with one E8M0 scale per 32 K elements of each row (as fp8_quantize_mx
+ * writes them for A [M][K] and for the weights B [N][K]).
+ *
+ * Defined by [VS] section 3 (block-32 scaled formats multiplied natively by
+ * the hardware) on the product of [FP8] section "FP8 矩阵乘" (FP8 products,
+ * fp32 accumulation):
+ *   C[m][n] = sum_k dec(a[m][k]) 2^(sa[m][k/32] - 127) * dec(b[n][k]) 2^(sb[n][k/32] - 127),
+ * the scales applied inside the matrix instruction (gfx950's scaled FP8 MFMA),
+ * summed in fp32 and rounded once to c_dtype.
+ *
+ *   a, b     device, uint8 codes of formats fmt_a / fmt_b, row strides lda / ldb bytes.
+ *   scale_a  device, uint8 [M][ld_sa] (ld_sa >= K / 32); scale_b likewise [N][ld_sb].
+ *   c        device, [M][N] of c_dtype (BF16 or F32), row stride ldc elements.
+ *
+ * Requirements: pointers non-null; M >= 0 (0 is a no-op), N > 0, K > 0, N and K
+ * multiples of 128 (else FP8BLK_EUNSUPPORTED); lda, ldb >= K, ldc >= N, all
+ * leading dimensions below 2^23; a, b, c 16-byte aligned with lda, ldb and
+ * ldc * sizeof(c_dtype) multiples of 16; scale arrays 4-byte aligned with ld_sa
+ * and ld_sb multiples of 4; codes finite; scale bytes not 0xFF; c must not
+ * overlap the inputs.
+ */
+fp8blk_status fp8_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* scale_a,
+                          int64_t ld_sa, const uint8_t* b, int64_t ldb, const uint8_t* scale_b, int64_t ld_sb,
+                          fp8blk_format fmt_a, fp8blk_format fmt_b, void* c, fp8blk_dtype c_dtype, int64_t ldc,
+                          void* stream);
+
+/*
  * fp8_kv_decode_attention -- one decode step of attention over the FP8 KV cache
  * that fp8_kv_quantize writes (grouped-query attention, one query token).
  *

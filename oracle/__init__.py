@@ -15,7 +15,9 @@ It is a plain, slow, NumPy implementation written straight from the pages:
 * ``gemm``  -- the block-scaled GEMM as dequantize-to-fp64 followed by a plain
   fp64 matmul, plus the tolerance base |A|.|W|^T;
 * ``attention`` -- decode attention over the FP8 KV cache, dequantized to fp64,
-  plus the tolerance base sum_t p_t |v_hat_t|.
+  plus the tolerance base sum_t p_t |v_hat_t|;
+* ``mx`` -- MX block-32 quantization with power-of-two (E8M0) scales and the
+  GEMM over MX operands.
 
 Every function cites the page and section it follows. Pages are cited as
 
@@ -28,4 +30,4 @@ Parity status: every function here is pinned by tests under ``tests/``
 invariants and brute force; none is "parity unpinned".
 """
 
-from . import e4m3, e5m2, quant, gemm, attention  # noqa: F401
+from . import e4m3, e5m2, quant, gemm, attention, mx  # noqa: F401

@@ -41,7 +41,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fp8_quantize", "fp8_block_gemm", "fp8_block_gemm_quant", "fp8_kv_quantize", "fp8_kv_dequantize",
-              "fp8_kv_decode_attention", "fp8_kv_decode_attention_workspace_size",
+              "fp8_kv_decode_attention", "fp8_kv_decode_attention_workspace_size", "fp8_quantize_mx", "fp8_mx_gemm",
               "fp8blk_status_string", "fp8blk_last_error", "fp8blk_abi_version"):
         assert n in names
 
@@ -193,6 +193,47 @@ def test_attention_workspace_size(lib):
     assert lib.fp8_kv_decode_attention_workspace_size(8, 1) == 8 * 1 * 130 * 4
     assert lib.fp8_kv_decode_attention_workspace_size(8, 4097) == 8 * 2 * 130 * 4
     assert lib.fp8_kv_decode_attention_workspace_size(0, 5) == 0
+
+
+def qmx(lib, x=PA, dt=BF16, rows=4, cols=256, ldx=256, fmt=E4M3, qp=PB, ldq=256, s=PC, lds=8):
+    return lib.fp8_quantize_mx(x, dt, rows, cols, ldx, fmt, qp, ldq, s, lds, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=0), EINVAL),
+    (dict(fmt=2), EINVAL),
+    (dict(dt=3), EINVAL),
+    (dict(rows=-1), EINVAL),
+    (dict(lds=7), EINVAL),                  # fewer than ceil(cols / 32) scale bytes per row
+    (dict(ldq=128), EINVAL),
+    (dict(x=PA + 2), EALIGN),
+    (dict(ldq=264, cols=256), EALIGN),
+    (dict(s=PB + 16), EINVAL),              # scales overlap the codes
+])
+def test_quantize_mx_rejects(lib, kw, status):
+    assert qmx(lib, **kw) == status
+    assert lib.fp8blk_last_error().decode().startswith("fp8_quantize_mx")
+
+
+def mxg(lib, M=256, N=256, K=256, a=PA, lda=256, sa=PB, ldsa=8, b=PC, ldb=256, sb=PB + 65536, ldsb=8,
+        fa=E4M3, fb=E4M3, c=PD, cdt=BF16, ldc=256):
+    return lib.fp8_mx_gemm(M, N, K, a, lda, sa, ldsa, b, ldb, sb, ldsb, fa, fb, c, cdt, ldc, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a=0), EINVAL),
+    (dict(sb=0), EINVAL),
+    (dict(fa=2), EINVAL),
+    (dict(cdt=2), EINVAL),
+    (dict(N=200), EUNSUPPORTED),
+    (dict(ldsa=4), EINVAL),                 # fewer than K / 32 scale bytes per row
+    (dict(ldsa=10), EALIGN),                # scale rows not 4-byte aligned
+    (dict(sa=PB + 2), EALIGN),
+    (dict(c=PA + 512), EINVAL),             # c overlaps a
+])
+def test_mx_gemm_rejects(lib, kw, status):
+    assert mxg(lib, **kw) == status
+    assert lib.fp8blk_last_error().decode().startswith("fp8_mx_gemm")
 
 
 def test_gemm_quant_empty_m_is_a_noop(lib):
