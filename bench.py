@@ -262,6 +262,21 @@ def main():
         bytes_qa = M * K * 2 + M * K + M * (K // 128) * 4
         passes["act_quant_1x128"] = {"us": t_qa * 1e6, "GB/s": bytes_qa / t_qa / 1e9,
                                      "frac_hbm": bytes_qa / t_qa / 1e9 / PEAK_HBM_GBPS}
+        if not args.no_secondary:
+            # Delayed scaling: the cast under a scale from the amax history,
+            # recording this tensor's amax into the history
+            hist = torch.full((16,), float(a_host.float().abs().max()), dtype=torch.float32, device=dev)
+            s_static = fp8.fp8_scale_from_amax_history(hist)
+
+            def quant_static(i):
+                j = i % nsets
+                fp8.fp8_quantize_static(a_sets[j], s_static, record_amax=True, out=qa_sets[j],
+                                        amax=hist[i % 16:i % 16 + 1])
+
+            t_qs = timer.run(quant_static, max(args.steps, 22), warmup=args.warmup, name="act_quant_static")
+            bytes_qs = M * K * 2 + M * K
+            passes["act_quant_static_amax"] = {"us": t_qs * 1e6, "GB/s": bytes_qs / t_qs / 1e9,
+                                               "frac_hbm": bytes_qs / t_qs / 1e9 / PEAK_HBM_GBPS}
         t_qw = timer.run(quant_w, 10, warmup=2, name="weight_quant_128x128_offline")
         bytes_qw = N * K * 2 + N * K + (N // 128) * (K // 128) * 4
         passes["weight_quant_128x128_offline"] = {"us": t_qw * 1e6, "GB/s": bytes_qw / t_qw / 1e9,

@@ -14,6 +14,8 @@ Entry points (same names as the C ABI):
 * ``fp8_kv_quantize(kv, token_block=128, fmt="e4m3")`` -> (codes uint8, scales fp32)
 * ``fp8_kv_dequantize(q, scales, token_block=128, fmt="e4m3")`` -> bf16
 * ``fp8_kv_decode_attention(q, k_codes, k_scales, v_codes, v_scales, softmax_scale, fmt="e4m3")`` -> [heads_q, 128]
+* ``fp8_quantize_static(x, scale, fmt="e4m3", record_amax=False)`` -> codes (, amax)
+* ``fp8_scale_from_amax_history(history, fmt="e4m3")`` -> scale [1]
 * ``fp8_quantize_mx(x, fmt="e4m3")`` -> (codes uint8, E8M0 scale bytes uint8 [rows, cols/32])
 * ``fp8_mx_gemm(qa, sa, qw, sw, out_dtype=torch.bfloat16)`` -> C
 
@@ -61,6 +63,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp8_block_gemm_quant.argtypes = [i64, i64, i64, vp, i64, vp, i32, i64, i64, vp, i64, vp, i32,
                                          i64, i64, i32, i32, i32, vp, i64, vp, i64, i64, vp]
     lib.fp8_block_gemm_quant.restype = i32
+    lib.fp8_quantize_static.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, i64, vp, vp]
+    lib.fp8_quantize_static.restype = i32
+    lib.fp8_scale_from_amax_history.argtypes = [vp, i64, i32, vp, vp]
+    lib.fp8_scale_from_amax_history.restype = i32
     lib.fp8_quantize_mx.argtypes = [vp, i32, i64, i64, i64, i32, vp, i64, vp, i64, vp]
     lib.fp8_quantize_mx.restype = i32
     lib.fp8_mx_gemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, i32, i32, vp, i32, i64, vp]
@@ -206,6 +212,50 @@ def fp8_block_gemm_quant(qa: torch.Tensor, sa: torch.Tensor, gran_a: str, qw: to
                                     _FMT[fmt_c], _ptr(out), out.stride(0), _ptr(scales), scales.stride(0),
                                     scales.stride(1), _stream(qa)))
     return out, scales
+
+
+def fp8_quantize_static(x: torch.Tensor, scale: torch.Tensor, fmt: str = "e4m3", record_amax: bool = False,
+                        out: torch.Tensor = None, amax: torch.Tensor = None):
+    """Quantize a 2-D bf16/fp32 tensor with the caller's scale (device fp32
+    tensor of one element). Returns codes, or (codes, amax [1]) with
+    record_amax."""
+    lib = load_library()
+    _require_cuda(x, scale)
+    if x.dim() != 2:
+        raise ValueError("fp8_quantize_static expects a 2-D tensor")
+    dt = BF16 if x.dtype == torch.bfloat16 else F32 if x.dtype == torch.float32 else None
+    if dt is None:
+        raise ValueError("fp8_quantize_static: x must be bf16 or fp32")
+    if x.stride(1) != 1:
+        x = x.contiguous()
+    if scale.dtype != torch.float32 or scale.numel() < 1:
+        raise ValueError("fp8_quantize_static: scale must be a float32 tensor holding the scale")
+    if amax is not None and (amax.dtype != torch.float32 or amax.numel() < 1 or not amax.is_cuda):
+        raise ValueError("fp8_quantize_static: amax must be a float32 GPU tensor of at least one element")
+    rows, cols = x.shape
+    if out is None:
+        ldq = ((cols + 15) // 16) * 16
+        out = torch.empty((rows, ldq), dtype=torch.uint8, device=x.device)[:, :cols]
+    if record_amax and amax is None:
+        amax = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(lib.fp8_quantize_static(_ptr(x), dt, rows, cols, x.stride(0), _FMT[fmt], _ptr(scale), _ptr(out),
+                                   out.stride(0), _ptr(amax) if record_amax else None, _stream(x)))
+    return (out, amax) if record_amax else out
+
+
+def fp8_scale_from_amax_history(history: torch.Tensor, fmt: str = "e4m3", out: torch.Tensor = None):
+    """Delayed-scaling scale max(history) / MAX as a device fp32 tensor [1]."""
+    lib = load_library()
+    _require_cuda(history)
+    if history.dtype != torch.float32:
+        raise ValueError("fp8_scale_from_amax_history: history must be float32")
+    history = history.contiguous()
+    if out is not None and (out.dtype != torch.float32 or out.numel() < 1 or not out.is_cuda):
+        raise ValueError("fp8_scale_from_amax_history: out must be a float32 GPU tensor")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=history.device)
+    _check(lib.fp8_scale_from_amax_history(_ptr(history), history.numel(), _FMT[fmt], _ptr(out), _stream(history)))
+    return out
 
 
 def fp8_quantize_mx(x: torch.Tensor, fmt: str = "e4m3", out: torch.Tensor = None, scales: torch.Tensor = None):

@@ -277,6 +277,59 @@ fp8blk_status fp8_block_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_
   return hip_status(fp8blk::launch_block_gemm(g, static_cast<hipStream_t>(stream)), fn);
 }
 
+fp8blk_status fp8_quantize_static(const void* x, fp8blk_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                  fp8blk_format fmt, const float* scale, uint8_t* q, int64_t ld_q, float* amax_out,
+                                  void* stream) {
+  const char* fn = "fp8_quantize_static";
+  if (!scale || ((!x || !q) && rows > 0 && cols > 0)) return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
+  if (x_dtype != FP8BLK_BF16 && x_dtype != FP8BLK_F32)
+    return fail(FP8BLK_EINVAL, "%s: unknown input dtype %d", fn, (int)x_dtype);
+  if (fp8blk_status st = check_format(fmt, fn)) return st;
+  if (rows < 0 || cols < 0) return fail(FP8BLK_EINVAL, "%s: negative size", fn);
+  if (rows >= kMaxDim || cols >= kMaxDim || ld_x >= kMaxDim || ld_q >= kMaxDim)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: dimension above 2^31", fn);
+  if (ld_x < cols || ld_q < cols) return fail(FP8BLK_EINVAL, "%s: leading dimension < cols", fn);
+  const int64_t esz = x_dtype == FP8BLK_BF16 ? 2 : 4;
+  if (!aligned16(x) || !aligned16(q)) return fail(FP8BLK_EALIGN, "%s: x and q must be 16-byte aligned", fn);
+  if ((ld_x * esz) % 16 != 0 || ld_q % 16 != 0)
+    return fail(FP8BLK_EALIGN, "%s: ld_x * elem_size and ld_q must be multiples of 16 bytes", fn);
+  if ((reinterpret_cast<uintptr_t>(scale) & 3u) != 0 || (reinterpret_cast<uintptr_t>(amax_out) & 3u) != 0)
+    return fail(FP8BLK_EALIGN, "%s: scale and amax_out must be 4-byte aligned", fn);
+  const Range rsc = range_grid(scale, 1, 1, 0, 0);
+  const Range ram = amax_out ? range_grid(amax_out, 1, 1, 0, 0) : Range{0, 0};
+  if (amax_out && overlap(rsc, ram)) return fail(FP8BLK_EINVAL, "%s: amax_out must not overlap scale", fn);
+  if (rows > 0 && cols > 0) {
+    const Range rx = range2d(x, rows, cols, ld_x, esz);
+    const Range rq = range2d(q, rows, cols, ld_q, 1);
+    if (overlap(rx, rq) || overlap(rq, rsc) || (amax_out && (overlap(rx, ram) || overlap(rq, ram))))
+      return fail(FP8BLK_EINVAL, "%s: x, q, scale and amax_out must not overlap", fn);
+  }
+  fp8blk::QuantArgs a = {};
+  a.x = x;
+  a.x_dtype = (int)x_dtype;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld_x = ld_x;
+  a.fmt = (int)fmt;
+  a.q = q;
+  a.ld_q = ld_q;
+  return hip_status(fp8blk::launch_quantize_static(a, scale, amax_out, static_cast<hipStream_t>(stream)), fn);
+}
+
+fp8blk_status fp8_scale_from_amax_history(const float* history, int64_t n, fp8blk_format fmt, float* scale_out,
+                                          void* stream) {
+  const char* fn = "fp8_scale_from_amax_history";
+  if (!history || !scale_out) return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
+  if (fp8blk_status st = check_format(fmt, fn)) return st;
+  if (n <= 0) return fail(FP8BLK_EINVAL, "%s: the history must hold at least one value", fn);
+  if (n >= kMaxDim) return fail(FP8BLK_EUNSUPPORTED, "%s: history longer than 2^31", fn);
+  if ((reinterpret_cast<uintptr_t>(history) & 3u) != 0 || (reinterpret_cast<uintptr_t>(scale_out) & 3u) != 0)
+    return fail(FP8BLK_EALIGN, "%s: pointers must be 4-byte aligned", fn);
+  if (overlap(range_grid(history, 1, n, 0, 1), range_grid(scale_out, 1, 1, 0, 0)))
+    return fail(FP8BLK_EINVAL, "%s: scale_out must not overlap the history", fn);
+  return hip_status(fp8blk::launch_scale_from_history(history, n, (int)fmt, scale_out, static_cast<hipStream_t>(stream)), fn);
+}
+
 fp8blk_status fp8_quantize_mx(const void* x, fp8blk_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                               fp8blk_format fmt, uint8_t* q, int64_t ld_q, uint8_t* scales, int64_t ld_s,
                               void* stream) {

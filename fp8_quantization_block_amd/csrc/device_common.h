@@ -226,6 +226,33 @@ __device__ __forceinline__ uint32_t cast4_f32(const GroupScale& g, float a, floa
   return exact4<kFmt>(g, a, b, c, d);
 }
 
+// A caller-supplied scale s (static or delayed scaling): the same reciprocal
+// as make_group_scale computes.
+__device__ __forceinline__ GroupScale make_given_scale(float s) {
+  GroupScale g;
+  g.s = s;
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  g.r = __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
+  return g;
+}
+
+// Codes of four elements under a caller-supplied scale, where |x / s| may lie
+// anywhere (saturation is real): the bracket of cast4_f32 with both brackets
+// clamped to +-MAX first for either format (a monotone, saturating
+// conversion, so the bracket argument holds), else the exact division. The
+// bracket needs a normal reciprocal, so s above 2^125 takes the exact path.
+template <int kFmt>
+__device__ __forceinline__ uint32_t cast4_sat(const GroupScale& g, float a, float b, float c, float d) {
+  if (g.s >= 0x1.0p-126f && g.s <= 0x1.0p125f) {
+    const float rl = g.r * (1.0f - 0x1.0p-20f);
+    const float rh = g.r * (1.0f + 0x1.0p-20f);
+    const uint32_t lo = pack4_sat<kFmt>(a * rl, b * rl, c * rl, d * rl);
+    const uint32_t hi = pack4_sat<kFmt>(a * rh, b * rh, c * rh, d * rh);
+    if (__builtin_expect(lo == hi, 1)) return lo;
+  }
+  return exact4<kFmt>(g, a, b, c, d);
+}
+
 // Codes of four elements of one group whose values are bf16 numbers.
 template <int kFmt>
 __device__ __forceinline__ uint32_t cast4_bf16(const GroupScale& g, float a, float b, float c, float d) {

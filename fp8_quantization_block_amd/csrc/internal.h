@@ -94,6 +94,10 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
 // MX blocks of 32 along the rows: a.scales points at uint8 E8M0 bytes, a.ss_row
 // is the byte stride between their rows.
 hipError_t launch_quantize_mx(const QuantArgs& a, hipStream_t st);
+// Codes under a caller-supplied scale (scale[0], device); amax_out (device,
+// may be null) receives max|x| of the tensor.
+hipError_t launch_quantize_static(const QuantArgs& a, const float* scale, float* amax_out, hipStream_t st);
+hipError_t launch_scale_from_history(const float* history, int64_t n, int fmt, float* scale_out, hipStream_t st);
 hipError_t launch_kv_decode_attention(const AttnArgs& a, hipStream_t st);
 hipError_t launch_kv_quantize(const KvArgs& a, hipStream_t st);
 hipError_t launch_kv_dequantize(const KvArgs& a, hipStream_t st);

@@ -71,6 +71,13 @@ struct Vec8<__hip_bfloat16> {
     r.y = cast4_bf16<kFmt>(g, bf16_lo_to_f32(w.z), bf16_hi_to_f32(w.z), bf16_lo_to_f32(w.w), bf16_hi_to_f32(w.w));
     return r;
   }
+  template <int kFmt>
+  __device__ __forceinline__ uint2 cast_sat(const GroupScale& g) const {
+    uint2 r;
+    r.x = cast4_sat<kFmt>(g, bf16_lo_to_f32(w.x), bf16_hi_to_f32(w.x), bf16_lo_to_f32(w.y), bf16_hi_to_f32(w.y));
+    r.y = cast4_sat<kFmt>(g, bf16_lo_to_f32(w.z), bf16_hi_to_f32(w.z), bf16_lo_to_f32(w.w), bf16_hi_to_f32(w.w));
+    return r;
+  }
   // codes of x * 2^e (exact scaling), saturating
   template <int kFmt>
   __device__ __forceinline__ uint2 cast_pow2(int e) const {
@@ -115,6 +122,13 @@ struct Vec8<float> {
     uint2 r;
     r.x = cast4_f32<kFmt>(g, a.x, a.y, a.z, a.w);
     r.y = cast4_f32<kFmt>(g, b.x, b.y, b.z, b.w);
+    return r;
+  }
+  template <int kFmt>
+  __device__ __forceinline__ uint2 cast_sat(const GroupScale& g) const {
+    uint2 r;
+    r.x = cast4_sat<kFmt>(g, a.x, a.y, a.z, a.w);
+    r.y = cast4_sat<kFmt>(g, b.x, b.y, b.z, b.w);
     return r;
   }
   template <int kFmt>
@@ -433,6 +447,54 @@ __global__ __launch_bounds__(256) void k_quant_mx(const T* __restrict__ x, int64
 }
 
 // ---------------------------------------------------------------------------
+// Static / delayed scaling ([MIXED] charles2530.github.io, "量化：FP8 与混合精度推理",
+// section "scale 是控制面": the scale may come from history instead of the
+// current batch, as Transformer Engine's delayed scaling updates it from
+// recorded amax values; [VS] api.makesence.top section 2 trains with delayed
+// scaling). The codes use a scale read from device memory; the pass can record
+// the tensor's own amax for the caller's history. The scale from a history is
+// max(history) / MAX.
+// ---------------------------------------------------------------------------
+template <typename T, int kFmt>
+__global__ __launch_bounds__(256) void k_cast_static(const T* __restrict__ x, int64_t ld_x, uint32_t cols,
+                                                     uint64_t nchunks, const float* __restrict__ scale,
+                                                     uint8_t* __restrict__ q, int64_t ld_q,
+                                                     float* __restrict__ amax_out) {
+  const GroupScale gs = make_given_scale(*scale);
+  const uint32_t cpr = (cols + 7u) >> 3;
+  uint32_t m = 0;
+  for (uint64_t c = (uint64_t)blockIdx.x * 256u + threadIdx.x; c < nchunks; c += (uint64_t)gridDim.x * 256u) {
+    const uint64_t r = c / cpr;
+    const uint32_t cc = (uint32_t)(c - r * cpr);
+    const uint32_t nv = min(8u, cols - cc * 8u);
+    Vec8<T> v;
+    v.load(x + (int64_t)r * ld_x + cc * 8u, nv);
+    if (amax_out) {
+      const uint32_t a = v.amax_bits();
+      m = a > m ? a : m;
+    }
+    store_codes8(q + (int64_t)r * ld_q + cc * 8u, v.template cast_sat<kFmt>(gs), nv);
+  }
+  if (amax_out) {
+    m = block256_max(m);
+    if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(amax_out), m);
+  }
+}
+
+// scale_out[0] = max(history[0 .. n)) / MAX (one workgroup; history >= 0).
+template <int kFmt>
+__global__ __launch_bounds__(256) void k_scale_from_history(const float* __restrict__ history, uint32_t n,
+                                                            float* __restrict__ scale_out) {
+  uint32_t m = 0;
+  for (uint32_t i = threadIdx.x; i < n; i += 256u) {
+    const uint32_t a = __float_as_uint(history[i]) & 0x7fffffffu;
+    m = a > m ? a : m;
+  }
+  m = block256_max(m);
+  if (threadIdx.x == 0) scale_out[0] = __uint_as_float(m) / Fp8<kFmt>::kMax;
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers (arguments already validated by the API layer).
 // ---------------------------------------------------------------------------
 namespace {
@@ -513,6 +575,37 @@ hipError_t launch_quantize_mx(const QuantArgs& a, hipStream_t st) {
     else
       hipLaunchKernelGGL((k_quant_mx<float, FMT_E4M3>), grid, dim3(256), 0, st, x, a.ld_x, cols, nblk, total, fd, a.q, a.ld_q, sc, a.ss_row);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_static(const QuantArgs& a, const float* scale, float* amax_out, hipStream_t st) {
+  const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
+  if (amax_out) hipLaunchKernelGGL(k_store_zero, dim3(1), dim3(64), 0, st, amax_out);
+  if (rows == 0 || cols == 0) return amax_out ? hipGetLastError() : hipSuccess;
+  const uint64_t nchunks = (uint64_t)rows * ((cols + 7u) >> 3);
+  const uint64_t want = (nchunks + 255) / 256;
+  const dim3 grid((uint32_t)(want < 4096 ? want : 4096));
+  if (a.x_dtype == DTYPE_BF16) {
+    const __hip_bfloat16* x = static_cast<const __hip_bfloat16*>(a.x);
+    if (a.fmt == FMT_E5M2)
+      hipLaunchKernelGGL((k_cast_static<__hip_bfloat16, FMT_E5M2>), grid, dim3(256), 0, st, x, a.ld_x, cols, nchunks, scale, a.q, a.ld_q, amax_out);
+    else
+      hipLaunchKernelGGL((k_cast_static<__hip_bfloat16, FMT_E4M3>), grid, dim3(256), 0, st, x, a.ld_x, cols, nchunks, scale, a.q, a.ld_q, amax_out);
+  } else {
+    const float* x = static_cast<const float*>(a.x);
+    if (a.fmt == FMT_E5M2)
+      hipLaunchKernelGGL((k_cast_static<float, FMT_E5M2>), grid, dim3(256), 0, st, x, a.ld_x, cols, nchunks, scale, a.q, a.ld_q, amax_out);
+    else
+      hipLaunchKernelGGL((k_cast_static<float, FMT_E4M3>), grid, dim3(256), 0, st, x, a.ld_x, cols, nchunks, scale, a.q, a.ld_q, amax_out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_from_history(const float* history, int64_t n, int fmt, float* scale_out, hipStream_t st) {
+  if (fmt == FMT_E5M2)
+    hipLaunchKernelGGL(k_scale_from_history<FMT_E5M2>, dim3(1), dim3(256), 0, st, history, (uint32_t)n, scale_out);
+  else
+    hipLaunchKernelGGL(k_scale_from_history<FMT_E4M3>, dim3(1), dim3(256), 0, st, history, (uint32_t)n, scale_out);
   return hipGetLastError();
 }
 

@@ -218,6 +218,45 @@ fp8blk_status fp8_kv_dequantize(const uint8_t* q, const float* scales, int64_t h
                                 fp8blk_format fmt, void* out_bf16, void* stream);
 
 /*
+ * fp8_quantize_static -- quantization with a caller-supplied per-tensor scale
+ * (static scaling, or delayed scaling with a scale derived from past amax
+ * values), optionally recording the tensor's own amax.
+ *
+ * Defined by [MIXED] section "scale 是控制面" (the scale can come from recorded
+ * history instead of the current batch: Transformer Engine's delayed scaling
+ * updates it from past amax statistics) and [VS] section 2 (delayed scaling in
+ * the FP8 forward pass); the cast is that of fp8_quantize: the code of the
+ * format value nearest to fl32(x / s), ties to even, saturating at +-MAX, the
+ * sign of a zero result that of x. s = scale[0] is read on the device and must
+ * be positive and finite (0 gives sign-only zero codes; other values give
+ * unspecified codes).
+ *
+ *   x, q        as fp8_quantize.
+ *   scale       device, one float, the dequantization multiplier s.
+ *   amax_out    device, one float, or NULL: receives max |x| over the tensor
+ *               (0 for an empty tensor), to append to the caller's history.
+ *
+ * Requirements: as fp8_quantize for x and q, except that x and q may be NULL
+ * when rows or cols is 0 (then only amax_out is written); scale and amax_out
+ * 4-byte aligned and not overlapping each other, x or q.
+ */
+fp8blk_status fp8_quantize_static(const void* x, fp8blk_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                  fp8blk_format fmt, const float* scale, uint8_t* q, int64_t ld_q, float* amax_out,
+                                  void* stream);
+
+/*
+ * fp8_scale_from_amax_history -- scale_out[0] = fl32(max_i history[i] / MAX)
+ * (MAX = 448 for E4M3, 57344 for E5M2): the delayed-scaling scale from a
+ * window of recorded amax values ([MIXED] section "scale 是控制面"; the same
+ * division as fp8_quantize's per-tensor scale).
+ *
+ *   history     device, n >= 1 non-negative floats.
+ *   scale_out   device, one float.
+ */
+fp8blk_status fp8_scale_from_amax_history(const float* history, int64_t n, fp8blk_format fmt, float* scale_out,
+                                          void* stream);
+
+/*
  * fp8_quantize_mx -- MX quantization: FP8 codes with one power-of-two scale per
  * 32 consecutive elements of a row.
  *

@@ -67,7 +67,10 @@ def scale_of(amax, fmt: str = "e4m3") -> np.ndarray:
 def cast(x32: np.ndarray, s32: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
     """Codes of fl32(x / s), elementwise; ``s`` broadcasts against ``x``.
 
-    Where s == 0 the code is the sign of x with a zero magnitude.
+    Where s == 0 the code is the sign of x with a zero magnitude. A quotient
+    that overflows fp32 (possible only with a caller-supplied scale) lies
+    beyond the format's range like any other, so it saturates: it is passed
+    to the encoder as the largest finite fp32 number of its sign.
     """
     enc = fmt_module(fmt).encode
     x32 = np.asarray(x32, dtype=np.float32)
@@ -81,9 +84,10 @@ def cast(x32: np.ndarray, s32: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
         xs = flat_x[lo:lo + step]
         ss = flat_s[lo:lo + step]
         zero = ss == 0
-        with np.errstate(divide="ignore", invalid="ignore"):
+        with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
             quot = xs / np.where(zero, np.float32(1), ss)   # fp32 / fp32, IEEE
         quot = np.where(zero, np.where(np.signbit(xs), np.float32(-0.0), np.float32(0.0)), quot)
+        quot = np.where(np.isinf(quot) & np.isfinite(xs), np.copysign(np.finfo(np.float32).max, quot), quot)
         flat_o[lo:lo + step] = enc(quot)
     return out
 
@@ -153,6 +157,22 @@ def kv_quantize(kv, token_block: int = GROUP, fmt: str = "e4m3") -> tuple:
     s = scale_of(amax, fmt)
     s_full = np.repeat(s, token_block, axis=1)[:, :t, None]
     return cast(x32, s_full, fmt), s
+
+
+def quantize_static(x, s, fmt: str = "e4m3") -> tuple:
+    """Static / delayed scaling ([MIXED] section "scale 是控制面": a scale taken
+    from history rather than the current batch): codes of fl32(x / s) under
+    the given fp32 scale s (saturating like every cast here), and the tensor's
+    own amax for the caller's history. Returns (codes, amax float32)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32)) if x32.size else np.float32(0)
+    return cast(x32, np.float32(s), fmt), np.float32(amax)
+
+
+def scale_from_history(history, fmt: str = "e4m3") -> np.float32:
+    """Delayed-scaling scale: fl32(max(history) / max_fmt) ([MIXED] section
+    "scale 是控制面", amax history)."""
+    return scale_of(np.max(np.abs(np.asarray(history, dtype=np.float32))), fmt)
 
 
 def f32_to_bf16_bits(x32) -> np.ndarray:

@@ -42,6 +42,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fp8_quantize", "fp8_block_gemm", "fp8_block_gemm_quant", "fp8_kv_quantize", "fp8_kv_dequantize",
               "fp8_kv_decode_attention", "fp8_kv_decode_attention_workspace_size", "fp8_quantize_mx", "fp8_mx_gemm",
+              "fp8_quantize_static", "fp8_scale_from_amax_history",
               "fp8blk_status_string", "fp8blk_last_error", "fp8blk_abi_version"):
         assert n in names
 
@@ -213,6 +214,47 @@ def qmx(lib, x=PA, dt=BF16, rows=4, cols=256, ldx=256, fmt=E4M3, qp=PB, ldq=256,
 def test_quantize_mx_rejects(lib, kw, status):
     assert qmx(lib, **kw) == status
     assert lib.fp8blk_last_error().decode().startswith("fp8_quantize_mx")
+
+
+def qst(lib, x=PA, dt=BF16, rows=4, cols=256, ldx=256, fmt=E4M3, s=PC, qp=PB, ldq=256, amax=PD):
+    return lib.fp8_quantize_static(x, dt, rows, cols, ldx, fmt, s, qp, ldq, amax, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=0), EINVAL),
+    (dict(s=0), EINVAL),                    # the scale is required
+    (dict(fmt=2), EINVAL),
+    (dict(dt=2), EINVAL),
+    (dict(cols=-1), EINVAL),
+    (dict(ldq=128), EINVAL),
+    (dict(x=PA + 8), EALIGN),
+    (dict(s=PC + 2), EALIGN),
+    (dict(amax=PD + 1), EALIGN),
+    (dict(amax=PC), EINVAL),                # amax_out is the scale
+    (dict(s=PB + 64), EINVAL),              # the scale lies inside the codes
+    (dict(rows=1 << 31), EUNSUPPORTED),
+])
+def test_quantize_static_rejects(lib, kw, status):
+    assert qst(lib, **kw) == status
+    assert lib.fp8blk_last_error().decode().startswith("fp8_quantize_static")
+
+
+def test_quantize_static_empty_without_amax_is_a_noop(lib):
+    assert qst(lib, rows=0, amax=None) == OK
+    assert qst(lib, cols=0, x=0, qp=0, amax=None) == OK     # no data pointers needed for an empty tensor
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 4, E4M3, PB), EINVAL),
+    ((PA, 0, E4M3, PB), EINVAL),            # empty history
+    ((PA, 4, 7, PB), EINVAL),
+    ((PA, 4, E4M3, 0), EINVAL),
+    ((PA + 2, 4, E4M3, PB), EALIGN),
+    ((PA, 4, E4M3, PA + 8), EINVAL),        # scale_out inside the history
+])
+def test_scale_from_history_rejects(lib, args, status):
+    assert lib.fp8_scale_from_amax_history(*args, None) == status
+    assert lib.fp8blk_last_error().decode().startswith("fp8_scale_from_amax_history")
 
 
 def mxg(lib, M=256, N=256, K=256, a=PA, lda=256, sa=PB, ldsa=8, b=PC, ldb=256, sb=PB + 65536, ldsb=8,
