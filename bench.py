@@ -46,7 +46,7 @@ def parse():
                     help="seconds of untimed steps run first, so the GPU clock has left its idle state")
     ap.add_argument("--no-secondary", action="store_true", help="skip the KV and decode passes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["gemm", "quant", "kv", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["gemm", "quant", "kv", "decode", "mx", "copy"], default=None,
                     help="time one pass only (for profiling runs); 'copy' times a plain 512 MB "
                          "device copy, the calibration kernel for the HBM byte counters")
     return ap.parse_args()
@@ -190,6 +190,30 @@ def main():
     torch.cuda.synchronize()
     settle(torch, step, args.settle_s)
 
+    # ---- the timed step: warmup, then exactly `steps` steps ---------------
+    # Timed first, straight after the settle phase: after a stretch of
+    # lighter passes the power controller lets the clock rise and then cuts it
+    # back hard once the GEMM resumes, which slowed the first GEMMs that
+    # followed the other passes by up to 25%.
+    t_step = None
+    if args.only is None:
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        e0.record(st)
+        for i in range(args.steps):
+            step(i)
+        e1.record(st)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        t_step = e0.elapsed_time(e1) * 1e-3 / args.steps
+        print(f"# timed {args.steps} steps: {t_step * 1e6:.1f} us/step (wall {wall:.3f} s)",
+              file=sys.stderr, flush=True)
+
     flops = 2.0 * M * N * K
     passes = {}
     if args.only in (None, "gemm"):
@@ -218,7 +242,7 @@ def main():
                                           "frac_fp8_peak": flops / t_f / 1e12 / PEAK_FP8_TFLOPS}
         passes["gemm_then_quantize_out"] = {"us": t_u * 1e6, "TFLOP/s": flops / t_u / 1e12}
         del qc, scq
-    if args.only is None and not args.no_secondary:
+    if args.only in (None, "mx") and not args.no_secondary:
         # MX operands (E4M3 codes, one power-of-two scale per 32 K elements):
         # the same step shape, the scales applied inside the scaled MFMA
         qamx = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(nsets)]
@@ -263,6 +287,18 @@ def main():
         passes["act_quant_1x128"] = {"us": t_qa * 1e6, "GB/s": bytes_qa / t_qa / 1e9,
                                      "frac_hbm": bytes_qa / t_qa / 1e9 / PEAK_HBM_GBPS}
         if not args.no_secondary:
+            # Per-tensor dynamic scaling: amax pass, then the cast (the tensor
+            # is read twice; algorithmic bytes count it once)
+            s_pt = torch.empty(1, dtype=torch.float32, device=dev)
+
+            def quant_pt(i):
+                j = i % nsets
+                fp8.fp8_quantize(a_sets[j], "per_tensor", out=qa_sets[j], scales=s_pt)
+
+            t_pt = timer.run(quant_pt, max(args.steps, 22), warmup=args.warmup, name="act_quant_per_tensor")
+            bytes_pt = M * K * 2 + M * K + 4
+            passes["act_quant_per_tensor"] = {"us": t_pt * 1e6, "GB/s": bytes_pt / t_pt / 1e9,
+                                              "frac_hbm": bytes_pt / t_pt / 1e9 / PEAK_HBM_GBPS}
             # Delayed scaling: the cast under a scale from the amax history,
             # recording this tensor's amax into the history
             hist = torch.full((16,), float(a_host.float().abs().max()), dtype=torch.float32, device=dev)
@@ -281,26 +317,6 @@ def main():
         bytes_qw = N * K * 2 + N * K + (N // 128) * (K // 128) * 4
         passes["weight_quant_128x128_offline"] = {"us": t_qw * 1e6, "GB/s": bytes_qw / t_qw / 1e9,
                                                   "frac_hbm": bytes_qw / t_qw / 1e9 / PEAK_HBM_GBPS}
-
-    # ---- the timed step: warmup, then exactly `steps` steps ---------------
-    t_step = None
-    if args.only is None:
-        for i in range(args.warmup):
-            step(i)
-        torch.cuda.synchronize()
-        st = torch.cuda.current_stream()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        wall0 = time.perf_counter()
-        e0.record(st)
-        for i in range(args.steps):
-            step(i)
-        e1.record(st)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        t_step = e0.elapsed_time(e1) * 1e-3 / args.steps
-        print(f"# timed {args.steps} steps: {t_step * 1e6:.1f} us/step (wall {wall:.3f} s)",
-              file=sys.stderr, flush=True)
 
     # ---- secondary passes: KV cache and decode-shaped GEMM ------------------
     if not args.no_secondary and args.only in (None, "kv"):

@@ -344,48 +344,106 @@ __global__ __launch_bounds__(256) void k_kv_dequant(
 }
 
 // ---------------------------------------------------------------------------
-// Per tensor: zero the accumulator, atomic max of |x| bits into scales[0],
-// cast with the scale derived from it, then store the scale itself.
+// Streaming passes over a whole [rows, cols] tensor in chunks of 8 elements
+// (16 B of bf16): each thread of a 256-thread workgroup loads U chunks that
+// lie 256 chunks apart before it converts any of them, so that U loads per
+// thread are in flight.
+// ---------------------------------------------------------------------------
+
+// Row and chunk column of flat chunk c: a 32-bit multiply-shift division below
+// 2^31 chunks, a 64-bit division above.
+template <bool kWide>
+struct ChunkMap {
+  uint32_t cpr;   // chunks per row
+  FastDiv fd;     // division by cpr
+  __device__ __forceinline__ void at(uint64_t c, uint64_t& r, uint32_t& cc) const {
+    if constexpr (kWide) {
+      r = c / cpr;
+      cc = (uint32_t)(c - r * cpr);
+    } else {
+      const uint32_t rr = fastdiv((uint32_t)c, fd);
+      r = rr;
+      cc = (uint32_t)c - rr * cpr;
+    }
+  }
+};
+
+template <typename T, int U, bool kWide, bool kStream, typename F>
+__device__ __forceinline__ void for_chunks(const T* __restrict__ x, int64_t ld_x, uint32_t cols, uint64_t nchunks,
+                                           const ChunkMap<kWide>& map, F&& f) {
+  const uint64_t stride = (uint64_t)gridDim.x * 256u * U;
+  for (uint64_t base = (uint64_t)blockIdx.x * 256u * U + threadIdx.x; base < nchunks; base += stride) {
+    Vec8<T> v[U];
+    uint64_t r[U];
+    uint32_t cc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t c = base + (uint64_t)u * 256u;
+      if (c < nchunks) {
+        map.at(c, r[u], cc[u]);
+        v[u].template load<kStream>(x + (int64_t)r[u] * ld_x + cc[u] * 8u, min(8u, cols - cc[u] * 8u));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (base + (uint64_t)u * 256u < nchunks) f(v[u], r[u], cc[u], min(8u, cols - cc[u] * 8u));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per tensor: max |x| over the whole tensor, the cast with s = amax / MAX, then
+// s itself into scales[0]. The max is taken in two steps and needs no buffer
+// of the library's own: each workgroup leaves its max in a 4-byte slot of the
+// code buffer q, which the cast rewrites afterwards, and one workgroup reduces
+// the slots into scales[0]. (Same-address atomics from thousands of
+// workgroups serialize at ~10 ns each, several times the pass itself.)
 // ---------------------------------------------------------------------------
 __global__ void k_store_zero(float* __restrict__ p) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *reinterpret_cast<uint32_t*>(p) = 0u;
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void k_amax_tensor(const T* __restrict__ x, int64_t ld_x,
-                                                     uint32_t cols, uint64_t nchunks,
-                                                     float* __restrict__ acc) {
-  const uint32_t cpr = (cols + 7u) >> 3;
+// Slot b: 4 bytes at row b / per_row, byte 4 * (b % per_row), of a row-major
+// byte buffer with row pitch ld (4-byte aligned rows).
+struct SlotMap {
+  uint8_t* base;
+  uint32_t per_row;
+  int64_t ld;
+  __device__ __forceinline__ uint32_t* at(uint32_t b) const {
+    return reinterpret_cast<uint32_t*>(base + (int64_t)(b / per_row) * ld + (int64_t)(b % per_row) * 4);
+  }
+};
+
+template <typename T, int U, bool kWide>
+__global__ __launch_bounds__(256) void k_amax_slots(const T* __restrict__ x, int64_t ld_x, uint32_t cols,
+                                                    uint64_t nchunks, ChunkMap<kWide> map, SlotMap slots) {
   uint32_t m = 0;
-  for (uint64_t c = (uint64_t)blockIdx.x * 256u + threadIdx.x; c < nchunks;
-       c += (uint64_t)gridDim.x * 256u) {
-    const uint64_t r = c / cpr;
-    const uint32_t cc = (uint32_t)(c - r * cpr);
-    Vec8<T> v;
-    v.template load<false>(x + (int64_t)r * ld_x + cc * 8u, min(8u, cols - cc * 8u));
+  for_chunks<T, U, kWide, false>(x, ld_x, cols, nchunks, map, [&](const Vec8<T>& v, uint64_t, uint32_t, uint32_t) {
     const uint32_t a = v.amax_bits();
     m = a > m ? a : m;
-  }
+  });
   m = block256_max(m);
-  if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(acc), m);
+  if (threadIdx.x == 0) *slots.at(blockIdx.x) = m;
 }
 
-template <typename T, int kFmt>
-__global__ __launch_bounds__(256) void k_cast_tensor(const T* __restrict__ x, int64_t ld_x,
-                                                     uint32_t cols, uint64_t nchunks,
-                                                     const float* __restrict__ acc,
-                                                     uint8_t* __restrict__ q, int64_t ld_q) {
-  const GroupScale gs = make_group_scale<kFmt>(*reinterpret_cast<const uint32_t*>(acc));
-  const uint32_t cpr = (cols + 7u) >> 3;
-  for (uint64_t c = (uint64_t)blockIdx.x * 256u + threadIdx.x; c < nchunks;
-       c += (uint64_t)gridDim.x * 256u) {
-    const uint64_t r = c / cpr;
-    const uint32_t cc = (uint32_t)(c - r * cpr);
-    const uint32_t nv = min(8u, cols - cc * 8u);
-    Vec8<T> v;
-    v.load(x + (int64_t)r * ld_x + cc * 8u, nv);
-    store_codes8(q + (int64_t)r * ld_q + cc * 8u, v.template cast<kFmt>(gs), nv);
+__global__ __launch_bounds__(256) void k_reduce_slots(SlotMap slots, uint32_t n, float* __restrict__ acc) {
+  uint32_t m = 0;
+  for (uint32_t b = threadIdx.x; b < n; b += 256u) {
+    const uint32_t v = *slots.at(b);
+    m = v > m ? v : m;
   }
+  m = block256_max(m);
+  if (threadIdx.x == 0) *reinterpret_cast<uint32_t*>(acc) = m;
+}
+
+template <typename T, int kFmt, int U, bool kWide>
+__global__ __launch_bounds__(256) void k_cast_tensor(const T* __restrict__ x, int64_t ld_x, uint32_t cols,
+                                                     uint64_t nchunks, ChunkMap<kWide> map,
+                                                     const float* __restrict__ acc, uint8_t* __restrict__ q,
+                                                     int64_t ld_q) {
+  const GroupScale gs = make_group_scale<kFmt>(*reinterpret_cast<const uint32_t*>(acc));
+  for_chunks<T, U, kWide, true>(x, ld_x, cols, nchunks, map, [&](const Vec8<T>& v, uint64_t r, uint32_t cc, uint32_t nv) {
+    store_codes8(q + (int64_t)r * ld_q + cc * 8u, v.template cast<kFmt>(gs), nv);
+  });
 }
 
 template <int kFmt>
@@ -455,29 +513,29 @@ __global__ __launch_bounds__(256) void k_quant_mx(const T* __restrict__ x, int64
 // the tensor's own amax for the caller's history. The scale from a history is
 // max(history) / MAX.
 // ---------------------------------------------------------------------------
-template <typename T, int kFmt>
+template <typename T, int kFmt, int U, bool kWide, bool kAmax>
 __global__ __launch_bounds__(256) void k_cast_static(const T* __restrict__ x, int64_t ld_x, uint32_t cols,
-                                                     uint64_t nchunks, const float* __restrict__ scale,
-                                                     uint8_t* __restrict__ q, int64_t ld_q,
-                                                     float* __restrict__ amax_out) {
+                                                     uint64_t nchunks, ChunkMap<kWide> map,
+                                                     const float* __restrict__ scale, uint8_t* __restrict__ q,
+                                                     int64_t ld_q, float* __restrict__ amax_out) {
   const GroupScale gs = make_given_scale(*scale);
-  const uint32_t cpr = (cols + 7u) >> 3;
   uint32_t m = 0;
-  for (uint64_t c = (uint64_t)blockIdx.x * 256u + threadIdx.x; c < nchunks; c += (uint64_t)gridDim.x * 256u) {
-    const uint64_t r = c / cpr;
-    const uint32_t cc = (uint32_t)(c - r * cpr);
-    const uint32_t nv = min(8u, cols - cc * 8u);
-    Vec8<T> v;
-    v.load(x + (int64_t)r * ld_x + cc * 8u, nv);
-    if (amax_out) {
+  for_chunks<T, U, kWide, true>(x, ld_x, cols, nchunks, map, [&](const Vec8<T>& v, uint64_t r, uint32_t cc, uint32_t nv) {
+    if constexpr (kAmax) {
       const uint32_t a = v.amax_bits();
       m = a > m ? a : m;
     }
     store_codes8(q + (int64_t)r * ld_q + cc * 8u, v.template cast_sat<kFmt>(gs), nv);
-  }
-  if (amax_out) {
+  });
+  if constexpr (kAmax) {
+    // The value only grows from the zero stored before this kernel, so a
+    // workgroup whose max does not exceed what amax_out already holds can skip
+    // its atomic; this removes most of the same-address atomics.
     m = block256_max(m);
-    if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(amax_out), m);
+    if (threadIdx.x == 0) {
+      unsigned int* p = reinterpret_cast<unsigned int*>(amax_out);
+      if (m > __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(p, m);
+    }
   }
 }
 
@@ -510,20 +568,66 @@ FastDiv make_fastdiv(uint32_t d) {
   return f;
 }
 
+constexpr int kAmaxUnroll = 4;            // chunks in flight per thread in the amax-only pass
+constexpr int kCastUnroll = 2;            // ... in the cast passes
+constexpr uint64_t kMaxStreamGrid = 8192;  // workgroups of a streaming pass (grid-stride beyond)
+
+uint32_t stream_grid(uint64_t nchunks, int unroll) {
+  const uint64_t want = (nchunks + 256ull * unroll - 1) / (256ull * unroll);
+  return (uint32_t)(want < kMaxStreamGrid ? want : kMaxStreamGrid);
+}
+
+template <bool kWide>
+ChunkMap<kWide> make_chunk_map(uint32_t cols) {
+  ChunkMap<kWide> m;
+  m.cpr = (cols + 7u) >> 3;
+  m.fd = make_fastdiv(m.cpr);
+  return m;
+}
+
+// amax into slots of q, slots into scales[0], cast, scale. Tensors with fewer
+// than 4 columns have no slot in q; one workgroup then writes scales[0] itself.
+template <typename T, int kFmt, bool kWide>
+void per_tensor_passes(const QuantArgs& a, const T* x, uint64_t nchunks, hipStream_t st) {
+  const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
+  const ChunkMap<kWide> map = make_chunk_map<kWide>(cols);
+  const uint64_t per_row = cols / 4u;
+  const uint64_t nslots = (uint64_t)rows * per_row;
+  uint32_t g = stream_grid(nchunks, kAmaxUnroll);
+  SlotMap sm;
+  if (nslots == 0) {
+    g = 1;
+    sm.base = reinterpret_cast<uint8_t*>(a.scales);
+    sm.per_row = 1;
+    sm.ld = 4;
+  } else {
+    if (g > nslots) g = (uint32_t)nslots;
+    sm.base = a.q;
+    sm.per_row = (uint32_t)per_row;
+    sm.ld = a.ld_q;
+  }
+  hipLaunchKernelGGL((k_amax_slots<T, kAmaxUnroll, kWide>), dim3(g), dim3(256), 0, st, x, a.ld_x, cols, nchunks,
+                     map, sm);
+  hipLaunchKernelGGL(k_reduce_slots, dim3(1), dim3(256), 0, st, sm, g, a.scales);
+  hipLaunchKernelGGL((k_cast_tensor<T, kFmt, kCastUnroll, kWide>), dim3(stream_grid(nchunks, kCastUnroll)), dim3(256),
+                     0, st, x, a.ld_x, cols, nchunks, map, a.scales, a.q, a.ld_q);
+  hipLaunchKernelGGL(k_finalize_tensor_scale<kFmt>, dim3(1), dim3(64), 0, st, a.scales);
+}
+
 template <typename T, int kFmt>
 hipError_t quantize_typed(const QuantArgs& a, hipStream_t st) {
   const T* x = static_cast<const T*>(a.x);
   const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
   if (a.gran == GRAN_PER_TENSOR) {
-    hipLaunchKernelGGL(k_store_zero, dim3(1), dim3(64), 0, st, a.scales);
-    if (rows == 0 || cols == 0) return hipGetLastError();
+    if (rows == 0 || cols == 0) {
+      hipLaunchKernelGGL(k_store_zero, dim3(1), dim3(64), 0, st, a.scales);
+      return hipGetLastError();
+    }
     const uint64_t nchunks = (uint64_t)rows * ((cols + 7u) >> 3);
-    const uint64_t want = (nchunks + 255) / 256;
-    const uint32_t grid = (uint32_t)(want < 4096 ? want : 4096);
-    hipLaunchKernelGGL(k_amax_tensor<T>, dim3(grid), dim3(256), 0, st, x, a.ld_x, cols, nchunks, a.scales);
-    hipLaunchKernelGGL((k_cast_tensor<T, kFmt>), dim3(grid), dim3(256), 0, st, x, a.ld_x, cols, nchunks,
-                       a.scales, a.q, a.ld_q);
-    hipLaunchKernelGGL(k_finalize_tensor_scale<kFmt>, dim3(1), dim3(64), 0, st, a.scales);
+    if (nchunks < (1ull << 31))
+      per_tensor_passes<T, kFmt, false>(a, x, nchunks, st);
+    else
+      per_tensor_passes<T, kFmt, true>(a, x, nchunks, st);
     return hipGetLastError();
   }
   if (rows == 0 || cols == 0) return hipSuccess;
@@ -578,25 +682,44 @@ hipError_t launch_quantize_mx(const QuantArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+namespace {
+template <typename T, int kFmt, bool kWide>
+void static_pass(const QuantArgs& a, uint64_t nchunks, const float* scale, float* amax_out, hipStream_t st) {
+  const T* x = static_cast<const T*>(a.x);
+  const uint32_t cols = (uint32_t)a.cols;
+  const ChunkMap<kWide> map = make_chunk_map<kWide>(cols);
+  if (amax_out)
+    hipLaunchKernelGGL((k_cast_static<T, kFmt, kAmaxUnroll, kWide, true>), dim3(stream_grid(nchunks, kAmaxUnroll)),
+                       dim3(256), 0, st, x, a.ld_x, cols, nchunks, map, scale, a.q, a.ld_q, amax_out);
+  else
+    hipLaunchKernelGGL((k_cast_static<T, kFmt, kCastUnroll, kWide, false>), dim3(stream_grid(nchunks, kCastUnroll)),
+                       dim3(256), 0, st, x, a.ld_x, cols, nchunks, map, scale, a.q, a.ld_q, amax_out);
+}
+
+template <typename T, int kFmt>
+void static_typed(const QuantArgs& a, uint64_t nchunks, const float* scale, float* amax_out, hipStream_t st) {
+  if (nchunks < (1ull << 31))
+    static_pass<T, kFmt, false>(a, nchunks, scale, amax_out, st);
+  else
+    static_pass<T, kFmt, true>(a, nchunks, scale, amax_out, st);
+}
+}  // namespace
+
 hipError_t launch_quantize_static(const QuantArgs& a, const float* scale, float* amax_out, hipStream_t st) {
   const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
   if (amax_out) hipLaunchKernelGGL(k_store_zero, dim3(1), dim3(64), 0, st, amax_out);
   if (rows == 0 || cols == 0) return amax_out ? hipGetLastError() : hipSuccess;
   const uint64_t nchunks = (uint64_t)rows * ((cols + 7u) >> 3);
-  const uint64_t want = (nchunks + 255) / 256;
-  const dim3 grid((uint32_t)(want < 4096 ? want : 4096));
   if (a.x_dtype == DTYPE_BF16) {
-    const __hip_bfloat16* x = static_cast<const __hip_bfloat16*>(a.x);
     if (a.fmt == FMT_E5M2)
-      hipLaunchKernelGGL((k_cast_static<__hip_bfloat16, FMT_E5M2>), grid, dim3(256), 0, st, x, a.ld_x, cols, nchunks, scale, a.q, a.ld_q, amax_out);
+      static_typed<__hip_bfloat16, FMT_E5M2>(a, nchunks, scale, amax_out, st);
     else
-      hipLaunchKernelGGL((k_cast_static<__hip_bfloat16, FMT_E4M3>), grid, dim3(256), 0, st, x, a.ld_x, cols, nchunks, scale, a.q, a.ld_q, amax_out);
+      static_typed<__hip_bfloat16, FMT_E4M3>(a, nchunks, scale, amax_out, st);
   } else {
-    const float* x = static_cast<const float*>(a.x);
     if (a.fmt == FMT_E5M2)
-      hipLaunchKernelGGL((k_cast_static<float, FMT_E5M2>), grid, dim3(256), 0, st, x, a.ld_x, cols, nchunks, scale, a.q, a.ld_q, amax_out);
+      static_typed<float, FMT_E5M2>(a, nchunks, scale, amax_out, st);
     else
-      hipLaunchKernelGGL((k_cast_static<float, FMT_E4M3>), grid, dim3(256), 0, st, x, a.ld_x, cols, nchunks, scale, a.q, a.ld_q, amax_out);
+      static_typed<float, FMT_E4M3>(a, nchunks, scale, amax_out, st);
   }
   return hipGetLastError();
 }

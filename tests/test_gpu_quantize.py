@@ -167,8 +167,8 @@ ORACLE = {"per_tensor": quant.quantize_per_tensor, "group_1x128": quant.quantize
 
 @pytest.mark.parametrize("gran", ["per_tensor", "group_1x128", "block_128x128"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("rows,cols,ld", [(1, 1, 8), (3, 8, 8), (5, 300, 304), (129, 131, 136),
-                                          (257, 1000, 1024), (130, 128, 128), (1, 4096, 4096)])
+@pytest.mark.parametrize("rows,cols,ld", [(1, 1, 8), (7, 3, 16), (300, 2, 16), (3, 8, 8), (5, 300, 304),
+                                          (129, 131, 136), (257, 1000, 1024), (130, 128, 128), (1, 4096, 4096)])
 def test_ragged_shapes(gpu_lib, gran, dtype, rows, cols, ld):
     rng = np.random.default_rng(rows * 7919 + cols)
     x = (rng.standard_normal((rows, cols)) * np.exp2(rng.uniform(-8, 8, size=(rows, 1)))).astype(np.float32)
@@ -268,3 +268,27 @@ def test_group_index_division(gpu_lib, ngroups):
     qg, sg = gpu_lib.fp8_quantize(xt.to(DEV), "group_1x128")
     assert_scales_equal(sg.cpu().numpy(), sr, "scales")
     assert_codes_equal(qg.cpu().numpy(), qr, x, "codes")
+
+
+def test_per_tensor_and_static_grid_stride(gpu_lib):
+    """A [16384, 8192] tensor: more chunks than the capped grids of the amax
+    and cast passes cover in one round, so every thread loops. The per-tensor
+    scale and the static pass's recorded amax are exact; codes are compared on
+    sampled rows, including the row that holds the single largest element."""
+    g = torch.Generator().manual_seed(5)
+    x = (torch.randn(16384, 8192, generator=g) * 3).to(torch.bfloat16)
+    x[12345, 777] = -300.0
+    x32 = x.float().numpy()
+    amax = np.float32(np.abs(x32).max())
+    assert amax == np.float32(300.0)
+    xd = x.to(DEV)
+    rows = np.unique(np.concatenate([np.random.default_rng(6).choice(16384, 40, replace=False), [0, 12345, 16383]]))
+    qg, sg = gpu_lib.fp8_quantize(xd, "per_tensor")
+    s_ref = quant.scale_of(amax)
+    assert_scales_equal(sg.cpu().numpy(), np.array([s_ref], np.float32), "per-tensor scale")
+    assert_codes_equal(qg.cpu().numpy()[rows], quant.cast(x32[rows], s_ref), x32[rows], "per-tensor codes")
+    s_static = torch.tensor([0.5], dtype=torch.float32, device=DEV)
+    qs, am = gpu_lib.fp8_quantize_static(xd, s_static, record_amax=True)
+    assert float(am.item()) == 300.0
+    qr, _ = quant.quantize_static(x32[rows], np.float32(0.5))
+    assert_codes_equal(qs.cpu().numpy()[rows], qr, x32[rows], "static codes")
