@@ -391,12 +391,12 @@ __device__ __forceinline__ void for_chunks(const T* __restrict__ x, int64_t ld_x
 }
 
 // ---------------------------------------------------------------------------
-// Per tensor: max |x| over the whole tensor, the cast with s = amax / MAX, then
-// s itself into scales[0]. The max is taken in two steps and needs no buffer
-// of the library's own: each workgroup leaves its max in a 4-byte slot of the
+// Per tensor: max |x| over the whole tensor, s = amax / MAX into scales[0],
+// then the cast with s. The max is taken in two steps and needs no buffer of
+// the library's own: each workgroup leaves its max in a 4-byte slot of the
 // code buffer q, which the cast rewrites afterwards, and one workgroup reduces
-// the slots into scales[0]. (Same-address atomics from thousands of
-// workgroups serialize at ~10 ns each, several times the pass itself.)
+// the slots. (Same-address atomics from thousands of workgroups serialize at
+// ~10 ns each, several times the pass itself.)
 // ---------------------------------------------------------------------------
 __global__ void k_store_zero(float* __restrict__ p) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *reinterpret_cast<uint32_t*>(p) = 0u;
@@ -425,33 +425,44 @@ __global__ __launch_bounds__(256) void k_amax_slots(const T* __restrict__ x, int
   if (threadIdx.x == 0) *slots.at(blockIdx.x) = m;
 }
 
-__global__ __launch_bounds__(256) void k_reduce_slots(SlotMap slots, uint32_t n, float* __restrict__ acc) {
-  uint32_t m = 0;
-  for (uint32_t b = threadIdx.x; b < n; b += 256u) {
-    const uint32_t v = *slots.at(b);
-    m = v > m ? v : m;
+// scales[0] = max over the n <= 1024 * kSlotsPerThread slots / MAX (the same
+// correctly rounded division as the group quantizers); one workgroup of 1024
+// threads, each with all of its slot loads in flight together.
+constexpr int kSlotsPerThread = 8;
+
+template <int kFmt>
+__global__ __launch_bounds__(1024) void k_reduce_slots(SlotMap slots, uint32_t n, float* __restrict__ scales) {
+  uint32_t v[kSlotsPerThread];
+#pragma unroll
+  for (int k = 0; k < kSlotsPerThread; ++k) {
+    const uint32_t b = threadIdx.x + 1024u * k;
+    v[k] = b < n ? *slots.at(b) : 0u;
   }
-  m = block256_max(m);
-  if (threadIdx.x == 0) *reinterpret_cast<uint32_t*>(acc) = m;
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < kSlotsPerThread; ++k) m = v[k] > m ? v[k] : m;
+  __shared__ uint32_t red[16];
+  m = wave_max(m);
+  if ((threadIdx.x & 63u) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r = red[i] > r ? red[i] : r;
+    scales[0] = make_group_scale<kFmt>(r).s;
+  }
 }
 
 template <typename T, int kFmt, int U, bool kWide>
 __global__ __launch_bounds__(256) void k_cast_tensor(const T* __restrict__ x, int64_t ld_x, uint32_t cols,
                                                      uint64_t nchunks, ChunkMap<kWide> map,
-                                                     const float* __restrict__ acc, uint8_t* __restrict__ q,
+                                                     const float* __restrict__ scales, uint8_t* __restrict__ q,
                                                      int64_t ld_q) {
-  const GroupScale gs = make_group_scale<kFmt>(*reinterpret_cast<const uint32_t*>(acc));
+  // s = amax / MAX, so |x / s| <= MAX and the group quantizers' cast applies
+  const GroupScale gs = make_given_scale(scales[0]);
   for_chunks<T, U, kWide, true>(x, ld_x, cols, nchunks, map, [&](const Vec8<T>& v, uint64_t r, uint32_t cc, uint32_t nv) {
     store_codes8(q + (int64_t)r * ld_q + cc * 8u, v.template cast<kFmt>(gs), nv);
   });
-}
-
-template <int kFmt>
-__global__ void k_finalize_tensor_scale(float* __restrict__ acc) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) {
-    const uint32_t bits = *reinterpret_cast<const uint32_t*>(acc);
-    acc[0] = __uint_as_float(bits) / Fp8<kFmt>::kMax;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -513,30 +524,102 @@ __global__ __launch_bounds__(256) void k_quant_mx(const T* __restrict__ x, int64
 // the tensor's own amax for the caller's history. The scale from a history is
 // max(history) / MAX.
 // ---------------------------------------------------------------------------
-template <typename T, int kFmt, int U, bool kWide, bool kAmax>
+// How the static cast records the tensor's amax.
+enum AmaxMode { AMAX_NONE = 0, AMAX_SLOTS = 1, AMAX_ATOMIC = 2 };
+
+// The slot of workgroup b of a streaming pass: 4 code bytes of its first chunk
+// c0 = b * 256 * U, or of the next chunk when c0 ends a row with fewer than 4
+// elements (the next chunk then starts a row, and rows hold >= 4 elements
+// where slots are used). None (~0) when c0 is the tensor's last chunk and
+// short; that workgroup then converts c0 alone.
+template <bool kWide>
+__device__ __forceinline__ uint64_t slot_chunk(uint64_t c0, uint64_t nchunks, const ChunkMap<kWide>& map,
+                                               uint32_t cols) {
+  uint64_t r;
+  uint32_t cc;
+  map.at(c0, r, cc);
+  if (cols - cc * 8u >= 4u) return c0;
+  if (c0 + 1 < nchunks) return c0 + 1;
+  return ~0ull;
+}
+
+// AMAX_SLOTS: each workgroup overwrites its slot (4 codes it has just written)
+// with its max; k_static_amax_restore then reduces the slots into amax_out and
+// writes the 4 codes of every slot again. No atomics and no buffer beyond q.
+// AMAX_ATOMIC (tensors narrower than 4 columns, which have no slots): an
+// atomic max after an agent-scope read of the current value.
+template <typename T, int kFmt, int U, bool kWide, int kAmax>
 __global__ __launch_bounds__(256) void k_cast_static(const T* __restrict__ x, int64_t ld_x, uint32_t cols,
                                                      uint64_t nchunks, ChunkMap<kWide> map,
                                                      const float* __restrict__ scale, uint8_t* __restrict__ q,
                                                      int64_t ld_q, float* __restrict__ amax_out) {
   const GroupScale gs = make_given_scale(*scale);
+  if constexpr (kAmax == AMAX_SLOTS) {
+    // k_static_amax_restore merges into amax_out after this kernel
+    if (blockIdx.x == 0 && threadIdx.x == 0) *reinterpret_cast<uint32_t*>(amax_out) = 0u;
+  }
   uint32_t m = 0;
   for_chunks<T, U, kWide, true>(x, ld_x, cols, nchunks, map, [&](const Vec8<T>& v, uint64_t r, uint32_t cc, uint32_t nv) {
-    if constexpr (kAmax) {
+    if constexpr (kAmax != AMAX_NONE) {
       const uint32_t a = v.amax_bits();
       m = a > m ? a : m;
     }
     store_codes8(q + (int64_t)r * ld_q + cc * 8u, v.template cast_sat<kFmt>(gs), nv);
   });
-  if constexpr (kAmax) {
-    // The value only grows from the zero stored before this kernel, so a
-    // workgroup whose max does not exceed what amax_out already holds can skip
-    // its atomic; this removes most of the same-address atomics.
+  if constexpr (kAmax == AMAX_SLOTS) {
+    m = block256_max(m);
+    const uint64_t c0 = (uint64_t)blockIdx.x * 256u * U;
+    const uint64_t sc = slot_chunk(c0, nchunks, map, cols);
+    // the thread that wrote the slot's codes (thread 0 or 1) overwrites them
+    if (sc != ~0ull && threadIdx.x == (uint32_t)(sc - c0)) {
+      uint64_t r;
+      uint32_t cc;
+      map.at(sc, r, cc);
+      *reinterpret_cast<uint32_t*>(q + (int64_t)r * ld_q + cc * 8u) = m;
+    }
+  } else if constexpr (kAmax == AMAX_ATOMIC) {
+    // the value only grows from the zero stored before this kernel, so a
+    // workgroup whose max does not exceed the current value skips its atomic
     m = block256_max(m);
     if (threadIdx.x == 0) {
       unsigned int* p = reinterpret_cast<unsigned int*>(amax_out);
       if (m > __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(p, m);
     }
   }
+}
+
+// amax_out[0] = max over the slots of the nblocks workgroups of
+// k_cast_static<..., AMAX_SLOTS> (or over the lone short chunk of a workgroup
+// without a slot), and the 4 codes of every slot written again with the same
+// conversion. One thread per slot; each workgroup merges its max into
+// amax_out (zeroed by the cast kernel) with one atomic, so a few atomics in
+// all.
+template <typename T, int kFmt, int U, bool kWide>
+__global__ __launch_bounds__(256) void k_static_amax_restore(const T* __restrict__ x, int64_t ld_x, uint32_t cols,
+                                                             uint64_t nchunks, ChunkMap<kWide> map, uint32_t nblocks,
+                                                             const float* __restrict__ scale,
+                                                             uint8_t* __restrict__ q, int64_t ld_q,
+                                                             float* __restrict__ amax_out) {
+  const uint32_t b = blockIdx.x * 256u + threadIdx.x;
+  uint32_t m = 0;
+  if (b < nblocks) {
+    const uint64_t c0 = (uint64_t)b * 256u * U;
+    const uint64_t sc = slot_chunk(c0, nchunks, map, cols);
+    uint64_t r;
+    uint32_t cc;
+    map.at(sc != ~0ull ? sc : c0, r, cc);
+    Vec8<T> v;
+    v.template load<false>(x + (int64_t)r * ld_x + cc * 8u, min(8u, cols - cc * 8u));
+    if (sc != ~0ull) {
+      uint32_t* p = reinterpret_cast<uint32_t*>(q + (int64_t)r * ld_q + cc * 8u);
+      m = *p;
+      *p = v.template cast_sat<kFmt>(make_given_scale(*scale)).x;
+    } else {
+      m = v.amax_bits();   // a workgroup without a slot had this one short chunk only
+    }
+  }
+  m = block256_max(m);
+  if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(amax_out), m);
 }
 
 // scale_out[0] = max(history[0 .. n)) / MAX (one workgroup; history >= 0).
@@ -585,8 +668,8 @@ ChunkMap<kWide> make_chunk_map(uint32_t cols) {
   return m;
 }
 
-// amax into slots of q, slots into scales[0], cast, scale. Tensors with fewer
-// than 4 columns have no slot in q; one workgroup then writes scales[0] itself.
+// amax into slots of q, slots into the scale, cast. Tensors with fewer than 4
+// columns have no slot in q; one workgroup then uses scales[0] as its slot.
 template <typename T, int kFmt, bool kWide>
 void per_tensor_passes(const QuantArgs& a, const T* x, uint64_t nchunks, hipStream_t st) {
   const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
@@ -594,6 +677,7 @@ void per_tensor_passes(const QuantArgs& a, const T* x, uint64_t nchunks, hipStre
   const uint64_t per_row = cols / 4u;
   const uint64_t nslots = (uint64_t)rows * per_row;
   uint32_t g = stream_grid(nchunks, kAmaxUnroll);
+  if (g > 1024u * kSlotsPerThread) g = 1024u * kSlotsPerThread;
   SlotMap sm;
   if (nslots == 0) {
     g = 1;
@@ -608,10 +692,9 @@ void per_tensor_passes(const QuantArgs& a, const T* x, uint64_t nchunks, hipStre
   }
   hipLaunchKernelGGL((k_amax_slots<T, kAmaxUnroll, kWide>), dim3(g), dim3(256), 0, st, x, a.ld_x, cols, nchunks,
                      map, sm);
-  hipLaunchKernelGGL(k_reduce_slots, dim3(1), dim3(256), 0, st, sm, g, a.scales);
+  hipLaunchKernelGGL(k_reduce_slots<kFmt>, dim3(1), dim3(1024), 0, st, sm, g, a.scales);
   hipLaunchKernelGGL((k_cast_tensor<T, kFmt, kCastUnroll, kWide>), dim3(stream_grid(nchunks, kCastUnroll)), dim3(256),
                      0, st, x, a.ld_x, cols, nchunks, map, a.scales, a.q, a.ld_q);
-  hipLaunchKernelGGL(k_finalize_tensor_scale<kFmt>, dim3(1), dim3(64), 0, st, a.scales);
 }
 
 template <typename T, int kFmt>
@@ -688,12 +771,22 @@ void static_pass(const QuantArgs& a, uint64_t nchunks, const float* scale, float
   const T* x = static_cast<const T*>(a.x);
   const uint32_t cols = (uint32_t)a.cols;
   const ChunkMap<kWide> map = make_chunk_map<kWide>(cols);
-  if (amax_out)
-    hipLaunchKernelGGL((k_cast_static<T, kFmt, kAmaxUnroll, kWide, true>), dim3(stream_grid(nchunks, kAmaxUnroll)),
+  if (!amax_out) {
+    hipLaunchKernelGGL((k_cast_static<T, kFmt, kCastUnroll, kWide, AMAX_NONE>), dim3(stream_grid(nchunks, kCastUnroll)),
                        dim3(256), 0, st, x, a.ld_x, cols, nchunks, map, scale, a.q, a.ld_q, amax_out);
-  else
-    hipLaunchKernelGGL((k_cast_static<T, kFmt, kCastUnroll, kWide, false>), dim3(stream_grid(nchunks, kCastUnroll)),
+  } else if (cols >= 4) {
+    // at most 2048 workgroups: at most 8 restore workgroups and atomics
+    uint32_t g = stream_grid(nchunks, kAmaxUnroll);
+    if (g > 2048u) g = 2048u;
+    hipLaunchKernelGGL((k_cast_static<T, kFmt, kAmaxUnroll, kWide, AMAX_SLOTS>), dim3(g), dim3(256), 0, st, x, a.ld_x,
+                       cols, nchunks, map, scale, a.q, a.ld_q, amax_out);
+    hipLaunchKernelGGL((k_static_amax_restore<T, kFmt, kAmaxUnroll, kWide>), dim3((g + 255u) / 256u), dim3(256), 0, st,
+                       x, a.ld_x, cols, nchunks, map, g, scale, a.q, a.ld_q, amax_out);
+  } else {
+    hipLaunchKernelGGL(k_store_zero, dim3(1), dim3(64), 0, st, amax_out);
+    hipLaunchKernelGGL((k_cast_static<T, kFmt, kAmaxUnroll, kWide, AMAX_ATOMIC>), dim3(stream_grid(nchunks, kAmaxUnroll)),
                        dim3(256), 0, st, x, a.ld_x, cols, nchunks, map, scale, a.q, a.ld_q, amax_out);
+  }
 }
 
 template <typename T, int kFmt>
@@ -707,8 +800,11 @@ void static_typed(const QuantArgs& a, uint64_t nchunks, const float* scale, floa
 
 hipError_t launch_quantize_static(const QuantArgs& a, const float* scale, float* amax_out, hipStream_t st) {
   const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
-  if (amax_out) hipLaunchKernelGGL(k_store_zero, dim3(1), dim3(64), 0, st, amax_out);
-  if (rows == 0 || cols == 0) return amax_out ? hipGetLastError() : hipSuccess;
+  if (rows == 0 || cols == 0) {
+    if (!amax_out) return hipSuccess;
+    hipLaunchKernelGGL(k_store_zero, dim3(1), dim3(64), 0, st, amax_out);
+    return hipGetLastError();
+  }
   const uint64_t nchunks = (uint64_t)rows * ((cols + 7u) >> 3);
   if (a.x_dtype == DTYPE_BF16) {
     if (a.fmt == FMT_E5M2)

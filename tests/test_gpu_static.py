@@ -8,7 +8,8 @@ recorded amax and the history scale are compared bit for bit with
 oracle.quant.quantize_static / scale_from_history on the same fp32 inputs
 (bf16 inputs converted exactly) and the same fp32 scale.
 
-Covers: ragged shapes in both input dtypes and formats; scales that leave
+Covers: ragged shapes in both input dtypes and formats; shapes that move a
+workgroup's amax slot or leave a workgroup without one; scales that leave
 headroom, that saturate most of the tensor, powers of two, values next to
 2^-126 and 2^125 (where the kernel changes method) and the largest finite
 float; every bf16 magnitude below sampled patterns; a zero scale; empty
@@ -59,6 +60,20 @@ def test_shapes(gpu_lib, fmt, dtype, rows, cols):
     for mult in (1.0, 1.7, 0.05):            # exact dynamic scale, headroom, most elements saturated
         s = np.float32(amax / quant.FORMAT_MAX[fmt] * mult)
         _check(gpu_lib, x, dtype, fmt, s, f"{rows}x{cols} {fmt} s*{mult}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rows,cols,peak", [(205, 33, (204, 32)), (410, 33, (204, 32)), (411, 33, (410, 32)),
+                                            (3, 2, (2, 1)), (1000, 3, (999, 2)), (1, 4, (0, 3)), (2, 1029, (1, 1028))])
+def test_amax_record_geometry(gpu_lib, dtype, rows, cols, peak):
+    """Shapes where a workgroup's first chunk is a short row end (its amax slot
+    moves to the next chunk), where the last workgroup holds one short chunk
+    and no slot, and tensors narrower than 4 columns; the largest element sits
+    in that chunk. Codes around every slot must be restored."""
+    rng = np.random.default_rng(rows * 3 + cols)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x[peak] = -50.0
+    _check(gpu_lib, x, dtype, "e4m3", np.float32(0.05), f"{rows}x{cols}")
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
