@@ -91,7 +91,9 @@ typedef enum fp8blk_dtype { FP8BLK_BF16 = 0, FP8BLK_F32 = 1 } fp8blk_dtype;
  * Requirements: x, q, scales non-null; rows, cols >= 0; ld_x >= cols and
  * ld_q >= cols; x and q 16-byte aligned; ld_x * sizeof(x_dtype) and ld_q
  * multiples of 16 (else FP8BLK_EALIGN); x, q and scales must not overlap.
- * PER_TENSOR uses scales[0] as an atomic max accumulator during the call.
+ * PER_TENSOR keeps per-workgroup maxima in q (below 4 columns: the raw amax
+ * in scales[0]) between the call's kernels; codes and scale replace them
+ * before the call ends.
  */
 fp8blk_status fp8_quantize(const void* x, fp8blk_dtype x_dtype, int64_t rows, int64_t cols,
                            int64_t ld_x, fp8blk_granularity gran, fp8blk_format fmt,
@@ -238,7 +240,9 @@ fp8blk_status fp8_kv_dequantize(const uint8_t* q, const float* scales, int64_t h
  *
  * Requirements: as fp8_quantize for x and q, except that x and q may be NULL
  * when rows or cols is 0 (then only amax_out is written); scale and amax_out
- * 4-byte aligned and not overlapping each other, x or q.
+ * 4-byte aligned and not overlapping each other, x or q. With amax_out, q
+ * holds per-workgroup maxima in a few 4-byte slots between the call's two
+ * kernels; the final codes replace them before the call ends.
  */
 fp8blk_status fp8_quantize_static(const void* x, fp8blk_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                                   fp8blk_format fmt, const float* scale, uint8_t* q, int64_t ld_q, float* amax_out,
