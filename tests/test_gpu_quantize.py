@@ -292,3 +292,40 @@ def test_per_tensor_and_static_grid_stride(gpu_lib):
     assert float(am.item()) == 300.0
     qr, _ = quant.quantize_static(x32[rows], np.float32(0.5))
     assert_codes_equal(qs.cpu().numpy()[rows], qr, x32[rows], "static codes")
+
+
+def test_past_2_31_chunks(gpu_lib):
+    """A [2^21 + 64, 8192] bf16 tensor (34 GB) has more than 2^31 chunks of 8
+    elements, so the per-tensor and static passes take their 64-bit chunk
+    indexing. Built on the device (small N(0, 0.01^2) values and one planted
+    maximum of -300 beyond chunk 2^31): the scale and the recorded amax are
+    known exactly; codes are compared on sampled rows on both sides of the
+    boundary, for per tensor, static and 1 x 128."""
+    rows, cols = (1 << 21) + 64, 8192
+    torch.manual_seed(7)
+    x = torch.randn((rows, cols), dtype=torch.bfloat16, device=DEV)
+    x.mul_(0.01)
+    x[rows - 10, 4000] = -300.0
+    assert (rows - 10) * (cols // 8) > (1 << 31)
+    sample = np.array([0, 5, (1 << 21) - 1, 1 << 21, (1 << 21) + 3, rows - 10, rows - 1])
+    xs = f32_of(x[torch.from_numpy(sample).to(DEV)])
+    try:
+        qg, sg = gpu_lib.fp8_quantize(x, "per_tensor")
+        s_ref = quant.scale_of(np.float32(300.0))
+        assert_scales_equal(sg.cpu().numpy(), np.array([s_ref], np.float32), "per-tensor scale")
+        assert_codes_equal(qg[torch.from_numpy(sample).to(DEV)].cpu().numpy(), quant.cast(xs, s_ref), xs,
+                           "per-tensor codes")
+        s_static = torch.tensor([0.25], dtype=torch.float32, device=DEV)
+        qs, am = gpu_lib.fp8_quantize_static(x, s_static, record_amax=True, out=qg)
+        assert float(am.item()) == 300.0
+        assert_codes_equal(qs[torch.from_numpy(sample).to(DEV)].cpu().numpy(),
+                           quant.quantize_static(xs, np.float32(0.25))[0], xs, "static codes")
+        del qs, qg
+        q1, s1 = gpu_lib.fp8_quantize(x, "group_1x128")
+        qr, sr = quant.quantize_group_1x128(xs)
+        idx = torch.from_numpy(sample).to(DEV)
+        assert_scales_equal(s1[idx].cpu().numpy(), sr, "1x128 scales")
+        assert_codes_equal(q1[idx].cpu().numpy(), qr, xs, "1x128 codes")
+    finally:
+        del x
+        torch.cuda.empty_cache()
