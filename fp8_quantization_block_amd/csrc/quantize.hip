@@ -1,5 +1,7 @@
 // Quantization kernels: per-tensor, 1x128 groups, 128x128 blocks, KV
-// (head x token block) groups, and the KV dequantizer.
+// (head x token block) groups, the KV dequantizer, MX blocks of 32 with
+// power-of-two scales, and the static / delayed-scaling cast under a
+// caller-supplied scale.
 //
 // Method ([FP8] wangyu.me, "大语言模型量化技术（五）：FP8"): per group, amax = max|x|,
 // s = amax / max_fmt, code = FP8(x / s) rounded to nearest even and saturated
