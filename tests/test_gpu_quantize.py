@@ -211,6 +211,23 @@ def test_kmajor_scale_layout(gpu_lib):
     assert_codes_equal(qg.cpu().numpy(), qr, None, "codes")
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rows,cols", [(1, 300), (7, 129), (33, 1000), (257, 256), (1000, 4096)])
+def test_kmajor_ragged(gpu_lib, fmt, dtype, rows, cols):
+    """K-block-major scales (workgroups then walk a column of groups down the
+    rows) on ragged shapes, both input dtypes and formats."""
+    rng = np.random.default_rng(rows * 13 + cols)
+    x = (rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-10, 10, size=(rows, 1)))).astype(np.float32)
+    ld = (cols + 15) // 16 * 16
+    xt = _padded(torch.from_numpy(x).to(dtype).float().numpy(), dtype, ld)
+    xr = f32_of(xt)
+    qr, sr = quant.quantize_group_1x128(xr, fmt)
+    qg, sg = gpu_lib.fp8_quantize(xt, "group_1x128", fmt=fmt, scale_layout="kmajor")
+    assert_scales_equal(sg.cpu().numpy(), sr, f"{rows}x{cols} kmajor scales")
+    assert_codes_equal(qg.cpu().numpy(), qr, xr, f"{rows}x{cols} kmajor codes")
+
+
 @pytest.mark.parametrize("config", [1, 2, 3, 4])
 def test_config_activations_full_size(gpu_lib, config):
     c = syn.CONFIGS[config]
