@@ -11,7 +11,9 @@ It is a plain, slow, NumPy implementation written straight from the pages:
   encoder that saturates at +-448;
 * ``e5m2``  -- the same for OCP E5M2 (largest value 57344, saturating);
 * ``quant`` -- the amax / scale / cast quantizer for every group shape the path
-  uses (per tensor, 1x128, 128x128, KV head x 128 tokens) and the KV dequantizer;
+  uses (per tensor, 1x128, 128x128, KV head x 128 tokens), the KV dequantizer,
+  and static / delayed scaling (a cast under a supplied scale that also records
+  the tensor's amax, and the scale taken from an amax history window);
 * ``gemm``  -- the block-scaled GEMM as dequantize-to-fp64 followed by a plain
   fp64 matmul, plus the tolerance base |A|.|W|^T;
 * ``attention`` -- decode attention over the FP8 KV cache, dequantized to fp64,
@@ -24,6 +26,7 @@ Every function cites the page and section it follows. Pages are cited as
 * [FP8]   wangyu.me, "大语言模型量化技术（五）：FP8" (LLM quantization part 5: FP8)
 * [MIXED] charles2530.github.io, "量化：FP8 与混合精度推理：它不是一个 dtype 开关"
 * [LONG]  pwwt.cn, Llama-3 FP8 and long-context practice notes
+* [VS]    api.makesence.top, "LLM推理量化：FP8 versus INT8"
 
 Parity status: every function here is pinned by tests under ``tests/``
 (``test_oracle_*.py``) against values the pages print, closed forms,
