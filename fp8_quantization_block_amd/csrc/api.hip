@@ -28,6 +28,22 @@ fp8blk_status ok() {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Scale strides are bounded so that every grid offset fits comfortably in
+// 64 bits (and in any real allocation).
+constexpr int64_t kMaxScaleStride = (int64_t)1 << 40;
+
+// True when the cells of a written scale grid [gr][gc] with element strides
+// (sr, sc) are distinct floats: one stride must step over the whole extent of
+// the other axis (row-major, column-major and padded layouts all do), so that
+// no two workgroups store to the same float.
+bool grid_cells_distinct(int64_t gr, int64_t gc, int64_t sr, int64_t sc) {
+  if (gr <= 1 && gc <= 1) return true;
+  if (gr <= 1) return sc > 0;
+  if (gc <= 1) return sr > 0;
+  return (sc > 0 && (__int128)sr >= (__int128)gc * sc) || (sr > 0 && (__int128)sc >= (__int128)gr * sr);
+}
 
 // Byte range [lo, hi) of a strided 2-D array with rows >= 1 and cols >= 1.
 struct Range {
@@ -96,8 +112,11 @@ fp8blk_status fp8_quantize(const void* x, fp8blk_dtype x_dtype, int64_t rows, in
   if (ld_x < cols || ld_q < cols) return fail(FP8BLK_EINVAL, "%s: leading dimension < cols", fn);
   if (scale_stride_row < 0 || scale_stride_col < 0)
     return fail(FP8BLK_EINVAL, "%s: negative scale stride", fn);
+  if (scale_stride_row >= kMaxScaleStride || scale_stride_col >= kMaxScaleStride)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: scale stride above 2^40", fn);
   const int64_t esz = x_dtype == FP8BLK_BF16 ? 2 : 4;
   if (!aligned16(x) || !aligned16(q)) return fail(FP8BLK_EALIGN, "%s: x and q must be 16-byte aligned", fn);
+  if (!aligned4(scales)) return fail(FP8BLK_EALIGN, "%s: scales must be 4-byte aligned", fn);
   if ((ld_x * esz) % 16 != 0 || ld_q % 16 != 0)
     return fail(FP8BLK_EALIGN, "%s: ld_x * elem_size and ld_q must be multiples of 16 bytes", fn);
   if (gran == FP8BLK_GROUP_1x128) {
@@ -114,11 +133,8 @@ fp8blk_status fp8_quantize(const void* x, fp8blk_dtype x_dtype, int64_t rows, in
                                                : range_grid(scales, gr, gc, scale_stride_row, scale_stride_col);
     if (overlap(rx, rq) || overlap(rx, rs) || overlap(rq, rs))
       return fail(FP8BLK_EINVAL, "%s: x, q and scales must not overlap", fn);
-    if (gran != FP8BLK_PER_TENSOR && (gr > 1 || gc > 1)) {
-      // distinct grid cells must be distinct floats
-      if ((gr > 1 && scale_stride_row == 0) || (gc > 1 && scale_stride_col == 0))
-        return fail(FP8BLK_EINVAL, "%s: zero scale stride on a grid axis longer than 1", fn);
-    }
+    if (gran != FP8BLK_PER_TENSOR && !grid_cells_distinct(gr, gc, scale_stride_row, scale_stride_col))
+      return fail(FP8BLK_EINVAL, "%s: scale strides map two grid cells to one float", fn);
   } else if (gran != FP8BLK_PER_TENSOR) {
     return ok();   // empty grid: nothing to write
   }
@@ -167,7 +183,12 @@ fp8blk_status check_gemm_inputs(const char* fn, int64_t M, int64_t N, int64_t K,
     return fail(FP8BLK_EUNSUPPORTED, "%s: lda and ldb must be below 2^23", fn);
   if (sa_stride_m < 0 || sa_stride_k < 0 || sb_stride_n < 0 || sb_stride_k < 0)
     return fail(FP8BLK_EINVAL, "%s: negative scale stride", fn);
+  if (sa_stride_m >= kMaxScaleStride || sa_stride_k >= kMaxScaleStride || sb_stride_n >= kMaxScaleStride ||
+      sb_stride_k >= kMaxScaleStride)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: scale stride above 2^40", fn);
   if (!aligned16(a) || !aligned16(b)) return fail(FP8BLK_EALIGN, "%s: a and b must be 16-byte aligned", fn);
+  if (!aligned4(scale_a) || !aligned4(scale_b))
+    return fail(FP8BLK_EALIGN, "%s: scale_a and scale_b must be 4-byte aligned", fn);
   if (lda % 16 != 0 || ldb % 16 != 0) return fail(FP8BLK_EALIGN, "%s: lda and ldb must be multiples of 16 bytes", fn);
   if (M > 0) {
     in[0] = range2d(a, M, K, lda, 1);
@@ -254,12 +275,15 @@ fp8blk_status fp8_block_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_
   if (fp8blk_status st = check_format(fmt_c, fn)) return st;
   if (ldqc < N) return fail(FP8BLK_EINVAL, "%s: leading dimension too small", fn);
   if (sc_stride_m < 0 || sc_stride_n < 0) return fail(FP8BLK_EINVAL, "%s: negative scale stride", fn);
+  if (sc_stride_m >= kMaxScaleStride || sc_stride_n >= kMaxScaleStride)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: scale stride above 2^40", fn);
   if (!aligned16(qc) || ldqc % 16 != 0)
     return fail(FP8BLK_EALIGN, "%s: qc must be 16-byte aligned and ldqc a multiple of 16", fn);
+  if (!aligned4(scale_c)) return fail(FP8BLK_EALIGN, "%s: scale_c must be 4-byte aligned", fn);
   if (M == 0) return ok();
   const int64_t groups = N / 128;
-  if ((M > 1 && sc_stride_m == 0) || (groups > 1 && sc_stride_n == 0))
-    return fail(FP8BLK_EINVAL, "%s: zero scale stride on a grid axis longer than 1", fn);
+  if (!grid_cells_distinct(M, groups, sc_stride_m, sc_stride_n))
+    return fail(FP8BLK_EINVAL, "%s: scale strides map two grid cells to one float", fn);
   const Range rq = range2d(qc, M, N, ldqc, 1);
   const Range rs = range_grid(scale_c, M, groups, sc_stride_m, sc_stride_n);
   if (overlaps_any(rq, in) || overlaps_any(rs, in) || overlap(rq, rs))
@@ -293,7 +317,7 @@ fp8blk_status fp8_quantize_static(const void* x, fp8blk_dtype x_dtype, int64_t r
   if (!aligned16(x) || !aligned16(q)) return fail(FP8BLK_EALIGN, "%s: x and q must be 16-byte aligned", fn);
   if ((ld_x * esz) % 16 != 0 || ld_q % 16 != 0)
     return fail(FP8BLK_EALIGN, "%s: ld_x * elem_size and ld_q must be multiples of 16 bytes", fn);
-  if ((reinterpret_cast<uintptr_t>(scale) & 3u) != 0 || (reinterpret_cast<uintptr_t>(amax_out) & 3u) != 0)
+  if (!aligned4(scale) || !aligned4(amax_out))
     return fail(FP8BLK_EALIGN, "%s: scale and amax_out must be 4-byte aligned", fn);
   const Range rsc = range_grid(scale, 1, 1, 0, 0);
   const Range ram = amax_out ? range_grid(amax_out, 1, 1, 0, 0) : Range{0, 0};
@@ -323,7 +347,7 @@ fp8blk_status fp8_scale_from_amax_history(const float* history, int64_t n, fp8bl
   if (fp8blk_status st = check_format(fmt, fn)) return st;
   if (n <= 0) return fail(FP8BLK_EINVAL, "%s: the history must hold at least one value", fn);
   if (n >= kMaxDim) return fail(FP8BLK_EUNSUPPORTED, "%s: history longer than 2^31", fn);
-  if ((reinterpret_cast<uintptr_t>(history) & 3u) != 0 || (reinterpret_cast<uintptr_t>(scale_out) & 3u) != 0)
+  if (!aligned4(history) || !aligned4(scale_out))
     return fail(FP8BLK_EALIGN, "%s: pointers must be 4-byte aligned", fn);
   if (overlap(range_grid(history, 1, n, 0, 1), range_grid(scale_out, 1, 1, 0, 0)))
     return fail(FP8BLK_EINVAL, "%s: scale_out must not overlap the history", fn);
@@ -453,8 +477,7 @@ fp8blk_status fp8_kv_decode_attention(const void* q, int64_t ld_q, int64_t heads
   if (ld_q < head_dim || ld_o < head_dim) return fail(FP8BLK_EINVAL, "%s: leading dimension too small", fn);
   if (!aligned16(q) || ld_q % 8 != 0)
     return fail(FP8BLK_EALIGN, "%s: q must be 16-byte aligned and ld_q a multiple of 8", fn);
-  if ((reinterpret_cast<uintptr_t>(out) & 3u) != 0 || (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0 ||
-      (reinterpret_cast<uintptr_t>(k_scales) & 3u) != 0 || (reinterpret_cast<uintptr_t>(v_scales) & 3u) != 0)
+  if (!aligned4(out) || !aligned4(workspace) || !aligned4(k_scales) || !aligned4(v_scales))
     return fail(FP8BLK_EALIGN, "%s: out, workspace and scales must be 4-byte aligned", fn);
   const size_t need = fp8_kv_decode_attention_workspace_size(heads_q, tokens);
   if (workspace_bytes < need) return fail(FP8BLK_EINVAL, "%s: workspace smaller than %zu bytes", fn, need);
@@ -513,6 +536,7 @@ fp8blk_status fp8_kv_quantize(const void* kv, int64_t heads, int64_t tokens, int
   if (stride_token < head_dim || stride_head < 0)
     return fail(FP8BLK_EINVAL, "%s: stride_token must be >= head_dim and stride_head >= 0", fn);
   if (!aligned16(kv) || !aligned16(q)) return fail(FP8BLK_EALIGN, "%s: kv and q must be 16-byte aligned", fn);
+  if (!aligned4(scales)) return fail(FP8BLK_EALIGN, "%s: scales must be 4-byte aligned", fn);
   if (stride_head % 8 != 0 || stride_token % 8 != 0)
     return fail(FP8BLK_EALIGN, "%s: strides must be multiples of 8 elements", fn);
   if (heads == 0 || tokens == 0) return ok();
@@ -545,6 +569,7 @@ fp8blk_status fp8_kv_dequantize(const uint8_t* q, const float* scales, int64_t h
   if (fp8blk_status st = check_kv_common(fn, heads, tokens, head_dim, token_block, fmt)) return st;
   if (!aligned16(q) || !aligned16(out_bf16))
     return fail(FP8BLK_EALIGN, "%s: q and out must be 16-byte aligned", fn);
+  if (!aligned4(scales)) return fail(FP8BLK_EALIGN, "%s: scales must be 4-byte aligned", fn);
   if (heads == 0 || tokens == 0) return ok();
   const int64_t nb = (tokens + token_block - 1) / token_block;
   const int64_t n = heads * tokens * head_dim;

@@ -89,8 +89,12 @@ typedef enum fp8blk_dtype { FP8BLK_BF16 = 0, FP8BLK_F32 = 1 } fp8blk_dtype;
  *   rows == 0 or cols == 0 is a no-op, except that PER_TENSOR sets scales[0] = 0.
  *
  * Requirements: x, q, scales non-null; rows, cols >= 0; ld_x >= cols and
- * ld_q >= cols; x and q 16-byte aligned; ld_x * sizeof(x_dtype) and ld_q
- * multiples of 16 (else FP8BLK_EALIGN); x, q and scales must not overlap.
+ * ld_q >= cols; x and q 16-byte aligned, scales 4-byte aligned; ld_x *
+ * sizeof(x_dtype) and ld_q multiples of 16 (else FP8BLK_EALIGN); scale strides
+ * >= 0 and below 2^40, and such that distinct grid cells are distinct floats
+ * (one stride at least the other axis's extent times its stride, as in
+ * row-major, K-block-major or padded layouts; else FP8BLK_EINVAL); x, q and
+ * scales must not overlap.
  * PER_TENSOR keeps per-workgroup maxima in q (below 4 columns: the raw amax
  * in scales[0]) between the call's kernels; codes and scale replace them
  * before the call ends.
@@ -128,7 +132,9 @@ fp8blk_status fp8_quantize(const void* x, fp8blk_dtype x_dtype, int64_t rows, in
  * N % 128 == 0 and K % 128 == 0 (else FP8BLK_EUNSUPPORTED); lda, ldb >= K and
  * below 2^23 (else FP8BLK_EUNSUPPORTED);
  * ldc >= N; a, b, c 16-byte aligned and lda, ldb, ldc * sizeof(c_dtype)
- * multiples of 16; gran_a in {PER_TENSOR, GROUP_1x128}; gran_b in {PER_TENSOR,
+ * multiples of 16; scale_a and scale_b 4-byte aligned, their strides >= 0 and
+ * below 2^40 (a zero stride broadcasts one scale along that axis);
+ * gran_a in {PER_TENSOR, GROUP_1x128}; gran_b in {PER_TENSOR,
  * BLOCK_128x128}; fmt_a, fmt_b in {E4M3, E5M2} (independently); codes must be
  * finite (E4M3: not S.1111.111; E5M2: exponent field not 11111), as every
  * code fp8_quantize writes is; c must not overlap the inputs.
@@ -161,9 +167,10 @@ fp8blk_status fp8_block_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, 
  *           fastest when qc is the next GEMM's A.
  *
  * Requirements: as fp8_block_gemm for the inputs; qc and scale_c non-null; qc
- * 16-byte aligned, ldqc >= N and a multiple of 16; strides >= 0, nonzero on a
- * grid axis longer than 1; qc and scale_c must not overlap each other or the
- * inputs. For M > 64 the results are bit-identical to fp8_quantize(GROUP_1x128)
+ * 16-byte aligned, ldqc >= N and a multiple of 16; scale_c 4-byte aligned;
+ * strides >= 0 and below 2^40, and such that distinct grid cells are distinct
+ * floats (as for fp8_quantize); qc and scale_c must not overlap each other or
+ * the inputs. For M > 64 the results are bit-identical to fp8_quantize(GROUP_1x128)
  * of the fp32 output of fp8_block_gemm on the same inputs (the same kernel
  * and summation order). For M <= 64 this entry point still runs that kernel,
  * while fp8_block_gemm takes a split-K kernel whose fp32 sums may differ in
@@ -197,9 +204,9 @@ fp8blk_status fp8_block_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_
  *
  * Requirements: pointers non-null; heads, tokens >= 0 (0 is a no-op);
  * head_dim > 0 and a multiple of 8; token_block > 0 and token_block * head_dim
- * <= 16384 (else FP8BLK_EUNSUPPORTED); kv and q 16-byte aligned; stride_head
- * and stride_token multiples of 8 with stride_token >= head_dim; outputs must
- * not overlap the input.
+ * <= 16384 (else FP8BLK_EUNSUPPORTED); kv and q 16-byte aligned, scales
+ * 4-byte aligned; stride_head and stride_token multiples of 8 with
+ * stride_token >= head_dim; outputs must not overlap the input.
  */
 fp8blk_status fp8_kv_quantize(const void* kv, int64_t heads, int64_t tokens, int64_t head_dim,
                               int64_t stride_head, int64_t stride_token, int64_t token_block,

@@ -84,6 +84,9 @@ def q(lib, x=PA, dt=BF16, rows=4, cols=256, ldx=256, gran=GROUP, fmt=E4M3, qp=PB
     (dict(qp=PA + 256), EINVAL),           # q overlaps x
     (dict(s=PB + 16), EINVAL),             # scales overlap q
     (dict(ssr=0, ssc=1), EINVAL),          # grid rows collapse onto one float
+    (dict(ssr=1, ssc=1), EINVAL),          # cells (i, j + 1) and (i + 1, j) share a float
+    (dict(s=PC + 2), EALIGN),              # scales not 4-byte aligned
+    (dict(ssr=1 << 40), EUNSUPPORTED),
     (dict(rows=1 << 31), EUNSUPPORTED),
 ])
 def test_quantize_rejects(lib, kw, status):
@@ -125,6 +128,9 @@ def g(lib, M=256, N=256, K=256, a=PA, lda=256, sa=PB, ga=GROUP, sam=2, sak=1, b=
     (dict(ldc=260), EALIGN),
     (dict(c=PA + 1024), EINVAL),           # c overlaps a
     (dict(sak=-2), EINVAL),
+    (dict(sa=PB + 2), EALIGN),             # scale arrays not 4-byte aligned
+    (dict(sb=PB + 65536 + 1), EALIGN),
+    (dict(sbk=1 << 40), EUNSUPPORTED),
 ])
 def test_gemm_rejects(lib, kw, status):
     assert g(lib, **kw) == status
@@ -152,6 +158,9 @@ def gq(lib, M=256, N=256, K=256, a=PA, lda=256, sa=PB, ga=GROUP, sam=2, sak=1, b
     (dict(scn=0), EINVAL),                   # groups collapse onto one scale
     (dict(qc=PA + 1024), EINVAL),            # codes overlap a
     (dict(sc=PD + 4096), EINVAL),            # scales overlap the codes
+    (dict(scm=1, scn=1), EINVAL),            # cells (m, g + 1) and (m + 1, g) share a float
+    (dict(sc=PD + (1 << 20) + 2), EALIGN),   # scales not 4-byte aligned
+    (dict(scn=1 << 40), EUNSUPPORTED),
 ])
 def test_gemm_quant_rejects(lib, kw, status):
     assert gq(lib, **kw) == status
@@ -303,6 +312,7 @@ def kvq(lib, kv=PA, h=2, t=300, d=128, sh=300 * 128, st=128, tb=128, fmt=E4M3, q
     (dict(kv=PA + 8), EALIGN),
     (dict(st=132), EALIGN),
     (dict(qp=PA + 4096), EINVAL),          # codes overlap the input
+    (dict(s=PC + 2), EALIGN),              # scales not 4-byte aligned
 ])
 def test_kv_quantize_rejects(lib, kw, status):
     assert kvq(lib, **kw) == status
@@ -320,6 +330,7 @@ def test_kv_empty_is_a_noop(lib):
     ((PB, PC, 2, 300, 100, 128, E4M3, PD), EUNSUPPORTED),
     ((PB, PC, 2, 300, 128, 128, E4M3, PD + 2), EALIGN),
     ((PB, PC, 2, 300, 128, 128, E4M3, PB + 64), EINVAL),   # out overlaps the codes
+    ((PB, PC + 2, 2, 300, 128, 128, E4M3, PD), EALIGN),    # scales not 4-byte aligned
 ])
 def test_kv_dequantize_rejects(lib, args, status):
     assert lib.fp8_kv_dequantize(*args, None) == status
