@@ -20,8 +20,10 @@ Printed: one JSON line. ``value`` is the step's throughput in TFLOP/s
 GEMM kernel's achieved TFLOP/s against the dense FP8 MFMA peak, measured with
 HIP events on the launch stream; ``passes`` lists every pass of the path with
 its own time and GB/s or TFLOP/s (the KV-cache passes at [8, 131072, 128] and
-the decode-shaped GEMM 16 x 28672 x 8192 included); ``cpu_baseline`` times the
-CPU oracle on a bounded sample of the same step.
+the decode-shaped GEMM 16 x 28672 x 8192 included); ``clocks`` gives the
+shader and memory clock levels the driver reported while the untimed settle
+phase ran the step; ``cpu_baseline`` times the CPU oracle on a bounded sample
+of the same step.
 """
 
 import argparse
@@ -121,6 +123,73 @@ def gemm_traffic_bytes():
     return (c["fetch_kib"] * FETCH_FACTOR + c["write_kib"] * WRITE_FACTOR) * 1024.0
 
 
+class ClockSampler:
+    """Samples the device's current shader, memory and fabric clock levels
+    (MHz) from the amdgpu driver's DPM tables in sysfs (the level marked '*')
+    every 0.1 s on a background thread, e.g. while the settle phase keeps the
+    GPU busy. Reports None where sysfs does not expose the tables."""
+
+    KEYS = ("sclk", "mclk", "fclk")
+
+    def __init__(self, torch):
+        self.base = None
+        try:
+            p = torch.cuda.get_device_properties(0)
+            self.base = (f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:"
+                         f"{p.pci_device_id:02x}.0")
+        except Exception:
+            pass
+        self.samples = {k: [] for k in self.KEYS}
+        self._stop = None
+        self._thread = None
+
+    def read(self):
+        import re
+        out = {}
+        if self.base is None:
+            return out
+        for k in self.KEYS:
+            try:
+                with open(os.path.join(self.base, f"pp_dpm_{k}")) as fh:
+                    text = fh.read()
+            except OSError:
+                continue
+            m = re.search(r"(\d+)\s*mhz\s*\*", text, re.I)
+            if m:
+                out[k] = int(m.group(1))
+        return out
+
+    def _run(self):
+        while not self._stop.wait(0.1):
+            for k, v in self.read().items():
+                self.samples[k].append(v)
+
+    def start(self):
+        import threading
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join(timeout=5)
+
+    def summary(self):
+        res = {}
+        for k, v in self.samples.items():
+            if v:
+                v = sorted(v)
+                res[f"{k}_mhz_median"] = v[len(v) // 2]
+                res[f"{k}_mhz_min"] = v[0]
+                res[f"{k}_mhz_max"] = v[-1]
+        if not res:
+            return None
+        res["samples"] = max(len(v) for v in self.samples.values())
+        res["source"] = "sysfs pp_dpm_* current level, sampled every 0.1 s during the untimed settle phase"
+        return res
+
+
 def settle(torch, fn, seconds: float) -> None:
     """Untimed launches of `fn` for about `seconds` of wall time. An idle GPU
     starts at a low clock and needs a fraction of a second of sustained load to
@@ -192,7 +261,10 @@ def main():
     for i in range(nsets):
         quant_a(i)
     torch.cuda.synchronize()
+    clocks = ClockSampler(torch)
+    clocks.start()
     settle(torch, step, args.settle_s)
+    clocks.stop()
 
     # ---- the timed step: warmup, then exactly `steps` steps ---------------
     # Timed first, straight after the settle phase: after a stretch of
@@ -444,6 +516,7 @@ def main():
         },
         "passes": passes,
         "mfma_ceiling": ceiling,
+        "clocks": clocks.summary(),
         "per_call": timer.stats,
         "cpu_baseline": cpu,
     }
