@@ -206,8 +206,9 @@ def settle(torch, fn, seconds: float) -> None:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the path shards by rows / heads with no exchange, see the design notes", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); the kernels are "
+              "measured at one GPU's full share of the workload, and the path would shard by rows, "
+              "weight columns or kv heads with no exchange", file=sys.stderr)
         sys.exit(2)
 
     import torch
