@@ -63,6 +63,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp8_block_gemm_quant.argtypes = [i64, i64, i64, vp, i64, vp, i32, i64, i64, vp, i64, vp, i32,
                                          i64, i64, i32, i32, i32, vp, i64, vp, i64, i64, vp]
     lib.fp8_block_gemm_quant.restype = i32
+    lib.fp8_pack_weights_decode.argtypes = [vp, i64, i64, i64, vp, vp]
+    lib.fp8_pack_weights_decode.restype = i32
+    lib.fp8_block_gemm_packed.argtypes = [i64, i64, i64, vp, i64, vp, i32, i64, i64, vp, vp, i32,
+                                          i64, i64, i32, i32, vp, i32, i64, vp]
+    lib.fp8_block_gemm_packed.restype = i32
     lib.fp8_quantize_static.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, i64, vp, vp]
     lib.fp8_quantize_static.restype = i32
     lib.fp8_scale_from_amax_history.argtypes = [vp, i64, i32, vp, vp]
@@ -177,6 +182,49 @@ def fp8_block_gemm(qa: torch.Tensor, sa: torch.Tensor, gran_a: str, qw: torch.Te
     _check(lib.fp8_block_gemm(M, N, K, _ptr(qa), qa.stride(0), _ptr(sa), ga, sam, sak,
                               _ptr(qw), qw.stride(0), _ptr(sw), gw, swn, swk, _FMT[fmt_a], _FMT[fmt_w],
                               _ptr(out), cdt, out.stride(0), _stream(qa)))
+    return out
+
+
+def fp8_pack_weights_decode(qw: torch.Tensor, out: torch.Tensor = None):
+    """Reorder row-major weight codes qw [N, K] (uint8) into the decode-packed
+    layout that fp8_block_gemm_packed reads; returns uint8 [K/128, N/16, 2048]
+    (one 2 KB block per K block and 16-row group). The scales are unchanged."""
+    lib = load_library()
+    _require_cuda(qw)
+    N, K = qw.shape
+    if out is None:
+        out = torch.empty((K // 128, N // 16, 2048), dtype=torch.uint8, device=qw.device)
+    if out.numel() != N * K or not out.is_contiguous():
+        raise ValueError("fp8_pack_weights_decode: out must be a contiguous tensor of N * K bytes")
+    _check(lib.fp8_pack_weights_decode(_ptr(qw), N, K, qw.stride(0), _ptr(out), _stream(qw)))
+    return out
+
+
+def fp8_block_gemm_packed(qa: torch.Tensor, sa: torch.Tensor, gran_a: str, qw_packed: torch.Tensor,
+                          sw: torch.Tensor, gran_w: str, out_dtype=torch.bfloat16, out: torch.Tensor = None,
+                          fmt_a: str = "e4m3", fmt_w: str = "e4m3"):
+    """fp8_block_gemm for M <= 64 with the weights packed by
+    fp8_pack_weights_decode (qw_packed [K/128, N/16, 2048]); bit-identical to
+    fp8_block_gemm on the row-major codes."""
+    lib = load_library()
+    _require_cuda(qa, sa, qw_packed, sw)
+    M, K = qa.shape
+    if qw_packed.dim() != 3 or qw_packed.shape[2] != 2048 or not qw_packed.is_contiguous():
+        raise ValueError("fp8_block_gemm_packed: qw_packed must be a contiguous [K/128, N/16, 2048] tensor")
+    N = qw_packed.shape[1] * 16
+    if qw_packed.shape[0] * 128 != K:
+        raise ValueError("fp8_block_gemm_packed: K mismatch")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=qa.device)
+    cdt = BF16 if out.dtype == torch.bfloat16 else F32
+    ga, gw = _GRAN[gran_a], _GRAN[gran_w]
+    sam = sa.stride(0) if sa.dim() == 2 else 0
+    sak = sa.stride(1) if sa.dim() == 2 else 0
+    swn = sw.stride(0) if sw.dim() == 2 else 0
+    swk = sw.stride(1) if sw.dim() == 2 else 0
+    _check(lib.fp8_block_gemm_packed(M, N, K, _ptr(qa), qa.stride(0), _ptr(sa), ga, sam, sak,
+                                     _ptr(qw_packed), _ptr(sw), gw, swn, swk, _FMT[fmt_a], _FMT[fmt_w],
+                                     _ptr(out), cdt, out.stride(0), _stream(qa)))
     return out
 
 

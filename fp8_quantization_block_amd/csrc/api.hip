@@ -258,6 +258,58 @@ fp8blk_status fp8_block_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, 
   return hip_status(fp8blk::launch_block_gemm(g, static_cast<hipStream_t>(stream)), fn);
 }
 
+fp8blk_status fp8_pack_weights_decode(const uint8_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* packed,
+                                      void* stream) {
+  const char* fn = "fp8_pack_weights_decode";
+  if (!w || !packed) return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
+  if (N <= 0 || K <= 0) return fail(FP8BLK_EINVAL, "%s: need N > 0 and K > 0", fn);
+  if (N >= kMaxDim || K >= kMaxDim || ldw >= kMaxDim) return fail(FP8BLK_EUNSUPPORTED, "%s: dimension above 2^31", fn);
+  if (N % 128 != 0 || K % 128 != 0) return fail(FP8BLK_EUNSUPPORTED, "%s: N and K must be multiples of 128", fn);
+  if (N * K > ((int64_t)1 << 40)) return fail(FP8BLK_EUNSUPPORTED, "%s: more than 2^40 weights", fn);
+  if (ldw < K) return fail(FP8BLK_EINVAL, "%s: leading dimension too small", fn);
+  if (!aligned16(w) || !aligned16(packed) || ldw % 16 != 0)
+    return fail(FP8BLK_EALIGN, "%s: w and packed must be 16-byte aligned and ldw a multiple of 16", fn);
+  const uintptr_t pb = reinterpret_cast<uintptr_t>(packed);
+  if (overlap(range2d(w, N, K, ldw, 1), Range{pb, pb + (uintptr_t)(N * K)}))
+    return fail(FP8BLK_EINVAL, "%s: packed must not overlap w", fn);
+  return hip_status(fp8blk::launch_pack_decode_weights(w, N, K, ldw, packed, static_cast<hipStream_t>(stream)), fn);
+}
+
+fp8blk_status fp8_block_gemm_packed(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                                    const float* scale_a, fp8blk_granularity gran_a, int64_t sa_stride_m,
+                                    int64_t sa_stride_k, const uint8_t* b_packed, const float* scale_b,
+                                    fp8blk_granularity gran_b, int64_t sb_stride_n, int64_t sb_stride_k,
+                                    fp8blk_format fmt_a, fp8blk_format fmt_b, void* c, fp8blk_dtype c_dtype,
+                                    int64_t ldc, void* stream) {
+  const char* fn = "fp8_block_gemm_packed";
+  fp8blk::GemmArgs g;
+  Range in[4] = {};
+  // the packed operand holds N * K contiguous bytes, the range of a row-major
+  // [N][K] array with ldb = K
+  if (fp8blk_status st = check_gemm_inputs(fn, M, N, K, a, lda, scale_a, gran_a, sa_stride_m, sa_stride_k,
+                                           b_packed, K, scale_b, gran_b, sb_stride_n, sb_stride_k, fmt_a, fmt_b,
+                                           g, in))
+    return st;
+  if (M > 64) return fail(FP8BLK_EUNSUPPORTED, "%s: packed weights serve M <= 64 (decode); got M = %lld", fn,
+                          (long long)M);
+  if (!c) return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
+  if (c_dtype != FP8BLK_BF16 && c_dtype != FP8BLK_F32)
+    return fail(FP8BLK_EINVAL, "%s: unknown output dtype %d", fn, (int)c_dtype);
+  if (ldc < N) return fail(FP8BLK_EINVAL, "%s: leading dimension too small", fn);
+  const int64_t csz = c_dtype == FP8BLK_BF16 ? 2 : 4;
+  if (!aligned16(c)) return fail(FP8BLK_EALIGN, "%s: c must be 16-byte aligned", fn);
+  if ((ldc * csz) % 16 != 0) return fail(FP8BLK_EALIGN, "%s: ldc * elem_size must be a multiple of 16 bytes", fn);
+  if (M == 0) return ok();
+  if (overlaps_any(range2d(c, M, N, ldc, csz), in)) return fail(FP8BLK_EINVAL, "%s: c must not overlap the inputs", fn);
+  g.c = c;
+  g.c_dtype = (int)c_dtype;
+  g.ldc = ldc;
+  g.quant_out = 0;
+  g.mx = 0;
+  g.b_packed = 1;
+  return hip_status(fp8blk::launch_block_gemm(g, static_cast<hipStream_t>(stream)), fn);
+}
+
 fp8blk_status fp8_block_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
                                    const float* scale_a, fp8blk_granularity gran_a, int64_t sa_stride_m,
                                    int64_t sa_stride_k, const uint8_t* b, int64_t ldb,

@@ -67,6 +67,9 @@ struct GemmArgs {
   uint8_t* qc;
   float* sc;
   int64_t sc_m, sc_n;
+  // b_packed: b is in the decode-packed layout written by
+  // launch_pack_decode_weights (ldb unused); M <= 64, bf16 or fp32 output
+  int b_packed;
 };
 
 struct AttnArgs {
@@ -102,5 +105,10 @@ hipError_t launch_kv_decode_attention(const AttnArgs& a, hipStream_t st);
 hipError_t launch_kv_quantize(const KvArgs& a, hipStream_t st);
 hipError_t launch_kv_dequantize(const KvArgs& a, hipStream_t st);
 hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t st);
+// Row-major weight codes [N][ldw] (N % 16 == 0, K % 128 == 0) to the
+// decode-packed layout: 2 KB per (16-row group rg, K block kb) at
+// (kb * N / 16 + rg) * 2048.
+hipError_t launch_pack_decode_weights(const uint8_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* packed,
+                                      hipStream_t st);
 
 }  // namespace fp8blk

@@ -185,6 +185,55 @@ fp8blk_status fp8_block_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_
                                    int64_t sc_stride_m, int64_t sc_stride_n, void* stream);
 
 /*
+ * fp8_pack_weights_decode -- copy row-major weight codes into the
+ * decode-packed layout read by fp8_block_gemm_packed.
+ *
+ * The weights of a decode step (a handful of tokens, M <= 64) are streamed
+ * from HBM once per call, so their memory order decides the GEMM's speed. The
+ * method fixes the codes and their 128 x 128 block scales ([FP8] section
+ * "权重量化：128×128 分块 FP8": weights are quantized once, offline) but not
+ * their order in memory; this is a one-time, offline reordering of the same
+ * bytes, done after fp8_quantize(BLOCK_128x128). The scales are unchanged.
+ *
+ *   w       device, uint8 codes [N][K], row stride ldw bytes.
+ *   packed  device, N * K bytes, caller-owned. One 2 KB block per (16-row
+ *           group rg, 128-wide K block kb), blocks stored K-block-major at byte
+ *           (kb * N / 16 + rg) * 2048. Inside a block, byte e (0..15) of half h
+ *           (0, 1) of lane l = r + 16 g (r 0..15, g 0..3) is at h * 1024 + 16 l + e
+ *           and holds w[16 rg + r][128 kb + 32 g + 16 h + e].
+ *
+ * Requirements: pointers non-null; N > 0, K > 0, both multiples of 128 and
+ * below 2^31, N * K <= 2^40 (else FP8BLK_EUNSUPPORTED); ldw >= K; w, packed
+ * 16-byte aligned and ldw a multiple of 16; packed must not overlap w.
+ */
+fp8blk_status fp8_pack_weights_decode(const uint8_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* packed,
+                                      void* stream);
+
+/*
+ * fp8_block_gemm_packed -- fp8_block_gemm for M <= 64 with the weights in the
+ * decode-packed layout of fp8_pack_weights_decode.
+ *
+ * The product, its numerics and every other argument are those of
+ * fp8_block_gemm ([FP8] sections "激活动态量化" and "FP8 矩阵乘"); the result
+ * is bit-identical to fp8_block_gemm on the row-major codes the packed array
+ * was made from (the same kernel and summation order, only the weight loads
+ * are addressed differently). In the packed order all workgroups read one
+ * K block's N * 128 bytes at a time instead of reads spread over the whole
+ * matrix.
+ *
+ *   b_packed device, N * K bytes written by fp8_pack_weights_decode(N, K).
+ *
+ * Requirements: as fp8_block_gemm, with ldb taken as K; M <= 64 (else
+ * FP8BLK_EUNSUPPORTED: prefill shapes take fp8_block_gemm); M == 0 is a no-op.
+ */
+fp8blk_status fp8_block_gemm_packed(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                                    const float* scale_a, fp8blk_granularity gran_a, int64_t sa_stride_m,
+                                    int64_t sa_stride_k, const uint8_t* b_packed, const float* scale_b,
+                                    fp8blk_granularity gran_b, int64_t sb_stride_n, int64_t sb_stride_k,
+                                    fp8blk_format fmt_a, fp8blk_format fmt_b, void* c, fp8blk_dtype c_dtype,
+                                    int64_t ldc, void* stream);
+
+/*
  * fp8_kv_quantize -- FP8 KV-cache quantization with one scale per (head, token block).
  *
  * Defined by [LONG] section 1 (K and V quantized to FP8 with separate scales)

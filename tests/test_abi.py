@@ -338,3 +338,52 @@ def test_kv_dequantize_rejects(lib, args, status):
 
 def test_gemm_rejects_huge_leading_dimension(lib):
     assert g(lib, lda=1 << 23) == EUNSUPPORTED
+
+
+def pk(lib, w=PA, N=256, K=256, ldw=256, out=PB):
+    return lib.fp8_pack_weights_decode(w, N, K, ldw, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=0), EINVAL),
+    (dict(out=0), EINVAL),
+    (dict(N=0), EINVAL),
+    (dict(K=-128), EINVAL),
+    (dict(N=200), EUNSUPPORTED),
+    (dict(K=200, ldw=208), EUNSUPPORTED),
+    (dict(N=1 << 31), EUNSUPPORTED),
+    (dict(ldw=128), EINVAL),
+    (dict(w=PA + 8), EALIGN),
+    (dict(ldw=264), EALIGN),
+    (dict(out=PA + 4096), EINVAL),          # packed overlaps w
+])
+def test_pack_weights_decode_rejects(lib, kw, status):
+    assert pk(lib, **kw) == status
+    assert lib.fp8blk_last_error().decode().startswith("fp8_pack_weights_decode")
+
+
+def gp(lib, M=16, N=256, K=256, a=PA, lda=256, sa=PB, ga=GROUP, sam=1, sak=16, b=PC, sb=PB + 65536, gb=BLOCK,
+       sbn=2, sbk=1, fa=E4M3, fb=E4M3, c=PD, cdt=BF16, ldc=256):
+    return lib.fp8_block_gemm_packed(M, N, K, a, lda, sa, ga, sam, sak, b, sb, gb, sbn, sbk, fa, fb, c, cdt, ldc,
+                                     None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=65), EUNSUPPORTED),             # prefill shapes take fp8_block_gemm
+    (dict(b=0), EINVAL),
+    (dict(c=0), EINVAL),
+    (dict(cdt=3), EINVAL),
+    (dict(N=200), EUNSUPPORTED),
+    (dict(ldc=128), EINVAL),
+    (dict(b=PC + 8), EALIGN),
+    (dict(sb=PB + 65536 + 2), EALIGN),
+    (dict(c=PC + 1024), EINVAL),            # c overlaps the packed weights (N * K bytes)
+    (dict(fb=9), EINVAL),
+])
+def test_gemm_packed_rejects(lib, kw, status):
+    assert gp(lib, **kw) == status
+    assert lib.fp8blk_last_error().decode().startswith("fp8_block_gemm_packed")
+
+
+def test_gemm_packed_empty_m_is_a_noop(lib):
+    assert gp(lib, M=0) == OK
