@@ -131,6 +131,20 @@ def test_gemms(gpu_lib, M):
     c.check(f"MX GEMM M={M}")
 
 
+def test_packed_decode(gpu_lib):
+    M, N, K = 40, 384, 256
+    qa, sa = gpu_lib.fp8_quantize(_x(M, K, M), "group_1x128", scale_layout="kmajor")
+    qw, sw = gpu_lib.fp8_quantize((_x(N, K, 7) * 0.02).contiguous(), "block_128x128")
+    pk = Guarded(1, N * K, N * K, torch.uint8)
+    packed = pk.view[0].view(K // 128, N // 16, 2048)
+    gpu_lib.fp8_pack_weights_decode(qw, out=packed)
+    pk.check("decode-packed weights")
+    for dtype, ld in ((torch.bfloat16, N + 8), (torch.float32, N + 4)):
+        c = Guarded(M, N, ld, dtype)
+        gpu_lib.fp8_block_gemm_packed(qa, sa, "group_1x128", packed, sw, "block_128x128", out=c.view)
+        c.check(f"packed decode GEMM {dtype}")
+
+
 def test_decode_attention(gpu_lib):
     lib = gpu_lib.load_library()
     hq, hkv, t = 16, 2, 5000
