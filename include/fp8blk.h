@@ -191,9 +191,10 @@ fp8blk_status fp8_block_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_
  * The weights of a decode step (a handful of tokens, M <= 64) are streamed
  * from HBM once per call, so their memory order decides the GEMM's speed. The
  * method fixes the codes and their 128 x 128 block scales ([FP8] section
- * "权重量化：128×128 分块 FP8": weights are quantized once, offline) but not
- * their order in memory; this is a one-time, offline reordering of the same
- * bytes, done after fp8_quantize(BLOCK_128x128). The scales are unchanged.
+ * "FP8 矩阵乘": the weights are cut into 128 x 128 blocks and quantized ahead
+ * of time, offline) but not their order in memory; this is a one-time, offline
+ * reordering of the same bytes, done after fp8_quantize(BLOCK_128x128). The
+ * scales are unchanged.
  *
  *   w       device, uint8 codes [N][K], row stride ldw bytes.
  *   packed  device, N * K bytes, caller-owned. One 2 KB block per (16-row
