@@ -273,7 +273,7 @@ __device__ __forceinline__ void k_loop(const Plan& pl, const uint8_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// MX operands ([VS] api.makesence.top, "LLM推理量化：FP8 versus INT8", section 3:
+// MX operands ([VS] api.makesence.top, "LLM推理量化:FP8 versus INT8", section 3:
 // one power-of-two scale per 32 elements of a row, applied by block-scaled
 // hardware). gfx950's v_mfma_scale_f32_16x16x128_f8f6f4 takes one E8M0 byte
 // per lane for each operand: lane group g = lane / 16 supplies the scale of

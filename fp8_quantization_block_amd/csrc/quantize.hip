@@ -11,7 +11,7 @@
 // Dequantization is x ~ q * s ([MIXED] charles2530.github.io, "量化：FP8 与混合精度推理",
 // section "E4M3 和 E5M2 是范围与格点的取舍"). Every kernel is instantiated for both
 // FP8 formats ([FP8] section "FP8 是什么", format table): E4M3 (max_fmt = 448)
-// and E5M2 (max_fmt = 57344; [VS] api.makesence.top, "LLM推理量化：FP8 versus INT8",
+// and E5M2 (max_fmt = 57344; [VS] api.makesence.top, "LLM推理量化:FP8 versus INT8",
 // section 2, serves a W8A8 E4M3 model with an E5M2 KV cache).
 //
 // All passes are HBM-bound: 16-byte loads, a max reduction in registers / DPP
@@ -470,7 +470,7 @@ __global__ __launch_bounds__(256) void k_cast_tensor(const T* __restrict__ x, in
 // ---------------------------------------------------------------------------
 // MX blocks: 32 consecutive elements of a row share one power-of-two scale
 // X = 2^k, stored as the byte k + 127 (E8M0), with k the smallest integer such
-// that amax <= MAX * 2^k ([VS] api.makesence.top, "LLM推理量化：FP8 versus INT8",
+// that amax <= MAX * 2^k ([VS] api.makesence.top, "LLM推理量化:FP8 versus INT8",
 // section 3: Microscaling with block size 32; the pages' s = amax / MAX rounded
 // up to a power of two, so that the block max never saturates). With
 // MAX = 0.875 * 2^E and amax = m * 2^e (m in [0.5, 1), frexp), k = e - E +

@@ -9,7 +9,7 @@
  *   [FP8]   wangyu.me, "大语言模型量化技术（五）：FP8" (LLM quantization part 5: FP8)
  *   [MIXED] charles2530.github.io, "量化：FP8 与混合精度推理：它不是一个 dtype 开关"
  *   [LONG]  pwwt.cn, Llama-3 FP8 and long-context practice notes
- *   [VS]    api.makesence.top, "LLM推理量化：FP8 versus INT8"
+ *   [VS]    api.makesence.top, "LLM推理量化:FP8 versus INT8"
  *
  * Numerics shared by every entry point:
  *   - FP8 formats ([FP8] section "FP8 是什么", format table): OCP E4M3 (bias 7,

@@ -26,7 +26,7 @@ Every function cites the page and section it follows. Pages are cited as
 * [FP8]   wangyu.me, "大语言模型量化技术（五）：FP8" (LLM quantization part 5: FP8)
 * [MIXED] charles2530.github.io, "量化：FP8 与混合精度推理：它不是一个 dtype 开关"
 * [LONG]  pwwt.cn, Llama-3 FP8 and long-context practice notes
-* [VS]    api.makesence.top, "LLM推理量化：FP8 versus INT8"
+* [VS]    api.makesence.top, "LLM推理量化:FP8 versus INT8"
 
 Parity status: every function here is pinned by tests under ``tests/``
 (``test_oracle_*.py``) against values the pages print, closed forms,

@@ -5,7 +5,7 @@ Follows [FP8] section "FP8 是什么" (format table: E5M2 has 1 sign, 5 exponent
 subnormal 2^-16; the wider range and coarser grid of the two FP8 formats) and
 section "什么是 FP8 量化" (the representable set is the quantization grid; values
 are rounded to the nearest grid point, ties to even). [VS] api.makesence.top,
-"LLM推理量化：FP8 versus INT8", section 1 gives the same range, and its section 2
+"LLM推理量化:FP8 versus INT8", section 1 gives the same range, and its section 2
 serves a W8A8 E4M3 model with an E5M2 KV cache.
 
 Readings taken where the pages are silent:

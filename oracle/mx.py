@@ -1,7 +1,7 @@
 """MX block formats: FP8 codes with one power-of-two (E8M0) scale per 32
 consecutive elements, and the GEMM over them (oracle; test infrastructure only).
 
-Follows [VS] api.makesence.top, "LLM推理量化：FP8 versus INT8", section 3
+Follows [VS] api.makesence.top, "LLM推理量化:FP8 versus INT8", section 3
 (Microscaling formats with a block size of 32: MXFP8 and MXINT8, a scale
 shared by each block of 32, run natively by block-scaled hardware); [FP8]
 wangyu.me, "大语言模型量化技术（五）：FP8", section "什么是 FP8 量化" (a scale maps the

@@ -1,6 +1,6 @@
 """Pins of the oracle's MX (block-32, power-of-two scale) quantizer and GEMM.
 
-Sources: api.makesence.top "LLM推理量化：FP8 versus INT8", section 3 (Microscaling,
+Sources: api.makesence.top "LLM推理量化:FP8 versus INT8", section 3 (Microscaling,
 block size 32); wangyu.me "大语言模型量化技术（五）：FP8", section "什么是 FP8 量化"
 (scale into the format's range, round to nearest even, saturate).
 

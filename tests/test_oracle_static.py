@@ -2,7 +2,7 @@
 
 Sources: charles2530.github.io "量化：FP8 与混合精度推理", section "scale 是控制面"
 (the scale may come from recorded amax history instead of the current batch);
-api.makesence.top "LLM推理量化：FP8 versus INT8", section 2 (delayed scaling);
+api.makesence.top "LLM推理量化:FP8 versus INT8", section 2 (delayed scaling);
 wangyu.me "大语言模型量化技术（五）：FP8", section "什么是 FP8 量化" (divide by the
 scale, round to nearest even, saturate).
 
