@@ -115,6 +115,20 @@ def _require_cuda(*ts):
             raise ValueError("fp8_quantization_block_amd: tensors must be on the GPU")
 
 
+def _require_rows(fn: str, dtypes, **ts):
+    """Each named tensor must be 2-D with unit stride along its last axis (the
+    C ABI takes a base pointer and a row stride) and of one of ``dtypes``."""
+    for name, t in ts.items():
+        if t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{fn}: {name} must be a 2-D tensor with contiguous rows")
+        if t.dtype not in dtypes:
+            raise ValueError(f"{fn}: {name} has dtype {t.dtype}, expected one of {dtypes}")
+
+
+_CODES = (torch.uint8,)
+_OUT = (torch.bfloat16, torch.float32)
+
+
 def fp8_quantize(x: torch.Tensor, granularity: str, fmt: str = "e4m3", scale_layout: str = "row",
                  out: torch.Tensor = None, scales: torch.Tensor = None):
     """Quantize a 2-D bf16/fp32 tensor to FP8 codes of format ``fmt`` (uint8) and fp32 scales.
@@ -173,6 +187,8 @@ def fp8_block_gemm(qa: torch.Tensor, sa: torch.Tensor, gran_a: str, qw: torch.Te
         raise ValueError("fp8_block_gemm: K mismatch")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=qa.device)
+    _require_rows("fp8_block_gemm", _CODES, qa=qa, qw=qw)
+    _require_rows("fp8_block_gemm", _OUT, out=out)
     cdt = BF16 if out.dtype == torch.bfloat16 else F32
     ga, gw = _GRAN[gran_a], _GRAN[gran_w]
     sam = sa.stride(0) if sa.dim() == 2 else 0
@@ -192,6 +208,7 @@ def fp8_pack_weights_decode(qw: torch.Tensor, out: torch.Tensor = None):
     lib = load_library()
     _require_cuda(qw)
     N, K = qw.shape
+    _require_rows("fp8_pack_weights_decode", _CODES, qw=qw)
     if out is None:
         out = torch.empty((K // 128, N // 16, 2048), dtype=torch.uint8, device=qw.device)
     if out.numel() != N * K or not out.is_contiguous():
@@ -216,6 +233,8 @@ def fp8_block_gemm_packed(qa: torch.Tensor, sa: torch.Tensor, gran_a: str, qw_pa
         raise ValueError("fp8_block_gemm_packed: K mismatch")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=qa.device)
+    _require_rows("fp8_block_gemm_packed", _CODES, qa=qa)
+    _require_rows("fp8_block_gemm_packed", _OUT, out=out)
     cdt = BF16 if out.dtype == torch.bfloat16 else F32
     ga, gw = _GRAN[gran_a], _GRAN[gran_w]
     sam = sa.stride(0) if sa.dim() == 2 else 0
@@ -244,6 +263,7 @@ def fp8_block_gemm_quant(qa: torch.Tensor, sa: torch.Tensor, gran_a: str, qw: to
         raise ValueError("fp8_block_gemm_quant: K mismatch")
     if out is None:
         out = torch.empty((M, N), dtype=torch.uint8, device=qa.device)
+    _require_rows("fp8_block_gemm_quant", _CODES, qa=qa, qw=qw, out=out)
     if scales is None:
         g = N // 128
         if scale_layout == "kmajor":
@@ -346,6 +366,8 @@ def fp8_mx_gemm(qa: torch.Tensor, sa: torch.Tensor, qw: torch.Tensor, sw: torch.
         raise ValueError("fp8_mx_gemm: K mismatch")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=qa.device)
+    _require_rows("fp8_mx_gemm", _CODES, qa=qa, sa=sa, qw=qw, sw=sw)
+    _require_rows("fp8_mx_gemm", _OUT, out=out)
     cdt = BF16 if out.dtype == torch.bfloat16 else F32
     _check(lib.fp8_mx_gemm(M, N, K, _ptr(qa), qa.stride(0), _ptr(sa), sa.stride(0), _ptr(qw), qw.stride(0),
                            _ptr(sw), sw.stride(0), _FMT[fmt_a], _FMT[fmt_w], _ptr(out), cdt, out.stride(0),

@@ -127,3 +127,19 @@ def test_packed_rejects_prefill_m(gpu_lib):
     with pytest.raises(gpu_lib.Fp8BlkError) as e:
         gpu_lib.fp8_block_gemm_packed(qa, sa, "group_1x128", packed, sw, "block_128x128")
     assert e.value.status == 3
+
+
+def test_binding_rejects_column_strided_codes(gpu_lib):
+    """The C ABI takes a base pointer and a row stride: the binding refuses
+    views whose rows are not contiguous, and codes that are not uint8."""
+    qa, sa, qw, sw = _quantized(gpu_lib, 16, 256, 256, variant=2)
+    with pytest.raises(ValueError):
+        gpu_lib.fp8_block_gemm(qa, sa, "group_1x128", qw.t(), sw, "block_128x128")
+    with pytest.raises(ValueError):
+        gpu_lib.fp8_pack_weights_decode(qw.t())
+    with pytest.raises(ValueError):
+        gpu_lib.fp8_block_gemm(qa.to(torch.int16), sa, "group_1x128", qw, sw, "block_128x128")
+    packed = gpu_lib.fp8_pack_weights_decode(qw)
+    out = torch.empty((256, 16), dtype=torch.bfloat16, device=DEV).t()
+    with pytest.raises(ValueError):
+        gpu_lib.fp8_block_gemm_packed(qa, sa, "group_1x128", packed, sw, "block_128x128", out=out)
