@@ -129,6 +129,33 @@ _CODES = (torch.uint8,)
 _OUT = (torch.bfloat16, torch.float32)
 
 
+def _require_scales(fn: str, name: str, s: torch.Tensor, gran: int, grid):
+    """A GEMM operand's fp32 scales must match its granularity: one element for
+    PER_TENSOR, else a 2-D tensor of shape ``grid`` (any strides; the C ABI
+    takes both)."""
+    if s.dtype != torch.float32:
+        raise ValueError(f"{fn}: {name} must be float32, got {s.dtype}")
+    if gran == PER_TENSOR:
+        if s.numel() < 1:
+            raise ValueError(f"{fn}: per-tensor {name} must hold one element")
+    elif s.dim() != 2 or tuple(s.shape) != tuple(grid):
+        raise ValueError(f"{fn}: {name} must have shape {tuple(grid)}, got {tuple(s.shape)}")
+
+
+def _gemm_scales(fn: str, sa: torch.Tensor, ga: int, sw: torch.Tensor, gw: int, M: int, N: int, K: int):
+    """Checks both GEMM scale operands and returns their element strides
+    (sa_m, sa_k, sw_n, sw_k); a per-tensor scale has strides 0."""
+    if ga not in (PER_TENSOR, GROUP_1x128):
+        raise ValueError(f"{fn}: gran_a must be per_tensor or group_1x128")
+    if gw not in (PER_TENSOR, BLOCK_128x128):
+        raise ValueError(f"{fn}: gran_w must be per_tensor or block_128x128")
+    _require_scales(fn, "sa", sa, ga, (M, (K + 127) // 128))
+    _require_scales(fn, "sw", sw, gw, ((N + 127) // 128, (K + 127) // 128))
+    sam, sak = (sa.stride(0), sa.stride(1)) if ga != PER_TENSOR else (0, 0)
+    swn, swk = (sw.stride(0), sw.stride(1)) if gw != PER_TENSOR else (0, 0)
+    return sam, sak, swn, swk
+
+
 def fp8_quantize(x: torch.Tensor, granularity: str, fmt: str = "e4m3", scale_layout: str = "row",
                  out: torch.Tensor = None, scales: torch.Tensor = None):
     """Quantize a 2-D bf16/fp32 tensor to FP8 codes of format ``fmt`` (uint8) and fp32 scales.
@@ -191,10 +218,7 @@ def fp8_block_gemm(qa: torch.Tensor, sa: torch.Tensor, gran_a: str, qw: torch.Te
     _require_rows("fp8_block_gemm", _OUT, out=out)
     cdt = BF16 if out.dtype == torch.bfloat16 else F32
     ga, gw = _GRAN[gran_a], _GRAN[gran_w]
-    sam = sa.stride(0) if sa.dim() == 2 else 0
-    sak = sa.stride(1) if sa.dim() == 2 else 0
-    swn = sw.stride(0) if sw.dim() == 2 else 0
-    swk = sw.stride(1) if sw.dim() == 2 else 0
+    sam, sak, swn, swk = _gemm_scales("fp8_block_gemm", sa, ga, sw, gw, M, N, K)
     _check(lib.fp8_block_gemm(M, N, K, _ptr(qa), qa.stride(0), _ptr(sa), ga, sam, sak,
                               _ptr(qw), qw.stride(0), _ptr(sw), gw, swn, swk, _FMT[fmt_a], _FMT[fmt_w],
                               _ptr(out), cdt, out.stride(0), _stream(qa)))
@@ -235,12 +259,11 @@ def fp8_block_gemm_packed(qa: torch.Tensor, sa: torch.Tensor, gran_a: str, qw_pa
         out = torch.empty((M, N), dtype=out_dtype, device=qa.device)
     _require_rows("fp8_block_gemm_packed", _CODES, qa=qa)
     _require_rows("fp8_block_gemm_packed", _OUT, out=out)
+    if qw_packed.dtype != torch.uint8:
+        raise ValueError("fp8_block_gemm_packed: qw_packed must be uint8 codes")
     cdt = BF16 if out.dtype == torch.bfloat16 else F32
     ga, gw = _GRAN[gran_a], _GRAN[gran_w]
-    sam = sa.stride(0) if sa.dim() == 2 else 0
-    sak = sa.stride(1) if sa.dim() == 2 else 0
-    swn = sw.stride(0) if sw.dim() == 2 else 0
-    swk = sw.stride(1) if sw.dim() == 2 else 0
+    sam, sak, swn, swk = _gemm_scales("fp8_block_gemm_packed", sa, ga, sw, gw, M, N, K)
     _check(lib.fp8_block_gemm_packed(M, N, K, _ptr(qa), qa.stride(0), _ptr(sa), ga, sam, sak,
                                      _ptr(qw_packed), _ptr(sw), gw, swn, swk, _FMT[fmt_a], _FMT[fmt_w],
                                      _ptr(out), cdt, out.stride(0), _stream(qa)))
@@ -270,11 +293,10 @@ def fp8_block_gemm_quant(qa: torch.Tensor, sa: torch.Tensor, gran_a: str, qw: to
             scales = torch.empty((g, M), dtype=torch.float32, device=qa.device).t()
         else:
             scales = torch.empty((M, g), dtype=torch.float32, device=qa.device)
+    if scales.dtype != torch.float32 or scales.dim() != 2 or tuple(scales.shape) != (M, N // 128):
+        raise ValueError(f"fp8_block_gemm_quant: scales must be float32 [{M}, {N // 128}]")
     ga, gw = _GRAN[gran_a], _GRAN[gran_w]
-    sam = sa.stride(0) if sa.dim() == 2 else 0
-    sak = sa.stride(1) if sa.dim() == 2 else 0
-    swn = sw.stride(0) if sw.dim() == 2 else 0
-    swk = sw.stride(1) if sw.dim() == 2 else 0
+    sam, sak, swn, swk = _gemm_scales("fp8_block_gemm_quant", sa, ga, sw, gw, M, N, K)
     _check(lib.fp8_block_gemm_quant(M, N, K, _ptr(qa), qa.stride(0), _ptr(sa), ga, sam, sak,
                                     _ptr(qw), qw.stride(0), _ptr(sw), gw, swn, swk, _FMT[fmt_a], _FMT[fmt_w],
                                     _FMT[fmt_c], _ptr(out), out.stride(0), _ptr(scales), scales.stride(0),
@@ -368,6 +390,8 @@ def fp8_mx_gemm(qa: torch.Tensor, sa: torch.Tensor, qw: torch.Tensor, sw: torch.
         out = torch.empty((M, N), dtype=out_dtype, device=qa.device)
     _require_rows("fp8_mx_gemm", _CODES, qa=qa, sa=sa, qw=qw, sw=sw)
     _require_rows("fp8_mx_gemm", _OUT, out=out)
+    if sa.shape[0] != M or sw.shape[0] != N or sa.shape[1] < K // 32 or sw.shape[1] < K // 32:
+        raise ValueError(f"fp8_mx_gemm: scale bytes must be [M, >= K/32] and [N, >= K/32]")
     cdt = BF16 if out.dtype == torch.bfloat16 else F32
     _check(lib.fp8_mx_gemm(M, N, K, _ptr(qa), qa.stride(0), _ptr(sa), sa.stride(0), _ptr(qw), qw.stride(0),
                            _ptr(sw), sw.stride(0), _FMT[fmt_a], _FMT[fmt_w], _ptr(out), cdt, out.stride(0),
@@ -405,6 +429,12 @@ def fp8_kv_decode_attention(q: torch.Tensor, k_codes: torch.Tensor, k_scales: to
     hkv, t, d2 = k_codes.shape
     if d2 != d or tuple(v_codes.shape) != (hkv, t, d):
         raise ValueError("fp8_kv_decode_attention: shape mismatch")
+    if k_codes.dtype != torch.uint8 or v_codes.dtype != torch.uint8:
+        raise ValueError("fp8_kv_decode_attention: k_codes and v_codes must be uint8 codes")
+    nb = (t + 127) // 128
+    for name, sc in (("k_scales", k_scales), ("v_scales", v_scales)):
+        if sc.dtype != torch.float32 or tuple(sc.shape) != (hkv, nb):
+            raise ValueError(f"fp8_kv_decode_attention: {name} must be float32 [{hkv}, {nb}]")
     k_codes, v_codes = k_codes.contiguous(), v_codes.contiguous()
     k_scales, v_scales = k_scales.contiguous(), v_scales.contiguous()
     if out is None:
@@ -424,8 +454,15 @@ def fp8_kv_dequantize(q: torch.Tensor, scales: torch.Tensor, token_block: int = 
     """Inverse of fp8_kv_quantize: bf16 [heads, tokens, head_dim] = bf16(dec(q) * s)."""
     lib = load_library()
     _require_cuda(q, scales)
+    if q.dtype != torch.uint8 or q.dim() != 3:
+        raise ValueError("fp8_kv_dequantize: q must be uint8 codes [heads, tokens, head_dim]")
     h, t, d = q.shape
+    nb = (t + token_block - 1) // token_block
+    if scales.dtype != torch.float32 or tuple(scales.shape) != (h, nb):
+        raise ValueError(f"fp8_kv_dequantize: scales must be float32 [{h}, {nb}]")
+    # the dense copies stay referenced until the call has been enqueued, so the
+    # caching allocator cannot hand one's memory to the other
+    qc, sc = q.contiguous(), scales.contiguous()
     out = torch.empty((h, t, d), dtype=torch.bfloat16, device=q.device)
-    _check(lib.fp8_kv_dequantize(_ptr(q.contiguous()), _ptr(scales.contiguous()), h, t, d, token_block,
-                                 _FMT[fmt], _ptr(out), _stream(q)))
+    _check(lib.fp8_kv_dequantize(_ptr(qc), _ptr(sc), h, t, d, token_block, _FMT[fmt], _ptr(out), _stream(q)))
     return out

@@ -70,6 +70,8 @@ fp8blk_status hip_status(hipError_t e, const char* what) {
 constexpr int64_t kMaxDim = (int64_t)1 << 31;   // indices are kept in 32 bits inside kernels
 // the GEMM addresses a 256-row operand tile with 32-bit byte offsets
 constexpr int64_t kMaxLdCodes = (int64_t)1 << 23;
+// ... and a scale grid with 32-bit byte offsets from its base
+constexpr int64_t kMaxScaleGridBytes = (int64_t)1 << 32;
 
 fp8blk_status check_format(fp8blk_format fmt, const char* what) {
   if (fmt == FP8BLK_E4M3 || fmt == FP8BLK_E5M2) return FP8BLK_OK;
@@ -191,6 +193,16 @@ fp8blk_status check_gemm_inputs(const char* fn, int64_t M, int64_t N, int64_t K,
     return fail(FP8BLK_EALIGN, "%s: scale_a and scale_b must be 4-byte aligned", fn);
   if (lda % 16 != 0 || ldb % 16 != 0) return fail(FP8BLK_EALIGN, "%s: lda and ldb must be multiples of 16 bytes", fn);
   if (M > 0) {
+    // The prefill kernel reads each scale grid through one buffer resource
+    // with 32-bit byte offsets from the grid's base, so a grid must span less
+    // than 4 GiB (its largest cell's byte offset + 4).
+    const int64_t nk = K / 128;
+    if (gran_a != FP8BLK_PER_TENSOR &&
+        ((M - 1) * sa_stride_m + (nk - 1) * sa_stride_k + 1) * 4 >= kMaxScaleGridBytes)
+      return fail(FP8BLK_EUNSUPPORTED, "%s: scale_a grid spans 4 GiB or more", fn);
+    if (gran_b != FP8BLK_PER_TENSOR &&
+        ((N / 128 - 1) * sb_stride_n + (nk - 1) * sb_stride_k + 1) * 4 >= kMaxScaleGridBytes)
+      return fail(FP8BLK_EUNSUPPORTED, "%s: scale_b grid spans 4 GiB or more", fn);
     in[0] = range2d(a, M, K, lda, 1);
     in[1] = range2d(b, N, K, ldb, 1);
     in[2] = gran_a == FP8BLK_PER_TENSOR ? range_grid(scale_a, 1, 1, 0, 0)

@@ -844,18 +844,22 @@ namespace {
 // of a wave reads 1 KB contiguous. All workgroups of the decode kernel then
 // stream one K block's region of N * 128 bytes at a time (39.7 us against
 // 47.6 us at 16 x 28672 x 8192 for row-major weights, whose concurrent reads
-// span the whole matrix). One thread per 16-byte chunk of the packed output.
+// span the whole matrix). A thread per 16-byte chunk of the packed output,
+// grid-stride over a capped grid (N * K may reach 2^40 bytes).
+constexpr uint64_t kPackMaxGrid = 1u << 20;
+
 __global__ __launch_bounds__(256) void k_pack_decode_weights(const uint8_t* __restrict__ w, int64_t ldw,
                                                              uint64_t row_groups, uint64_t chunks,
                                                              uint8_t* __restrict__ out) {
-  const uint64_t t = (uint64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= chunks) return;
-  const uint64_t l = t & 63, h = (t >> 6) & 1;
-  const uint64_t block = t >> 7;   // kb * row_groups + rg
-  const uint64_t kb = block / row_groups, rg = block - kb * row_groups;
-  const uint64_t row = rg * 16 + (l & 15);
-  const uint64_t col = kb * 128 + 32 * (l >> 4) + 16 * h;
-  *reinterpret_cast<uint4*>(out + t * 16) = *reinterpret_cast<const uint4*>(w + row * (uint64_t)ldw + col);
+  const uint64_t stride = (uint64_t)gridDim.x * 256;
+  for (uint64_t t = (uint64_t)blockIdx.x * 256 + threadIdx.x; t < chunks; t += stride) {
+    const uint64_t l = t & 63, h = (t >> 6) & 1;
+    const uint64_t block = t >> 7;   // kb * row_groups + rg
+    const uint64_t kb = block / row_groups, rg = block - kb * row_groups;
+    const uint64_t row = rg * 16 + (l & 15);
+    const uint64_t col = kb * 128 + 32 * (l >> 4) + 16 * h;
+    *reinterpret_cast<uint4*>(out + t * 16) = *reinterpret_cast<const uint4*>(w + row * (uint64_t)ldw + col);
+  }
 }
 
 }  // namespace
@@ -864,7 +868,7 @@ hipError_t launch_pack_decode_weights(const uint8_t* w, int64_t N, int64_t K, in
                                       hipStream_t st) {
   const uint64_t chunks = (uint64_t)N * (uint64_t)K / 16;
   if (chunks == 0) return hipSuccess;
-  const uint64_t grid = (chunks + 255) / 256;
+  const uint64_t grid = min((chunks + 255) / 256, kPackMaxGrid);
   hipLaunchKernelGGL(k_pack_decode_weights, dim3((unsigned)grid), dim3(256), 0, st, w, ldw, (uint64_t)N / 16,
                      chunks, packed);
   return hipGetLastError();

@@ -133,7 +133,9 @@ fp8blk_status fp8_quantize(const void* x, fp8blk_dtype x_dtype, int64_t rows, in
  * below 2^23 (else FP8BLK_EUNSUPPORTED);
  * ldc >= N; a, b, c 16-byte aligned and lda, ldb, ldc * sizeof(c_dtype)
  * multiples of 16; scale_a and scale_b 4-byte aligned, their strides >= 0 and
- * below 2^40 (a zero stride broadcasts one scale along that axis);
+ * below 2^40 (a zero stride broadcasts one scale along that axis), and each
+ * block-scaled grid spanning less than 4 GiB, i.e. (offset of its last cell +
+ * 1) * 4 < 2^32 (else FP8BLK_EUNSUPPORTED);
  * gran_a in {PER_TENSOR, GROUP_1x128}; gran_b in {PER_TENSOR,
  * BLOCK_128x128}; fmt_a, fmt_b in {E4M3, E5M2} (independently); codes must be
  * finite (E4M3: not S.1111.111; E5M2: exponent field not 11111), as every

@@ -131,6 +131,11 @@ def g(lib, M=256, N=256, K=256, a=PA, lda=256, sa=PB, ga=GROUP, sam=2, sak=1, b=
     (dict(sa=PB + 2), EALIGN),             # scale arrays not 4-byte aligned
     (dict(sb=PB + 65536 + 1), EALIGN),
     (dict(sbk=1 << 40), EUNSUPPORTED),
+    # scale grids spanning 4 GiB or more (the prefill kernel addresses a grid
+    # with 32-bit byte offsets): a padded weight grid, a padded activation grid
+    (dict(sbn=1 << 30), EUNSUPPORTED),
+    (dict(sam=1 << 23), EUNSUPPORTED),
+    (dict(ga=PER_TENSOR, sam=1 << 22, c=PA + 1024), EINVAL),   # per tensor ignores the strides (then: c overlaps a)
 ])
 def test_gemm_rejects(lib, kw, status):
     assert g(lib, **kw) == status
@@ -161,6 +166,7 @@ def gq(lib, M=256, N=256, K=256, a=PA, lda=256, sa=PB, ga=GROUP, sam=2, sak=1, b
     (dict(scm=1, scn=1), EINVAL),            # cells (m, g + 1) and (m + 1, g) share a float
     (dict(sc=PD + (1 << 20) + 2), EALIGN),   # scales not 4-byte aligned
     (dict(scn=1 << 40), EUNSUPPORTED),
+    (dict(sbn=1 << 30), EUNSUPPORTED),       # weight scale grid spanning 4 GiB
 ])
 def test_gemm_quant_rejects(lib, kw, status):
     assert gq(lib, **kw) == status
@@ -379,6 +385,7 @@ def gp(lib, M=16, N=256, K=256, a=PA, lda=256, sa=PB, ga=GROUP, sam=1, sak=16, b
     (dict(sb=PB + 65536 + 2), EALIGN),
     (dict(c=PC + 1024), EINVAL),            # c overlaps the packed weights (N * K bytes)
     (dict(fb=9), EINVAL),
+    (dict(sak=1 << 30), EUNSUPPORTED),      # activation scale grid spanning 4 GiB
 ])
 def test_gemm_packed_rejects(lib, kw, status):
     assert gp(lib, **kw) == status

@@ -5,8 +5,8 @@ is exactly 1), fp32 quotients placed next to every kind of E4M3 midpoint,
 random bf16 groups over the whole bf16 range (subnormal to max), all three
 granularities on ragged shapes with padded leading dimensions, both input
 dtypes, both scale layouts, and the activation / weight tensors of every
-configuration at full size (weights sampled by 128-row slabs where the oracle
-would take minutes).
+configuration at full size, and every bf16 value under every bf16 amax whose
+scale takes the reciprocal fast path.
 """
 
 import numpy as np
@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import synth_inputs as syn
-from gpu_helpers import assert_codes_equal, assert_scales_equal, f32_of
+from gpu_helpers import assert_codes_equal, assert_scales_equal, f32_of, pmap
 from oracle import e4m3, quant
 
 pytestmark = pytest.mark.gpu
@@ -154,6 +154,51 @@ def test_bf16_every_value_below_sampled_amax(gpu_lib):
     assert_codes_equal(qg.cpu().numpy(), qr, x, "codes")
 
 
+def _fast_path_amax_patterns():
+    """Every positive finite bf16 pattern A whose scale fl32(A / 448) lies in
+    [2^-64, 2^64]: the groups whose bf16 elements the 1x128 quantizer divides
+    through its Newton reciprocal and one residual correction."""
+    bits = np.arange(1, 0x7F80, dtype=np.uint16)
+    s = quant.scale_of(quant.bf16_bits_to_f32(bits))
+    keep = (s >= np.float32(2.0 ** -64)) & (s <= np.float32(2.0 ** 64))
+    return bits[keep].astype(np.int64)
+
+
+def _sweep_groups(amax):
+    """1x128 groups holding, for each amax pattern A, every bf16 pattern with
+    |x| <= A in both signs (-0 included), 127 per group after one A; the last
+    group of each A is padded with +0. Returns uint16 bits [groups, 128]."""
+    n = 2 * (amax + 1)
+    rows_per = -(-n // 127)
+    starts = np.cumsum(rows_per) - rows_per
+    r_in = np.arange(rows_per.sum()) - np.repeat(starts, rows_per)
+    i = r_in[:, None] * 127 + np.arange(127)[None, :]
+    valid = i < np.repeat(n, rows_per)[:, None]
+    pat = np.where(valid, (i >> 1) | ((i & 1) << 15), 0)
+    return np.concatenate([np.repeat(amax, rows_per)[:, None], pat], axis=1).astype(np.uint16)
+
+
+def test_bf16_fast_path_exhaustive(gpu_lib):
+    """Every bf16 amax whose scale lies in [2^-64, 2^64] (16385 patterns) and,
+    under each, every bf16 |x| <= amax in both signs: 5.7e8 elements in 4.5e6
+    groups, codes and scales against the oracle, in chunks of 256 amax
+    patterns."""
+    amax = _fast_path_amax_patterns()
+    assert amax.size == 16385
+    checked = 0
+    for c0 in range(0, amax.size, 256):
+        bits = _sweep_groups(amax[c0:c0 + 256])
+        qg, sg = gpu_lib.fp8_quantize(torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16),
+                                      "group_1x128")
+        qg, sg = qg.cpu().numpy(), sg.cpu().numpy()
+        x = quant.bf16_bits_to_f32(bits)
+        parts = pmap(lambda r: quant.quantize_group_1x128(x[r:r + 8192]), range(0, x.shape[0], 8192))
+        assert_scales_equal(sg, np.concatenate([p[1] for p in parts]), f"amax chunk {c0} scales")
+        assert_codes_equal(qg, np.concatenate([p[0] for p in parts]), x, f"amax chunk {c0} codes")
+        checked += x.shape[0] * 127
+    print(f"bf16 fast path: {checked} element slots under {amax.size} amax patterns match the oracle")
+
+
 def _padded(x32: np.ndarray, dtype, ld: int) -> torch.Tensor:
     rows, cols = x32.shape
     buf = torch.full((rows, ld), float("nan"), dtype=dtype)
@@ -241,23 +286,23 @@ def test_config_activations_full_size(gpu_lib, config):
 
 @pytest.mark.parametrize("config", [1, 2, 3, 4])
 def test_config_weights_full_size(gpu_lib, config):
+    """Every code and scale of each configuration's weights (up to 28672 x
+    8192), the oracle run on 128-row slabs in parallel host threads."""
     c = syn.CONFIGS[config]
     w = syn.weights(config)
     qg, sg = gpu_lib.fp8_quantize(w.to(DEV), c["gran_w"])
     qg, sg = qg.cpu().numpy(), sg.cpu().numpy()
+    w32 = f32_of(w)
+    del w
     if c["gran_w"] == "per_tensor":
-        qr, sr = quant.quantize_per_tensor(f32_of(w))
+        qr, sr = quant.quantize_per_tensor(w32)
         assert_scales_equal(sg, sr, "scales")
         assert_codes_equal(qg, qr, None, "codes")
         return
-    n_slabs = c["N"] // 128
-    rng = np.random.default_rng(config)
-    slabs = sorted(set([0, n_slabs - 1] + list(rng.choice(n_slabs, size=min(n_slabs, 12), replace=False))))
-    for sl in slabs:
-        w32 = f32_of(w[sl * 128:(sl + 1) * 128])
-        qr, sr = quant.quantize_block_128x128(w32)
-        assert_scales_equal(sg[sl:sl + 1], sr, f"slab {sl} scales")
-        assert_codes_equal(qg[sl * 128:(sl + 1) * 128], qr, None, f"slab {sl} codes")
+    slabs = pmap(lambda sl: quant.quantize_block_128x128(w32[sl * 128:(sl + 1) * 128]),
+                 range((w32.shape[0] + 127) // 128))
+    assert_scales_equal(sg, np.concatenate([s for _, s in slabs]), "scales")
+    assert_codes_equal(qg, np.concatenate([q for q, _ in slabs]), None, "codes")
 
 
 def test_repeated_calls_and_scale_buffer_reuse(gpu_lib):
