@@ -14,6 +14,7 @@ Entry points (same names as the C ABI):
 * ``fp8_kv_quantize(kv, token_block=128, fmt="e4m3")`` -> (codes uint8, scales fp32)
 * ``fp8_kv_dequantize(q, scales, token_block=128, fmt="e4m3")`` -> bf16
 * ``fp8_kv_decode_attention(q, k_codes, k_scales, v_codes, v_scales, softmax_scale, fmt="e4m3")`` -> [heads_q, 128]
+* ``fp8_kv_decode_attention_noalloc(...)``: the same with the library's fixed workspace
 * ``fp8_quantize_static(x, scale, fmt="e4m3", record_amax=False)`` -> codes (, amax)
 * ``fp8_scale_from_amax_history(history, fmt="e4m3")`` -> scale [1]
 * ``fp8_quantize_mx(x, fmt="e4m3")`` -> (codes uint8, E8M0 scale bytes uint8 [rows, cols/32])
@@ -81,6 +82,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp8_kv_decode_attention.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, i64, i32, ctypes.c_float,
                                             vp, i32, i64, vp, ctypes.c_size_t, vp]
     lib.fp8_kv_decode_attention.restype = i32
+    lib.fp8_kv_decode_attention_noalloc.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, i64, i32,
+                                                    ctypes.c_float, vp, i32, i64, vp]
+    lib.fp8_kv_decode_attention_noalloc.restype = i32
     lib.fp8_kv_quantize.argtypes = [vp, i64, i64, i64, i64, i64, i64, i32, vp, vp, vp]
     lib.fp8_kv_dequantize.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp, vp]
     for f in ("fp8_quantize", "fp8_block_gemm", "fp8_kv_quantize", "fp8_kv_dequantize"):
@@ -414,6 +418,27 @@ def fp8_kv_quantize(kv: torch.Tensor, token_block: int = 128, fmt: str = "e4m3")
     return q, s
 
 
+def _attention_operands(fn, q, k_codes, k_scales, v_codes, v_scales):
+    """Checks the decode-attention operands; returns (hq, hkv, t, d) and
+    contiguous codes and scales (the caller keeps them referenced until the
+    call has been enqueued)."""
+    _require_cuda(q, k_codes, k_scales, v_codes, v_scales)
+    if q.dtype != torch.bfloat16 or q.dim() != 2 or q.stride(1) != 1:
+        raise ValueError(f"{fn}: q must be bf16 [heads_q, head_dim] with contiguous rows")
+    hq, d = q.shape
+    hkv, t, d2 = k_codes.shape
+    if d2 != d or tuple(v_codes.shape) != (hkv, t, d):
+        raise ValueError(f"{fn}: shape mismatch")
+    if k_codes.dtype != torch.uint8 or v_codes.dtype != torch.uint8:
+        raise ValueError(f"{fn}: k_codes and v_codes must be uint8 codes")
+    nb = (t + 127) // 128
+    for name, sc in (("k_scales", k_scales), ("v_scales", v_scales)):
+        if sc.dtype != torch.float32 or tuple(sc.shape) != (hkv, nb):
+            raise ValueError(f"{fn}: {name} must be float32 [{hkv}, {nb}]")
+    return (hq, hkv, t, d), (k_codes.contiguous(), k_scales.contiguous(), v_codes.contiguous(),
+                             v_scales.contiguous())
+
+
 def fp8_kv_decode_attention(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, v_codes: torch.Tensor,
                             v_scales: torch.Tensor, softmax_scale: float, fmt: str = "e4m3",
                             out_dtype=torch.bfloat16, out: torch.Tensor = None, workspace: torch.Tensor = None):
@@ -422,31 +447,37 @@ def fp8_kv_decode_attention(q: torch.Tensor, k_codes: torch.Tensor, k_scales: to
     [heads_kv, ceil(tokens/128)] (as fp8_kv_quantize writes them). Returns
     [heads_q, 128] in out_dtype. The workspace is allocated here unless given."""
     lib = load_library()
-    _require_cuda(q, k_codes, k_scales, v_codes, v_scales)
-    if q.dtype != torch.bfloat16 or q.dim() != 2 or q.stride(1) != 1:
-        raise ValueError("fp8_kv_decode_attention: q must be bf16 [heads_q, head_dim] with contiguous rows")
-    hq, d = q.shape
-    hkv, t, d2 = k_codes.shape
-    if d2 != d or tuple(v_codes.shape) != (hkv, t, d):
-        raise ValueError("fp8_kv_decode_attention: shape mismatch")
-    if k_codes.dtype != torch.uint8 or v_codes.dtype != torch.uint8:
-        raise ValueError("fp8_kv_decode_attention: k_codes and v_codes must be uint8 codes")
-    nb = (t + 127) // 128
-    for name, sc in (("k_scales", k_scales), ("v_scales", v_scales)):
-        if sc.dtype != torch.float32 or tuple(sc.shape) != (hkv, nb):
-            raise ValueError(f"fp8_kv_decode_attention: {name} must be float32 [{hkv}, {nb}]")
-    k_codes, v_codes = k_codes.contiguous(), v_codes.contiguous()
-    k_scales, v_scales = k_scales.contiguous(), v_scales.contiguous()
+    (hq, hkv, t, d), (kc, ks, vc, vs) = _attention_operands("fp8_kv_decode_attention", q, k_codes, k_scales,
+                                                            v_codes, v_scales)
     if out is None:
         out = torch.empty((hq, d), dtype=out_dtype, device=q.device)
     need = lib.fp8_kv_decode_attention_workspace_size(hq, t)
     if workspace is None:
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
     odt = BF16 if out.dtype == torch.bfloat16 else F32
-    _check(lib.fp8_kv_decode_attention(_ptr(q), q.stride(0), hq, hkv, t, d, _ptr(k_codes), _ptr(k_scales),
-                                       _ptr(v_codes), _ptr(v_scales), 128, _FMT[fmt], float(softmax_scale),
-                                       _ptr(out), odt, out.stride(0), _ptr(workspace), workspace.numel(),
-                                       _stream(q)))
+    _check(lib.fp8_kv_decode_attention(_ptr(q), q.stride(0), hq, hkv, t, d, _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs),
+                                       128, _FMT[fmt], float(softmax_scale), _ptr(out), odt, out.stride(0),
+                                       _ptr(workspace), workspace.numel(), _stream(q)))
+    return out
+
+
+def fp8_kv_decode_attention_noalloc(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor,
+                                    v_codes: torch.Tensor, v_scales: torch.Tensor, softmax_scale: float,
+                                    out: torch.Tensor, fmt: str = "e4m3"):
+    """fp8_kv_decode_attention into the caller's ``out`` (bf16 or fp32 [heads_q,
+    128]) with the library's fixed workspace: the C call allocates nothing.
+    The operands must already be contiguous (no copies are made here)."""
+    lib = load_library()
+    (hq, hkv, t, d), ops = _attention_operands("fp8_kv_decode_attention_noalloc", q, k_codes, k_scales,
+                                               v_codes, v_scales)
+    if any(a.data_ptr() != b.data_ptr() for a, b in zip(ops, (k_codes, k_scales, v_codes, v_scales))):
+        raise ValueError("fp8_kv_decode_attention_noalloc: codes and scales must be contiguous")
+    _require_cuda(out)
+    _require_rows("fp8_kv_decode_attention_noalloc", _OUT, out=out)
+    odt = BF16 if out.dtype == torch.bfloat16 else F32
+    _check(lib.fp8_kv_decode_attention_noalloc(_ptr(q), q.stride(0), hq, hkv, t, d, _ptr(k_codes), _ptr(k_scales),
+                                               _ptr(v_codes), _ptr(v_scales), 128, _FMT[fmt], float(softmax_scale),
+                                               _ptr(out), odt, out.stride(0), _stream(q)))
     return out
 
 

@@ -516,14 +516,19 @@ size_t fp8_kv_decode_attention_workspace_size(int64_t heads_q, int64_t tokens) {
          sizeof(float);
 }
 
-fp8blk_status fp8_kv_decode_attention(const void* q, int64_t ld_q, int64_t heads_q, int64_t heads_kv,
-                                      int64_t tokens, int64_t head_dim, const uint8_t* k_codes,
-                                      const float* k_scales, const uint8_t* v_codes, const float* v_scales,
-                                      int64_t token_block, fp8blk_format fmt, float softmax_scale, void* out,
-                                      fp8blk_dtype out_dtype, int64_t ld_o, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
-  const char* fn = "fp8_kv_decode_attention";
-  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !out || !workspace)
+}  // extern "C"
+
+namespace {
+
+// Validation shared by both decode-attention entry points. `workspace` is the
+// caller's workspace of `workspace_bytes` bytes, or null for the fixed one
+// (then only its capacity is checked). Fills `a` except for a.ws.
+fp8blk_status check_attention(const char* fn, const void* q, int64_t ld_q, int64_t heads_q, int64_t heads_kv,
+                              int64_t tokens, int64_t head_dim, const uint8_t* k_codes, const float* k_scales,
+                              const uint8_t* v_codes, const float* v_scales, int64_t token_block,
+                              fp8blk_format fmt, float softmax_scale, void* out, fp8blk_dtype out_dtype,
+                              int64_t ld_o, const void* workspace, size_t workspace_bytes, fp8blk::AttnArgs& a) {
+  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !out)
     return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
   if (fp8blk_status st = check_format(fmt, fn)) return st;
   if (out_dtype != FP8BLK_BF16 && out_dtype != FP8BLK_F32)
@@ -544,7 +549,14 @@ fp8blk_status fp8_kv_decode_attention(const void* q, int64_t ld_q, int64_t heads
   if (!aligned4(out) || !aligned4(workspace) || !aligned4(k_scales) || !aligned4(v_scales))
     return fail(FP8BLK_EALIGN, "%s: out, workspace and scales must be 4-byte aligned", fn);
   const size_t need = fp8_kv_decode_attention_workspace_size(heads_q, tokens);
-  if (workspace_bytes < need) return fail(FP8BLK_EINVAL, "%s: workspace smaller than %zu bytes", fn, need);
+  if (workspace == nullptr) {
+    if (need > fp8blk::attention_scratch_bytes())
+      return fail(FP8BLK_EUNSUPPORTED, "%s: needs %zu bytes of workspace; the fixed workspace holds %zu "
+                  "(heads_q * ceil(tokens / 4096) <= %zu)", fn, need, fp8blk::attention_scratch_bytes(),
+                  fp8blk::attention_scratch_bytes() / ((size_t)fp8blk::attention_partial_floats() * sizeof(float)));
+  } else if (workspace_bytes < need) {
+    return fail(FP8BLK_EINVAL, "%s: workspace smaller than %zu bytes", fn, need);
+  }
   const int64_t nb = (tokens + 127) / 128;
   const int64_t osz = out_dtype == FP8BLK_BF16 ? 2 : 4;
   const Range in[5] = {range2d(q, heads_q, head_dim, ld_q, 2),
@@ -552,11 +564,15 @@ fp8blk_status fp8_kv_decode_attention(const void* q, int64_t ld_q, int64_t heads
                        {reinterpret_cast<uintptr_t>(v_codes), reinterpret_cast<uintptr_t>(v_codes) + (uintptr_t)(heads_kv * tokens * head_dim)},
                        range_grid(k_scales, heads_kv, nb, nb, 1), range_grid(v_scales, heads_kv, nb, nb, 1)};
   const Range ro = range2d(out, heads_q, head_dim, ld_o, osz);
-  const Range rw = {reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
   for (const Range& r : in)
-    if (overlap(r, ro) || overlap(r, rw)) return fail(FP8BLK_EINVAL, "%s: out and workspace must not overlap the inputs", fn);
-  if (overlap(ro, rw)) return fail(FP8BLK_EINVAL, "%s: out must not overlap the workspace", fn);
-  fp8blk::AttnArgs a;
+    if (overlap(r, ro)) return fail(FP8BLK_EINVAL, "%s: out must not overlap the inputs", fn);
+  if (workspace != nullptr) {
+    const Range rw = {reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+    for (const Range& r : in)
+      if (overlap(r, rw)) return fail(FP8BLK_EINVAL, "%s: workspace must not overlap the inputs", fn);
+    if (overlap(ro, rw)) return fail(FP8BLK_EINVAL, "%s: out must not overlap the workspace", fn);
+  }
+  a = fp8blk::AttnArgs{};
   a.q = q;
   a.ld_q = ld_q;
   a.heads_q = heads_q;
@@ -568,10 +584,50 @@ fp8blk_status fp8_kv_decode_attention(const void* q, int64_t ld_q, int64_t heads
   a.sv = v_scales;
   a.fmt = (int)fmt;
   a.softmax_scale = softmax_scale;
-  a.ws = static_cast<float*>(workspace);
   a.out = out;
   a.out_dtype = (int)out_dtype;
   a.ld_o = ld_o;
+  return FP8BLK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8blk_status fp8_kv_decode_attention(const void* q, int64_t ld_q, int64_t heads_q, int64_t heads_kv,
+                                      int64_t tokens, int64_t head_dim, const uint8_t* k_codes,
+                                      const float* k_scales, const uint8_t* v_codes, const float* v_scales,
+                                      int64_t token_block, fp8blk_format fmt, float softmax_scale, void* out,
+                                      fp8blk_dtype out_dtype, int64_t ld_o, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  const char* fn = "fp8_kv_decode_attention";
+  if (!workspace) return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
+  fp8blk::AttnArgs a;
+  if (fp8blk_status st = check_attention(fn, q, ld_q, heads_q, heads_kv, tokens, head_dim, k_codes, k_scales,
+                                         v_codes, v_scales, token_block, fmt, softmax_scale, out, out_dtype, ld_o,
+                                         workspace, workspace_bytes, a))
+    return st;
+  a.ws = static_cast<float*>(workspace);
+  return hip_status(fp8blk::launch_kv_decode_attention(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+fp8blk_status fp8_kv_decode_attention_noalloc(const void* q, int64_t ld_q, int64_t heads_q, int64_t heads_kv,
+                                              int64_t tokens, int64_t head_dim, const uint8_t* k_codes,
+                                              const float* k_scales, const uint8_t* v_codes,
+                                              const float* v_scales, int64_t token_block, fp8blk_format fmt,
+                                              float softmax_scale, void* out, fp8blk_dtype out_dtype, int64_t ld_o,
+                                              void* stream) {
+  const char* fn = "fp8_kv_decode_attention_noalloc";
+  fp8blk::AttnArgs a;
+  if (fp8blk_status st = check_attention(fn, q, ld_q, heads_q, heads_kv, tokens, head_dim, k_codes, k_scales,
+                                         v_codes, v_scales, token_block, fmt, softmax_scale, out, out_dtype, ld_o,
+                                         nullptr, 0, a))
+    return st;
+  // the fixed workspace of the current device (its address is looked up on
+  // the first call on each device)
+  float* ws = nullptr;
+  if (fp8blk_status st = hip_status(fp8blk::attention_scratch(&ws), fn)) return st;
+  a.ws = ws;
   return hip_status(fp8blk::launch_kv_decode_attention(a, static_cast<hipStream_t>(stream)), fn);
 }
 

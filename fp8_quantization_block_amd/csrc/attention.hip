@@ -32,6 +32,8 @@
 #include <hip/hip_bf16.h>
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -398,6 +400,42 @@ __global__ __launch_bounds__(kCombThreads) void k_fp8kv_attn_combine(AttnParams 
 
 int attention_splits(int64_t tokens) { return (int)((tokens + kSplitTokens - 1) / kSplitTokens); }
 int64_t attention_partial_floats() { return kPartial; }
+
+// ---------------------------------------------------------------------------
+// The fixed workspace of fp8_kv_decode_attention_noalloc, for callers that
+// cannot allocate device memory: a file-scope device array, 8 MiB (the split
+// partials of heads_q * ceil(tokens / 4096) <= 16131 query-head splits, e.g.
+// 64 query heads over 1M tokens), one copy on every device the library runs
+// on, held until the process ends. In host code the array's name is only a
+// stand-in for it: its device address is looked up once per device with that
+// device current and cached, and only that address is handed to kernels.
+// Calls on one device share the array, so calls that overlap in time on one
+// device race.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+size_t attention_scratch_bytes() { return kScratchBytes; }
+
+hipError_t attention_scratch(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_kv_decode_attention(const AttnArgs& a, hipStream_t st) {
   AttnParams p;

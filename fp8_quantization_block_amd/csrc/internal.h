@@ -92,6 +92,10 @@ struct AttnArgs {
 // head, split).
 int attention_splits(int64_t tokens);
 int64_t attention_partial_floats();
+// The fixed decode-attention workspace (a device array of attention_scratch_bytes()
+// bytes, one per device): its device address on the current device.
+size_t attention_scratch_bytes();
+hipError_t attention_scratch(float** ptr);
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
 // MX blocks of 32 along the rows: a.scales points at uint8 E8M0 bytes, a.ss_row

@@ -416,6 +416,31 @@ fp8blk_status fp8_kv_decode_attention(const void* q, int64_t ld_q, int64_t heads
                                       fp8blk_dtype out_dtype, int64_t ld_o, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
+/*
+ * fp8_kv_decode_attention_noalloc -- fp8_kv_decode_attention with a fixed
+ * workspace inside the library instead of a caller-owned one, for callers
+ * that cannot allocate device memory (code under HIP graph capture, serving
+ * loops that must not call the allocator, harnesses that forbid it). It calls
+ * no allocator: the split partials live in a file-scope device array of
+ * 8 MiB, one per device, kept until the process ends.
+ *
+ * Arguments, numerics, results and requirements: those of
+ * fp8_kv_decode_attention without the workspace (the same kernels, so the
+ * outputs are bit-identical). The partials need
+ * fp8_kv_decode_attention_workspace_size(heads_q, tokens) <= 8 MiB, i.e.
+ * heads_q * ceil(tokens / 4096) <= 16131 (else FP8BLK_EUNSUPPORTED, before any
+ * HIP call). The first call on a device looks up the array's address there
+ * (FP8BLK_EHIP if that fails). Every call on one device uses the same array:
+ * calls that overlap in time on one device (other streams, other threads)
+ * race and give unspecified results; its contents between calls do not matter.
+ */
+fp8blk_status fp8_kv_decode_attention_noalloc(const void* q, int64_t ld_q, int64_t heads_q, int64_t heads_kv,
+                                              int64_t tokens, int64_t head_dim, const uint8_t* k_codes,
+                                              const float* k_scales, const uint8_t* v_codes,
+                                              const float* v_scales, int64_t token_block, fp8blk_format fmt,
+                                              float softmax_scale, void* out, fp8blk_dtype out_dtype, int64_t ld_o,
+                                              void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* fp8blk_status_string(fp8blk_status s);
 /* Message for the last non-OK status returned on the calling thread ("" if none). */

@@ -42,7 +42,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fp8_quantize", "fp8_block_gemm", "fp8_block_gemm_quant", "fp8_kv_quantize", "fp8_kv_dequantize",
               "fp8_kv_decode_attention", "fp8_kv_decode_attention_workspace_size", "fp8_quantize_mx", "fp8_mx_gemm",
-              "fp8_quantize_static", "fp8_scale_from_amax_history",
+              "fp8_quantize_static", "fp8_scale_from_amax_history", "fp8_kv_decode_attention_noalloc",
               "fp8blk_status_string", "fp8blk_last_error", "fp8blk_abi_version"):
         assert n in names
 
@@ -199,6 +199,24 @@ def att(lib, q=PA, ldq=128, hq=64, hkv=8, t=300, d=128, kc=PB, ks=PC, vc=PB + (1
 ])
 def test_attention_rejects(lib, kw, status):
     assert att(lib, **kw) == status
+
+
+def att_noalloc(lib, q=PA, ldq=128, hq=64, hkv=8, t=300, d=128, kc=PB, ks=PC, vc=PB + (1 << 24), vs=PC + 4096,
+                tb=128, fmt=E4M3, scale=0.088, out=PD, odt=BF16, ldo=128):
+    return lib.fp8_kv_decode_attention_noalloc(q, ldq, hq, hkv, t, d, kc, ks, vc, vs, tb, fmt, scale, out, odt, ldo,
+                                               None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), EINVAL),
+    (dict(hq=60), EINVAL),
+    (dict(d=64), EUNSUPPORTED),
+    (dict(out=PB + 64), EINVAL),               # out overlaps the K codes
+    (dict(hq=128, t=127 * 4096), EUNSUPPORTED),  # 16256 split partials: beyond the fixed 8 MiB
+])
+def test_attention_noalloc_rejects(lib, kw, status):
+    assert att_noalloc(lib, **kw) == status
+    assert lib.fp8blk_last_error().decode().startswith("fp8_kv_decode_attention_noalloc")
     assert lib.fp8blk_last_error().decode().startswith("fp8_kv_decode_attention")
 
 

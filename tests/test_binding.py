@@ -15,7 +15,7 @@ LIB = os.path.join(ROOT, "fp8_quantization_block_amd", "libfp8blk.so")
 
 NAMES = ("fp8_quantize", "fp8_block_gemm", "fp8_block_gemm_quant", "fp8_kv_quantize", "fp8_kv_dequantize",
          "fp8_kv_decode_attention", "fp8_quantize_static", "fp8_scale_from_amax_history", "fp8_quantize_mx",
-         "fp8_mx_gemm", "fp8_pack_weights_decode", "fp8_block_gemm_packed")
+         "fp8_mx_gemm", "fp8_pack_weights_decode", "fp8_block_gemm_packed", "fp8_kv_decode_attention_noalloc")
 
 
 @pytest.fixture(scope="module")
@@ -54,6 +54,10 @@ def test_host_tensors_are_refused(fp8):
         lambda: fp8.fp8_kv_decode_attention(torch.zeros(8, 128, dtype=torch.bfloat16),
                                             torch.zeros(1, 128, 128, dtype=torch.uint8), torch.ones(1, 1),
                                             torch.zeros(1, 128, 128, dtype=torch.uint8), torch.ones(1, 1), 0.1),
+        lambda: fp8.fp8_kv_decode_attention_noalloc(torch.zeros(8, 128, dtype=torch.bfloat16),
+                                                    torch.zeros(1, 128, 128, dtype=torch.uint8), torch.ones(1, 1),
+                                                    torch.zeros(1, 128, 128, dtype=torch.uint8), torch.ones(1, 1), 0.1,
+                                                    torch.zeros(8, 128)),
     ]
     for c in calls:
         with pytest.raises(ValueError):
