@@ -86,45 +86,3 @@ def bf16_round_f32(y32: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 (nearest even) via the oracle's rounding, returned as fp32 values."""
     return quant.bf16_bits_to_f32(quant.f32_to_bf16_bits(np.asarray(y32, dtype=np.float32)))
 
-
-# Unit roundoff of fp32 (round to nearest).
-U32 = 2.0 ** -24
-
-
-def fp32_accumulation_bound(k: int) -> float:
-    """Bound on |y32 - y| / T for the block GEMM's fp32 output, y the exact
-    product and T = |A_hat| . |W_hat|^T, for inner dimension k (nb = k / 128
-    scale blocks). First-order terms:
-
-    * each block product P_j is a sum of 128 exact FP8 x FP8 products formed
-      in the matrix unit; any fp32 summation order with at most one ulp of
-      error per addition (round to nearest or truncation) gives
-      |P~_j - P_j| <= 127 * 2^-23 * sum |products| = 254 u sum |products|;
-    * the scale product fl32(s_a * s_w) adds u relative;
-    * the promotion acc = fma(P~_j, c_j, acc) over nb blocks adds at most
-      nb u relative to sum_j |c_j P~_j| (the decode kernel sums its four
-      split-K partials in three more fp32 additions, within the same count
-      since its waves each promote nb / 4 blocks);
-
-    and sum_j |c_j| sum |products_j| = T. So |y32 - y| <= (255 + nb) u T; one
-    u more covers the second-order terms and the oracle's own fp64 rounding
-    (below k 2^-53 T)."""
-    nb = max(1, k // 128)
-    return (256 + nb) * U32
-
-
-def check_fp32_accumulation(y32, y64, t, k: int, what=""):
-    """|y32 - y64| <= fp32_accumulation_bound(k) * T per element; returns the
-    largest |y32 - y64| / T (0 where T is 0, where y32 must equal y64)."""
-    y32 = np.asarray(y32, dtype=np.float64)
-    err = np.abs(y32 - y64)
-    bound = fp32_accumulation_bound(k)
-    bad = np.argwhere(err > bound * t)
-    if bad.size:
-        idx = tuple(bad[0])
-        raise AssertionError(f"{what}: {len(bad)} fp32 outputs beyond {bound:.3e} T; first at {idx}: "
-                             f"gpu {y32[idx]!r} oracle {y64[idx]!r} T {t[idx]!r} "
-                             f"(err/T {err[idx] / t[idx] if t[idx] else float('inf'):.3e})")
-    with np.errstate(divide="ignore", invalid="ignore"):
-        ratio = np.where(t > 0, err / np.where(t > 0, t, 1.0), 0.0)
-    return float(ratio.max()) if ratio.size else 0.0

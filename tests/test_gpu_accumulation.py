@@ -1,98 +1,215 @@
-"""How the block GEMM sums a 128-deep K block: crafted dot products.
+"""How the FP8 matrix instruction sums a 128-deep K block: each rule of the
+model in tests/mfma_model.py, pinned by crafted dot products.
 
-[MIXED] charles2530.github.io, "量化：FP8 与混合精度推理", section "混合精度才是生产形态":
-low-precision products do not mean low-precision sums; the FP8 x FP8
-products are exact and their sum must be kept in a wider type. Here the
-GPU's fp32-mode output for one 128-wide K block with unit scales is the
-matrix unit's block sum itself (promotion multiplies it by exactly 1 and adds
-it to 0), so each crafted row pair shows how that sum is formed:
+[MIXED] charles2530.github.io, "量化：FP8 与混合精度推理", section
+"混合精度才是生产形态": low-precision products do not mean low-precision sums.
+With K = 128 and unit scales, the GEMM's fp32 output is the instruction's
+block sum itself (the promotion multiplies it by exactly 1 and adds it to 0),
+so each output below shows that sum directly. M = 16 runs the decode kernel,
+M > 64 the prefill kernel; both issue the same instruction, with different
+operand layouts (the tests address real k, which both layouts keep in runs of
+8 within an 8-aligned group).
 
-* sums whose every partial sum is an exact fp32 number (128 x 448^2; +-448^2
-  cancelling in any order) must come back exact;
-* one 448^2 term next to 127 terms of 2^-7 (exact sum 200704 + 127/128, which
-  needs 25 significant bits) and a cancelling +-448^2 pair next to 2^-18
-  terms show whether small terms are lost behind a large one;
-* every result must lie within the fp32-accumulation bound
-  gpu_helpers.fp32_accumulation_bound(128) * T of the exact sum, T being the
-  sum of the terms' magnitudes.
-
-Both kernels are covered: M = 16 runs the decode kernel, M = 80 the prefill
-kernel. The oracle's fp64 sums of these products are exact (multiples of
-2^-18 below 2^25).
+Pinned:
+* grouping: a small product next to a large one is truncated exactly when
+  both lie in the same group of 8 consecutive k;
+* resolution: next to 448 * 1 (exponent sum 8) every other code v becomes
+  trunc(v / 2^-5) * 2^-5, toward zero for both signs, i.e. 13 fraction bits
+  below the group's largest exponent sum;
+* exponent sums, not values, set that resolution: 448 * 448 (exponent sum
+  16, value 1.53 * 2^17) next to seven products of 28 loses 7 * (28 mod 8);
+* subnormal codes enter with exponent 1 - bias, in both formats (rows that
+  mix every subnormal code with every small product match the model bit for
+  bit);
+* random blocks in every format pair stay within the group-combination bound
+  of the model (36 * 2^-24 of the block's sum of |products|);
+* sums whose every partial sum is an exact fp32 number come back exact.
 """
 
 import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import check_fp32_accumulation, fp32_accumulation_bound
-from oracle import e4m3, gemm as ogemm
+from mfma_model import U32, exponents, group_sums
+from oracle import e4m3, e5m2, gemm as ogemm
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
-C448, CM448, C2M3, C2M4, C2M9, C1 = 0x7E, 0xFE, 0x20, 0x18, 0x01, 0x38
-assert e4m3.decode(np.array([C448, CM448, C2M3, C2M4, C2M9, C1])).tolist() == [448, -448, 2 ** -3, 2 ** -4,
-                                                                               2 ** -9, 1]
+C448, CM448, C1 = 0x7E, 0xFE, 0x38
+assert e4m3.decode(np.array([C448, CM448, C1])).tolist() == [448, -448, 1]
 
 
-def _crafted():
-    """(name, a codes [128], w codes [128]) per case."""
+def _block(gpu_lib, qa, qw, fa="e4m3", fw="e4m3"):
+    """fp32 C = A . W^T for K = 128 with unit scales (one block)."""
+    M, N = qa.shape[0], qw.shape[0]
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    return gpu_lib.fp8_block_gemm(t(qa), t(np.ones((M, 1), np.float32)), "group_1x128", t(qw),
+                                  t(np.ones((N // 128, 1), np.float32)), "block_128x128", out_dtype=torch.float32,
+                                  fmt_a=fa, fmt_w=fw).cpu().numpy()
+
+
+def _dec(c, fmt="e4m3"):
+    return (e4m3 if fmt == "e4m3" else e5m2).decode(np.asarray(c, np.uint8))
+
+
+@pytest.mark.parametrize("kernel", ["decode", "prefill"])
+def test_products_are_aligned_in_groups_of_eight(gpu_lib, kernel):
+    """448 at k = i and 2^-9 at k = j (W = 1): the small product vanishes
+    exactly when i // 8 == j // 8."""
+    big_at = range(128) if kernel == "prefill" else (0, 5, 7, 8, 63, 64, 100, 127)
+    pairs = [(i, j) for i in big_at for j in range(128) if j != i]
+    qw = np.full((128, 128), C1, np.uint8)
+    lost = np.zeros(len(pairs), bool)
+    step = len(pairs) if kernel == "prefill" else 64
+    for c0 in range(0, len(pairs), step):
+        chunk = pairs[c0:c0 + step]
+        qa = np.zeros((max(len(chunk), 65) if kernel == "prefill" else len(chunk), 128), np.uint8)
+        for r, (i, j) in enumerate(chunk):
+            qa[r, i], qa[r, j] = C448, 0x01
+        y = _block(gpu_lib, qa, qw)[:len(chunk), 0]
+        assert np.all((y == 448.0) | (y == 448.0 + 2.0 ** -9)), "unexpected block sum"
+        lost[c0:c0 + len(chunk)] = y == 448.0
+    same = np.array([i // 8 == j // 8 for i, j in pairs])
+    bad = np.nonzero(lost != same)[0]
+    assert bad.size == 0, f"{len(bad)} pairs break the groups of 8; first {pairs[bad[0]]} lost={lost[bad[0]]}"
+
+
+@pytest.mark.parametrize("M", [16, 260])
+def test_every_code_next_to_448(gpu_lib, M):
+    """448 * 1 at k = 0 and v * 1 at k = 1 for every finite E4M3 code v (both
+    signs): the block sum is 448 + trunc(v / 2^-5) * 2^-5 exactly."""
+    codes = e4m3.finite_codes()
+    codes = codes[codes != 0]
+    qw = np.zeros((128, 128), np.uint8)
+    qw[0, :2] = C1
+    got = []
+    for c0 in range(0, codes.size, M):
+        cs = codes[c0:c0 + M]
+        qa = np.zeros((M, 128), np.uint8)
+        qa[:, 0] = C448
+        qa[:len(cs), 1] = cs
+        got.append(_block(gpu_lib, qa, qw)[:len(cs), 0])
+    got = np.concatenate(got)
+    v = _dec(codes)
+    expect = 448.0 + np.trunc(v / 2.0 ** -5) * 2.0 ** -5
+    bad = np.nonzero(got != expect)[0]
+    assert bad.size == 0, f"code 0x{codes[bad[0]]:02x}: gpu {got[bad[0]]!r}, expected {expect[bad[0]]!r}"
+
+
+def test_exponent_sum_sets_the_resolution(gpu_lib):
+    """A = 448 everywhere; W row 0 = (448, 2^-4 x 127), so the block holds
+    448^2 = 3.0625 * 2^16 at k = 0 and 127 products of 28. Group 0's
+    resolution is 2^(16 - 13) = 8 (the exponent sum, not the value's 2^17),
+    so its seven 28s become 24 each: the sum is 204260 - 28. W row 1 moves
+    the 448 to k = 8: then group 1 loses 28 likewise."""
+    qa = np.full((80, 128), C448, np.uint8)
+    qw = np.zeros((128, 128), np.uint8)
+    qw[0] = 0x18
+    qw[0, 0] = C448
+    qw[1] = 0x18
+    qw[1, 8] = C448
+    assert _dec(0x18) == 2.0 ** -4
+    y = _block(gpu_lib, qa, qw)
+    assert y[0, 0] == 204232.0 and y[0, 1] == 204232.0, (y[0, 0], y[0, 1])
+
+
+@pytest.mark.parametrize("fmt_w", ["e4m3", "e5m2"])
+def test_subnormal_codes_use_exponent_one_minus_bias(gpu_lib, fmt_w):
+    """448 * w0 at k = 0 for subnormal and small normal codes w0 of W's
+    format, next to every E4M3 code v times W's smallest subnormal at k = 1;
+    and (E4M3) both operands subnormal at k = 0. Every block sum equals the
+    model's (group exponent from the exponent fields, subnormals at 1 - bias)
+    bit for bit."""
+    small = np.arange(1, 127, dtype=np.uint8)
+    w0s = list(range(1, 8)) + [0x08, 0x10] if fmt_w == "e4m3" else [0x01, 0x02, 0x03, 0x04, 0x05]
+    qa = np.zeros((126, 128), np.uint8)
+    qa[:, 0], qa[:, 1] = C448, small
+    qw = np.zeros((128, 128), np.uint8)
+    for n, w0 in enumerate(w0s):
+        qw[n, 0], qw[n, 1] = w0, 0x01
+    y = _block(gpu_lib, qa, qw, "e4m3", fmt_w)[:, :len(w0s)]
+    model = np.stack([group_sums(qa[m], qw[:len(w0s)], "e4m3", fmt_w)[0].sum(axis=1) for m in range(126)])
+    bad = np.argwhere(y != np.float32(model))
+    assert bad.size == 0, f"first at small code 0x{small[bad[0][0]]:02x}, w0 0x{w0s[bad[0][1]]:02x}: gpu {y[tuple(bad[0])]!r} model {model[tuple(bad[0])]!r}"
+    if fmt_w == "e4m3":
+        for a0 in range(1, 8):
+            qa2 = np.zeros((126, 128), np.uint8)
+            qa2[:, 0], qa2[:, 1] = a0, small
+            qw2 = np.zeros((128, 128), np.uint8)
+            qw2[:7, 0] = np.arange(1, 8)
+            qw2[:7, 1] = 0x01
+            y2 = _block(gpu_lib, qa2, qw2)[:, :7]
+            m2 = np.stack([group_sums(qa2[m], qw2[:7])[0].sum(axis=1) for m in range(126)])
+            assert np.array_equal(y2, np.float32(m2)), f"both subnormal, a0 = 0x{a0:02x}"
+    # the exponent rule itself
+    assert exponents(np.array([0x01, 0x07, 0x08, 0x38, 0x7E]), "e4m3").tolist() == [-6, -6, -6, 0, 8]
+    assert exponents(np.array([0x01, 0x03, 0x04, 0x3C]), "e5m2").tolist() == [-14, -14, -14, 0]
+
+
+def _finite(rng, shape, fmt):
+    c = rng.integers(0, 256, size=shape)
+    if fmt == "e4m3":
+        c = np.where((c & 0x7F) == 0x7F, c ^ 1, c)
+    else:
+        c = np.where((c & 0x7C) == 0x7C, c & 0x83, c)
+    return c.astype(np.uint8)
+
+
+@pytest.mark.parametrize("fa,fw", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2")])
+@pytest.mark.parametrize("M", [64, 320])
+def test_random_blocks_within_the_combination_bound(gpu_lib, fa, fw, M):
+    """Uniformly random finite codes, one block: |y - sum of the model's
+    group sums| <= 36 * 2^-24 * sum |products|, for every output."""
+    rng = np.random.default_rng(900 + M + 7 * len(fa + fw))
+    qa, qw = _finite(rng, (M, 128), fa), _finite(rng, (128, 128), fw)
+    y = _block(gpu_lib, qa, qw, fa, fw).astype(np.float64)
+    worst = 0.0
+    for m in range(M):
+        s, t = group_sums(qa[m], qw, fa, fw)
+        err, tt = np.abs(y[m] - s.sum(axis=1)), t.sum(axis=1)
+        assert np.all(err <= 36 * U32 * tt), f"row {m}: {(err / tt).max():.3e} of sum|p|"
+        worst = max(worst, float((err / np.where(tt > 0, tt, 1)).max()))
+    print(f"{fa} x {fw}, M={M}: max |y - model| / sum|p| = {worst:.3e} ({worst / U32:.2f} x 2^-24)")
+
+
+def test_exact_sums_and_crafted_cases(gpu_lib):
+    """Sums whose every partial sum is exact in fp32 come back exact; the
+    crafted cases (one +-448^2 among tiny terms, cancellations) meet the
+    model within its bound and are printed against the exact sum."""
+    big, nbig, small7, small18 = (C448, C448), (CM448, C448), (0x20, 0x18), (0x01, 0x01)
     cases = []
 
-    def pair(name, terms):
-        a = np.zeros(128, np.uint8)
-        w = np.zeros(128, np.uint8)
+    def case(name, terms):
+        a, w = np.zeros(128, np.uint8), np.zeros(128, np.uint8)
         for k, (ca, cw) in terms.items():
             a[k], w[k] = ca, cw
         cases.append((name, a, w))
 
-    big, nbig, small7, small18 = (C448, C448), (CM448, C448), (C2M3, C2M4), (C2M9, C2M9)
-    pair("128 x 448^2", {k: big for k in range(128)})
+    case("128 x 448^2", {k: big for k in range(128)})
+    case("alternating +-448^2", {k: (big if k % 2 == 0 else nbig) for k in range(128)})
+    case("64 x +448^2 then 64 x -448^2", {k: (big if k < 64 else nbig) for k in range(128)})
     for pos in (0, 64, 127):
-        pair(f"448^2 at k={pos} + 127 x 2^-7", {k: (big if k == pos else small7) for k in range(128)})
-    pair("+448^2 k=0, -448^2 k=127, 126 x 2^-18",
+        case(f"448^2 at k={pos} + 127 x 2^-7", {k: (big if k == pos else small7) for k in range(128)})
+    case("+448^2 k=0, -448^2 k=127, 126 x 2^-18",
          {k: (big if k == 0 else nbig if k == 127 else small18) for k in range(128)})
-    pair("+448^2 k=0, -448^2 k=1, 126 x 2^-18",
-         {k: (big if k == 0 else nbig if k == 1 else small18) for k in range(128)})
-    pair("alternating +-448^2", {k: (big if k % 2 == 0 else nbig) for k in range(128)})
-    pair("64 x +448^2 then 64 x -448^2", {k: (big if k < 64 else nbig) for k in range(128)})
-    pair("-448^2 at k=5 + 127 x 2^-18", {k: (nbig if k == 5 else small18) for k in range(128)})
-    rng = np.random.default_rng(4242)
-    for r in range(7):
-        c = rng.integers(0, 256, size=(2, 128))
-        c = np.where((c & 0x7F) == 0x7F, c ^ 1, c).astype(np.uint8)
-        cases.append((f"random codes {r}", c[0], c[1]))
-    return cases
-
-
-# cases whose every partial sum, in any order, is an exact fp32 number
-EXACT_IN_ANY_ORDER = ("128 x 448^2", "alternating +-448^2", "64 x +448^2 then 64 x -448^2")
-
-
-@pytest.mark.parametrize("M", [16, 80])
-def test_block_sums_of_crafted_dot_products(gpu_lib, M):
-    cases = _crafted()
-    n = len(cases)
-    assert n <= 16
-    qa = np.zeros((M, 128), np.uint8)
+    case("+448^2 k=0, -448^2 k=1, 126 x 2^-18", {k: (big if k == 0 else nbig if k == 1 else small18) for k in range(128)})
+    case("-448^2 at k=5 + 127 x 2^-18", {k: (nbig if k == 5 else small18) for k in range(128)})
+    qa = np.zeros((80, 128), np.uint8)
     qw = np.zeros((128, 128), np.uint8)
     for i, (_, a, w) in enumerate(cases):
         qa[i], qw[i] = a, w
-    sa = np.ones((M, 1), np.float32)
-    sw = np.ones((1, 1), np.float32)
-    t = lambda x: torch.from_numpy(x).to(DEV)
-    y32 = gpu_lib.fp8_block_gemm(t(qa), t(sa), "group_1x128", t(qw), t(sw), "block_128x128",
-                                 out_dtype=torch.float32).cpu().numpy()
-    y64, tt = ogemm.block_gemm(qa, sa, "group_1x128", qw, sw, "block_128x128")
-    # the whole output (crafted rows against every weight row) within the bound
-    worst = check_fp32_accumulation(y32, y64, tt, 128, what=f"M={M}")
+    y = _block(gpu_lib, qa, qw)
+    y64, _ = ogemm.block_gemm(qa, np.ones((80, 1), np.float32), "group_1x128", qw, np.ones((1, 1), np.float32),
+                              "block_128x128")
     lines = []
-    for i, (name, _, _) in enumerate(cases):
-        got, exact, mag = float(y32[i, i]), float(y64[i, i]), float(tt[i, i])
-        if name in EXACT_IN_ANY_ORDER:
+    for i, (name, a, w) in enumerate(cases):
+        s, t = group_sums(a, w[None, :])
+        model, mag = float(s.sum()), float(t.sum())
+        got, exact = float(y[i, i]), float(y64[i, i])
+        if i < 3:
             assert got == exact, f"{name}: gpu {got!r}, exact {exact!r}"
-        lines.append(f"  {name:40s} gpu {got!r:>22} exact {exact!r:>22} rne32(exact) {float(np.float32(exact))!r:>14}"
-                     f" err/T {abs(got - exact) / mag if mag else 0.0:.2e}")
-    print(f"M={M} ({'decode' if M <= 64 else 'prefill'} kernel), bound {fp32_accumulation_bound(128):.2e} T, "
-          f"max err/T {worst:.2e}\n" + "\n".join(lines))
+        assert abs(got - model) <= 36 * U32 * mag, f"{name}: gpu {got!r}, model {model!r}"
+        lines.append(f"  {name:40s} gpu {got!r:>20} model {model!r:>20} exact {exact!r:>20} "
+                     f"|gpu-exact|/T {abs(got - exact) / mag if mag else 0.0:.2e}")
+    print("\n".join(lines))
