@@ -1,10 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the W8A8 FP8 hot path on one MI355X (gfx950).
 
-Workload (one "step"): the Llama-3-8B MLP up/gate prefill shape, M = 4096
-tokens, K = 4096, N = 14336:
+Workload (one "step"): the Llama-3-70B fused QKV projection prefill, M = 8192
+tokens, K = 8192, N = 10240 ((64 + 2 x 8) heads x 128), the largest
+configuration:
 
-  1. dynamic activation quantization of a bf16 [4096, 4096] tensor with one
+  1. dynamic activation quantization of a bf16 [8192, 8192] tensor with one
      scale per 1 x 128 token group (fp8_quantize, K-block-major scales);
   2. the block-scaled FP8 GEMM against E4M3 weights with 128 x 128 block
      scales, fp32 accumulation, bf16 output (fp8_block_gemm).
@@ -12,19 +13,22 @@ tokens, K = 4096, N = 14336:
 The weights are quantized once beforehand (offline, as the method prescribes)
 and that pass is timed separately. Inputs are seeded synthetic tensors of the
 workload's shapes and value structure (synth_inputs), resident in HBM before
-timing starts; activation buffers are rotated through 11 copies (> 256 MB
-Infinity Cache) so the quantize pass reads HBM.
+timing starts; activation buffers are rotated through 3 copies (more than the
+256 MB Infinity Cache) so the quantize pass reads HBM.
 
 Printed: one JSON line. ``value`` is the step's throughput in TFLOP/s
 (2 M N K per step over the step time, quantize included); ``roofline`` is the
-GEMM kernel's achieved TFLOP/s against the dense FP8 MFMA peak, measured with
-HIP events on the launch stream; ``passes`` lists every pass of the path with
-its own time and GB/s or TFLOP/s (the KV-cache passes at [8, 131072, 128] and
-the decode-shaped GEMM 16 x 28672 x 8192 on row-major and on decode-packed
-weights included); ``clocks`` gives the
-shader and memory clock levels the driver reported while the untimed settle
-phase ran the step; ``cpu_baseline`` times the CPU oracle on a bounded sample
-of the same step.
+GEMM kernel's achieved TFLOP/s against the dense FP8 MFMA peak, from HIP event
+pairs around each GEMM launch of the timed steps on the launch stream;
+``passes`` lists the other passes of every configuration with their own time
+and GB/s or TFLOP/s: the 4096 x 14336 x 4096 prefill GEMM and its variants,
+the activation quantizers (1x128, per tensor, static, MX), the offline weight
+passes, the per-tensor 64 x 512 x 512 calls in microseconds, the KV-cache
+passes and decode attention at [8, 131072, 128], and the decode-shaped GEMM
+16 x 28672 x 8192 on row-major and on decode-packed weights; ``clocks`` gives
+the shader and memory clock levels the driver reported while the untimed
+settle phase ran the step; ``cpu_baseline`` times the CPU oracle on the same
+step.
 """
 
 import argparse
@@ -49,9 +53,12 @@ def parse():
                     help="seconds of untimed steps run first, so the GPU clock has left its idle state")
     ap.add_argument("--no-secondary", action="store_true", help="skip the KV and decode passes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["gemm", "quant", "kv", "decode", "mx", "copy"], default=None,
-                    help="time one pass only (for profiling runs); 'copy' times a plain 512 MB "
-                         "device copy, the calibration kernel for the HBM byte counters")
+    ap.add_argument("--only", choices=["gemm", "quant", "prefill2", "mx", "small", "kv", "decode", "copy"],
+                    default=None,
+                    help="time one group of passes only (for profiling runs): 'gemm' the timed step's "
+                         "GEMM, 'quant' the quantizers, 'prefill2' the 4096 x 14336 x 4096 GEMMs, 'small' "
+                         "the per-tensor 64 x 512 x 512 calls; 'copy' times a plain 512 MB device copy, the "
+                         "calibration kernel for the HBM byte counters")
     return ap.parse_args()
 
 
@@ -94,16 +101,16 @@ class Timer:
         return mean
 
 
-# HBM bytes per launch of the prefill GEMM kernel (M = 4096, N = 14336, K = 4096),
-# read from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) and scaled by
-# what the same counters read for a plain device copy of known size (FETCH_SIZE
-# x 2.0, WRITE_SIZE x 1.0). Valid only for the kernel source they were taken on:
-# the key is the SHA-256 of the GEMM source files' code (comments and blank
-# lines removed); any other code gives null.
+# HBM bytes per launch of the step's GEMM kernel (M = 8192, N = 10240,
+# K = 8192), read from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+# and scaled by what the same counters read for a plain device copy of known
+# size (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0). Valid only for the kernel source
+# they were taken on: the key is the SHA-256 of the GEMM source files' code
+# (comments and blank lines removed); any other code gives null.
 GEMM_COUNTERS = {
-    "sources_sha256": "6dc4a46f3a87d82f1f13153f63bd6762dbba6fea673a0708aaaf5e7b66778ca5",
-    "fetch_kib": 192721.0,
-    "write_kib": 114726.9,
+    "sources_sha256": None,
+    "fetch_kib": None,
+    "write_kib": None,
 }
 FETCH_FACTOR = 2.0
 WRITE_FACTOR = 1.0
@@ -230,26 +237,26 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     timer = Timer(torch)
-    c = syn.CONFIGS[2]
-    M, N, K = c["M"], c["N"], c["K"]
     if args.only == "copy":
         copy_calibration(torch, timer, dev)
         return
+    c = syn.CONFIGS[4]
+    M, N, K = c["M"], c["N"], c["K"]
     print(f"# bench: {c['workload']} on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
 
-    # ---- inputs resident in HBM -------------------------------------------
-    a_host = syn.activations(2)
-    w = syn.weights(2).to(dev)
-    nsets = 11
+    # ---- the step's inputs, resident in HBM ---------------------------------
+    # 3 rotating activation sets of 134 MB bf16 + 67 MB codes: more than the
+    # 256 MB Infinity Cache, so the quantize pass reads HBM
+    a_host = syn.activations(4)
+    w = syn.weights(4).to(dev)
+    nsets = 3
     a_sets = [a_host.to(dev) for _ in range(nsets)]
     qa_sets = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(nsets)]
     sa_sets = [torch.empty((K // 128, M), dtype=torch.float32, device=dev).t() for _ in range(nsets)]
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     qw = torch.empty((N, K), dtype=torch.uint8, device=dev)
     sw = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
-
-    # the weight-quantization pass rotates 3 copies of the 117 MB weights, so
-    # that its input comes from HBM rather than the 256 MB Infinity Cache
+    # the offline weight pass rotates 3 copies of the 168 MB weights
     w_sets = [w, w.clone(), w.clone()]
 
     def quant_w(i):
@@ -277,39 +284,146 @@ def main():
     clocks.stop()
 
     # ---- the timed step: warmup, then exactly `steps` steps ---------------
-    # Timed first, straight after the settle phase: after a stretch of
-    # lighter passes the power controller lets the clock rise and then cuts it
-    # back hard once the GEMM resumes, which slowed the first GEMMs that
-    # followed the other passes by up to 25%.
-    t_step = None
-    if args.only is None:
+    # Timed first, straight after the settle phase (after a stretch of lighter
+    # passes the power controller lets the clock rise and then cuts it back
+    # hard once the GEMM resumes). An event pair around each GEMM launch, on
+    # the launch stream, gives the GEMM kernel's own duration inside the timed
+    # region, from which the roofline is computed.
+    flops = 2.0 * M * N * K
+    t_step = t_gemm = None
+    if args.only in (None, "gemm"):
         for i in range(args.warmup):
             step(i)
         torch.cuda.synchronize()
         st = torch.cuda.current_stream()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        e0, e1 = ev(), ev()
+        g_ev = [(ev(), ev()) for _ in range(args.steps)]
         wall0 = time.perf_counter()
         e0.record(st)
         for i in range(args.steps):
-            step(i)
+            quant_a(i)
+            g_ev[i][0].record(st)
+            gemm(i)
+            g_ev[i][1].record(st)
         e1.record(st)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
         t_step = e0.elapsed_time(e1) * 1e-3 / args.steps
-        print(f"# timed {args.steps} steps: {t_step * 1e6:.1f} us/step (wall {wall:.3f} s)",
-              file=sys.stderr, flush=True)
+        g_us = sorted(a.elapsed_time(b) * 1e3 for a, b in g_ev)
+        t_gemm = sum(g_us) / len(g_us) * 1e-6
+        timer.stats["gemm_8192x10240x8192_in_step"] = {"median_us": g_us[len(g_us) // 2], "min_us": g_us[0],
+                                                       "p90_us": g_us[min(len(g_us) - 1, (9 * len(g_us)) // 10)],
+                                                       "calls": len(g_us)}
+        print(f"# timed {args.steps} steps: {t_step * 1e6:.1f} us/step, GEMM {t_gemm * 1e6:.1f} us "
+              f"(wall {wall:.3f} s)", file=sys.stderr, flush=True)
 
-    flops = 2.0 * M * N * K
     passes = {}
-    if args.only in (None, "gemm"):
-        t_gemm = timer.run(gemm, max(args.steps, 10), warmup=args.warmup, name="gemm")
-        passes["gemm"] = {"us": t_gemm * 1e6, "TFLOP/s": flops / t_gemm / 1e12,
-                          "frac_fp8_peak": flops / t_gemm / 1e12 / PEAK_FP8_TFLOPS}
-    if args.only is None and not args.no_secondary:
-        # The GEMM's output quantized for the next layer (1 x 128 groups along
-        # N): fused into the GEMM epilogue, against the GEMM's bf16 output
-        # followed by the stand-alone quantizer over it.
+    if t_gemm is not None:
+        passes["gemm_8192x10240x8192"] = {"us": t_gemm * 1e6, "TFLOP/s": flops / t_gemm / 1e12,
+                                          "frac_fp8_peak": flops / t_gemm / 1e12 / PEAK_FP8_TFLOPS,
+                                          "timing": "mean of the event pairs around each GEMM of the timed steps"}
+    if args.only in (None, "quant"):
+        t_qa = timer.run(quant_a, 30, warmup=args.warmup, name="act_quant_1x128_8192x8192")
+        bytes_qa = M * K * 2 + M * K + M * (K // 128) * 4
+        passes["act_quant_1x128_8192x8192"] = {"us": t_qa * 1e6, "GB/s": bytes_qa / t_qa / 1e9,
+                                               "frac_hbm": bytes_qa / t_qa / 1e9 / PEAK_HBM_GBPS}
+        t_qw = timer.run(quant_w, 12, warmup=3, name="weight_quant_128x128_offline_10240x8192")
+        bytes_qw = N * K * 2 + N * K + (N // 128) * (K // 128) * 4
+        passes["weight_quant_128x128_offline_10240x8192"] = {
+            "us": t_qw * 1e6, "GB/s": bytes_qw / t_qw / 1e9, "frac_hbm": bytes_qw / t_qw / 1e9 / PEAK_HBM_GBPS}
+    ceiling = None
+    if args.only is None:
+        ceiling = mfma_ceiling(torch, dev, qa_sets[0], qw)
+        if ceiling and t_gemm:
+            ceiling["gemm_frac_of_mfma_plus_4_fma"] = flops / t_gemm / 1e12 / ceiling["mfma_plus_4_fma"]
+    del a_sets, qa_sets, sa_sets, w_sets, w, out
+
+    if not args.no_secondary and args.only in (None, "prefill2", "mx", "quant"):
+        passes.update(passes_config2(args, torch, syn, fp8, timer, dev))
+    if not args.no_secondary and args.only in (None, "small"):
+        passes.update(passes_config1(args, torch, syn, fp8, timer, dev))
+    if not args.no_secondary and args.only in (None, "kv"):
+        passes.update(passes_kv(args, torch, syn, fp8, timer, dev))
+    if not args.no_secondary and args.only in (None, "decode"):
+        passes.update(passes_decode(args, torch, syn, fp8, timer, dev))
+
+    # ---- CPU oracle on the same step ------------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline and args.only is None:
+        cpu = cpu_baseline(syn, qw.cpu().numpy(), sw.cpu().numpy(), M, N, K)
+
+    result = {
+        "metric": "block-scaled FP8 GEMM TFLOP/s (%FP8 MFMA peak) + quantize/KV GB/s (%HBM)",
+        "value": (flops / t_step / 1e12) if t_step else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": (t_step * 1e3) if t_step else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3-mfma/fp32-acc/bf16-out",
+        "data": "synthetic (seeded Llama-3-70B QKV-shaped activations with outlier channels, N(0,0.02) weights)",
+        "config": {"workload": c["workload"], "M": M, "N": N, "K": K,
+                   "act_scales": "1x128 dynamic", "weight_scales": "128x128", "parallelism": "single-gpu"},
+        "roofline": None if t_gemm is None else {
+            "kernel": "k_gemm_fp8_block (fp8_block_gemm), 8192 x 10240 x 8192",
+            "bound": "mfma",
+            "achieved": flops / t_gemm / 1e12,
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": flops / t_gemm / 1e12 / PEAK_FP8_TFLOPS,
+            "traffic": gemm_traffic_bytes(),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
+            "algorithmic_bytes": float(M * K + N * K + 2 * M * N + 4 * (M * (K // 128) + (N // 128) * (K // 128))),
+        },
+        "passes": passes,
+        "mfma_ceiling": ceiling,
+        "clocks": clocks.summary(),
+        "per_call": timer.stats,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def passes_config2(args, torch, syn, fp8, timer, dev):
+    """Llama-3-8B MLP up/gate prefill, 4096 x 14336 x 4096: the GEMM and its
+    variants (output quantized in the epilogue, E5M2 activations, MX operands),
+    and the activation quantizers at [4096, 4096] (1x128, per tensor, static
+    with the amax recorded), plus the offline weight pass."""
+    c = syn.CONFIGS[2]
+    M, N, K = c["M"], c["N"], c["K"]
+    flops = 2.0 * M * N * K
+    res = {}
+    a_host = syn.activations(2)
+    w = syn.weights(2).to(dev)
+    nsets = 11   # 11 x 50.9 MB: more than the Infinity Cache
+    a_sets = [a_host.to(dev) for _ in range(nsets)]
+    qa_sets = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    sa_sets = [torch.empty((K // 128, M), dtype=torch.float32, device=dev).t() for _ in range(nsets)]
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    qw, sw = fp8.fp8_quantize(w, "block_128x128")
+    w_sets = [w, w.clone(), w.clone()]
+
+    def quant_a(i):
+        j = i % nsets
+        fp8.fp8_quantize(a_sets[j], "group_1x128", out=qa_sets[j], scales=sa_sets[j])
+
+    def gemm(i):
+        j = i % nsets
+        fp8.fp8_block_gemm(qa_sets[j], sa_sets[j], "group_1x128", qw, sw, "block_128x128", out=out)
+
+    for i in range(nsets):
+        quant_a(i)
+    if args.only in (None, "prefill2"):
+        t_g = timer.run(gemm, 30, warmup=args.warmup, name="gemm_4096x14336x4096")
+        res["gemm_4096x14336x4096"] = {"us": t_g * 1e6, "TFLOP/s": flops / t_g / 1e12,
+                                       "frac_fp8_peak": flops / t_g / 1e12 / PEAK_FP8_TFLOPS}
+        # the GEMM's output quantized for the next layer (1 x 128 groups along
+        # N) in the GEMM epilogue, against the bf16 GEMM followed by the
+        # stand-alone quantizer over its output
         qc = torch.empty((M, N), dtype=torch.uint8, device=dev)
         scq = torch.empty((N // 128, M), dtype=torch.float32, device=dev).t()
 
@@ -322,15 +436,27 @@ def main():
             gemm(i)
             fp8.fp8_quantize(out, "group_1x128", out=qc, scales=scq)
 
-        t_f = timer.run(fused, max(args.steps, 10), warmup=args.warmup, name="gemm_fused_quant_out")
-        t_u = timer.run(unfused, max(args.steps, 10), warmup=args.warmup, name="gemm_then_quantize_out")
-        passes["gemm_fused_quant_out"] = {"us": t_f * 1e6, "TFLOP/s": flops / t_f / 1e12,
-                                          "frac_fp8_peak": flops / t_f / 1e12 / PEAK_FP8_TFLOPS}
-        passes["gemm_then_quantize_out"] = {"us": t_u * 1e6, "TFLOP/s": flops / t_u / 1e12}
+        t_f = timer.run(fused, 20, warmup=args.warmup, name="gemm_fused_quant_out")
+        t_u = timer.run(unfused, 20, warmup=args.warmup, name="gemm_then_quantize_out")
+        res["gemm_fused_quant_out_4096x14336x4096"] = {"us": t_f * 1e6, "TFLOP/s": flops / t_f / 1e12,
+                                                       "frac_fp8_peak": flops / t_f / 1e12 / PEAK_FP8_TFLOPS}
+        res["gemm_then_quantize_out_4096x14336x4096"] = {"us": t_u * 1e6, "TFLOP/s": flops / t_u / 1e12}
         del qc, scq
-    if args.only in (None, "mx") and not args.no_secondary:
-        # MX operands (E4M3 codes, one power-of-two scale per 32 K elements):
-        # the same step shape, the scales applied inside the scaled MFMA
+        # E5M2 activations (1x128) against the E4M3 weights
+        qa5 = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        sa5 = torch.empty((K // 128, M), dtype=torch.float32, device=dev).t()
+        fp8.fp8_quantize(a_sets[0], "group_1x128", fmt="e5m2", out=qa5, scales=sa5)
+
+        def gemm5(i):
+            fp8.fp8_block_gemm(qa5, sa5, "group_1x128", qw, sw, "block_128x128", out=out, fmt_a="e5m2")
+
+        t5 = timer.run(gemm5, 20, warmup=args.warmup, name="gemm_e5m2_act")
+        res["gemm_e5m2_act_4096x14336x4096"] = {"us": t5 * 1e6, "TFLOP/s": flops / t5 / 1e12,
+                                                "frac_fp8_peak": flops / t5 / 1e12 / PEAK_FP8_TFLOPS}
+        del qa5, sa5
+    if args.only in (None, "mx", "prefill2"):
+        # MX operands (E4M3 codes, one power-of-two scale per 32 K elements),
+        # the scales applied inside the scaled MFMA
         qamx = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(nsets)]
         samx = [torch.empty((M, K // 32), dtype=torch.uint8, device=dev) for _ in range(nsets)]
         qwmx, swmx = fp8.fp8_quantize_mx(w)
@@ -345,213 +471,210 @@ def main():
 
         for i in range(nsets):
             quant_mx(i)
-        t_qmx = timer.run(quant_mx, max(args.steps, 22), warmup=args.warmup, name="act_quant_mx32")
-        t_gmx = timer.run(gemm_mx, max(args.steps, 10), warmup=args.warmup, name="gemm_mx32")
+        t_qmx = timer.run(quant_mx, 33, warmup=args.warmup, name="act_quant_mx32")
+        t_gmx = timer.run(gemm_mx, 20, warmup=args.warmup, name="gemm_mx32")
         bytes_qmx = M * K * 2 + M * K + M * (K // 32)
-        passes["act_quant_mx32"] = {"us": t_qmx * 1e6, "GB/s": bytes_qmx / t_qmx / 1e9,
-                                    "frac_hbm": bytes_qmx / t_qmx / 1e9 / PEAK_HBM_GBPS}
-        passes["gemm_mx32"] = {"us": t_gmx * 1e6, "TFLOP/s": flops / t_gmx / 1e12,
-                               "frac_fp8_peak": flops / t_gmx / 1e12 / PEAK_FP8_TFLOPS}
+        res["act_quant_mx32_4096x4096"] = {"us": t_qmx * 1e6, "GB/s": bytes_qmx / t_qmx / 1e9,
+                                           "frac_hbm": bytes_qmx / t_qmx / 1e9 / PEAK_HBM_GBPS}
+        res["gemm_mx32_4096x14336x4096"] = {"us": t_gmx * 1e6, "TFLOP/s": flops / t_gmx / 1e12,
+                                            "frac_fp8_peak": flops / t_gmx / 1e12 / PEAK_FP8_TFLOPS}
         del qamx, samx, qwmx, swmx
-    if args.only is None and not args.no_secondary:
-        # E5M2 activations (1x128) against the E4M3 weights: the same GEMM
-        # kernel with the MFMA's A operand decoded as E5M2
-        qa5 = torch.empty((M, K), dtype=torch.uint8, device=dev)
-        sa5 = torch.empty((K // 128, M), dtype=torch.float32, device=dev).t()
-        fp8.fp8_quantize(a_sets[0], "group_1x128", fmt="e5m2", out=qa5, scales=sa5)
-
-        def gemm5(i):
-            fp8.fp8_block_gemm(qa5, sa5, "group_1x128", qw, sw, "block_128x128", out=out, fmt_a="e5m2")
-
-        t5 = timer.run(gemm5, max(args.steps, 10), warmup=args.warmup, name="gemm_e5m2_act")
-        passes["gemm_e5m2_act"] = {"us": t5 * 1e6, "TFLOP/s": flops / t5 / 1e12,
-                                   "frac_fp8_peak": flops / t5 / 1e12 / PEAK_FP8_TFLOPS}
-        del qa5, sa5
     if args.only in (None, "quant"):
-        t_qa = timer.run(quant_a, max(args.steps, 22), warmup=args.warmup, name="act_quant_1x128")
+        t_qa = timer.run(quant_a, 33, warmup=args.warmup, name="act_quant_1x128_4096x4096")
         bytes_qa = M * K * 2 + M * K + M * (K // 128) * 4
-        passes["act_quant_1x128"] = {"us": t_qa * 1e6, "GB/s": bytes_qa / t_qa / 1e9,
-                                     "frac_hbm": bytes_qa / t_qa / 1e9 / PEAK_HBM_GBPS}
-        if not args.no_secondary:
-            # Per-tensor dynamic scaling: amax pass, then the cast (the tensor
-            # is read twice; algorithmic bytes count it once)
-            s_pt = torch.empty(1, dtype=torch.float32, device=dev)
+        res["act_quant_1x128_4096x4096"] = {"us": t_qa * 1e6, "GB/s": bytes_qa / t_qa / 1e9,
+                                            "frac_hbm": bytes_qa / t_qa / 1e9 / PEAK_HBM_GBPS}
+        # per-tensor dynamic scaling: amax pass, then the cast (the tensor is
+        # read twice; algorithmic bytes count it once)
+        s_pt = torch.empty(1, dtype=torch.float32, device=dev)
 
-            def quant_pt(i):
-                j = i % nsets
-                fp8.fp8_quantize(a_sets[j], "per_tensor", out=qa_sets[j], scales=s_pt)
+        def quant_pt(i):
+            j = i % nsets
+            fp8.fp8_quantize(a_sets[j], "per_tensor", out=qa_sets[j], scales=s_pt)
 
-            t_pt = timer.run(quant_pt, max(args.steps, 22), warmup=args.warmup, name="act_quant_per_tensor")
-            bytes_pt = M * K * 2 + M * K + 4
-            passes["act_quant_per_tensor"] = {"us": t_pt * 1e6, "GB/s": bytes_pt / t_pt / 1e9,
-                                              "frac_hbm": bytes_pt / t_pt / 1e9 / PEAK_HBM_GBPS}
-            # Delayed scaling: the cast under a scale from the amax history,
-            # recording this tensor's amax into the history
-            hist = torch.full((16,), float(a_host.float().abs().max()), dtype=torch.float32, device=dev)
-            s_static = fp8.fp8_scale_from_amax_history(hist)
+        t_pt = timer.run(quant_pt, 33, warmup=args.warmup, name="act_quant_per_tensor_4096x4096")
+        bytes_pt = M * K * 2 + M * K + 4
+        res["act_quant_per_tensor_4096x4096"] = {"us": t_pt * 1e6, "GB/s": bytes_pt / t_pt / 1e9,
+                                                 "frac_hbm": bytes_pt / t_pt / 1e9 / PEAK_HBM_GBPS}
+        # delayed scaling: the cast under a scale from the amax history,
+        # recording this tensor's amax into the history
+        hist = torch.full((16,), float(a_host.float().abs().max()), dtype=torch.float32, device=dev)
+        s_static = fp8.fp8_scale_from_amax_history(hist)
 
-            def quant_static(i):
-                j = i % nsets
-                fp8.fp8_quantize_static(a_sets[j], s_static, record_amax=True, out=qa_sets[j],
-                                        amax=hist[i % 16:i % 16 + 1])
+        def quant_static(i):
+            j = i % nsets
+            fp8.fp8_quantize_static(a_sets[j], s_static, record_amax=True, out=qa_sets[j],
+                                    amax=hist[i % 16:i % 16 + 1])
 
-            t_qs = timer.run(quant_static, max(args.steps, 22), warmup=args.warmup, name="act_quant_static")
-            bytes_qs = M * K * 2 + M * K
-            passes["act_quant_static_amax"] = {"us": t_qs * 1e6, "GB/s": bytes_qs / t_qs / 1e9,
-                                               "frac_hbm": bytes_qs / t_qs / 1e9 / PEAK_HBM_GBPS}
-        t_qw = timer.run(quant_w, 10, warmup=2, name="weight_quant_128x128_offline")
+        t_qs = timer.run(quant_static, 33, warmup=args.warmup, name="act_quant_static_4096x4096")
+        bytes_qs = M * K * 2 + M * K
+        res["act_quant_static_amax_4096x4096"] = {"us": t_qs * 1e6, "GB/s": bytes_qs / t_qs / 1e9,
+                                                  "frac_hbm": bytes_qs / t_qs / 1e9 / PEAK_HBM_GBPS}
+
+        def quant_w(i):
+            fp8.fp8_quantize(w_sets[i % 3], "block_128x128", out=qw, scales=sw)
+
+        t_qw = timer.run(quant_w, 12, warmup=3, name="weight_quant_128x128_offline_14336x4096")
         bytes_qw = N * K * 2 + N * K + (N // 128) * (K // 128) * 4
-        passes["weight_quant_128x128_offline"] = {"us": t_qw * 1e6, "GB/s": bytes_qw / t_qw / 1e9,
-                                                  "frac_hbm": bytes_qw / t_qw / 1e9 / PEAK_HBM_GBPS}
+        res["weight_quant_128x128_offline_14336x4096"] = {
+            "us": t_qw * 1e6, "GB/s": bytes_qw / t_qw / 1e9, "frac_hbm": bytes_qw / t_qw / 1e9 / PEAK_HBM_GBPS}
+    return res
 
-    # ---- secondary passes: KV cache and decode-shaped GEMM ------------------
-    if not args.no_secondary and args.only in (None, "kv"):
-        c5 = syn.CONFIGS[5]
-        kh, vh = syn.kv_pair(5)
-        kd, vd = kh.to(dev), vh.to(dev)
-        del kh, vh
-        H, T, D = c5["heads"], c5["tokens"], c5["head_dim"]
-        qk = torch.empty((H, T, D), dtype=torch.uint8, device=dev)
-        qv = torch.empty_like(qk)
-        sk = torch.empty((H, T // 128), dtype=torch.float32, device=dev)
-        sv = torch.empty_like(sk)
-        ok = torch.empty((H, T, D), dtype=torch.bfloat16, device=dev)
-        ov = torch.empty_like(ok)
-        lib = fp8.load_library()
-        stream = torch.cuda.current_stream().cuda_stream
 
-        n = 2 * H * T * D
-        kv_bytes = n * 2 + n + 2 * H * (T // 128) * 4
-        # E4M3 (the default KV format) and E5M2 (the KV format of the serving
-        # recipe on the pages); same bytes, same kernels up to the conversion
-        for fmt, tag in ((fp8.E4M3, ""), (fp8.E5M2, "_e5m2")):
-            def kvq(i, fmt=fmt):
-                fp8._check(lib.fp8_kv_quantize(kd.data_ptr(), H, T, D, T * D, D, 128, fmt, qk.data_ptr(), sk.data_ptr(), stream))
-                fp8._check(lib.fp8_kv_quantize(vd.data_ptr(), H, T, D, T * D, D, 128, fmt, qv.data_ptr(), sv.data_ptr(), stream))
+def passes_config1(args, torch, syn, fp8, timer, dev):
+    """Per-tensor E4M3 at 64 x 512 x 512: latency-bound, so microseconds per
+    call (median of per-call event pairs) and no roofline claim. The step is
+    the activation quantize (amax pass, scale, cast) then the GEMM; the weight
+    quantize is the offline pass."""
+    c = syn.CONFIGS[1]
+    M, N, K = c["M"], c["N"], c["K"]
+    a = syn.activations(1).to(dev)
+    w = syn.weights(1).to(dev)
+    qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sa = torch.empty(1, dtype=torch.float32, device=dev)
+    qw = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    sw = torch.empty(1, dtype=torch.float32, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
-            def kvd(i, fmt=fmt):
-                fp8._check(lib.fp8_kv_dequantize(qk.data_ptr(), sk.data_ptr(), H, T, D, 128, fmt, ok.data_ptr(), stream))
-                fp8._check(lib.fp8_kv_dequantize(qv.data_ptr(), sv.data_ptr(), H, T, D, 128, fmt, ov.data_ptr(), stream))
+    def qa_call(i):
+        fp8.fp8_quantize(a, "per_tensor", out=qa, scales=sa)
 
-            t_kvq = timer.run(kvq, 20, warmup=3, name="kv_quant_K+V" + tag)
-            t_kvd = timer.run(kvd, 20, warmup=3, name="kv_dequant_K+V" + tag)
-            passes["kv_quant_K+V" + tag] = {"us": t_kvq * 1e6, "GB/s": kv_bytes / t_kvq / 1e9,
-                                            "frac_hbm": kv_bytes / t_kvq / 1e9 / PEAK_HBM_GBPS}
-            passes["kv_dequant_K+V" + tag] = {"us": t_kvd * 1e6, "GB/s": kv_bytes / t_kvd / 1e9,
-                                              "frac_hbm": kv_bytes / t_kvd / 1e9 / PEAK_HBM_GBPS}
-            # decode attention of 64 query heads (8 per kv head) over the codes
-            # just written: algorithmic bytes = both code tensors, their
-            # scales, the bf16 query and output
-            hq = c5["heads_q"]
-            qd = syn.decode_queries(heads_q=hq).to(dev)
-            od = torch.empty((hq, D), dtype=torch.bfloat16, device=dev)
-            ws = torch.empty(lib.fp8_kv_decode_attention_workspace_size(hq, T), dtype=torch.uint8, device=dev)
-            fname = "e5m2" if fmt == fp8.E5M2 else "e4m3"
+    def qw_call(i):
+        fp8.fp8_quantize(w, "per_tensor", out=qw, scales=sw)
 
-            # two copies of the 268 MB cache, alternated: more than the
-            # Infinity Cache, so the codes stream from HBM
-            caches = [(qk, sk, qv, sv), (qk.clone(), sk, qv.clone(), sv)]
+    def gemm(i):
+        fp8.fp8_block_gemm(qa, sa, "per_tensor", qw, sw, "per_tensor", out=out)
 
-            def att(i, fname=fname):
-                ck, cks, cv, cvs = caches[i % 2]
-                fp8.fp8_kv_decode_attention(qd, ck, cks, cv, cvs, 1.0 / 128 ** 0.5, fmt=fname, out=od, workspace=ws)
+    def step(i):
+        qa_call(i)
+        gemm(i)
 
-            att_bytes = n + 2 * H * (T // 128) * 4 + 2 * hq * D * 2
-            t_att = timer.run(att, 20, warmup=3, name="kv_decode_attention" + tag)
-            passes["kv_decode_attention" + tag] = {"us": t_att * 1e6, "GB/s": att_bytes / t_att / 1e9,
-                                                   "frac_hbm": att_bytes / t_att / 1e9 / PEAK_HBM_GBPS}
-            del qd, od, ws, caches
-        del kd, vd, qk, qv, ok, ov
-    if not args.no_secondary and args.only in (None, "decode"):
-        c3 = syn.CONFIGS[3]
-        m3, n3, k3 = c3["M"], c3["N"], c3["K"]
-        a3 = syn.activations(3).to(dev)
-        w3 = syn.weights(3).to(dev)
-        qa3, sa3 = fp8.fp8_quantize(a3, "group_1x128", scale_layout="kmajor")
-        qw3, sw3 = fp8.fp8_quantize(w3, "block_128x128")
-        del w3
-        o3 = torch.empty((m3, n3), dtype=torch.bfloat16, device=dev)
-        # 3 copies of the 235 MB weight codes, rotated: the weights stream from
-        # HBM on every call instead of staying in the Infinity Cache
-        qw3_sets = [qw3, qw3.clone(), qw3.clone()]
+    qw_call(0)
+    qa_call(0)
+    res = {}
+    for name, fn in (("act_quant", qa_call), ("weight_quant_offline", qw_call), ("gemm", gemm),
+                     ("step_act_quant_and_gemm", step)):
+        key = f"per_tensor_64x512x512_{name}"
+        t = timer.run(fn, 200, warmup=20, name=key)
+        res[key] = {"us_per_call_median": timer.stats[key]["median_us"],
+                    "us_back_to_back": t * 1e6, "note": "latency-bound; no roofline claim"}
+    return res
 
-        def dec(i):
-            fp8.fp8_block_gemm(qa3, sa3, "group_1x128", qw3_sets[i % 3], sw3, "block_128x128", out=o3)
 
-        t_dec = timer.run(dec, 50, warmup=5, name="decode_gemm_16x28672x8192")
-        dec_bytes = m3 * k3 + n3 * k3 + 4 * (m3 * (k3 // 128) + (n3 // 128) * (k3 // 128)) + 2 * m3 * n3
-        passes["decode_gemm_16x28672x8192"] = {"us": t_dec * 1e6, "GB/s": dec_bytes / t_dec / 1e9,
-                                               "frac_hbm": dec_bytes / t_dec / 1e9 / PEAK_HBM_GBPS,
-                                               "TFLOP/s": 2.0 * m3 * n3 * k3 / t_dec / 1e12}
-        # the same GEMM on weights packed once, offline, into the decode-packed
-        # layout (one K block's N x 128 bytes contiguous), 3 rotating copies
-        del qw3_sets
-        pk3_sets = [fp8.fp8_pack_weights_decode(qw3) for _ in range(3)]
-        del qw3
+def passes_kv(args, torch, syn, fp8, timer, dev):
+    """FP8 KV cache, K and V [8, 131072, 128]: quantize and dequantize in E4M3
+    and E5M2, and decode attention of 64 query heads over the codes."""
+    c5 = syn.CONFIGS[5]
+    kh, vh = syn.kv_pair(5)
+    kd, vd = kh.to(dev), vh.to(dev)
+    del kh, vh
+    H, T, D = c5["heads"], c5["tokens"], c5["head_dim"]
+    qk = torch.empty((H, T, D), dtype=torch.uint8, device=dev)
+    qv = torch.empty_like(qk)
+    sk = torch.empty((H, T // 128), dtype=torch.float32, device=dev)
+    sv = torch.empty_like(sk)
+    ok = torch.empty((H, T, D), dtype=torch.bfloat16, device=dev)
+    ov = torch.empty_like(ok)
+    lib = fp8.load_library()
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    n = 2 * H * T * D
+    kv_bytes = n * 2 + n + 2 * H * (T // 128) * 4
+    # E4M3 (the default KV format) and E5M2 (the KV format of the serving
+    # recipe on the pages); same bytes, same kernels up to the conversion
+    for fmt, tag in ((fp8.E4M3, ""), (fp8.E5M2, "_e5m2")):
+        def kvq(i, fmt=fmt):
+            fp8._check(lib.fp8_kv_quantize(kd.data_ptr(), H, T, D, T * D, D, 128, fmt, qk.data_ptr(),
+                                           sk.data_ptr(), stream))
+            fp8._check(lib.fp8_kv_quantize(vd.data_ptr(), H, T, D, T * D, D, 128, fmt, qv.data_ptr(),
+                                           sv.data_ptr(), stream))
 
-        def dec_packed(i):
-            fp8.fp8_block_gemm_packed(qa3, sa3, "group_1x128", pk3_sets[i % 3], sw3, "block_128x128", out=o3)
+        def kvd(i, fmt=fmt):
+            fp8._check(lib.fp8_kv_dequantize(qk.data_ptr(), sk.data_ptr(), H, T, D, 128, fmt, ok.data_ptr(),
+                                             stream))
+            fp8._check(lib.fp8_kv_dequantize(qv.data_ptr(), sv.data_ptr(), H, T, D, 128, fmt, ov.data_ptr(),
+                                             stream))
 
-        t_decp = timer.run(dec_packed, 50, warmup=5, name="decode_gemm_packed_16x28672x8192")
-        passes["decode_gemm_packed_16x28672x8192"] = {"us": t_decp * 1e6, "GB/s": dec_bytes / t_decp / 1e9,
-                                                      "frac_hbm": dec_bytes / t_decp / 1e9 / PEAK_HBM_GBPS,
-                                                      "TFLOP/s": 2.0 * m3 * n3 * k3 / t_decp / 1e12}
-        # the one-time packing pass itself: N x K bytes read and written
-        def pack(i):
-            fp8.fp8_pack_weights_decode(pk3_sets[i % 3].view(n3, k3), out=pk3_sets[(i + 1) % 3])
+        t_kvq = timer.run(kvq, 20, warmup=3, name="kv_quant_K+V" + tag)
+        t_kvd = timer.run(kvd, 20, warmup=3, name="kv_dequant_K+V" + tag)
+        res["kv_quant_K+V_8x131072x128" + tag] = {"us": t_kvq * 1e6, "GB/s": kv_bytes / t_kvq / 1e9,
+                                                  "frac_hbm": kv_bytes / t_kvq / 1e9 / PEAK_HBM_GBPS}
+        res["kv_dequant_K+V_8x131072x128" + tag] = {"us": t_kvd * 1e6, "GB/s": kv_bytes / t_kvd / 1e9,
+                                                    "frac_hbm": kv_bytes / t_kvd / 1e9 / PEAK_HBM_GBPS}
+        # decode attention of 64 query heads (8 per kv head) over the codes
+        # just written: algorithmic bytes = both code tensors, their scales,
+        # the bf16 query and output
+        hq = c5["heads_q"]
+        qd = syn.decode_queries(heads_q=hq).to(dev)
+        od = torch.empty((hq, D), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(lib.fp8_kv_decode_attention_workspace_size(hq, T), dtype=torch.uint8, device=dev)
+        fname = "e5m2" if fmt == fp8.E5M2 else "e4m3"
+        # two copies of the 268 MB cache, alternated: more than the Infinity
+        # Cache, so the codes stream from HBM
+        caches = [(qk, sk, qv, sv), (qk.clone(), sk, qv.clone(), sv)]
 
-        t_pack = timer.run(pack, 10, warmup=2, name="pack_weights_decode_28672x8192")
-        passes["pack_weights_decode_28672x8192_offline"] = {"us": t_pack * 1e6,
-                                                            "GB/s": 2.0 * n3 * k3 / t_pack / 1e9,
-                                                            "frac_hbm": 2.0 * n3 * k3 / t_pack / 1e9 / PEAK_HBM_GBPS}
-        del pk3_sets
+        def att(i, fname=fname):
+            ck, cks, cv, cvs = caches[i % 2]
+            fp8.fp8_kv_decode_attention(qd, ck, cks, cv, cvs, 1.0 / 128 ** 0.5, fmt=fname, out=od, workspace=ws)
 
-    # ---- measured MFMA ceiling on the workload's own codes --------------------
-    ceiling = None
-    if args.only is None:
-        ceiling = mfma_ceiling(torch, dev, qa_sets[0], qw)
-        if ceiling and passes.get("gemm"):
-            ceiling["gemm_frac_of_mfma_plus_4_fma"] = passes["gemm"]["TFLOP/s"] / ceiling["mfma_plus_4_fma"]
+        att_bytes = n + 2 * H * (T // 128) * 4 + 2 * hq * D * 2
+        t_att = timer.run(att, 20, warmup=3, name="kv_decode_attention" + tag)
+        res["kv_decode_attention_64q_8x131072x128" + tag] = {
+            "us": t_att * 1e6, "GB/s": att_bytes / t_att / 1e9, "frac_hbm": att_bytes / t_att / 1e9 / PEAK_HBM_GBPS}
+        del qd, od, ws, caches
+    return res
 
-    # ---- CPU oracle on a bounded sample of the step -------------------------
-    cpu = None
-    if not args.no_cpu_baseline and args.only is None:
-        cpu = cpu_baseline(syn, M, N, K)
 
-    gemm_p = passes.get("gemm")
-    result = {
-        "metric": "block-scaled FP8 GEMM TFLOP/s (%FP8 MFMA peak) + quantize/KV GB/s (%HBM)",
-        "value": (flops / t_step / 1e12) if t_step else None,
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": (t_step * 1e3) if t_step else None,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8e4m3-mfma/fp32-acc/bf16-out",
-        "data": "synthetic (seeded Llama-3-8B MLP-shaped activations with outlier channels, N(0,0.02) weights)",
-        "config": {"workload": c["workload"], "M": M, "N": N, "K": K,
-                   "act_scales": "1x128 dynamic", "weight_scales": "128x128", "parallelism": "single-gpu"},
-        "roofline": None if gemm_p is None else {
-            "kernel": "k_gemm_fp8_block (fp8_block_gemm)",
-            "bound": "mfma",
-            "achieved": gemm_p["TFLOP/s"],
-            "peak": PEAK_FP8_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": gemm_p["TFLOP/s"] / PEAK_FP8_TFLOPS,
-            "traffic": gemm_traffic_bytes(),
-            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
-            "algorithmic_bytes": float(M * K + N * K + 2 * M * N + 4 * (M * (K // 128) + (N // 128) * (K // 128))),
-        },
-        "passes": passes,
-        "mfma_ceiling": ceiling,
-        "clocks": clocks.summary(),
-        "per_call": timer.stats,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(result), flush=True)
+def passes_decode(args, torch, syn, fp8, timer, dev):
+    """Llama-3-70B MLP up, decode shape 16 x 28672 x 8192: HBM-bound GEMM on
+    row-major and on decode-packed weights (3 rotating copies of the 235 MB
+    codes), the packing pass, and the [16, 8192] activation quantize."""
+    c3 = syn.CONFIGS[3]
+    m3, n3, k3 = c3["M"], c3["N"], c3["K"]
+    a3 = syn.activations(3).to(dev)
+    w3 = syn.weights(3).to(dev)
+    qa3, sa3 = fp8.fp8_quantize(a3, "group_1x128", scale_layout="kmajor")
+    qw3, sw3 = fp8.fp8_quantize(w3, "block_128x128")
+    del w3
+    res = {}
+
+    def qa_call(i):
+        fp8.fp8_quantize(a3, "group_1x128", out=qa3, scales=sa3)
+
+    timer.run(qa_call, 200, warmup=20, name="act_quant_1x128_16x8192")
+    res["act_quant_1x128_16x8192"] = {"us_per_call_median": timer.stats["act_quant_1x128_16x8192"]["median_us"],
+                                      "note": "0.4 MB: latency-bound; no roofline claim"}
+    o3 = torch.empty((m3, n3), dtype=torch.bfloat16, device=dev)
+    qw3_sets = [qw3, qw3.clone(), qw3.clone()]
+
+    def dec(i):
+        fp8.fp8_block_gemm(qa3, sa3, "group_1x128", qw3_sets[i % 3], sw3, "block_128x128", out=o3)
+
+    t_dec = timer.run(dec, 50, warmup=5, name="decode_gemm_16x28672x8192")
+    dec_bytes = m3 * k3 + n3 * k3 + 4 * (m3 * (k3 // 128) + (n3 // 128) * (k3 // 128)) + 2 * m3 * n3
+    res["decode_gemm_16x28672x8192"] = {"us": t_dec * 1e6, "GB/s": dec_bytes / t_dec / 1e9,
+                                        "frac_hbm": dec_bytes / t_dec / 1e9 / PEAK_HBM_GBPS,
+                                        "TFLOP/s": 2.0 * m3 * n3 * k3 / t_dec / 1e12}
+    del qw3_sets
+    pk3_sets = [fp8.fp8_pack_weights_decode(qw3) for _ in range(3)]
+    del qw3
+
+    def dec_packed(i):
+        fp8.fp8_block_gemm_packed(qa3, sa3, "group_1x128", pk3_sets[i % 3], sw3, "block_128x128", out=o3)
+
+    t_decp = timer.run(dec_packed, 50, warmup=5, name="decode_gemm_packed_16x28672x8192")
+    res["decode_gemm_packed_16x28672x8192"] = {"us": t_decp * 1e6, "GB/s": dec_bytes / t_decp / 1e9,
+                                               "frac_hbm": dec_bytes / t_decp / 1e9 / PEAK_HBM_GBPS,
+                                               "TFLOP/s": 2.0 * m3 * n3 * k3 / t_decp / 1e12}
+
+    def pack(i):
+        fp8.fp8_pack_weights_decode(pk3_sets[i % 3].view(n3, k3), out=pk3_sets[(i + 1) % 3])
+
+    t_pack = timer.run(pack, 10, warmup=2, name="pack_weights_decode_28672x8192")
+    res["pack_weights_decode_28672x8192_offline"] = {"us": t_pack * 1e6, "GB/s": 2.0 * n3 * k3 / t_pack / 1e9,
+                                                     "frac_hbm": 2.0 * n3 * k3 / t_pack / 1e9 / PEAK_HBM_GBPS}
+    del pk3_sets
+    return res
 
 
 def copy_calibration(torch, timer, dev):
@@ -613,19 +736,16 @@ def mfma_ceiling(torch, dev, qa, qw):
     return res
 
 
-def cpu_baseline(syn, M, N, K):
+def cpu_baseline(syn, qw, sw, M, N, K):
     """The oracle timed on the whole step at full size: 1x128 quantization of
-    the [4096, 4096] activations, then the oracle GEMM 4096 x 14336 x 4096
-    (dequantize to fp64 and one fp64 matmul, plus the tolerance base). The
-    weights are quantized by the oracle beforehand, untimed, as the offline
-    pass."""
+    the [8192, 8192] activations, then the oracle GEMM 8192 x 10240 x 8192
+    (dequantize to fp64 and one fp64 matmul, plus the tolerance base), as the
+    oracle stands (its matmuls use NumPy's BLAS thread pool). The weight codes
+    and scales are the offline pass's, as in the GPU step."""
     import threadpoolctl
     from oracle import quant, gemm
 
-    a = syn.activations(2).float().numpy()
-    w = syn.weights(2).float().numpy()
-    qw, sw = quant.quantize_block_128x128(w)
-    del w
+    a = syn.activations(4).float().numpy()
     t0 = time.perf_counter()
     qa, sa = quant.quantize_group_1x128(a)
     gemm.block_gemm(qa, sa, "group_1x128", qw, sw, "block_128x128")
