@@ -75,20 +75,26 @@ struct AttnParams {
 };
 
 // 8 codes (two words) -> 8 bf16, exact (an FP8 value has at most 4
-// significant bits and an exponent inside bf16's range): decode to fp32 and
-// keep the upper halves.
+// significant bits and an exponent inside bf16's range): gfx950's packed
+// conversion, two codes per instruction, with a unit scale (checked against
+// the decode tables on every code of both formats).
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+template <int kFmt>
+__device__ __forceinline__ v2bf cvt2_bf16(uint32_t w, bool hi) {
+  if constexpr (kFmt == FMT_E4M3)
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  else
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, false);
+}
+
 template <int kFmt>
 __device__ __forceinline__ v8bf codes_to_bf16(uint32_t w0, uint32_t w1) {
-  const auto a = Fp8<kFmt>::template decode2<false>(w0);
-  const auto b = Fp8<kFmt>::template decode2<true>(w0);
-  const auto c = Fp8<kFmt>::template decode2<false>(w1);
-  const auto d = Fp8<kFmt>::template decode2<true>(w1);
-  v4u r;
-  r[0] = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
-  r[1] = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
-  r[2] = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
-  r[3] = __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), 0x07060302u);
-  return __builtin_bit_cast(v8bf, r);
+  const v2bf a = cvt2_bf16<kFmt>(w0, false), b = cvt2_bf16<kFmt>(w0, true);
+  const v2bf c = cvt2_bf16<kFmt>(w1, false), d = cvt2_bf16<kFmt>(w1, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // Upper halves of two fp32 values as two bf16 (exact when the low halves are

@@ -173,13 +173,21 @@ __device__ __forceinline__ uint32_t block256_max(uint32_t m) {
 // ---------------------------------------------------------------------------
 // 1x128 groups: 8 lanes (half a DPP row) per group, 16 elements per lane in
 // two 16-byte chunks (elements 8 l .. 8 l + 7 and 64 + 8 l .. 64 + 8 l + 7),
-// kUnroll groups per lane with all loads issued before any arithmetic.
-// Group g of the flat (row, group) index space: row = g / ngroups.
+// kUnroll units of 32 groups per workgroup with all loads issued before any
+// arithmetic.
+// * kColumns = false (scales row-major): a unit is 32 consecutive groups of
+//   the flat (row, group) index space, row = g / ngroups, so a workgroup's
+//   scales are contiguous.
+// * kColumns = true (scales K-block-major, consecutive rows' scales of one
+//   group adjacent): a unit is 8 rows x 4 groups; wave w takes group 4 gb + w
+//   of the 8 rows, so its 8 scale stores are one contiguous 32-byte run
+//   (row by row they would be 4-byte writes 4 * rows bytes apart), and the
+//   workgroup reads 1 KB of each row.
 // ---------------------------------------------------------------------------
-template <typename T, int kUnroll, int kFmt>
+template <typename T, int kUnroll, int kFmt, bool kColumns>
 __global__ __launch_bounds__(256) void k_quant_group_1x128(
-    const T* __restrict__ x, int64_t ld_x, uint32_t cols, uint32_t ngroups, uint32_t total_groups,
-    FastDiv div_groups, uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ sc,
+    const T* __restrict__ x, int64_t ld_x, uint32_t rows, uint32_t cols, uint32_t ngroups, uint32_t total_units,
+    FastDiv div_units, uint32_t units_per_row, uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ sc,
     int64_t ss_row, int64_t ss_col) {
   const uint32_t lane8 = threadIdx.x & 7u;
   const uint32_t slot = threadIdx.x >> 3;
@@ -188,10 +196,19 @@ __global__ __launch_bounds__(256) void k_quant_group_1x128(
   bool live[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
-    const uint32_t g = (blockIdx.x * kUnroll + u) * 32u + slot;
-    live[u] = g < total_groups;
-    row[u] = live[u] ? fastdiv(g, div_groups) : 0u;
-    grp[u] = g - row[u] * ngroups;
+    if constexpr (kColumns) {
+      const uint32_t unit = blockIdx.x * kUnroll + u;   // (row block of 8, group block of 4)
+      const uint32_t rb = fastdiv(unit, div_units);
+      row[u] = rb * 8u + (slot & 7u);
+      grp[u] = (unit - rb * units_per_row) * 4u + (slot >> 3);
+      live[u] = unit < total_units && row[u] < rows && grp[u] < ngroups;
+      if (!live[u]) row[u] = grp[u] = 0u;
+    } else {
+      const uint32_t g = (blockIdx.x * kUnroll + u) * 32u + slot;
+      live[u] = g < total_units;
+      row[u] = live[u] ? fastdiv(g, div_units) : 0u;
+      grp[u] = g - row[u] * ngroups;
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t col0 = grp[u] * 128u + h * 64u + lane8 * 8u;
@@ -718,12 +735,22 @@ hipError_t quantize_typed(const QuantArgs& a, hipStream_t st) {
   if (rows == 0 || cols == 0) return hipSuccess;
   if (a.gran == GRAN_GROUP_1x128) {
     const uint32_t ngroups = (cols + 127u) / 128u;
-    const uint32_t total = rows * ngroups;
-    const uint32_t per_block = 32u * kGroupUnroll;
-    const uint32_t grid = (total + per_block - 1) / per_block;
-    hipLaunchKernelGGL((k_quant_group_1x128<T, kGroupUnroll, kFmt>), dim3(grid), dim3(256), 0, st, x,
-                       a.ld_x, cols, ngroups, total, make_fastdiv(ngroups), a.q, a.ld_q, a.scales,
-                       a.ss_row, a.ss_col);
+    if (a.ss_row == 1 && ngroups > 1 && rows >= 8) {
+      // K-block-major scales: units of 8 rows x 4 groups
+      const uint32_t gunits = (ngroups + 3u) / 4u;
+      const uint32_t total = ((rows + 7u) / 8u) * gunits;
+      const uint32_t grid = (total + kGroupUnroll - 1) / kGroupUnroll;
+      hipLaunchKernelGGL((k_quant_group_1x128<T, kGroupUnroll, kFmt, true>), dim3(grid), dim3(256), 0, st, x,
+                         a.ld_x, rows, cols, ngroups, total, make_fastdiv(gunits), gunits, a.q, a.ld_q, a.scales,
+                         a.ss_row, a.ss_col);
+    } else {
+      const uint32_t total = rows * ngroups;
+      const uint32_t per_block = 32u * kGroupUnroll;
+      const uint32_t grid = (total + per_block - 1) / per_block;
+      hipLaunchKernelGGL((k_quant_group_1x128<T, kGroupUnroll, kFmt, false>), dim3(grid), dim3(256), 0, st, x,
+                         a.ld_x, rows, cols, ngroups, total, make_fastdiv(ngroups), ngroups, a.q, a.ld_q, a.scales,
+                         a.ss_row, a.ss_col);
+    }
     return hipGetLastError();
   }
   // 128x128 blocks
