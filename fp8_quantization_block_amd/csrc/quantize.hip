@@ -484,6 +484,50 @@ __global__ __launch_bounds__(256) void k_cast_tensor(const T* __restrict__ x, in
   });
 }
 
+// Per tensor, small tensors (at most kSmallChunks * 1024 chunks of 8, 64K
+// elements): one workgroup of 1024 threads holds the whole tensor in
+// registers, takes the max, stores s = amax / MAX and the codes, in one
+// launch instead of three. Same scale and cast as the three-kernel path.
+constexpr int kSmallChunks = 8;
+
+template <typename T, int kFmt>
+__global__ __launch_bounds__(1024) void k_quant_tensor_small(const T* __restrict__ x, int64_t ld_x, uint32_t cols,
+                                                             uint32_t nchunks, FastDiv div_cpr, uint32_t cpr,
+                                                             uint8_t* __restrict__ q, int64_t ld_q,
+                                                             float* __restrict__ scales) {
+  Vec8<T> v[kSmallChunks];
+  uint32_t r[kSmallChunks], cc[kSmallChunks], nv[kSmallChunks];
+#pragma unroll
+  for (int i = 0; i < kSmallChunks; ++i) {
+    const uint32_t c = threadIdx.x + 1024u * i;
+    r[i] = c < nchunks ? fastdiv(c, div_cpr) : 0u;
+    cc[i] = c - r[i] * cpr;
+    nv[i] = c < nchunks ? min(8u, cols - cc[i] * 8u) : 0u;
+    if (nv[i] > 0)
+      v[i].template load<false>(x + (int64_t)r[i] * ld_x + cc[i] * 8u, nv[i]);
+    else
+      v[i].zero();
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < kSmallChunks; ++i) {
+    const uint32_t a = v[i].amax_bits();
+    m = a > m ? a : m;
+  }
+  __shared__ uint32_t red[16];
+  m = wave_max(m);
+  if ((threadIdx.x & 63u) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = red[i] > m ? red[i] : m;
+  const GroupScale gs = make_group_scale<kFmt>(m);
+#pragma unroll
+  for (int i = 0; i < kSmallChunks; ++i)
+    if (nv[i] > 0) store_codes8(q + (int64_t)r[i] * ld_q + cc[i] * 8u, v[i].template cast<kFmt>(gs), nv[i]);
+  if (threadIdx.x == 0) scales[0] = gs.s;
+}
+
 // ---------------------------------------------------------------------------
 // MX blocks: 32 consecutive elements of a row share one power-of-two scale
 // X = 2^k, stored as the byte k + 127 (E8M0), with k the smallest integer such
@@ -726,7 +770,11 @@ hipError_t quantize_typed(const QuantArgs& a, hipStream_t st) {
       return hipGetLastError();
     }
     const uint64_t nchunks = (uint64_t)rows * ((cols + 7u) >> 3);
-    if (nchunks < (1ull << 31))
+    if (nchunks <= 1024ull * kSmallChunks) {
+      const uint32_t cpr = (cols + 7u) >> 3;
+      hipLaunchKernelGGL((k_quant_tensor_small<T, kFmt>), dim3(1), dim3(1024), 0, st, x, a.ld_x, cols,
+                         (uint32_t)nchunks, make_fastdiv(cpr), cpr, a.q, a.ld_q, a.scales);
+    } else if (nchunks < (1ull << 31))
       per_tensor_passes<T, kFmt, false>(a, x, nchunks, st);
     else
       per_tensor_passes<T, kFmt, true>(a, x, nchunks, st);
