@@ -95,9 +95,9 @@ typedef enum fp8blk_dtype { FP8BLK_BF16 = 0, FP8BLK_F32 = 1 } fp8blk_dtype;
  * (one stride at least the other axis's extent times its stride, as in
  * row-major, K-block-major or padded layouts; else FP8BLK_EINVAL); x, q and
  * scales must not overlap.
- * PER_TENSOR keeps per-workgroup maxima in q (below 4 columns: the raw amax
- * in scales[0]) between the call's kernels; codes and scale replace them
- * before the call ends.
+ * PER_TENSOR on more than 64K elements keeps per-workgroup maxima in q
+ * (below 4 columns: the raw amax in scales[0]) between the call's kernels;
+ * codes and scale replace them before the call ends.
  */
 fp8blk_status fp8_quantize(const void* x, fp8blk_dtype x_dtype, int64_t rows, int64_t cols,
                            int64_t ld_x, fp8blk_granularity gran, fp8blk_format fmt,
