@@ -143,3 +143,31 @@ def test_binding_rejects_column_strided_codes(gpu_lib):
     out = torch.empty((256, 16), dtype=torch.bfloat16, device=DEV).t()
     with pytest.raises(ValueError):
         gpu_lib.fp8_block_gemm_packed(qa, sa, "group_1x128", packed, sw, "block_128x128", out=out)
+
+
+def test_pack_past_4_gib(gpu_lib):
+    """N x K = 40960 x 131072 codes (5 GiB): more 16-byte chunks than the
+    packing kernel's capped grid covers in one pass (2^20 workgroups x 256
+    threads = 4 GiB), so its threads loop. 2 KB blocks on both sides of the
+    4 GiB boundary, and the last one, are compared byte for byte with the
+    layout built from the row-major codes by index arithmetic."""
+    N, K = 40960, 131072
+    assert N * K > (1 << 32)
+    g = torch.Generator(device=DEV).manual_seed(11)
+    qw = torch.randint(0, 256, (N, K), dtype=torch.uint8, device=DEV, generator=g)
+    try:
+        packed = gpu_lib.fp8_pack_weights_decode(qw).view(-1)
+        torch.cuda.synchronize()
+        rg_count = N // 16
+        first_past = (1 << 32) // 2048            # the first block at or past byte 2^32
+        blocks = sorted(set([0, 1, first_past - 1, first_past, first_past + 1, N * K // 2048 - 1] +
+                            [int(b) for b in np.random.default_rng(12).integers(0, N * K // 2048, 24)]))
+        for b in blocks:
+            kb, rg = divmod(b, rg_count)
+            w = qw[16 * rg:16 * rg + 16, 128 * kb:128 * kb + 128].reshape(16, 4, 2, 16)   # [r, g, h, e]
+            expect = w.permute(2, 1, 0, 3).reshape(-1)                                     # h, l = r + 16 g, e
+            got = packed[b * 2048:(b + 1) * 2048]
+            assert torch.equal(got, expect), f"block {b} (kb {kb}, rg {rg}) differs"
+    finally:
+        del qw
+        torch.cuda.empty_cache()
