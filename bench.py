@@ -206,6 +206,14 @@ class ClockSampler:
         return res
 
 
+def sha256_of(t) -> str:
+    """SHA-256 of a CPU bf16 tensor's bytes, read as int16 (numpy has no
+    bf16), so that a run's seeded inputs can be checked against another's."""
+    import hashlib
+    import torch
+    return hashlib.sha256(t.contiguous().view(torch.int16).numpy().tobytes()).hexdigest()
+
+
 def settle(torch, fn, seconds: float) -> None:
     """Untimed launches of `fn` for about `seconds` of wall time. An idle GPU
     starts at a low clock and needs a fraction of a second of sustained load to
@@ -248,7 +256,10 @@ def main():
     # 3 rotating activation sets of 134 MB bf16 + 67 MB codes: more than the
     # 256 MB Infinity Cache, so the quantize pass reads HBM
     a_host = syn.activations(4)
-    w = syn.weights(4).to(dev)
+    w_host = syn.weights(4)
+    inputs_sha256 = {"activations_bf16": sha256_of(a_host), "weights_bf16": sha256_of(w_host)}
+    w = w_host.to(dev)
+    del w_host
     nsets = 3
     a_sets = [a_host.to(dev) for _ in range(nsets)]
     qa_sets = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(nsets)]
@@ -379,6 +390,7 @@ def main():
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
             "algorithmic_bytes": float(M * K + N * K + 2 * M * N + 4 * (M * (K // 128) + (N // 128) * (K // 128))),
         },
+        "inputs_sha256": inputs_sha256,
         "passes": passes,
         "mfma_ceiling": ceiling,
         "clocks": clocks.summary(),

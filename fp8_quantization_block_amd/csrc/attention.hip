@@ -8,11 +8,12 @@
 // [MIXED] charles2530.github.io, "量化：FP8 与混合精度推理", section "scale 是控制面"
 // (KV-cache scales per head, read by the attention backend).
 //
-// Design (gfx950), one workgroup of 4 waves per (kv head, 4096-token split):
-// * Each wave streams its 1024 tokens in 32-token units through a ring of 4
-//   LDS stages: the K and V codes of the unit three ahead go into the wave's
-//   own stage by direct global -> LDS copies while the current unit is
-//   computed (24 KB in flight per wave). Rows are
+// Design (gfx950), one workgroup of 4 waves per (kv head, 2048-token split),
+// two workgroups per compute unit (64 KB of LDS each):
+// * Each wave streams its 512 tokens in 32-token units through a ring of 2
+//   LDS stages: the K and V codes of the next unit go into the wave's own
+//   stage by direct global -> LDS copies (non-temporal) while the current
+//   unit is computed. Rows are
 //   128 bytes; logical 16-byte chunk c of row r is stored at c ^ (r % 8), so
 //   that 16 lanes reading one chunk of 16 consecutive rows hit distinct banks.
 //   The kernel is bound by reading the codes from HBM.
@@ -52,9 +53,9 @@ constexpr int kWaves = 4;
 constexpr int kThreadsA = kWaves * 64;
 constexpr int kUnit = 32;                  // tokens per unit
 constexpr int kSub = kUnit / 16;           // 16-token subtiles per unit
-constexpr int kUnitsPerWave = 32;          // 1024 tokens per wave
-constexpr int kStages = 4;                 // LDS ring per wave (3 units in flight)
-constexpr int kSplitTokens = kWaves * kUnitsPerWave * kUnit;   // 4096
+constexpr int kUnitsPerWave = 16;          // 512 tokens per wave
+constexpr int kStages = 2;                 // LDS ring per wave (1 unit in flight)
+constexpr int kSplitTokens = kWaves * kUnitsPerWave * kUnit;   // 2048
 constexpr int kUnitBytes = kUnit * kD;     // 4 KB of codes per tensor
 constexpr int kCopies = kUnitBytes / 1024; // 1 KB copies per tensor and unit
 constexpr int kPartial = kD + 2;           // floats per (query head, split): O[128], m, l
@@ -106,11 +107,12 @@ __device__ __forceinline__ uint32_t hi2(uint32_t a, uint32_t b) {
 // Codes of one unit (32 token rows of 128 bytes) into an LDS buffer: 4
 // copies of 1 KB. Lane l of copy i fills row 8 i + l / 8, physical chunk l % 8,
 // i.e. logical chunk (l % 8) ^ (row % 8). Every offset is in the VGPR offset,
-// which the buffer's range check covers (rows past T read zero).
+// which the buffer's range check covers (rows past T read zero). The codes
+// are read once per call, so the copies carry the non-temporal hint.
 __device__ __forceinline__ void load_unit(__amdgpu_buffer_rsrc_t r, uint32_t unit_off, uint32_t lane_voff,
                                           uint8_t* buf) {
 #pragma unroll
-  for (int i = 0; i < kCopies; ++i) dma16(r, unit_off + (uint32_t)(i * 1024) + lane_voff, 0u, buf + i * 1024);
+  for (int i = 0; i < kCopies; ++i) dma16_nt(r, unit_off + (uint32_t)(i * 1024) + lane_voff, 0u, buf + i * 1024);
 }
 
 // Byte offset of logical byte `b` of row `row` in a swizzled buffer.
@@ -208,20 +210,18 @@ __device__ __forceinline__ void unit_step(const uint8_t* kb, const uint8_t* vb, 
   }
 }
 
-// The wave's loop over its units through a ring of 4 LDS stages (K and V
-// codes). Every step copies the unit three ahead unconditionally (its index
-// clamped to the wave's last unit, so tail copies repeat one nobody reads
-// again; a stage is refilled only after its unit has been computed), waits
-// for the current unit's copies, then computes it. Distinct __restrict__
+// The wave's loop over its units through a ring of 2 LDS stages (K and V
+// codes). Every step copies the next unit unconditionally (its index clamped
+// to the wave's last unit, so the tail copy repeats one nobody reads again; a
+// stage is refilled only after its unit has been computed, every LDS read of
+// which has returned), waits for the current unit's copies, then computes it. Distinct __restrict__
 // stages and arrays, and resources built here, let the compiler see that
 // reading one stage does not wait for the copies into the others.
 template <int kFmt>
 __device__ __forceinline__ void wave_loop(const AttnParams& p, const uint8_t* __restrict__ kh,
                                           const uint8_t* __restrict__ vh, uint32_t head_bytes,
                                           uint8_t* __restrict__ k0, uint8_t* __restrict__ v0,
-                                          uint8_t* __restrict__ k1, uint8_t* __restrict__ v1,
-                                          uint8_t* __restrict__ k2, uint8_t* __restrict__ v2,
-                                          uint8_t* __restrict__ k3, uint8_t* __restrict__ v3, const v8bf (&qb)[4],
+                                          uint8_t* __restrict__ k1, uint8_t* __restrict__ v1, const v8bf (&qb)[4],
                                           Run& st, int h, int t_begin, int nunits, int lane) {
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh, head_bytes);
@@ -245,28 +245,16 @@ __device__ __forceinline__ void wave_loop(const AttnParams& p, const uint8_t* __
   };
   constexpr int kAhead = (kStages - 1) * 2 * kCopies;   // copies in flight beyond the current unit
   copy(0, k0, v0);
-  copy(1, k1, v1);
-  copy(2, k2, v2);
-  for (int u = 0; u < nunits; u += 4) {
-    copy(u + 3, k3, v3);
+  for (int u = 0; u < nunits; u += 2) {
+    copy(u + 1, k1, v1);
     wait_vm<kAhead>();
     asm volatile("" ::: "memory");
     step(u, k0, v0);
     if (u + 1 >= nunits) break;
-    copy(u + 4, k0, v0);
+    copy(u + 2, k0, v0);
     wait_vm<kAhead>();
     asm volatile("" ::: "memory");
     step(u + 1, k1, v1);
-    if (u + 2 >= nunits) break;
-    copy(u + 5, k1, v1);
-    wait_vm<kAhead>();
-    asm volatile("" ::: "memory");
-    step(u + 2, k2, v2);
-    if (u + 3 >= nunits) break;
-    copy(u + 6, k2, v2);
-    wait_vm<kAhead>();
-    asm volatile("" ::: "memory");
-    step(u + 3, k3, v3);
   }
   wait_vm<0>();
 }
@@ -274,7 +262,7 @@ __device__ __forceinline__ void wave_loop(const AttnParams& p, const uint8_t* __
 // grid (splits, Hkv), 256 threads.
 template <int kFmt>
 __global__ __launch_bounds__(kThreadsA) void k_fp8kv_decode_attn(AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kWaves * kStages * 2 * kUnitBytes];   // 128 KB
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kWaves * kStages * 2 * kUnitBytes];   // 64 KB
   const int split = blockIdx.x, h = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -305,8 +293,7 @@ __global__ __launch_bounds__(kThreadsA) void k_fp8kv_decode_attn(AttnParams p) {
   uint8_t* const b = smem + wave * kStages * 2 * kUnitBytes;
   if (nunits > 0)
     wave_loop<kFmt>(p, p.k + (int64_t)h * p.T * kD, p.v + (int64_t)h * p.T * kD, head_bytes, b, b + kUnitBytes,
-                    b + 2 * kUnitBytes, b + 3 * kUnitBytes, b + 4 * kUnitBytes, b + 5 * kUnitBytes,
-                    b + 6 * kUnitBytes, b + 7 * kUnitBytes, qb, st, h, t_begin, nunits, lane);
+                    b + 2 * kUnitBytes, b + 3 * kUnitBytes, qb, st, h, t_begin, nunits, lane);
 
   // ---- merge the 4 waves through LDS (the stages are free: every wave
   // has waited for its last copies and passes this barrier first)
@@ -410,8 +397,8 @@ int64_t attention_partial_floats() { return kPartial; }
 // ---------------------------------------------------------------------------
 // The fixed workspace of fp8_kv_decode_attention_noalloc, for callers that
 // cannot allocate device memory: a file-scope device array, 8 MiB (the split
-// partials of heads_q * ceil(tokens / 4096) <= 16131 query-head splits, e.g.
-// 64 query heads over 1M tokens), one copy on every device the library runs
+// partials of heads_q * ceil(tokens / 2048) <= 16131 query-head splits, e.g.
+// 64 query heads over 512K tokens), one copy on every device the library runs
 // on, held until the process ends. In host code the array's name is only a
 // stand-in for it: its device address is looked up once per device with that
 // device current and cached, and only that address is handed to kernels.

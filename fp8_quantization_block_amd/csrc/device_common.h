@@ -41,6 +41,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
 }
+// The same with the non-temporal hint (nt), for data read once.
+__device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 2);
+}
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
 }
@@ -52,10 +56,33 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(((n >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (n & 15));
 }
 
-// Workgroup barrier; the empty asm statements keep the compiler from moving
-// memory accesses across it.
+// s_waitcnt with lgkmcnt(n) only (vmcnt and expcnt left at their maxima).
+template <int n>
+__device__ __forceinline__ void wait_lgkm() {
+  static_assert(n >= 0 && n < 16, "lgkmcnt");
+  __builtin_amdgcn_s_waitcnt((3 << 14) | (n << 8) | (0x7 << 4) | 0xF);
+}
+
+// Workgroup barrier. s_barrier alone does not wait for the wave's own LDS
+// accesses, so the wave first waits for them (lgkmcnt(0)): LDS writes made
+// before the barrier are then complete when other waves read after it, and
+// LDS reads made before it are complete when other waves overwrite the data.
+// Vector memory operations, the direct global -> LDS copies among them, are
+// waited for separately (wait_vm). The empty asm statements keep the compiler
+// from moving memory accesses across the barrier.
 __device__ __forceinline__ void raw_barrier() {
   asm volatile("" ::: "memory");
+  wait_lgkm<0>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The same barrier after this wave's vector memory operations (the direct
+// copies into LDS among them) have also completed: one s_waitcnt vmcnt(0)
+// lgkmcnt(0), then s_barrier.
+__device__ __forceinline__ void copies_done_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((0x7 << 4));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }

@@ -239,8 +239,7 @@ __device__ __forceinline__ void k_step(const Plan& pl, __amdgpu_buffer_rsrc_t ra
                                        float* ns, float* sink, bool active, Pipe& pp, v4f (&acc)[4][8]) {
   issue(pl, ra, rb, rs, min(kb + 1, nk - 1), na, nb, ns, sink);
   if (active) mma_block<first, kFa, kFb>(pl, ca, cb, cs, pp, acc);
-  wait_vm<0>();
-  raw_barrier();
+  copies_done_barrier();
 }
 
 // The K loop over the two stages. Every pointer the copies touch (both
@@ -260,8 +259,7 @@ __device__ __forceinline__ void k_loop(const Plan& pl, const uint8_t* __restrict
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(gs, gs_bytes);
   Pipe pp;
   issue(pl, ra, rb, rs, 0, a0, b0, s0, sink);
-  wait_vm<0>();
-  raw_barrier();
+  copies_done_barrier();
   k_step<true, kFa, kFb>(pl, ra, rb, rs, 0, nk, a0, b0, s0, a1, b1, s1, sink, active, pp, acc);
   int kb = 1;
   for (; kb + 1 < nk; kb += 2) {
@@ -337,8 +335,7 @@ __device__ __forceinline__ void k_step_mx(const Plan& pl, __amdgpu_buffer_rsrc_t
                                           bool active, v4f (&acc)[4][8]) {
   issue_mx(pl, ra, rb, rs, min(kb + 1, nk - 1), na, nb, ns);
   if (active) mma_block_mx<kFa, kFb>(pl, ca, cb, cs, acc);
-  wait_vm<0>();
-  raw_barrier();
+  copies_done_barrier();
 }
 
 // The MX K loop over two stages (distinct __restrict__ stages and arrays, as
@@ -355,8 +352,7 @@ __device__ __forceinline__ void k_loop_mx(const Plan& pl, const uint8_t* __restr
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(gb, gb_bytes);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(gs, gs_bytes);
   issue_mx(pl, ra, rb, rs, 0, a0, b0, s0);
-  wait_vm<0>();
-  raw_barrier();
+  copies_done_barrier();
   int kb = 0;
   for (; kb + 1 < nk; kb += 2) {
     k_step_mx<kFa, kFb>(pl, ra, rb, rs, kb, nk, a0, b0, s0, a1, b1, s1, active, acc);

@@ -212,7 +212,7 @@ def att_noalloc(lib, q=PA, ldq=128, hq=64, hkv=8, t=300, d=128, kc=PB, ks=PC, vc
     (dict(hq=60), EINVAL),
     (dict(d=64), EUNSUPPORTED),
     (dict(out=PB + 64), EINVAL),               # out overlaps the K codes
-    (dict(hq=128, t=127 * 4096), EUNSUPPORTED),  # 16256 split partials: beyond the fixed 8 MiB
+    (dict(hq=128, t=127 * 2048), EUNSUPPORTED),  # 16256 split partials: beyond the fixed 8 MiB
 ])
 def test_attention_noalloc_rejects(lib, kw, status):
     assert att_noalloc(lib, **kw) == status
@@ -222,10 +222,12 @@ def test_attention_noalloc_rejects(lib, kw, status):
 
 def test_attention_workspace_size(lib):
     lib.fp8_kv_decode_attention_workspace_size.restype = ctypes.c_size_t
-    # 64 query heads, 131072 tokens: 32 splits of 4096 tokens, 130 floats each
-    assert lib.fp8_kv_decode_attention_workspace_size(64, 131072) == 64 * 32 * 130 * 4
+    # 64 query heads, 131072 tokens: 64 splits of 2048 tokens, 130 floats each
+    assert lib.fp8_kv_decode_attention_workspace_size(64, 131072) == 64 * 64 * 130 * 4
     assert lib.fp8_kv_decode_attention_workspace_size(8, 1) == 8 * 1 * 130 * 4
-    assert lib.fp8_kv_decode_attention_workspace_size(8, 4097) == 8 * 2 * 130 * 4
+    assert lib.fp8_kv_decode_attention_workspace_size(8, 2048) == 8 * 1 * 130 * 4
+    assert lib.fp8_kv_decode_attention_workspace_size(8, 2049) == 8 * 2 * 130 * 4
+    assert lib.fp8_kv_decode_attention_workspace_size(8, 4097) == 8 * 3 * 130 * 4
     assert lib.fp8_kv_decode_attention_workspace_size(0, 5) == 0
 
 

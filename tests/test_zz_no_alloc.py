@@ -59,11 +59,11 @@ def test_noalloc_equals_workspace_entry_point(gpu_lib, fmt, out_dtype):
 
 
 def test_noalloc_rejects_partials_beyond_the_fixed_workspace(gpu_lib):
-    """128 query heads over 520,000 tokens need 128 * 127 = 16256 split
-    partials, more than the 16131 the 8 MiB array holds: refused on the host
-    (no kernel runs, the output keeps its contents)."""
+    """128 query heads over 260,000 tokens need 128 * 127 = 16256 split
+    partials of 2048 tokens, more than the 16131 the 8 MiB array holds:
+    refused on the host (no kernel runs, the output keeps its contents)."""
     lib = gpu_lib.load_library()
-    hq, hkv, t = 128, 8, 520000
+    hq, hkv, t = 128, 8, 260000
     assert lib.fp8_kv_decode_attention_workspace_size(hq, t) > 8 << 20
     kc = torch.zeros((hkv, t, 128), dtype=torch.uint8, device=DEV)
     ks = torch.zeros((hkv, (t + 127) // 128), dtype=torch.float32, device=DEV)
@@ -74,5 +74,5 @@ def test_noalloc_rejects_partials_beyond_the_fixed_workspace(gpu_lib):
     assert "fixed workspace" in lib.fp8blk_last_error().decode()
     torch.cuda.synchronize()
     assert bool(torch.all(out == 7.0))
-    # one split fewer fits: 128 heads over 126 * 4096 tokens
-    assert lib.fp8_kv_decode_attention_workspace_size(hq, 126 * 4096) <= 8 << 20
+    # one split fewer fits: 128 heads over 126 * 2048 tokens
+    assert lib.fp8_kv_decode_attention_workspace_size(hq, 126 * 2048) <= 8 << 20
