@@ -341,45 +341,46 @@ __global__ __launch_bounds__(kThreadsA) void k_fp8kv_decode_attn(AttnParams p) {
 
 // Merge of the splits of each query head; grid (Hq, 4), 512 threads: a
 // workgroup takes 32 dims of one query head, thread t dim t % 32 over the
-// splits s = t / 32 (mod 16), so that 16 independent streams of loads are in
-// flight per dim; the global max comes first from a block reduction.
+// splits s = t / 32 (mod 16). Each thread merges its splits online (running
+// max, sum and output, rescaled by exp2 of the change of max), with the loads of all
+// its splits independent of the arithmetic, so one round trip to memory; the
+// 16 parts of a dim are then merged through LDS.
 constexpr int kCombThreads = 512;
 constexpr int kCombDims = 32;
 constexpr int kCombParts = kCombThreads / kCombDims;
 
 template <bool kBf16Out>
 __global__ __launch_bounds__(kCombThreads) void k_fp8kv_attn_combine(AttnParams p) {
-  __shared__ float red[kCombThreads];
-  __shared__ float po[kCombParts][kCombDims], pl[kCombParts][kCombDims];
+  __shared__ float pm[kCombParts][kCombDims], pl[kCombParts][kCombDims], po[kCombParts][kCombDims];
   const int hq = blockIdx.x, t = threadIdx.x;
   const int dl = t % kCombDims, part = t / kCombDims, d = blockIdx.y * kCombDims + dl;
   const float* base = p.ws + (int64_t)hq * p.splits * kPartial;
-  float m = kNegBig;
-  for (int s = t; s < p.splits; s += kCombThreads) m = fmaxf(m, base[(int64_t)s * kPartial + kD]);
-  red[t] = m;
-  __syncthreads();
-  for (int w = kCombThreads / 2; w > 0; w >>= 1) {
-    if (t < w) red[t] = fmaxf(red[t], red[t + w]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  float o = 0.f, L = 0.f;
-#pragma unroll 2
+  // online merge of the part's splits: running max M, sum L and output o
+  float M = kNegBig, L = 0.f, o = 0.f;
+#pragma unroll 4
   for (int s = part; s < p.splits; s += kCombParts) {
     const float* ps = base + (int64_t)s * kPartial;
-    const float w = __builtin_amdgcn_exp2f(ps[kD] - M);
-    o += ps[d] * w;
-    L += ps[kD + 1] * w;
+    const float m = ps[kD], l = ps[kD + 1], v = ps[d];
+    const float mn = fmaxf(M, m);
+    const float a = __builtin_amdgcn_exp2f(M - mn), b = __builtin_amdgcn_exp2f(m - mn);
+    L = L * a + l * b;
+    o = o * a + v * b;
+    M = mn;
   }
-  po[part][dl] = o;
+  pm[part][dl] = M;
   pl[part][dl] = L;
+  po[part][dl] = o;
   __syncthreads();
   if (part == 0) {
+    float mx = kNegBig;
+#pragma unroll
+    for (int i = 0; i < kCombParts; ++i) mx = fmaxf(mx, pm[i][dl]);
     float os = 0.f, ls = 0.f;
 #pragma unroll
     for (int i = 0; i < kCombParts; ++i) {
-      os += po[i][dl];
-      ls += pl[i][dl];
+      const float w = __builtin_amdgcn_exp2f(pm[i][dl] - mx);
+      os += po[i][dl] * w;
+      ls += pl[i][dl] * w;
     }
     const float r = os / ls;
     if (kBf16Out)
