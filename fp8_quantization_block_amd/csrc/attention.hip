@@ -211,10 +211,12 @@ __device__ __forceinline__ void unit_step(const uint8_t* kb, const uint8_t* vb, 
 }
 
 // The wave's loop over its units through a ring of 2 LDS stages (K and V
-// codes). Every step copies the next unit unconditionally (its index clamped
-// to the wave's last unit, so the tail copy repeats one nobody reads again; a
-// stage is refilled only after its unit has been computed, every LDS read of
-// which has returned), waits for the current unit's copies, then computes it. Distinct __restrict__
+// codes). Every step but the last copies the next unit into the other stage
+// and waits for the current unit's copies (the last step waits for all), then
+// computes the current unit. A stage is refilled only after its unit has been
+// computed, every LDS read of which has returned. (A repeated copy of the last
+// unit in place of the missing one would read it from HBM again: the codes
+// are fetched with the non-temporal hint.) Distinct __restrict__
 // stages and arrays, and resources built here, let the compiler see that
 // reading one stage does not wait for the copies into the others.
 template <int kFmt>
@@ -232,8 +234,7 @@ __device__ __forceinline__ void wave_loop(const AttnParams& p, const uint8_t* __
   typedef const __attribute__((address_space(4))) float* cf_ptr;
   const cf_ptr skh = (cf_ptr)(p.sk + (int64_t)h * p.nb);
   const cf_ptr svh = (cf_ptr)(p.sv + (int64_t)h * p.nb);
-  const int last = nunits - 1;
-  auto unit_off = [&](int u) { return (uint32_t)(t_begin + min(u, last) * kUnit) * kD; };
+  auto unit_off = [&](int u) { return (uint32_t)(t_begin + u * kUnit) * kD; };
   auto copy = [&](int u, uint8_t* kb, uint8_t* vb) {
     load_unit(rk, unit_off(u), lane_voff, kb);
     load_unit(rv, unit_off(u), lane_voff, vb);
@@ -246,13 +247,21 @@ __device__ __forceinline__ void wave_loop(const AttnParams& p, const uint8_t* __
   constexpr int kAhead = (kStages - 1) * 2 * kCopies;   // copies in flight beyond the current unit
   copy(0, k0, v0);
   for (int u = 0; u < nunits; u += 2) {
-    copy(u + 1, k1, v1);
-    wait_vm<kAhead>();
+    if (u + 1 < nunits) {
+      copy(u + 1, k1, v1);
+      wait_vm<kAhead>();
+    } else {
+      wait_vm<0>();
+    }
     asm volatile("" ::: "memory");
     step(u, k0, v0);
     if (u + 1 >= nunits) break;
-    copy(u + 2, k0, v0);
-    wait_vm<kAhead>();
+    if (u + 2 < nunits) {
+      copy(u + 2, k0, v0);
+      wait_vm<kAhead>();
+    } else {
+      wait_vm<0>();
+    }
     asm volatile("" ::: "memory");
     step(u + 1, k1, v1);
   }
