@@ -173,14 +173,16 @@ __device__ __forceinline__ uint32_t pack4_sat(float a, float b, float c, float d
 // quotient; the per-element division is replaced by multiplications with a
 // per-group reciprocal r: v_rcp_f32(s) (1 ulp) refined by one Newton step.
 //
-// bf16 inputs to E4M3 (cast4_bf16): q = fl32(x r), then one residual correction
-// q' = q - fl32(s q - x) r with fused multiply-adds. An exhaustive sweep over
-// every bf16 amax and every bf16 |x| <= amax whose scale lies in
-// [2^-64, 2^64] finds the code of q' equal to the code of fl32(x / s) in all
-// 2.8e8 cases (the quotient itself can differ by one ulp, never across a code
-// boundary); tests/test_gpu_quantize.py re-checks a sample against the CPU
-// oracle. The residual is negated so that x = -0 keeps its sign. Groups whose
-// scale lies outside that range, or is zero, divide exactly.
+// bf16 inputs (cast4_bf16): q = fl32(x r), then one residual correction
+// q' = q - fl32(s q - x) r with fused multiply-adds. For each format, an
+// exhaustive sweep over every bf16 amax whose scale lies in [2^-64, 2^64] and,
+// under each, every bf16 |x| <= amax in both signs finds the code of q' equal
+// to the code of fl32(x / s) (the quotient itself can differ by one ulp, never
+// across a code boundary of either grid); tests/test_gpu_quantize.py runs the
+// sweep against the CPU oracle for E4M3 and E5M2. The residual is negated so
+// that x = -0 keeps its sign. E5M2 quotients are clamped to +-57344 before the
+// conversion (saturation). Groups whose scale lies outside that range, or is
+// zero, divide exactly.
 //
 // fp32 inputs, and every input to E5M2 (cast4_f32): the products fl32(x rl) and fl32(x rh) with
 // rl = r (1 - 2^-20), rh = r (1 + 2^-20) bracket fl32(x / s) strictly in
@@ -192,11 +194,9 @@ __device__ __forceinline__ uint32_t pack4_sat(float a, float b, float c, float d
 // exceeds 448 (|x| <= amax), where the hardware conversion is exact; the upper
 // one may exceed it by a hair, and if the conversion then disagrees the exact
 // path decides. For E5M2 both are clamped to +-57344 first (a monotone,
-// saturating conversion), so the argument holds unchanged. The E5M2 fast path
-// for bf16 inputs is this bracket too: the residual-corrected quotient's code
-// equality was established for the E4M3 grid only. Quotients below the fp32
-// normal range give code 0 (signed) on every path. Groups whose scale is zero
-// or an fp32 subnormal always take the exact division.
+// saturating conversion), so the argument holds unchanged. Quotients below the
+// fp32 normal range give code 0 (signed) on every path. Groups whose scale is
+// zero or an fp32 subnormal always take the exact division.
 // ---------------------------------------------------------------------------
 struct GroupScale {
   float s;  // fl32(amax / max_fmt)
@@ -283,14 +283,15 @@ __device__ __forceinline__ uint32_t cast4_sat(const GroupScale& g, float a, floa
 // Codes of four elements of one group whose values are bf16 numbers.
 template <int kFmt>
 __device__ __forceinline__ uint32_t cast4_bf16(const GroupScale& g, float a, float b, float c, float d) {
-  if constexpr (kFmt == FMT_E4M3) {
-    if (__builtin_expect(bf16_fast_ok(g), 1))
-      return Fp8<kFmt>::pack4_raw(quotient_bf16(g, a), quotient_bf16(g, b), quotient_bf16(g, c),
-                                  quotient_bf16(g, d));
-    return exact4<kFmt>(g, a, b, c, d);
-  } else {
-    return cast4_f32<kFmt>(g, a, b, c, d);
+  if (__builtin_expect(bf16_fast_ok(g), 1)) {
+    const float qa = quotient_bf16(g, a), qb = quotient_bf16(g, b), qc = quotient_bf16(g, c),
+                qd = quotient_bf16(g, d);
+    if constexpr (kFmt == FMT_E4M3)
+      return Fp8<kFmt>::pack4_raw(qa, qb, qc, qd);
+    else
+      return pack4_sat<kFmt>(qa, qb, qc, qd);
   }
+  return exact4<kFmt>(g, a, b, c, d);
 }
 
 // Max over the 8 lanes of each half of a DPP row; every lane of the half gets it.

@@ -154,12 +154,12 @@ def test_bf16_every_value_below_sampled_amax(gpu_lib):
     assert_codes_equal(qg.cpu().numpy(), qr, x, "codes")
 
 
-def _fast_path_amax_patterns():
-    """Every positive finite bf16 pattern A whose scale fl32(A / 448) lies in
+def _fast_path_amax_patterns(fmt="e4m3"):
+    """Every positive finite bf16 pattern A whose scale fl32(A / MAX) lies in
     [2^-64, 2^64]: the groups whose bf16 elements the 1x128 quantizer divides
     through its Newton reciprocal and one residual correction."""
     bits = np.arange(1, 0x7F80, dtype=np.uint16)
-    s = quant.scale_of(quant.bf16_bits_to_f32(bits))
+    s = quant.scale_of(quant.bf16_bits_to_f32(bits), fmt)
     keep = (s >= np.float32(2.0 ** -64)) & (s <= np.float32(2.0 ** 64))
     return bits[keep].astype(np.int64)
 
@@ -178,25 +178,26 @@ def _sweep_groups(amax):
     return np.concatenate([np.repeat(amax, rows_per)[:, None], pat], axis=1).astype(np.uint16)
 
 
-def test_bf16_fast_path_exhaustive(gpu_lib):
-    """Every bf16 amax whose scale lies in [2^-64, 2^64] (16385 patterns) and,
-    under each, every bf16 |x| <= amax in both signs: 5.7e8 elements in 4.5e6
-    groups, codes and scales against the oracle, in chunks of 256 amax
-    patterns."""
-    amax = _fast_path_amax_patterns()
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_bf16_fast_path_exhaustive(gpu_lib, fmt):
+    """Every bf16 amax whose scale lies in [2^-64, 2^64] (16385 patterns for
+    either format) and, under each, every bf16 |x| <= amax in both signs:
+    5.7e8 (E4M3) and 6.0e8 (E5M2) elements in 4.5e6 and 4.7e6 groups, codes
+    and scales against the oracle, in chunks of 256 amax patterns."""
+    amax = _fast_path_amax_patterns(fmt)
     assert amax.size == 16385
     checked = 0
     for c0 in range(0, amax.size, 256):
         bits = _sweep_groups(amax[c0:c0 + 256])
         qg, sg = gpu_lib.fp8_quantize(torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16),
-                                      "group_1x128")
+                                      "group_1x128", fmt=fmt)
         qg, sg = qg.cpu().numpy(), sg.cpu().numpy()
         x = quant.bf16_bits_to_f32(bits)
-        parts = pmap(lambda r: quant.quantize_group_1x128(x[r:r + 8192]), range(0, x.shape[0], 8192))
-        assert_scales_equal(sg, np.concatenate([p[1] for p in parts]), f"amax chunk {c0} scales")
-        assert_codes_equal(qg, np.concatenate([p[0] for p in parts]), x, f"amax chunk {c0} codes")
+        parts = pmap(lambda r: quant.quantize_group_1x128(x[r:r + 8192], fmt), range(0, x.shape[0], 8192))
+        assert_scales_equal(sg, np.concatenate([p[1] for p in parts]), f"{fmt} amax chunk {c0} scales")
+        assert_codes_equal(qg, np.concatenate([p[0] for p in parts]), x, f"{fmt} amax chunk {c0} codes")
         checked += x.shape[0] * 127
-    print(f"bf16 fast path: {checked} element slots under {amax.size} amax patterns match the oracle")
+    print(f"bf16 fast path ({fmt}): {checked} element slots under {amax.size} amax patterns match the oracle")
 
 
 def _padded(x32: np.ndarray, dtype, ld: int) -> torch.Tensor:
