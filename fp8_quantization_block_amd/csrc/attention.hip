@@ -13,10 +13,10 @@
 // * Each wave streams its 512 tokens in 32-token units through a ring of 2
 //   LDS stages: the K and V codes of the next unit go into the wave's own
 //   stage by direct global -> LDS copies (non-temporal) while the current
-//   unit is computed. Rows are
-//   128 bytes; logical 16-byte chunk c of row r is stored at c ^ (r % 8), so
-//   that 16 lanes reading one chunk of 16 consecutive rows hit distinct banks.
-//   The kernel is bound by reading the codes from HBM.
+//   unit is computed. Rows are 128 bytes; logical 16-byte chunk c of row r is
+//   stored at c ^ (r % 8), so that 16 lanes reading one chunk of 16
+//   consecutive rows hit distinct banks. The kernel is bound by reading the
+//   codes from HBM.
 // * Scores S^T = K Q^T on the bf16 MFMA (16 x 16 x 32): FP8 codes convert to
 //   bf16 exactly and the query is bf16; the 16 MFMA columns are the G query
 //   heads that share the kv head (G <= 16). Head_dim is permuted the same way
