@@ -63,6 +63,26 @@ def test_formats_and_outputs(gpu_lib, fmt, out_dtype):
     _check(got, ref, t_o, out_dtype == torch.bfloat16, f"{fmt} {out_dtype}")
 
 
+def test_strided_query_and_output(gpu_lib):
+    """q rows with a pitch of 256 elements whose other 128 hold NaN (never
+    read) and an fp32 output with a pitch of 200 whose columns past 128 keep
+    their sentinel."""
+    hq, hkv, t = 16, 2, 3000
+    k, v = syn.kv_pair(heads=hkv, tokens=t, head_dim=128, variant=31)
+    kc, ks = gpu_lib.fp8_kv_quantize(k.to(DEV), 128)
+    vc, vs = gpu_lib.fp8_kv_quantize(v.to(DEV), 128)
+    q = syn.decode_queries(heads_q=hq, variant=31)
+    qbuf = torch.full((hq, 256), float("nan"), dtype=torch.bfloat16, device=DEV)
+    qbuf[:, :128] = q.to(DEV)
+    obuf = torch.full((hq, 200), 7.0, dtype=torch.float32, device=DEV)
+    c = 1.0 / np.sqrt(128)
+    gpu_lib.fp8_kv_decode_attention(qbuf[:, :128], kc, ks, vc, vs, c, out=obuf[:, :128])
+    ref, t_o = attention.decode_attention(f32_of(q), kc.cpu().numpy(), ks.cpu().numpy(), vc.cpu().numpy(),
+                                          vs.cpu().numpy(), np.float32(c), "e4m3")
+    _check(obuf[:, :128].cpu().numpy().astype(np.float64), ref, t_o, False, "strided q / out")
+    assert bool(torch.all(obuf[:, 128:] == 7.0))
+
+
 def test_peaked_softmax(gpu_lib):
     """A large softmax scale concentrates the weights on few tokens."""
     got, ref, t_o = _run(gpu_lib, 8, 1, 3000, "e4m3", torch.float32, variant=9, scale=0.8)

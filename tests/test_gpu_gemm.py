@@ -90,6 +90,30 @@ def test_small_shapes_full_compare(gpu_lib, M, N, K):
     _compare(gpu_lib, qa, sa, ga, qw, sw, gw, what=f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(16, 256, 512), (300, 384, 640)])
+def test_strided_operands_and_output(gpu_lib, M, N, K):
+    """A, W and C as row slices of wider buffers (lda = K + 128, ldb = K + 256,
+    ldc = N + 64), on the decode (M <= 64) and the prefill kernel. The padding
+    of A and W holds code 0x7E (448 in E4M3), which must never be read; the
+    padding of C holds a sentinel that must survive. Both output types equal
+    the dense call's bit for bit, and the fp32 output meets the oracle."""
+    qa, sa, ga, qw, sw, gw = _quantized(gpu_lib, 2, M=M, N=N, K=K, variant=K)
+    abuf = torch.full((M, K + 128), 0x7E, dtype=torch.uint8, device=DEV)
+    abuf[:, :K] = qa
+    wbuf = torch.full((N, K + 256), 0x7E, dtype=torch.uint8, device=DEV)
+    wbuf[:, :K] = qw
+    y64, t = ogemm.block_gemm(qa.cpu().numpy(), sa.cpu().numpy(), ga, qw.cpu().numpy(), sw.cpu().numpy(), gw)
+    for dt, bits in ((torch.float32, torch.int32), (torch.bfloat16, torch.int16)):
+        cbuf = torch.full((M, N + 64), 3.0, dtype=dt, device=DEV)
+        gpu_lib.fp8_block_gemm(abuf[:, :K], sa, ga, wbuf[:, :K], sw, gw, out=cbuf[:, :N])
+        dense = gpu_lib.fp8_block_gemm(qa, sa, ga, qw, sw, gw, out_dtype=dt)
+        torch.cuda.synchronize()
+        assert torch.equal(cbuf[:, :N].contiguous().view(bits), dense.view(bits)), f"{M}x{N}x{K} {dt}: strided != dense"
+        assert bool(torch.all(cbuf[:, N:] == 3.0)), f"{M}x{N}x{K} {dt}: output padding overwritten"
+        if dt == torch.float32:
+            check_gemm_tolerance(cbuf[:, :N].cpu().numpy(), y64, t, bf16=False, what=f"strided {M}x{N}x{K}")
+
+
 def test_kmajor_activation_scales(gpu_lib):
     qa, sa, ga, qw, sw, gw = _quantized(gpu_lib, 2, M=300, N=512, K=1024, kmajor=True, variant=3)
     assert sa.stride(0) == 1
