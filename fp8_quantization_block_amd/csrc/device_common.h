@@ -184,7 +184,7 @@ __device__ __forceinline__ uint32_t pack4_sat(float a, float b, float c, float d
 // conversion (saturation). Groups whose scale lies outside that range, or is
 // zero, divide exactly.
 //
-// fp32 inputs, and every input to E5M2 (cast4_f32): the products fl32(x rl) and fl32(x rh) with
+// fp32 inputs (cast4_f32), either format: the products fl32(x rl) and fl32(x rh) with
 // rl = r (1 - 2^-20), rh = r (1 + 2^-20) bracket fl32(x / s) strictly in
 // magnitude (their relative offsets exceed 2^-20 - 2^-22 - 3 * 2^-24 > 2^-24,
 // the fp32 rounding bound) whenever the quotient is an fp32 normal.
