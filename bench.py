@@ -100,6 +100,41 @@ class Timer:
                                 "p90_us": t[min(len(t) - 1, (9 * len(t)) // 10)], "calls": len(t)}
         return mean
 
+    def run_queued(self, fn, iters: int):
+        """Device seconds per call with the calls already queued: a spin kernel
+        (torch.cuda._sleep) holds the stream while the host enqueues every
+        call, so the event pair around them times the device running them back
+        to back, without the host's per-call cost. The spin is sized to twice
+        the host's measured enqueue time; returns (seconds per call, True if
+        the host finished enqueueing before the spin was over)."""
+        torch = self.torch
+        st = torch.cuda.current_stream()
+        # spin cycles per microsecond of device time
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        torch.cuda._sleep(2_000_000)
+        e1.record(st)
+        torch.cuda.synchronize()
+        cycles_per_us = 2_000_000 / max(e0.elapsed_time(e1) * 1e3, 1.0)
+        # the host's enqueue time for `iters` calls
+        h0 = time.perf_counter()
+        for i in range(iters):
+            fn(i)
+        host_s = time.perf_counter() - h0
+        torch.cuda.synchronize()
+        spin_us = 2.0 * host_s * 1e6 + 500.0
+        torch.cuda._sleep(int(spin_us * cycles_per_us))
+        h0 = time.perf_counter()
+        e0.record(st)
+        for i in range(iters):
+            fn(i)
+        e1.record(st)
+        queued = (time.perf_counter() - h0) * 1e6 < spin_us
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters * 1e-3, queued
+
 
 # HBM bytes per launch of the step's GEMM kernel (M = 8192, N = 10240,
 # K = 8192), read from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
@@ -108,9 +143,9 @@ class Timer:
 # they were taken on: the key is the SHA-256 of the GEMM source files' code
 # (comments and blank lines removed); any other code gives null.
 GEMM_COUNTERS = {
-    "sources_sha256": "97253e27d7c60878f560d22fa329f7074e05a9561ef07967bb4b3e0755622029",
-    "fetch_kib": 502834.3,
-    "write_kib": 163872.5,
+    "sources_sha256": "75371f8ba725b1258b9cc63f0df6bc98a6ff29dcf1f70c2d102f454b607d1403",
+    "fetch_kib": 530863.7,
+    "write_kib": 163911.3,
 }
 FETCH_FACTOR = 2.0
 WRITE_FACTOR = 1.0
@@ -538,9 +573,13 @@ def passes_config2(args, torch, syn, fp8, timer, dev):
 
 def passes_config1(args, torch, syn, fp8, timer, dev):
     """Per-tensor E4M3 at 64 x 512 x 512: latency-bound, so microseconds per
-    call (median of per-call event pairs) and no roofline claim. The step is
-    the activation quantize (amax pass, scale, cast) then the GEMM; the weight
-    quantize is the offline pass."""
+    call and no roofline claim: the median of per-call event pairs and the
+    mean of back-to-back calls (both include the host's per-call cost when it
+    exceeds the device's), and the device's own back-to-back time with the
+    calls queued behind a spin (Timer.run_queued). The step is
+    the activation quantize (amax pass, scale, cast) then the GEMM, as two
+    calls and as the one-launch fp8_quantize_gemm_decode; the weight quantize
+    is the offline pass."""
     c = syn.CONFIGS[1]
     M, N, K = c["M"], c["N"], c["K"]
     a = syn.activations(1).to(dev)
@@ -564,15 +603,21 @@ def passes_config1(args, torch, syn, fp8, timer, dev):
         qa_call(i)
         gemm(i)
 
+    def fused_step(i):
+        fp8.fp8_quantize_gemm_decode(a, qw, sw, "per_tensor", out=out)
+
     qw_call(0)
     qa_call(0)
     res = {}
     for name, fn in (("act_quant", qa_call), ("weight_quant_offline", qw_call), ("gemm", gemm),
-                     ("step_act_quant_and_gemm", step)):
+                     ("step_act_quant_and_gemm", step), ("step_fused_one_launch", fused_step)):
         key = f"per_tensor_64x512x512_{name}"
         t = timer.run(fn, 200, warmup=20, name=key)
+        tq, queued = timer.run_queued(fn, 200)
         res[key] = {"us_per_call_median": timer.stats[key]["median_us"],
-                    "us_back_to_back": t * 1e6, "note": "latency-bound; no roofline claim"}
+                    "us_back_to_back": t * 1e6,
+                    "us_device_back_to_back": tq * 1e6 if queued else None,
+                    "note": "latency-bound; no roofline claim"}
     return res
 
 
@@ -644,8 +689,9 @@ def passes_decode(args, torch, syn, fp8, timer, dev):
     """Llama-3-70B MLP up, decode shape 16 x 28672 x 8192: the offline 128x128
     weight quantization (2 rotating copies of the 470 MB bf16 weights), the
     HBM-bound GEMM on row-major and on decode-packed weights (3 rotating copies
-    of the 235 MB codes), the packing pass, and the [16, 8192] activation
-    quantize."""
+    of the 235 MB codes), the whole step from bf16 activations (1x128 quantize
+    then GEMM, and the two in one launch) on both weight layouts, the packing
+    pass, and the [16, 8192] activation quantize."""
     c3 = syn.CONFIGS[3]
     m3, n3, k3 = c3["M"], c3["N"], c3["K"]
     a3 = syn.activations(3).to(dev)
@@ -684,6 +730,22 @@ def passes_decode(args, torch, syn, fp8, timer, dev):
     res["decode_gemm_16x28672x8192"] = {"us": t_dec * 1e6, "GB/s": dec_bytes / t_dec / 1e9,
                                         "frac_hbm": dec_bytes / t_dec / 1e9 / PEAK_HBM_GBPS,
                                         "TFLOP/s": 2.0 * m3 * n3 * k3 / t_dec / 1e12}
+    # the whole decode step from bf16 activations: the 1x128 quantize then the
+    # GEMM, and the two in one launch (fp8_quantize_gemm_decode); bytes of the
+    # fused step: x in bf16 instead of codes and scales
+    fused_bytes = 2 * m3 * k3 + n3 * k3 + 4 * (n3 // 128) * (k3 // 128) + 2 * m3 * n3
+
+    def step_two(i):
+        qa_call(i)
+        dec(i)
+
+    def step_fused(i):
+        fp8.fp8_quantize_gemm_decode(a3, qw3_sets[i % 3], sw3, "block_128x128", gran_a="group_1x128", out=o3)
+
+    for key, fn in (("decode_step_quantize_then_gemm_16x28672x8192", step_two),
+                    ("decode_step_fused_16x28672x8192", step_fused)):
+        t = timer.run(fn, 50, warmup=5, name=key)
+        res[key] = {"us": t * 1e6, "GB/s": fused_bytes / t / 1e9, "frac_hbm": fused_bytes / t / 1e9 / PEAK_HBM_GBPS}
     del qw3_sets
     pk3_sets = [fp8.fp8_pack_weights_decode(qw3) for _ in range(3)]
     del qw3
@@ -695,6 +757,18 @@ def passes_decode(args, torch, syn, fp8, timer, dev):
     res["decode_gemm_packed_16x28672x8192"] = {"us": t_decp * 1e6, "GB/s": dec_bytes / t_decp / 1e9,
                                                "frac_hbm": dec_bytes / t_decp / 1e9 / PEAK_HBM_GBPS,
                                                "TFLOP/s": 2.0 * m3 * n3 * k3 / t_decp / 1e12}
+
+    def step_two_packed(i):
+        qa_call(i)
+        dec_packed(i)
+
+    def step_fused_packed(i):
+        fp8.fp8_quantize_gemm_decode(a3, pk3_sets[i % 3], sw3, "block_128x128", gran_a="group_1x128", out=o3)
+
+    for key, fn in (("decode_step_quantize_then_gemm_packed_16x28672x8192", step_two_packed),
+                    ("decode_step_fused_packed_16x28672x8192", step_fused_packed)):
+        t = timer.run(fn, 50, warmup=5, name=key)
+        res[key] = {"us": t * 1e6, "GB/s": fused_bytes / t / 1e9, "frac_hbm": fused_bytes / t / 1e9 / PEAK_HBM_GBPS}
 
     def pack(i):
         fp8.fp8_pack_weights_decode(pk3_sets[i % 3].view(n3, k3), out=pk3_sets[(i + 1) % 3])

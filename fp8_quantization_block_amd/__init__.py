@@ -11,6 +11,8 @@ Entry points (same names as the C ABI):
 * ``fp8_quantize(x, granularity, fmt="e4m3", scale_layout="row")`` -> (codes uint8, scales fp32)
 * ``fp8_block_gemm(qa, sa, gran_a, qw, sw, gran_w, out_dtype=torch.bfloat16, fmt_a="e4m3", fmt_w="e4m3")``
 * ``fp8_block_gemm_quant(qa, sa, gran_a, qw, sw, gran_w, fmt_c="e4m3", ...)`` -> (codes uint8, scales fp32)
+* ``fp8_quantize_gemm_decode(x, qw, sw, gran_w, gran_a="per_tensor", ...)`` -> C, or (C, codes, scales): the
+  activations quantized (per tensor or 1x128) inside the decode GEMM (M <= 64), one launch
 * ``fp8_kv_quantize(kv, token_block=128, fmt="e4m3")`` -> (codes uint8, scales fp32)
 * ``fp8_kv_dequantize(q, scales, token_block=128, fmt="e4m3")`` -> bf16
 * ``fp8_kv_decode_attention(q, k_codes, k_scales, v_codes, v_scales, softmax_scale, fmt="e4m3")`` -> [heads_q, 128]
@@ -64,6 +66,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp8_block_gemm_quant.argtypes = [i64, i64, i64, vp, i64, vp, i32, i64, i64, vp, i64, vp, i32,
                                          i64, i64, i32, i32, i32, vp, i64, vp, i64, i64, vp]
     lib.fp8_block_gemm_quant.restype = i32
+    lib.fp8_quantize_gemm_decode.argtypes = [vp, i32, i64, i64, i64, i64, i32, i32, vp, i64, i32, vp, i32, i64, i64,
+                                             i32, vp, i32, i64, vp, i64, vp, i64, i64, vp]
+    lib.fp8_quantize_gemm_decode.restype = i32
     lib.fp8_pack_weights_decode.argtypes = [vp, i64, i64, i64, vp, vp]
     lib.fp8_pack_weights_decode.restype = i32
     lib.fp8_block_gemm_packed.argtypes = [i64, i64, i64, vp, i64, vp, i32, i64, i64, vp, vp, i32,
@@ -227,6 +232,83 @@ def fp8_block_gemm(qa: torch.Tensor, sa: torch.Tensor, gran_a: str, qw: torch.Te
                               _ptr(qw), qw.stride(0), _ptr(sw), gw, swn, swk, _FMT[fmt_a], _FMT[fmt_w],
                               _ptr(out), cdt, out.stride(0), _stream(qa)))
     return out
+
+
+def fp8_quantize_gemm_decode(x: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor, gran_w: str,
+                             gran_a: str = "per_tensor", fmt_a: str = "e4m3", fmt_w: str = "e4m3",
+                             out_dtype=torch.bfloat16, out: torch.Tensor = None, return_codes: bool = False,
+                             codes: torch.Tensor = None, scales: torch.Tensor = None, scale_layout: str = "row"):
+    """C = fp8_block_gemm(fp8_quantize(x, gran_a, fmt_a), W) in one launch, for
+    decode shapes: x bf16/fp32 [M, K] with M <= 64 (per_tensor: also M * K <=
+    65536). The weights are qw as fp8_block_gemm takes them (uint8 [N, K]) or
+    as fp8_pack_weights_decode returns them ([K/128, N/16, 2048]), with scales
+    sw. The activation codes [M, K] and scales (per_tensor [1]; group_1x128
+    [M, K/128], with scale_layout "kmajor" stored transposed as fp8_quantize
+    does) are written to ``codes`` / ``scales`` when given (allocated here with
+    return_codes), and returned with C when return_codes is set."""
+    fn = "fp8_quantize_gemm_decode"
+    lib = load_library()
+    _require_cuda(x, qw, sw)
+    if x.dim() != 2 or x.stride(1) != 1 or x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"{fn}: x must be a bf16 or fp32 [M, K] tensor with contiguous rows")
+    M, K = x.shape
+    if qw.dtype != torch.uint8:
+        raise ValueError(f"{fn}: qw must be uint8 codes")
+    packed = qw.dim() == 3
+    if packed:
+        if qw.shape[2] != 2048 or not qw.is_contiguous() or qw.shape[0] * 128 != K:
+            raise ValueError(f"{fn}: packed qw must be a contiguous [K/128, N/16, 2048] tensor")
+        N, ldb = qw.shape[1] * 16, K
+    else:
+        N, K2 = qw.shape
+        if K != K2:
+            raise ValueError(f"{fn}: K mismatch")
+        _require_rows(fn, _CODES, qw=qw)
+        ldb = qw.stride(0)
+    ga, gw = _GRAN[gran_a], _GRAN[gran_w]
+    if ga not in (PER_TENSOR, GROUP_1x128):
+        raise ValueError(f"{fn}: gran_a must be per_tensor or group_1x128")
+    if gw not in (PER_TENSOR, BLOCK_128x128):
+        raise ValueError(f"{fn}: gran_w must be per_tensor or block_128x128")
+    _require_scales(fn, "sw", sw, gw, ((N + 127) // 128, (K + 127) // 128))
+    swn, swk = (sw.stride(0), sw.stride(1)) if gw != PER_TENSOR else (0, 0)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    _require_rows(fn, _OUT, out=out)
+    q, sc = codes, scales
+    if return_codes and q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if return_codes and sc is None:
+        if ga == PER_TENSOR:
+            sc = torch.empty(1, dtype=torch.float32, device=x.device)
+        elif scale_layout == "kmajor":
+            sc = torch.empty((K // 128, M), dtype=torch.float32, device=x.device).t()
+        else:
+            sc = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    if q is not None:
+        _require_cuda(q)
+        _require_rows(fn, _CODES, codes=q)
+        if tuple(q.shape) != (M, K):
+            raise ValueError(f"{fn}: codes must be uint8 [M, K]")
+    som = sok = 0
+    if sc is not None:
+        _require_cuda(sc)
+        if sc.dtype != torch.float32:
+            raise ValueError(f"{fn}: scales must be float32")
+        if ga == PER_TENSOR:
+            if sc.numel() < 1:
+                raise ValueError(f"{fn}: per_tensor scales need at least one element")
+        else:
+            if sc.dim() != 2 or tuple(sc.shape) != (M, K // 128):
+                raise ValueError(f"{fn}: group_1x128 scales must be [M, K/128]")
+            som, sok = sc.stride(0), sc.stride(1)
+    _check(lib.fp8_quantize_gemm_decode(_ptr(x), BF16 if x.dtype == torch.bfloat16 else F32, M, N, K, x.stride(0),
+                                        ga, _FMT[fmt_a], _ptr(qw), ldb, 1 if packed else 0, _ptr(sw), gw, swn, swk,
+                                        _FMT[fmt_w], _ptr(out), BF16 if out.dtype == torch.bfloat16 else F32,
+                                        out.stride(0), _ptr(q) if q is not None else None,
+                                        q.stride(0) if q is not None else 0, _ptr(sc) if sc is not None else None,
+                                        som, sok, _stream(x)))
+    return (out, q, sc) if return_codes else out
 
 
 def fp8_pack_weights_decode(qw: torch.Tensor, out: torch.Tensor = None):

@@ -270,6 +270,93 @@ fp8blk_status fp8_block_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, 
   return hip_status(fp8blk::launch_block_gemm(g, static_cast<hipStream_t>(stream)), fn);
 }
 
+fp8blk_status fp8_quantize_gemm_decode(const void* x, fp8blk_dtype x_dtype, int64_t M, int64_t N, int64_t K,
+                                       int64_t ld_x, fp8blk_granularity gran_a, fp8blk_format fmt_a,
+                                       const uint8_t* b, int64_t ldb, int b_packed, const float* scale_b,
+                                       fp8blk_granularity gran_b, int64_t sb_stride_n, int64_t sb_stride_k,
+                                       fp8blk_format fmt_b, void* c, fp8blk_dtype c_dtype, int64_t ldc,
+                                       uint8_t* q_out, int64_t ld_q, float* scale_out, int64_t so_stride_m,
+                                       int64_t so_stride_k, void* stream) {
+  const char* fn = "fp8_quantize_gemm_decode";
+  if (!x || !b || !scale_b || !c) return fail(FP8BLK_EINVAL, "%s: null pointer", fn);
+  if (x_dtype != FP8BLK_BF16 && x_dtype != FP8BLK_F32)
+    return fail(FP8BLK_EINVAL, "%s: unknown input dtype %d", fn, (int)x_dtype);
+  if (c_dtype != FP8BLK_BF16 && c_dtype != FP8BLK_F32)
+    return fail(FP8BLK_EINVAL, "%s: unknown output dtype %d", fn, (int)c_dtype);
+  if (gran_a != FP8BLK_PER_TENSOR && gran_a != FP8BLK_GROUP_1x128)
+    return fail(FP8BLK_EINVAL, "%s: gran_a must be PER_TENSOR or GROUP_1x128", fn);
+  if (gran_b != FP8BLK_PER_TENSOR && gran_b != FP8BLK_BLOCK_128x128)
+    return fail(FP8BLK_EINVAL, "%s: gran_b must be PER_TENSOR or BLOCK_128x128", fn);
+  if (b_packed != 0 && b_packed != 1) return fail(FP8BLK_EINVAL, "%s: b_packed must be 0 or 1", fn);
+  if (fp8blk_status st = check_format(fmt_a, fn)) return st;
+  if (fp8blk_status st = check_format(fmt_b, fn)) return st;
+  if (M < 1 || N <= 0 || K <= 0) return fail(FP8BLK_EINVAL, "%s: need M >= 1, N > 0, K > 0", fn);
+  if (M > 64 || N >= kMaxDim || K >= kMaxDim)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: M must be at most 64 and N, K below 2^31", fn);
+  if (N % 128 != 0 || K % 128 != 0) return fail(FP8BLK_EUNSUPPORTED, "%s: N and K must be multiples of 128", fn);
+  if (gran_a == FP8BLK_PER_TENSOR && M * K > 65536)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: per-tensor M * K above 65536 (quantize and multiply in two calls)", fn);
+  if (b_packed) ldb = K;   // the packed operand spans N * K contiguous bytes
+  if (ld_x < K || ldb < K || ldc < N || (q_out && ld_q < K))
+    return fail(FP8BLK_EINVAL, "%s: leading dimension too small", fn);
+  if (ld_x >= kMaxDim || ldb >= kMaxLdCodes || ldc >= kMaxDim || ld_q >= kMaxDim)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: leading dimension too large", fn);
+  if (sb_stride_n < 0 || sb_stride_k < 0 || so_stride_m < 0 || so_stride_k < 0)
+    return fail(FP8BLK_EINVAL, "%s: negative scale stride", fn);
+  if (sb_stride_n >= kMaxScaleStride || sb_stride_k >= kMaxScaleStride || so_stride_m >= kMaxScaleStride ||
+      so_stride_k >= kMaxScaleStride)
+    return fail(FP8BLK_EUNSUPPORTED, "%s: scale stride above 2^40", fn);
+  const bool group = gran_a == FP8BLK_GROUP_1x128;
+  if (group && scale_out && !grid_cells_distinct(M, K / 128, so_stride_m, so_stride_k))
+    return fail(FP8BLK_EINVAL, "%s: scale_out strides map distinct scales to one float", fn);
+  const int64_t xsz = x_dtype == FP8BLK_BF16 ? 2 : 4;
+  const int64_t csz = c_dtype == FP8BLK_BF16 ? 2 : 4;
+  if (!aligned16(x) || !aligned16(b) || !aligned16(c) || (q_out && !aligned16(q_out)))
+    return fail(FP8BLK_EALIGN, "%s: x, b, c and q_out must be 16-byte aligned", fn);
+  if (!aligned4(scale_b) || (scale_out && !aligned4(scale_out)))
+    return fail(FP8BLK_EALIGN, "%s: scale_b and scale_out must be 4-byte aligned", fn);
+  if ((ld_x * xsz) % 16 != 0 || ldb % 16 != 0 || (ldc * csz) % 16 != 0 || (q_out && ld_q % 16 != 0))
+    return fail(FP8BLK_EALIGN, "%s: ld_x, ldb, ldc and ld_q must span multiples of 16 bytes", fn);
+  const Range in[4] = {range2d(x, M, K, ld_x, xsz), range2d(b, N, K, ldb, 1),
+                       gran_b == FP8BLK_PER_TENSOR ? range_grid(scale_b, 1, 1, 0, 0)
+                                                   : range_grid(scale_b, N / 128, K / 128, sb_stride_n, sb_stride_k),
+                       Range{0, 0}};
+  const Range rc = range2d(c, M, N, ldc, csz);
+  const Range rq = q_out ? range2d(q_out, M, K, ld_q, 1) : Range{0, 0};
+  const Range rs = !scale_out ? Range{0, 0}
+                   : group    ? range_grid(scale_out, M, K / 128, so_stride_m, so_stride_k)
+                              : range_grid(scale_out, 1, 1, 0, 0);
+  if (overlaps_any(rc, in) || overlaps_any(rq, in) || overlaps_any(rs, in) || overlap(rc, rq) || overlap(rc, rs) ||
+      overlap(rq, rs))
+    return fail(FP8BLK_EINVAL, "%s: outputs must not overlap the inputs or each other", fn);
+  fp8blk::QuantGemmDecodeArgs a{};
+  a.g.M = M;
+  a.g.N = N;
+  a.g.K = K;
+  a.g.b = b;
+  a.g.ldb = ldb;
+  a.g.sb = scale_b;
+  a.g.gran_b = (int)gran_b;
+  a.g.sb_n = sb_stride_n;
+  a.g.sb_k = sb_stride_k;
+  a.g.fmt_a = (int)fmt_a;
+  a.g.fmt_b = (int)fmt_b;
+  a.g.c = c;
+  a.g.c_dtype = (int)c_dtype;
+  a.g.ldc = ldc;
+  a.x = x;
+  a.x_dtype = (int)x_dtype;
+  a.ld_x = ld_x;
+  a.gran_a = (int)gran_a;
+  a.packed = b_packed;
+  a.q_out = q_out;
+  a.ld_q = q_out ? ld_q : 0;
+  a.s_out = scale_out;
+  a.so_m = group ? so_stride_m : 0;
+  a.so_k = group ? so_stride_k : 0;
+  return hip_status(fp8blk::launch_quant_gemm_decode(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 fp8blk_status fp8_pack_weights_decode(const uint8_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* packed,
                                       void* stream) {
   const char* fn = "fp8_pack_weights_decode";

@@ -606,18 +606,131 @@ __device__ __forceinline__ v8i load_frag32(const uint8_t* p, int hi_off = 16) {
   return f;
 }
 
+// Two floats to bf16 (the same rounding as __float2bfloat16), low one first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)__bfloat16_as_ushort(__float2bfloat16(lo)) |
+         ((uint32_t)__bfloat16_as_ushort(__float2bfloat16(hi)) << 16);
+}
+
+// The decode kernels' K loop, split-K merge and stores for the 64 output
+// columns at n0. The loader has three stages: fetch(kb) issues the loads of K
+// block kb that go to HBM (a block ahead) and returns them raw; near(kb)
+// issues block kb's loads that hit in L2, before the next fetch, so that
+// waiting for them (load counters drain in issue order) leaves that fetch in
+// flight; frags(raw, near, kb) makes the block's MFMA fragments and scales.
+// `first` is block kb0's fetch, made by the caller (who may issue it early).
+// With kFetchAlways the fetch is made on the last block too (again of that
+// block): a branch around it would leave the compiler unable to count the
+// loads in flight, and it would then wait for all of them before the
+// multiply; and the loop alternates two named buffers, so that no register
+// copy at its back edge waits for the fetch either. The arithmetic (MFMA per block, promotion FMAs, the fixed order of the four
+// waves' sums) does not depend on the loader. red: kDecSplit x (4 MT 64 4)
+// floats of LDS.
+__device__ __forceinline__ int decode_kb0(int K, int wave) { return ((K / 128) * wave) / kDecSplit; }
+__device__ __forceinline__ int decode_kb1(int K, int wave) { return ((K / 128) * (wave + 1)) / kDecSplit; }
+
+template <int MT, bool kBf16Out, int kFa, int kFb, bool kFetchAlways, typename Raw, typename Fetch, typename Near,
+          typename Frags>
+__device__ __forceinline__ void decode_tile(const GemmParams& p, int n0, float* red, Raw first, Fetch&& fetch,
+                                            Near&& near, Frags&& frags) {
+  constexpr int kRed = 4 * MT * 64 * 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kb0 = decode_kb0(p.K, wave);
+  const int kb1 = decode_kb1(p.K, wave);
+
+  v4f acc[4][MT];
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[ns][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  auto multiply = [&](const DecFrags<MT>& f) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const float comb = f.sa[mt] * f.sw;
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) {
+        // weights are the first MFMA operand here
+        const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.w[ns], f.a[mt], zero, kFb, kFa, 0, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[ns][mt][v] = __builtin_fmaf(part[v], comb, acc[ns][mt][v]);
+      }
+    }
+  };
+  if constexpr (kFetchAlways) {
+    Raw ra = first;
+    Raw rb;
+    for (int kb = kb0; kb < kb1;) {
+      const auto na = near(kb);
+      rb = fetch(min(kb + 1, kb1 - 1));
+      multiply(frags(ra, na, kb));
+      if (++kb >= kb1) break;
+      const auto nb = near(kb);
+      ra = fetch(min(kb + 1, kb1 - 1));
+      multiply(frags(rb, nb, kb));
+      ++kb;
+    }
+  } else if (kb0 < kb1) {
+    Raw cur = first;
+    for (int kb = kb0; kb < kb1; ++kb) {
+      const auto nr = near(kb);
+      Raw nxt = cur;
+      if (kb + 1 < kb1) nxt = fetch(kb + 1);
+      multiply(frags(cur, nr, kb));
+      cur = nxt;
+    }
+  }
+
+  // partial sums to LDS: index ((ns * MT + mt) * 64 + lane) * 4 + v
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      *reinterpret_cast<v4f*>(&red[wave * kRed + ((ns * MT + mt) * 64 + lane) * 4]) = acc[ns][mt];
+  __syncthreads();
+
+  // each thread adds the four waves' v4f of one (ns, mt, lane) slot, in wave
+  // order, and stores the 4 adjacent outputs at once (c is 16-byte aligned
+  // with a 16-byte row pitch; n is a multiple of 4)
+  static_assert((kRed / 4) % kDecThreads == 0, "merge slots must split evenly over the threads");
+#pragma unroll
+  for (int i = 0; i < kRed / 4 / kDecThreads; ++i) {
+    const int o = i * kDecThreads + threadIdx.x;
+    v4f sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kDecSplit; ++w) {
+      const v4f r = *reinterpret_cast<const v4f*>(&red[w * kRed + o * 4]);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sum[v] += r[v];
+    }
+    const int ln = o & 63;
+    const int mt = (o >> 6) % MT;
+    const int ns = (o >> 6) / MT;
+    const int m = mt * 16 + (ln & 15);
+    const int n = n0 + ns * 16 + 4 * (ln >> 4);
+    if (m < p.M) {
+      if (kBf16Out) {
+        uint2 pk;
+        pk.x = pack_bf16x2(sum[0], sum[1]);
+        pk.y = pack_bf16x2(sum[2], sum[3]);
+        *reinterpret_cast<uint2*>(static_cast<__hip_bfloat16*>(p.c) + (int64_t)m * p.ldc + n) = pk;
+      } else {
+        *reinterpret_cast<v4f*>(static_cast<float*>(p.c) + (int64_t)m * p.ldc + n) = sum;
+      }
+    }
+  }
+}
+
 // kPacked: the weights are in the decode-packed layout (see
 // k_pack_decode_weights) instead of row-major [N][ldb].
 template <int MT, bool kBf16Out, int kFa, int kFb, bool kPacked>
 __global__ __launch_bounds__(kDecThreads) void k_gemm_fp8_decode(GemmParams p) {
-  __shared__ float red[kDecSplit][4 * MT * 64 * 4];
+  __shared__ float red[kDecSplit * 4 * MT * 64 * 4];
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * kDecBN;
-  const int nk = p.K / 128;
-  const int kb0 = (nk * wave) / kDecSplit;
-  const int kb1 = (nk * (wave + 1)) / kDecSplit;
   const int r16 = lane & 15;
   const int kq = (lane >> 4) * 32;          // this lane's 32 bytes of a K block
 
@@ -654,59 +767,190 @@ __global__ __launch_bounds__(kDecThreads) void k_gemm_fp8_decode(GemmParams p) {
     f.sw = swrow[(int64_t)kb * p.sb_k];
     return f;
   };
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kb0 = decode_kb0(p.K, wave);
+  DecFrags<MT> first;
+  if (kb0 < decode_kb1(p.K, wave)) first = load(kb0);
+  decode_tile<MT, kBf16Out, kFa, kFb, false>(
+      p, n0, red, first, load, [](int) { return 0; }, [](const DecFrags<MT>& f, int, int) { return f; });
+}
 
-  v4f acc[4][MT];
+// The 32 codes of a lane's A fragment, four chunks of values of one group
+// with scale g. With kHoist and bf16 values the scale's fast-path check is
+// made once for all 32 rather than per four (the same codes: Vec8::cast_fast
+// is the fast branch of Vec8::cast); it costs registers, which four M tiles
+// do not have to spare below 256.
+template <int kFmt, bool kHoist, typename T>
+__device__ __forceinline__ void quant_frag(const Vec8<T> (&v)[4], const GroupScale& g, v8i& a) {
+  if constexpr (kHoist && std::is_same<T, __hip_bfloat16>::value) {
+    if (__builtin_expect(bf16_fast_ok(g), 1)) {
 #pragma unroll
-  for (int ns = 0; ns < 4; ++ns)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[ns][mt] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  if (kb0 < kb1) {
-    DecFrags<MT> cur = load(kb0);
-    for (int kb = kb0; kb < kb1; ++kb) {
-      DecFrags<MT> nxt = cur;
-      if (kb + 1 < kb1) nxt = load(kb + 1);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const float comb = cur.sa[mt] * cur.sw;
-#pragma unroll
-        for (int ns = 0; ns < 4; ++ns) {
-          // weights are the first MFMA operand here
-          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur.w[ns], cur.a[mt], zero, kFb, kFa, 0, 0, 0, 0);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[ns][mt][v] = __builtin_fmaf(part[v], comb, acc[ns][mt][v]);
-        }
+      for (int ch = 0; ch < 4; ++ch) {
+        const uint2 cd = v[ch].template cast_fast<kFmt>(g);
+        a[2 * ch] = (int)cd.x;
+        a[2 * ch + 1] = (int)cd.y;
       }
-      cur = nxt;
+      return;
     }
   }
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) {
+    const uint2 cd = v[ch].template cast<kFmt>(g);
+    a[2 * ch] = (int)cd.x;
+    a[2 * ch + 1] = (int)cd.y;
+  }
+}
 
-  // partial sums to LDS: index ((ns * MT + mt) * 64 + lane) * 4 + v
+// Dynamic activation quantization inside the decode GEMM (M <= 64): x is read
+// as bf16 or fp32 and each A fragment is quantized in registers just before
+// the MFMAs that consume it. [FP8] wangyu.me, "大语言模型量化技术（五）：FP8",
+// section "激活动态量化" (activation scales taken at run time, just before the
+// matmul, per tensor or per token and 128-channel group). The weights stream
+// from HBM as in k_gemm_fp8_decode (row-major or decode-packed), which leaves
+// the vector ALUs time to quantize.
+//   kGroup (1x128): lane l's 32 values of a fragment (row 16 mt + l % 16, K
+//   block kb, from value 32 (l / 16)) are a quarter of one group; lanes l ^ 16,
+//   l ^ 32 and l ^ 48 hold the rest, so the group's max is two lane exchanges
+//   away, and its scale is the s_a of that lane's MFMA results.
+//   Per tensor: every workgroup takes the max over the whole (small) tensor
+//   itself (a few L2-resident KB), so no workgroup waits for another.
+// Scales and casts are the quantizer's own (make_group_scale, Vec8::cast), so
+// codes, scales and C equal those of fp8_quantize followed by the decode GEMM
+// bit for bit. With q_out / s_out the codes and scales are stored as well:
+// K block kb by workgroup kb % gridDim.x, from the fragments it multiplies.
+template <int MT, bool kBf16Out, int kFa, int kFb, typename T, bool kGroup>
+__global__ __launch_bounds__(kDecThreads) void k_quant_gemm_decode(GemmParams p, const T* __restrict__ x,
+                                                                   int64_t ld_x, FastDiv div_cpr, int packed,
+                                                                   uint8_t* __restrict__ q_out, int64_t ld_q,
+                                                                   float* __restrict__ s_out, int64_t so_m,
+                                                                   int64_t so_k) {
+  __shared__ float red[kDecSplit * 4 * MT * 64 * 4];
+  __shared__ uint32_t mred[kDecSplit];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+
+  // the weights do not depend on the activation scales: this wave's first K
+  // block of them is fetched before anything else, and the per-tensor max's
+  // latency then covers theirs. Addresses as in k_gemm_fp8_decode.
+  const int n0 = blockIdx.x * kDecBN;
+  const int r16 = lane & 15;
+  const int kq = (lane >> 4) * 32;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kb0 = decode_kb0(p.K, wave);
+  const uint8_t* wrow[4];
 #pragma unroll
   for (int ns = 0; ns < 4; ++ns)
+    wrow[ns] = packed ? p.b + (int64_t)((n0 >> 4) + ns) * 2048 + lane * 16
+                      : p.b + (int64_t)(n0 + ns * 16 + r16) * p.ldb + kq;
+  const int64_t w_kstep = packed ? (int64_t)(p.N >> 4) * 2048 : 128;
+  const int w_hi = packed ? 1024 : 16;
+  const float* swrow = p.sb + (int64_t)(n0 >> 7) * p.sb_n;
+  struct WFrags {
+    v8i w[4];
+    float sw;
+  };
+  auto fetch = [&](int kb) {
+    WFrags r;
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) r.w[ns] = load_frag32(wrow[ns] + (int64_t)kb * w_kstep, w_hi);
+    r.sw = swrow[(int64_t)kb * p.sb_k];
+    return r;
+  };
+  WFrags first;
+  if (kb0 < decode_kb1(p.K, wave)) first = fetch(kb0);
+
+  GroupScale gs_tensor{};
+  if constexpr (!kGroup) {
+    // max |x| over the tensor: batches of 16 chunk loads per thread, all
+    // issued before the first is used; past the end a thread reads the last
+    // chunk again (no branch, and a repeat cannot change a max)
+    const uint32_t cpr = (uint32_t)p.K >> 3;   // chunks of 8 elements per row (K % 128 == 0)
+    const uint32_t nchunks = (uint32_t)p.M * cpr;
+    uint32_t m = 0;
+    constexpr int kBatch = 16;
+    for (uint32_t c0 = tid; c0 < nchunks; c0 += kBatch * kDecThreads) {
+      Vec8<T> v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t c = min(c0 + (uint32_t)u * kDecThreads, nchunks - 1);
+        const uint32_t r = fastdiv(c, div_cpr);
+        v[u].template load<false>(x + (int64_t)r * ld_x + (c - r * cpr) * 8u, 8u);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t a = v[u].amax_bits();
+        m = a > m ? a : m;
+      }
+    }
+    m = wave_max(m);
+    if (lane == 0) mred[wave] = m;
+    __syncthreads();
+    m = 0;
+#pragma unroll
+    for (int w = 0; w < kDecSplit; ++w) m = mred[w] > m ? mred[w] : m;
+    gs_tensor = make_group_scale<kFa>(m);
+    if (s_out != nullptr && blockIdx.x == 0 && tid == 0) *s_out = gs_tensor.s;
+  }
+
+  // the A fragments, quantized from x (lane l: values 32 (l / 16) .. + 31 of
+  // the K block of row 16 mt + l % 16; rows past M repeat row M - 1 and are
+  // neither stored nor multiplied into C)
+  const T* xrow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) xrow[mt] = x + (int64_t)min(mt * 16 + r16, p.M - 1) * ld_x + kq;
+  const bool store_any = q_out != nullptr || (kGroup && s_out != nullptr);
+  struct XRaw {
+    Vec8<T> v[MT][4];
+  };
+  auto near = [&](int kb) {
+    XRaw xr;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      *reinterpret_cast<v4f*>(&red[wave][((ns * MT + mt) * 64 + lane) * 4]) = acc[ns][mt];
-  __syncthreads();
-
-  for (int o = threadIdx.x; o < 4 * MT * 64 * 4; o += kDecThreads) {
-    float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecSplit; ++w) sum += red[w][o];
-    const int v = o & 3;
-    const int ln = (o >> 2) & 63;
-    const int mt = (o >> 8) % MT;
-    const int ns = (o >> 8) / MT;
-    const int m = mt * 16 + (ln & 15);
-    const int n = n0 + ns * 16 + 4 * (ln >> 4) + v;
-    if (m < p.M) {
-      if (kBf16Out)
-        static_cast<__hip_bfloat16*>(p.c)[(int64_t)m * p.ldc + n] = __float2bfloat16(sum);
-      else
-        static_cast<float*>(p.c)[(int64_t)m * p.ldc + n] = sum;
+      for (int ch = 0; ch < 4; ++ch) xr.v[mt][ch].template load<false>(xrow[mt] + (int64_t)kb * 128 + ch * 8, 8u);
+    return xr;
+  };
+  auto frags = [&](const WFrags& r, const XRaw& xr, int kb) {
+    DecFrags<MT> f;
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) f.w[ns] = r.w[ns];
+    const bool store = store_any && (uint32_t)kb % gridDim.x == blockIdx.x;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      GroupScale g = gs_tensor;
+      if constexpr (kGroup) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+          const uint32_t a = xr.v[mt][ch].amax_bits();
+          m = a > m ? a : m;
+        }
+        uint32_t o = (uint32_t)__shfl_xor((int)m, 16);
+        m = o > m ? o : m;
+        o = (uint32_t)__shfl_xor((int)m, 32);
+        m = o > m ? o : m;
+        g = make_group_scale<kFa>(m);
+      }
+      quant_frag<kFa, MT <= 2>(xr.v[mt], g, f.a[mt]);
+      f.sa[mt] = g.s;
+      if (store) {
+        const int row = mt * 16 + r16;
+        if (row < p.M) {
+          if (q_out != nullptr) {
+            uint4* dst = reinterpret_cast<uint4*>(q_out + (int64_t)row * ld_q + (int64_t)kb * 128 + kq);
+            dst[0] = make_uint4((uint32_t)f.a[mt][0], (uint32_t)f.a[mt][1], (uint32_t)f.a[mt][2],
+                                (uint32_t)f.a[mt][3]);
+            dst[1] = make_uint4((uint32_t)f.a[mt][4], (uint32_t)f.a[mt][5], (uint32_t)f.a[mt][6],
+                                (uint32_t)f.a[mt][7]);
+          }
+          if (kGroup && s_out != nullptr && kq == 0) s_out[(int64_t)row * so_m + (int64_t)kb * so_k] = g.s;
+        }
+      }
     }
-  }
+    f.sw = r.sw;
+    return f;
+  };
+  decode_tile<MT, kBf16Out, kFa, kFb, true>(p, n0, red, first, fetch, near, frags);
 }
 
 template <int MT, int kFa, int kFb>
@@ -769,6 +1013,65 @@ int device_cu_count() {
     cached[dev] = n;
   }
   return cached[dev];
+}
+
+namespace {
+template <int MT, int kFa, int kFb, typename T, bool kGroup>
+void launch_quant_gemm_decode_mt(const GemmParams& p, const QuantGemmDecodeArgs& a, FastDiv fd, bool bf16,
+                                 hipStream_t st) {
+  const dim3 grid((unsigned)(p.N / kDecBN));
+  const T* x = static_cast<const T*>(a.x);
+  if (bf16)
+    hipLaunchKernelGGL((k_quant_gemm_decode<MT, true, kFa, kFb, T, kGroup>), grid, dim3(kDecThreads), 0, st, p, x,
+                       a.ld_x, fd, a.packed, a.q_out, a.ld_q, a.s_out, a.so_m, a.so_k);
+  else
+    hipLaunchKernelGGL((k_quant_gemm_decode<MT, false, kFa, kFb, T, kGroup>), grid, dim3(kDecThreads), 0, st, p, x,
+                       a.ld_x, fd, a.packed, a.q_out, a.ld_q, a.s_out, a.so_m, a.so_k);
+}
+
+template <int kFa, int kFb, typename T, bool kGroup>
+void launch_quant_gemm_decode_gran(const GemmParams& p, const QuantGemmDecodeArgs& a, FastDiv fd, bool bf16,
+                                   hipStream_t st) {
+  if (p.M <= 16) launch_quant_gemm_decode_mt<1, kFa, kFb, T, kGroup>(p, a, fd, bf16, st);
+  else if (p.M <= 32) launch_quant_gemm_decode_mt<2, kFa, kFb, T, kGroup>(p, a, fd, bf16, st);
+  else launch_quant_gemm_decode_mt<4, kFa, kFb, T, kGroup>(p, a, fd, bf16, st);
+}
+
+template <int kFa, int kFb>
+void launch_quant_gemm_decode_fmt(const GemmParams& p, const QuantGemmDecodeArgs& a, FastDiv fd, bool bf16,
+                                  hipStream_t st) {
+  const bool group = a.gran_a == GRAN_GROUP_1x128;
+  if (a.x_dtype == DTYPE_BF16) {
+    if (group) launch_quant_gemm_decode_gran<kFa, kFb, __hip_bfloat16, true>(p, a, fd, bf16, st);
+    else launch_quant_gemm_decode_gran<kFa, kFb, __hip_bfloat16, false>(p, a, fd, bf16, st);
+  } else {
+    if (group) launch_quant_gemm_decode_gran<kFa, kFb, float, true>(p, a, fd, bf16, st);
+    else launch_quant_gemm_decode_gran<kFa, kFb, float, false>(p, a, fd, bf16, st);
+  }
+}
+}  // namespace
+
+hipError_t launch_quant_gemm_decode(const QuantGemmDecodeArgs& a, hipStream_t st) {
+  const GemmArgs& g = a.g;
+  GemmParams p{};
+  p.b = g.b;
+  p.sb = g.sb;
+  p.c = g.c;
+  p.ldb = g.ldb;
+  p.ldc = g.ldc;
+  p.sb_n = g.gran_b == GRAN_PER_TENSOR ? 0 : g.sb_n;
+  p.sb_k = g.gran_b == GRAN_PER_TENSOR ? 0 : g.sb_k;
+  p.M = (int)g.M;
+  p.N = (int)g.N;
+  p.K = (int)g.K;
+  const FastDiv fd = make_fastdiv((uint32_t)(g.K / 8));
+  const bool bf16 = g.c_dtype == DTYPE_BF16;
+  const bool a5 = g.fmt_a == FMT_E5M2, b5 = g.fmt_b == FMT_E5M2;
+  if (!a5 && !b5) launch_quant_gemm_decode_fmt<FMT_E4M3, FMT_E4M3>(p, a, fd, bf16, st);
+  else if (!a5 && b5) launch_quant_gemm_decode_fmt<FMT_E4M3, FMT_E5M2>(p, a, fd, bf16, st);
+  else if (a5 && !b5) launch_quant_gemm_decode_fmt<FMT_E5M2, FMT_E4M3>(p, a, fd, bf16, st);
+  else launch_quant_gemm_decode_fmt<FMT_E5M2, FMT_E5M2>(p, a, fd, bf16, st);
+  return hipGetLastError();
 }
 
 hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t st) {

@@ -72,6 +72,26 @@ struct GemmArgs {
   int b_packed;
 };
 
+// Dynamic activation quantization inside the decode GEMM: g holds M (<= 64),
+// N, K, the weights (row-major, or decode-packed with packed != 0), their
+// scales and the output as for launch_block_gemm (g.fmt_a is the format of
+// the activation codes); x [M][ld_x] of x_dtype; gran_a GRAN_PER_TENSOR
+// (M * K <= 65536) or GRAN_GROUP_1x128; q_out (row stride ld_q) and s_out
+// (per tensor: s_out[0]; 1x128: s_out[m * so_m + j * so_k]) may be null.
+struct QuantGemmDecodeArgs {
+  GemmArgs g;
+  const void* x;
+  int x_dtype;
+  int64_t ld_x;
+  int gran_a;
+  int packed;
+  uint8_t* q_out;
+  int64_t ld_q;
+  float* s_out;
+  int64_t so_m;
+  int64_t so_k;
+};
+
 struct AttnArgs {
   const void* q;          // bf16 [heads_q][ld_q]
   int64_t ld_q;
@@ -109,6 +129,7 @@ hipError_t launch_kv_decode_attention(const AttnArgs& a, hipStream_t st);
 hipError_t launch_kv_quantize(const KvArgs& a, hipStream_t st);
 hipError_t launch_kv_dequantize(const KvArgs& a, hipStream_t st);
 hipError_t launch_block_gemm(const GemmArgs& a, hipStream_t st);
+hipError_t launch_quant_gemm_decode(const QuantGemmDecodeArgs& a, hipStream_t st);
 // Row-major weight codes [N][ldw] (N % 16 == 0, K % 128 == 0) to the
 // decode-packed layout: 2 KB per (16-row group rg, K block kb) at
 // (kb * N / 16 + rg) * 2048.

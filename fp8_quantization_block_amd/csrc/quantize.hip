@@ -24,138 +24,6 @@
 
 namespace fp8blk {
 
-// ---------------------------------------------------------------------------
-// Eight consecutive input elements of one lane.
-//
-// Loads are streaming (nontemporal) by default: every quantizer reads its
-// input exactly once, and keeping it out of the caches measured 8-17% faster
-// on the large passes. The per-tensor amax pass reads with normal loads so
-// that its second (cast) pass can hit the Infinity Cache.
-// ---------------------------------------------------------------------------
-typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-
-template <bool kStream>
-__device__ __forceinline__ uint4 load16(const void* p) {
-  if (kStream) {
-    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
-    return make_uint4(t[0], t[1], t[2], t[3]);
-  }
-  return *reinterpret_cast<const uint4*>(p);
-}
-
-template <typename T>
-struct Vec8;
-
-template <>
-struct Vec8<__hip_bfloat16> {
-  uint4 w;
-  template <bool kStream = true>
-  __device__ __forceinline__ void load(const __hip_bfloat16* p, uint32_t nvalid) {
-    if (nvalid >= 8) {
-      w = load16<kStream>(p);
-    } else {
-      const uint16_t* h = reinterpret_cast<const uint16_t*>(p);
-      uint32_t e[8];
-#pragma unroll
-      for (uint32_t i = 0; i < 8; ++i) e[i] = i < nvalid ? (uint32_t)h[i] : 0u;
-      w.x = e[0] | (e[1] << 16);
-      w.y = e[2] | (e[3] << 16);
-      w.z = e[4] | (e[5] << 16);
-      w.w = e[6] | (e[7] << 16);
-    }
-  }
-  __device__ __forceinline__ void zero() { w = make_uint4(0, 0, 0, 0); }
-  __device__ __forceinline__ uint32_t amax_bits() const { return amax_bf16x8(w); }
-  template <int kFmt>
-  __device__ __forceinline__ uint2 cast(const GroupScale& g) const {
-    uint2 r;
-    r.x = cast4_bf16<kFmt>(g, bf16_lo_to_f32(w.x), bf16_hi_to_f32(w.x), bf16_lo_to_f32(w.y), bf16_hi_to_f32(w.y));
-    r.y = cast4_bf16<kFmt>(g, bf16_lo_to_f32(w.z), bf16_hi_to_f32(w.z), bf16_lo_to_f32(w.w), bf16_hi_to_f32(w.w));
-    return r;
-  }
-  template <int kFmt>
-  __device__ __forceinline__ uint2 cast_sat(const GroupScale& g) const {
-    uint2 r;
-    r.x = cast4_sat<kFmt>(g, bf16_lo_to_f32(w.x), bf16_hi_to_f32(w.x), bf16_lo_to_f32(w.y), bf16_hi_to_f32(w.y));
-    r.y = cast4_sat<kFmt>(g, bf16_lo_to_f32(w.z), bf16_hi_to_f32(w.z), bf16_lo_to_f32(w.w), bf16_hi_to_f32(w.w));
-    return r;
-  }
-  // codes of x * 2^e (exact scaling), saturating
-  template <int kFmt>
-  __device__ __forceinline__ uint2 cast_pow2(int e) const {
-    uint2 r;
-    r.x = pack4_sat<kFmt>(__builtin_amdgcn_ldexpf(bf16_lo_to_f32(w.x), e), __builtin_amdgcn_ldexpf(bf16_hi_to_f32(w.x), e),
-                          __builtin_amdgcn_ldexpf(bf16_lo_to_f32(w.y), e), __builtin_amdgcn_ldexpf(bf16_hi_to_f32(w.y), e));
-    r.y = pack4_sat<kFmt>(__builtin_amdgcn_ldexpf(bf16_lo_to_f32(w.z), e), __builtin_amdgcn_ldexpf(bf16_hi_to_f32(w.z), e),
-                          __builtin_amdgcn_ldexpf(bf16_lo_to_f32(w.w), e), __builtin_amdgcn_ldexpf(bf16_hi_to_f32(w.w), e));
-    return r;
-  }
-};
-
-template <>
-struct Vec8<float> {
-  float4 a, b;
-  template <bool kStream = true>
-  __device__ __forceinline__ void load(const float* p, uint32_t nvalid) {
-    if (nvalid >= 8) {
-      const uint4 ua = load16<kStream>(p), ub = load16<kStream>(p + 4);
-      a = make_float4(__uint_as_float(ua.x), __uint_as_float(ua.y), __uint_as_float(ua.z), __uint_as_float(ua.w));
-      b = make_float4(__uint_as_float(ub.x), __uint_as_float(ub.y), __uint_as_float(ub.z), __uint_as_float(ub.w));
-    } else {
-      float e[8];
-#pragma unroll
-      for (uint32_t i = 0; i < 8; ++i) e[i] = i < nvalid ? p[i] : 0.0f;
-      a = make_float4(e[0], e[1], e[2], e[3]);
-      b = make_float4(e[4], e[5], e[6], e[7]);
-    }
-  }
-  __device__ __forceinline__ void zero() {
-    a = make_float4(0, 0, 0, 0);
-    b = a;
-  }
-  __device__ __forceinline__ uint32_t amax_bits() const {
-    uint32_t m = 0;
-    m = amax_f32(a.x, m); m = amax_f32(a.y, m); m = amax_f32(a.z, m); m = amax_f32(a.w, m);
-    m = amax_f32(b.x, m); m = amax_f32(b.y, m); m = amax_f32(b.z, m); m = amax_f32(b.w, m);
-    return m;
-  }
-  template <int kFmt>
-  __device__ __forceinline__ uint2 cast(const GroupScale& g) const {
-    uint2 r;
-    r.x = cast4_f32<kFmt>(g, a.x, a.y, a.z, a.w);
-    r.y = cast4_f32<kFmt>(g, b.x, b.y, b.z, b.w);
-    return r;
-  }
-  template <int kFmt>
-  __device__ __forceinline__ uint2 cast_sat(const GroupScale& g) const {
-    uint2 r;
-    r.x = cast4_sat<kFmt>(g, a.x, a.y, a.z, a.w);
-    r.y = cast4_sat<kFmt>(g, b.x, b.y, b.z, b.w);
-    return r;
-  }
-  template <int kFmt>
-  __device__ __forceinline__ uint2 cast_pow2(int e) const {
-    uint2 r;
-    r.x = pack4_sat<kFmt>(__builtin_amdgcn_ldexpf(a.x, e), __builtin_amdgcn_ldexpf(a.y, e),
-                          __builtin_amdgcn_ldexpf(a.z, e), __builtin_amdgcn_ldexpf(a.w, e));
-    r.y = pack4_sat<kFmt>(__builtin_amdgcn_ldexpf(b.x, e), __builtin_amdgcn_ldexpf(b.y, e),
-                          __builtin_amdgcn_ldexpf(b.z, e), __builtin_amdgcn_ldexpf(b.w, e));
-    return r;
-  }
-};
-
-__device__ __forceinline__ void store_codes8(uint8_t* p, uint2 c, uint32_t nvalid) {
-  if (nvalid >= 8) {
-    *reinterpret_cast<uint2*>(p) = c;
-  } else {
-#pragma unroll
-    for (uint32_t i = 0; i < 8; ++i) {
-      const uint32_t word = i < 4 ? c.x : c.y;
-      if (i < nvalid) p[i] = (uint8_t)(word >> (8 * (i & 3)));
-    }
-  }
-}
-
 // Block-wide max over non-negative fp32 bit patterns (blockDim.x == 256).
 __device__ __forceinline__ uint32_t block256_max(uint32_t m) {
   __shared__ uint32_t red[4];
@@ -356,9 +224,9 @@ __global__ __launch_bounds__(256) void k_kv_dequant(
       o[2 * k + 1] = (uint32_t)__bfloat16_as_ushort(e2) | ((uint32_t)__bfloat16_as_ushort(e3) << 16);
     }
     // streaming store: the output is written once (measured 22% faster)
-    v4u t;
+    v4u32 t;
     t[0] = o[0]; t[1] = o[1]; t[2] = o[2]; t[3] = o[3];
-    __builtin_nontemporal_store(t, reinterpret_cast<v4u*>(dst + c));
+    __builtin_nontemporal_store(t, reinterpret_cast<v4u32*>(dst + c));
   }
 }
 
@@ -703,16 +571,6 @@ __global__ __launch_bounds__(256) void k_scale_from_history(const float* __restr
 // ---------------------------------------------------------------------------
 namespace {
 constexpr int kGroupUnroll = 1;   // 1 group per 8 lanes: measured 6-10% faster than 2 or 4
-
-// Multiplier and shift for fastdiv by d >= 1 (see device_common.h).
-FastDiv make_fastdiv(uint32_t d) {
-  uint32_t l = 0;
-  while ((1ull << l) < d) ++l;
-  FastDiv f;
-  f.m = (uint32_t)((((1ull << l) - d) << 32) / d + 1);
-  f.l = l;
-  return f;
-}
 
 constexpr int kAmaxUnroll = 4;            // chunks in flight per thread in the amax-only pass
 constexpr int kCastUnroll = 2;            // ... in the cast passes

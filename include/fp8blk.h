@@ -187,6 +187,58 @@ fp8blk_status fp8_block_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_
                                    int64_t sc_stride_m, int64_t sc_stride_n, void* stream);
 
 /*
+ * fp8_quantize_gemm_decode -- dynamic quantization of a decode step's
+ * activations inside the block-scaled GEMM that consumes them, in one launch
+ * (M <= 64): C = fp8_block_gemm(fp8_quantize(x, gran_a, fmt_a), W).
+ *
+ * The activation scales are taken at run time, just before the matmul that
+ * consumes the codes ([FP8] wangyu.me, "大语言模型量化技术（五）：FP8", section
+ * "激活动态量化"): per tensor, or per token and 128-channel group; s =
+ * fl32(amax(|x|) / MAX) and q = FP8(fl32(x / s)) with the saturating
+ * round-to-nearest-even cast. At decode shapes the GEMM is bound by streaming
+ * the weights from HBM, and each of its workgroups quantizes the activation
+ * fragments it multiplies in registers: a 1x128 group lies within one
+ * fragment, and a per-tensor max is taken by every workgroup over the whole,
+ * small, tensor. Codes, scales and C are bit-identical to fp8_quantize(x,
+ * gran_a, fmt_a) followed by fp8_block_gemm (row-major weights) or
+ * fp8_block_gemm_packed (b_packed = 1) on those codes and scales.
+ *
+ *   x          device, [M][ld_x] of x_dtype (BF16 or F32), row-major.
+ *   gran_a     PER_TENSOR or GROUP_1x128.
+ *   fmt_a      format of the activation codes.
+ *   b, ldb     device weight codes: row-major [N][ldb] bytes (b_packed = 0),
+ *              or the decode-packed layout of fp8_pack_weights_decode
+ *              (b_packed = 1; ldb is then ignored).
+ *   scale_b, gran_b, sb_stride_n, sb_stride_k, fmt_b
+ *              the weight scales and format, as for fp8_block_gemm.
+ *   c          device, [M][ldc] of c_dtype (BF16 or F32).
+ *   q_out      device, [M][ld_q] uint8, or NULL: if given, the activation
+ *              codes, as fp8_quantize writes them.
+ *   scale_out  device fp32, or NULL: if given, the activation scales, as
+ *              fp8_quantize writes them: scale_out[0] for PER_TENSOR; for
+ *              GROUP_1x128 the [M][K / 128] grid at
+ *              scale_out[m * so_stride_m + j * so_stride_k] (the strides are
+ *              ignored for PER_TENSOR).
+ *
+ * Requirements: x, b, scale_b, c non-null; 1 <= M <= 64 (M < 1: FP8BLK_EINVAL;
+ * M > 64: FP8BLK_EUNSUPPORTED, prefill shapes take the two calls); N, K
+ * positive multiples of 128 below 2^31; PER_TENSOR needs M * K <= 65536 (else
+ * FP8BLK_EUNSUPPORTED); b_packed 0 or 1; ld_x >= K, x 16-byte aligned and
+ * ld_x * elem_size a multiple of 16; the weights' and C's requirements of
+ * fp8_block_gemm; q_out, if given, 16-byte aligned with ld_q >= K a multiple
+ * of 16; scale_out 4-byte aligned, its strides >= 0, below 2^40 and mapping
+ * distinct grid cells to distinct floats. The outputs must not overlap the
+ * inputs or each other. Any failure is reported before anything is written.
+ */
+fp8blk_status fp8_quantize_gemm_decode(const void* x, fp8blk_dtype x_dtype, int64_t M, int64_t N, int64_t K,
+                                       int64_t ld_x, fp8blk_granularity gran_a, fp8blk_format fmt_a,
+                                       const uint8_t* b, int64_t ldb, int b_packed, const float* scale_b,
+                                       fp8blk_granularity gran_b, int64_t sb_stride_n, int64_t sb_stride_k,
+                                       fp8blk_format fmt_b, void* c, fp8blk_dtype c_dtype, int64_t ldc,
+                                       uint8_t* q_out, int64_t ld_q, float* scale_out, int64_t so_stride_m,
+                                       int64_t so_stride_k, void* stream);
+
+/*
  * fp8_pack_weights_decode -- copy row-major weight codes into the
  * decode-packed layout read by fp8_block_gemm_packed.
  *

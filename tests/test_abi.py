@@ -43,6 +43,7 @@ def test_header_declares_the_entry_points():
     for n in ("fp8_quantize", "fp8_block_gemm", "fp8_block_gemm_quant", "fp8_kv_quantize", "fp8_kv_dequantize",
               "fp8_kv_decode_attention", "fp8_kv_decode_attention_workspace_size", "fp8_quantize_mx", "fp8_mx_gemm",
               "fp8_quantize_static", "fp8_scale_from_amax_history", "fp8_kv_decode_attention_noalloc",
+              "fp8_quantize_gemm_decode",
               "fp8blk_status_string", "fp8blk_last_error", "fp8blk_abi_version"):
         assert n in names
 
@@ -364,6 +365,45 @@ def test_kv_dequantize_rejects(lib, args, status):
 
 def test_gemm_rejects_huge_leading_dimension(lib):
     assert g(lib, lda=1 << 23) == EUNSUPPORTED
+
+
+def qgd(lib, x=PA, xdt=BF16, M=64, N=512, K=512, ldx=512, ga=PER_TENSOR, fa=E4M3, b=PB, ldb=512, packed=0, sb=PC,
+        gb=PER_TENSOR, sbn=0, sbk=0, fb=E4M3, c=PD, cdt=BF16, ldc=512, q=PD + (1 << 20), ldq=512, s=PD + (2 << 20),
+        som=0, sok=0):
+    return lib.fp8_quantize_gemm_decode(x, xdt, M, N, K, ldx, ga, fa, b, ldb, packed, sb, gb, sbn, sbk, fb, c, cdt,
+                                        ldc, q, ldq, s, som, sok, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=0), EINVAL),
+    (dict(c=0), EINVAL),
+    (dict(xdt=2), EINVAL),
+    (dict(cdt=2), EINVAL),
+    (dict(gb=GROUP), EINVAL),
+    (dict(ga=2), EINVAL),                       # activation scales are per tensor or 1x128
+    (dict(packed=2), EINVAL),
+    (dict(fa=2), EINVAL),
+    (dict(M=0), EINVAL),
+    (dict(M=65), EUNSUPPORTED),                 # prefill shapes take the two calls
+    (dict(M=64, K=1152, ldx=1152, ldb=1152, ldq=1152), EUNSUPPORTED),   # per tensor: M * K above 65536
+    (dict(N=192, ldc=192), EUNSUPPORTED),
+    (dict(K=200, ldx=200, ldb=208, ldq=208), EUNSUPPORTED),
+    (dict(ldx=256), EINVAL),
+    (dict(ldq=256), EINVAL),
+    (dict(x=PA + 8), EALIGN),
+    (dict(ldx=516), EALIGN),
+    (dict(s=PD + (2 << 20) + 2), EALIGN),
+    (dict(q=PD + 1024), EINVAL),               # codes overlap the output
+    (dict(c=PA + 1024), EINVAL),               # output overlaps the activations
+    (dict(ga=GROUP, som=-1, sok=64), EINVAL),
+    (dict(ga=GROUP, som=1, sok=1), EINVAL),    # two scales of the grid on one float
+    (dict(ga=GROUP, som=1 << 40, sok=1), EUNSUPPORTED),
+    (dict(ga=GROUP, som=4, sok=1, s=PD + 4), EINVAL),   # scale grid overlaps the output
+    (dict(ga=GROUP, packed=1, ldb=7, c=PB + 1024), EINVAL),   # packed: ldb ignored, the N * K bytes still checked
+])
+def test_quantize_gemm_decode_rejects(lib, kw, status):
+    assert qgd(lib, **kw) == status
+    assert lib.fp8blk_last_error().decode().startswith("fp8_quantize_gemm_decode")
 
 
 def pk(lib, w=PA, N=256, K=256, ldw=256, out=PB):

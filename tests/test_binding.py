@@ -15,7 +15,8 @@ LIB = os.path.join(ROOT, "fp8_quantization_block_amd", "libfp8blk.so")
 
 NAMES = ("fp8_quantize", "fp8_block_gemm", "fp8_block_gemm_quant", "fp8_kv_quantize", "fp8_kv_dequantize",
          "fp8_kv_decode_attention", "fp8_quantize_static", "fp8_scale_from_amax_history", "fp8_quantize_mx",
-         "fp8_mx_gemm", "fp8_pack_weights_decode", "fp8_block_gemm_packed", "fp8_kv_decode_attention_noalloc")
+         "fp8_mx_gemm", "fp8_pack_weights_decode", "fp8_block_gemm_packed", "fp8_kv_decode_attention_noalloc",
+         "fp8_quantize_gemm_decode")
 
 
 @pytest.fixture(scope="module")
@@ -47,6 +48,7 @@ def test_host_tensors_are_refused(fp8):
         lambda: fp8.fp8_block_gemm_quant(u8, s, "per_tensor", u8, s, "per_tensor"),
         lambda: fp8.fp8_mx_gemm(u8, u8, u8, u8),
         lambda: fp8.fp8_pack_weights_decode(u8),
+        lambda: fp8.fp8_quantize_gemm_decode(x, u8, s, "per_tensor"),
         lambda: fp8.fp8_block_gemm_packed(u8, s, "per_tensor", torch.zeros(2, 16, 2048, dtype=torch.uint8), s,
                                           "per_tensor"),
         lambda: fp8.fp8_kv_quantize(torch.zeros(1, 128, 128, dtype=torch.bfloat16)),

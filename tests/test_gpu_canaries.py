@@ -131,6 +131,30 @@ def test_gemms(gpu_lib, M):
     c.check(f"MX GEMM M={M}")
 
 
+@pytest.mark.parametrize("gran_a", ["per_tensor", "group_1x128"])
+@pytest.mark.parametrize("packed", [False, True])
+def test_quantize_gemm_decode(gpu_lib, gran_a, packed):
+    M, N, K = 40, 384, 512
+    x = _x(M, K, 9)
+    qw, sw = gpu_lib.fp8_quantize((_x(N, K, 8) * 0.02).contiguous(), "block_128x128")
+    w_arg = gpu_lib.fp8_pack_weights_decode(qw) if packed else qw
+    for dtype, ld in ((torch.bfloat16, N + 8), (torch.float32, N + 4)):
+        c = Guarded(M, N, ld, dtype)
+        q = Guarded(M, K, K + 16, torch.uint8)
+        if gran_a == "per_tensor":
+            s = Guarded(1, 1, 4, torch.float32)
+            sv = s.view[0]
+        else:
+            s = Guarded(K // 128, M, M + 3, torch.float32)   # K-block-major grid, padded
+            sv = s.view.t()
+        gpu_lib.fp8_quantize_gemm_decode(x, w_arg, sw, "block_128x128", gran_a=gran_a, out=c.view, codes=q.view,
+                                         scales=sv)
+        what = f"quantize inside the decode GEMM ({gran_a}, packed={packed}) {dtype}"
+        c.check(what + " output")
+        q.check(what + " codes")
+        s.check(what + " scales")
+
+
 def test_packed_decode(gpu_lib):
     M, N, K = 40, 384, 256
     qa, sa = gpu_lib.fp8_quantize(_x(M, K, M), "group_1x128", scale_layout="kmajor")
