@@ -6,6 +6,7 @@ Usage: python -m fp8_quantization_block_amd.build [--verbose]
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -41,19 +42,30 @@ def build(verbose: bool = False) -> str:
     return _compile(SOURCES, LIB, verbose)
 
 
-def _compile(sources, lib, verbose):
-    srcs = [os.path.join(CSRC, s) for s in sources]
-    tmp = lib + ".tmp"
-    cmd = [HIPCC] + FLAGS + srcs + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in res.stdout.splitlines()
                     if "packed-fp32-ops" not in l and "is not a recognized feature" not in l)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + out)
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + out)
     if verbose and out.strip():
         print(out)
+
+
+def _compile(sources, lib, verbose):
+    """Each source to an object in parallel (each carries its own gfx950 code
+    object), then one link into the shared library."""
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    objs = [lib + "." + os.path.splitext(s)[0] + ".o" for s in sources]
+    cmds = [[HIPCC] + compile_flags + ["-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(sources, objs)]
+    with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1, 8)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = lib + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
+    for o in objs:
+        os.remove(o)
     os.replace(tmp, lib)
     return lib
 
