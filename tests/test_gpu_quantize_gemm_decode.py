@@ -178,3 +178,33 @@ def test_decode_step_against_the_oracle(gpu_lib, packed):
                               cols=cols)
     check_gemm_tolerance(y.cpu().numpy()[:, cols], y64, t, bf16=False, what="decode step fused")
     assert y.shape == (M, N)
+
+
+@pytest.mark.parametrize("gran_a", ["per_tensor", "group_1x128"])
+@pytest.mark.parametrize("packed", [False, True])
+def test_nonfinite_inputs_as_the_two_calls(gpu_lib, gran_a, packed):
+    """NaN and infinities in x are outside the quantizers' contract (their
+    codes are unspecified), but the one-launch call still returns normally
+    and computes what the two calls compute: codes and scales bit for bit, C
+    bit for bit wherever it is finite and non-finite in the same places."""
+    M, N, K = 48, 256, 512
+    x = syn.activations(3, M=M, K=K, variant=13).to(DEV).float()
+    x[0, 5] = float("nan")
+    x[9, 130] = float("inf")
+    x[20, 300] = float("-inf")
+    x = x.to(torch.bfloat16)
+    qw, sw = _weights(gpu_lib, N, K, "block_128x128", "e4m3", 14, config=3)
+    qw_packed = gpu_lib.fp8_pack_weights_decode(qw) if packed else None
+    y, q, s = gpu_lib.fp8_quantize_gemm_decode(x, qw_packed if packed else qw, sw, "block_128x128", gran_a=gran_a,
+                                               out_dtype=torch.float32, return_codes=True)
+    y2, q2, s2 = _two_calls(gpu_lib, x, qw, sw, "block_128x128", gran_a, "e4m3", "e4m3", torch.float32, qw_packed,
+                            "row")
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(s), _bits(s2)), "scales differ"
+    assert torch.equal(q, q2), "codes differ"
+    fin = torch.isfinite(y2)
+    assert torch.equal(torch.isfinite(y), fin), "non-finite outputs in different places"
+    assert torch.equal(torch.isnan(y), torch.isnan(y2)), "NaN outputs in different places"
+    assert torch.equal(_bits(torch.where(fin, y, 0.0)), _bits(torch.where(fin, y2, 0.0))), "finite outputs differ"
+    if gran_a == "group_1x128":
+        assert fin.sum() > 0, "every output non-finite: the clean groups were disturbed"
