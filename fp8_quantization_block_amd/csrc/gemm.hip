@@ -813,7 +813,8 @@ __device__ __forceinline__ void quant_frag(const Vec8<T> (&v)[4], const GroupSca
 //   l ^ 32 and l ^ 48 hold the rest, so the group's max is two lane exchanges
 //   away, and its scale is the s_a of that lane's MFMA results.
 //   Per tensor: every workgroup takes the max over the whole (small) tensor
-//   itself (a few L2-resident KB), so no workgroup waits for another.
+//   itself (at most 64K elements, 128 KB of bf16, mostly read from L2), so no
+//   workgroup waits for another.
 // Scales and casts are the quantizer's own (make_group_scale, Vec8::cast), so
 // codes, scales and C equal those of fp8_quantize followed by the decode GEMM
 // bit for bit. With q_out / s_out the codes and scales are stored as well:
