@@ -668,14 +668,17 @@ def passes_kv(args, torch, syn, fp8, timer, dev):
         qd = syn.decode_queries(heads_q=hq).to(dev)
         od = torch.empty((hq, D), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(lib.fp8_kv_decode_attention_workspace_size(hq, T), dtype=torch.uint8, device=dev)
-        fname = "e5m2" if fmt == fp8.E5M2 else "e4m3"
         # two copies of the 268 MB cache, alternated: more than the Infinity
         # Cache, so the codes stream from HBM
         caches = [(qk, sk, qv, sv), (qk.clone(), sk, qv.clone(), sv)]
 
-        def att(i, fname=fname):
+        # through the C ABI, like the quantize calls above: the binding's
+        # per-call shape checks would otherwise add host time to a 50 us call
+        def att(i, fmt=fmt):
             ck, cks, cv, cvs = caches[i % 2]
-            fp8.fp8_kv_decode_attention(qd, ck, cks, cv, cvs, 1.0 / 128 ** 0.5, fmt=fname, out=od, workspace=ws)
+            fp8._check(lib.fp8_kv_decode_attention(qd.data_ptr(), D, hq, H, T, D, ck.data_ptr(), cks.data_ptr(),
+                                                   cv.data_ptr(), cvs.data_ptr(), 128, fmt, 1.0 / 128 ** 0.5,
+                                                   od.data_ptr(), fp8.BF16, D, ws.data_ptr(), ws.numel(), stream))
 
         att_bytes = n + 2 * H * (T // 128) * 4 + 2 * hq * D * 2
         t_att = timer.run(att, 20, warmup=3, name="kv_decode_attention" + tag)

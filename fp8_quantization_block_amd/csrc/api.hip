@@ -639,7 +639,7 @@ fp8blk_status check_attention(const char* fn, const void* q, int64_t ld_q, int64
   if (workspace == nullptr) {
     if (need > fp8blk::attention_scratch_bytes())
       return fail(FP8BLK_EUNSUPPORTED, "%s: needs %zu bytes of workspace; the fixed workspace holds %zu "
-                  "(heads_q * ceil(tokens / 2048) <= %zu)", fn, need, fp8blk::attention_scratch_bytes(),
+                  "(heads_q * ceil(tokens / 1408) <= %zu)", fn, need, fp8blk::attention_scratch_bytes(),
                   fp8blk::attention_scratch_bytes() / ((size_t)fp8blk::attention_partial_floats() * sizeof(float)));
   } else if (workspace_bytes < need) {
     return fail(FP8BLK_EINVAL, "%s: workspace smaller than %zu bytes", fn, need);

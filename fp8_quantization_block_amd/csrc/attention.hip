@@ -8,13 +8,19 @@
 // [MIXED] charles2530.github.io, "量化：FP8 与混合精度推理", section "scale 是控制面"
 // (KV-cache scales per head, read by the attention backend).
 //
-// Design (gfx950), one workgroup of 4 waves per (kv head, 2048-token split),
-// two workgroups per compute unit (64 KB of LDS each):
-// * Each wave streams its 512 tokens in 32-token units through a ring of 2
-//   LDS stages: the K and V codes of the next unit go into the wave's own
-//   stage by direct global -> LDS copies (non-temporal) while the current
-//   unit is computed. Rows are 128 bytes; logical 16-byte chunk c of row r is
-//   stored at c ^ (r % 8), so that 16 lanes reading one chunk of 16
+// Design (gfx950), one workgroup of 4 waves per (kv head, 1408-token split),
+// 48 KB of LDS each, three workgroups per compute unit (for the 8 x 131072
+// cache: 94 splits x 8 heads = 752 workgroups, one round on 256 compute
+// units; measured 48.1 us against 51.7 us for 2048-token splits with K and V
+// both staged in the LDS, two workgroups per compute unit):
+// * Each wave streams its 352 tokens in 32-token units, two units ahead of
+//   the one it computes (16 KB of codes in flight per wave, 192 KB per compute
+//   unit): the K codes of a unit go straight into registers (each lane loads
+//   the 32 bytes of a key that it multiplies), the V codes into a ring of 3
+//   LDS stages of the wave's own by direct global -> LDS copies; both carry
+//   the non-temporal hint. Keeping K out of the LDS is what lets three
+//   workgroups share a compute unit. V rows are 128 bytes; logical 16-byte chunk c of
+//   row r is stored at c ^ (r % 8), so that 16 lanes reading one chunk of 16
 //   consecutive rows hit distinct banks. The kernel is bound by reading the
 //   codes from HBM.
 // * Scores S^T = K Q^T on the bf16 MFMA (16 x 16 x 32): FP8 codes convert to
@@ -53,9 +59,9 @@ constexpr int kWaves = 4;
 constexpr int kThreadsA = kWaves * 64;
 constexpr int kUnit = 32;                  // tokens per unit
 constexpr int kSub = kUnit / 16;           // 16-token subtiles per unit
-constexpr int kUnitsPerWave = 16;          // 512 tokens per wave
-constexpr int kStages = 2;                 // LDS ring per wave (1 unit in flight)
-constexpr int kSplitTokens = kWaves * kUnitsPerWave * kUnit;   // 2048
+constexpr int kUnitsPerWave = 11;          // 352 tokens per wave
+constexpr int kStages = 3;                 // V stages per wave (2 units in flight)
+constexpr int kSplitTokens = kWaves * kUnitsPerWave * kUnit;   // 1408
 constexpr int kUnitBytes = kUnit * kD;     // 4 KB of codes per tensor
 constexpr int kCopies = kUnitBytes / 1024; // 1 KB copies per tensor and unit
 constexpr int kPartial = kD + 2;           // floats per (query head, split): O[128], m, l
@@ -104,7 +110,7 @@ __device__ __forceinline__ uint32_t hi2(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
-// Codes of one unit (32 token rows of 128 bytes) into an LDS buffer: 4
+// V codes of one unit (32 token rows of 128 bytes) into an LDS buffer: 4
 // copies of 1 KB. Lane l of copy i fills row 8 i + l / 8, physical chunk l % 8,
 // i.e. logical chunk (l % 8) ^ (row % 8). Every offset is in the VGPR offset,
 // which the buffer's range check covers (rows past T read zero). The codes
@@ -113,6 +119,22 @@ __device__ __forceinline__ void load_unit(__amdgpu_buffer_rsrc_t r, uint32_t uni
                                           uint8_t* buf) {
 #pragma unroll
   for (int i = 0; i < kCopies; ++i) dma16_nt(r, unit_off + (uint32_t)(i * 1024) + lane_voff, 0u, buf + i * 1024);
+}
+
+// K codes of one unit in registers: for subtile i, the lane's A operand of
+// the score MFMAs, i.e. bytes 32 g .. 32 g + 31 of token row 16 i + c (g =
+// lane / 16, c = lane % 16), as two 16-byte words. Loaded through the buffer
+// resource (rows past T read zero) with the non-temporal hint.
+struct KRegs {
+  v4u w[kSub][2];
+};
+
+__device__ __forceinline__ void load_k(__amdgpu_buffer_rsrc_t r, uint32_t unit_off, uint32_t k_voff, KRegs& k) {
+#pragma unroll
+  for (int i = 0; i < kSub; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      k.w[i][h] = __builtin_amdgcn_raw_buffer_load_b128(r, unit_off + (uint32_t)(i * 16 * kD + 16 * h) + k_voff, 0, 2);
 }
 
 // Byte offset of logical byte `b` of row `row` in a swizzled buffer.
@@ -127,11 +149,11 @@ struct Run {
   v4f o[8];       // O^T, dims 16 j + 4 g + v, query column lane % 16
 };
 
-// One unit: scores, softmax update, P V. `kr` holds the unit's K codes, `vb`
-// its V codes in LDS. unit_t0: first token of the unit; s_scale: c * s_k *
+// One unit: scores, softmax update, P V. `kr` holds the unit's K codes (in
+// registers), `vb` its V codes in LDS. unit_t0: first token of the unit; s_scale: c * s_k *
 // log2 e of the unit's token block; s_v: its V scale.
 template <int kFmt>
-__device__ __forceinline__ void unit_step(const uint8_t* kb, const uint8_t* vb, const v8bf (&qb)[4], Run& st,
+__device__ __forceinline__ void unit_step(const KRegs& kr, const uint8_t* vb, const v8bf (&qb)[4], Run& st,
                                           int unit_t0, int T, float s_scale, float s_v, int lane) {
   const int g = lane >> 4, c = lane & 15;
   // ---- scores: S^T[token 16 i + 4 g + v][query c]; the lane's A operand is
@@ -139,9 +161,8 @@ __device__ __forceinline__ void unit_step(const uint8_t* kb, const uint8_t* vb, 
   v4f s[kSub];
 #pragma unroll
   for (int i = 0; i < kSub; ++i) {
-    const int row = 16 * i + c;
-    const v4u w0 = *reinterpret_cast<const v4u*>(kb + swz_off(row, 32 * g));
-    const v4u w1 = *reinterpret_cast<const v4u*>(kb + swz_off(row, 32 * g + 16));
+    const v4u w0 = kr.w[i][0];
+    const v4u w1 = kr.w[i][1];
     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl) {
@@ -210,60 +231,65 @@ __device__ __forceinline__ void unit_step(const uint8_t* kb, const uint8_t* vb, 
   }
 }
 
-// The wave's loop over its units through a ring of 2 LDS stages (K and V
-// codes). Every step but the last copies the next unit into the other stage
-// and waits for the current unit's copies (the last step waits for all), then
-// computes the current unit. A stage is refilled only after its unit has been
-// computed, every LDS read of which has returned. (A repeated copy of the last
-// unit in place of the missing one would read it from HBM again: the codes
-// are fetched with the non-temporal hint.) Distinct __restrict__
-// stages and arrays, and resources built here, let the compiler see that
-// reading one stage does not wait for the copies into the others.
+// The wave's loop over its units, two units ahead: unit u + 2 is issued (K
+// into register slot (u + 2) % 3, V into LDS stage (u + 2) % 3) before unit u
+// is computed, after a wait that leaves only the 2 later units' memory
+// operations in flight. The issues and waits run in every step of the loop,
+// up to 2 steps past the wave's last unit (those steps compute nothing), and
+// past the last unit the issue reads at an offset beyond the resource's end:
+// the range check makes those loads return zeros without touching memory.
+// So every path has the same operations in flight, the compiler's own waits
+// for the K registers keep the same depth, and no load sits in a conditional
+// block next to its use (where the compiler would sink it, to just before
+// the unit that needs it). A slot or stage is refilled only after its
+// previous unit has been computed, every LDS read and register use of which
+// has completed. Distinct __restrict__ stages and arrays, and resources built
+// here, let the compiler see that reading one stage does not wait for the
+// copies into the others.
 template <int kFmt>
 __device__ __forceinline__ void wave_loop(const AttnParams& p, const uint8_t* __restrict__ kh,
                                           const uint8_t* __restrict__ vh, uint32_t head_bytes,
-                                          uint8_t* __restrict__ k0, uint8_t* __restrict__ v0,
-                                          uint8_t* __restrict__ k1, uint8_t* __restrict__ v1, const v8bf (&qb)[4],
-                                          Run& st, int h, int t_begin, int nunits, int lane) {
+                                          uint8_t* __restrict__ v0, uint8_t* __restrict__ v1,
+                                          uint8_t* __restrict__ v2, const v8bf (&qb)[4], Run& st, int h,
+                                          int t_begin, int nunits, int lane) {
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh, head_bytes);
   const int crow = lane >> 3;
   const uint32_t lane_voff = (uint32_t)(crow * kD + (((lane & 7) ^ (crow & 7)) << 4));
+  const uint32_t k_voff = (uint32_t)((lane & 15) * kD + 32 * (lane >> 4));
   // per-token-block scales, read through the constant address space (scalar
   // loads: they are inputs the kernel never writes)
   typedef const __attribute__((address_space(4))) float* cf_ptr;
   const cf_ptr skh = (cf_ptr)(p.sk + (int64_t)h * p.nb);
   const cf_ptr svh = (cf_ptr)(p.sv + (int64_t)h * p.nb);
-  auto unit_off = [&](int u) { return (uint32_t)(t_begin + u * kUnit) * kD; };
-  auto copy = [&](int u, uint8_t* kb, uint8_t* vb) {
-    load_unit(rk, unit_off(u), lane_voff, kb);
+  constexpr int kOps = kSub * 2 + kCopies;   // memory operations per unit
+  // units past the wave's last read at the resource's end (zeros, no memory
+  // access). The lanes add less than 4 KB to it; only for T > 2^25 - 32 can the
+  // 32-bit sum wrap, and then it addresses the head's own codes (in bounds),
+  // whose values go into a slot that is never computed.
+  auto unit_off = [&](int u) { return u < nunits ? (uint32_t)(t_begin + u * kUnit) * kD : head_bytes; };
+  auto issue = [&](int u, KRegs& kr, uint8_t* vb) {
+    load_k(rk, unit_off(u), k_voff, kr);
     load_unit(rv, unit_off(u), lane_voff, vb);
   };
-  auto step = [&](int u, const uint8_t* kb, const uint8_t* vb) {
-    const int t0 = t_begin + u * kUnit;
-    const int blk = t0 >> 7;
-    unit_step<kFmt>(kb, vb, qb, st, t0, p.T, skh[blk] * p.c_log2, svh[blk], lane);
+  // issue unit u + 2 into (kn, vn), wait for unit u, compute it from (kc, vc)
+  auto step = [&](int u, const KRegs& kc, const uint8_t* vc, KRegs& kn, uint8_t* vn) {
+    issue(u + 2, kn, vn);
+    wait_vm<2 * kOps>();
+    asm volatile("" ::: "memory");
+    if (u < nunits) {
+      const int t0 = t_begin + u * kUnit;
+      const int blk = t0 >> 7;
+      unit_step<kFmt>(kc, vc, qb, st, t0, p.T, skh[blk] * p.c_log2, svh[blk], lane);
+    }
   };
-  constexpr int kAhead = (kStages - 1) * 2 * kCopies;   // copies in flight beyond the current unit
-  copy(0, k0, v0);
-  for (int u = 0; u < nunits; u += 2) {
-    if (u + 1 < nunits) {
-      copy(u + 1, k1, v1);
-      wait_vm<kAhead>();
-    } else {
-      wait_vm<0>();
-    }
-    asm volatile("" ::: "memory");
-    step(u, k0, v0);
-    if (u + 1 >= nunits) break;
-    if (u + 2 < nunits) {
-      copy(u + 2, k0, v0);
-      wait_vm<kAhead>();
-    } else {
-      wait_vm<0>();
-    }
-    asm volatile("" ::: "memory");
-    step(u + 1, k1, v1);
+  KRegs k0, k1, k2;
+  issue(0, k0, v0);
+  issue(1, k1, v1);
+  for (int u = 0; u < nunits; u += 3) {
+    step(u, k0, v0, k2, v2);
+    step(u + 1, k1, v1, k0, v0);
+    step(u + 2, k2, v2, k1, v1);
   }
   wait_vm<0>();
 }
@@ -271,7 +297,7 @@ __device__ __forceinline__ void wave_loop(const AttnParams& p, const uint8_t* __
 // grid (splits, Hkv), 256 threads.
 template <int kFmt>
 __global__ __launch_bounds__(kThreadsA) void k_fp8kv_decode_attn(AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kWaves * kStages * 2 * kUnitBytes];   // 64 KB
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kWaves * kStages * kUnitBytes];   // 48 KB
   const int split = blockIdx.x, h = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -299,10 +325,10 @@ __global__ __launch_bounds__(kThreadsA) void k_fp8kv_decode_attn(AttnParams p) {
   const int left = p.T - t_begin;
   const int nunits = left <= 0 ? 0 : min(kUnitsPerWave, (left + kUnit - 1) / kUnit);
   const uint32_t head_bytes = (uint32_t)p.T * kD;
-  uint8_t* const b = smem + wave * kStages * 2 * kUnitBytes;
+  uint8_t* const b = smem + wave * kStages * kUnitBytes;
   if (nunits > 0)
     wave_loop<kFmt>(p, p.k + (int64_t)h * p.T * kD, p.v + (int64_t)h * p.T * kD, head_bytes, b, b + kUnitBytes,
-                    b + 2 * kUnitBytes, b + 3 * kUnitBytes, qb, st, h, t_begin, nunits, lane);
+                    b + 2 * kUnitBytes, qb, st, h, t_begin, nunits, lane);
 
   // ---- merge the 4 waves through LDS (the stages are free: every wave
   // has waited for its last copies and passes this barrier first)
@@ -310,6 +336,7 @@ __global__ __launch_bounds__(kThreadsA) void k_fp8kv_decode_attn(AttnParams p) {
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
   raw_barrier();
+  static_assert(kWaves * 16 * kPartial * sizeof(float) <= sizeof(smem), "merge buffer exceeds the LDS");
   float* const red = reinterpret_cast<float*>(smem);      // [wave][16 q][kPartial]
   float* const mine = red + wave * 16 * kPartial;
 #pragma unroll
@@ -406,8 +433,8 @@ int64_t attention_partial_floats() { return kPartial; }
 
 // ---------------------------------------------------------------------------
 // The fixed workspace of fp8_kv_decode_attention_noalloc, for callers that
-// cannot allocate device memory: a file-scope device array, 8 MiB (the split
-// partials of heads_q * ceil(tokens / 2048) <= 16131 query-head splits, e.g.
+// cannot allocate device memory: a file-scope device array, 12 MiB (the split
+// partials of heads_q * ceil(tokens / 1408) <= 24197 query-head splits, e.g.
 // 64 query heads over 512K tokens), one copy on every device the library runs
 // on, held until the process ends. In host code the array's name is only a
 // stand-in for it: its device address is looked up once per device with that
@@ -415,7 +442,7 @@ int64_t attention_partial_floats() { return kPartial; }
 // Calls on one device share the array, so calls that overlap in time on one
 // device race.
 // ---------------------------------------------------------------------------
-constexpr size_t kScratchBytes = (size_t)8 << 20;
+constexpr size_t kScratchBytes = (size_t)12 << 20;
 static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
 
 size_t attention_scratch_bytes() { return kScratchBytes; }

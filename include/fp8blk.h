@@ -474,13 +474,13 @@ fp8blk_status fp8_kv_decode_attention(const void* q, int64_t ld_q, int64_t heads
  * that cannot allocate device memory (code under HIP graph capture, serving
  * loops that must not call the allocator, harnesses that forbid it). It calls
  * no allocator: the split partials live in a file-scope device array of
- * 8 MiB, one per device, kept until the process ends.
+ * 12 MiB, one per device, kept until the process ends.
  *
  * Arguments, numerics, results and requirements: those of
  * fp8_kv_decode_attention without the workspace (the same kernels, so the
  * outputs are bit-identical). The partials need
- * fp8_kv_decode_attention_workspace_size(heads_q, tokens) <= 8 MiB, i.e.
- * heads_q * ceil(tokens / 2048) <= 16131 (else FP8BLK_EUNSUPPORTED, before any
+ * fp8_kv_decode_attention_workspace_size(heads_q, tokens) <= 12 MiB, i.e.
+ * heads_q * ceil(tokens / 1408) <= 24197 (else FP8BLK_EUNSUPPORTED, before any
  * HIP call). The first call on a device looks up the array's address there
  * (FP8BLK_EHIP if that fails). Every call on one device uses the same array:
  * calls that overlap in time on one device (other streams, other threads)

@@ -213,7 +213,7 @@ def att_noalloc(lib, q=PA, ldq=128, hq=64, hkv=8, t=300, d=128, kc=PB, ks=PC, vc
     (dict(hq=60), EINVAL),
     (dict(d=64), EUNSUPPORTED),
     (dict(out=PB + 64), EINVAL),               # out overlaps the K codes
-    (dict(hq=128, t=127 * 2048), EUNSUPPORTED),  # 16256 split partials: beyond the fixed 8 MiB
+    (dict(hq=128, t=190 * 1408), EUNSUPPORTED),  # 24320 split partials: beyond the fixed 12 MiB
 ])
 def test_attention_noalloc_rejects(lib, kw, status):
     assert att_noalloc(lib, **kw) == status
@@ -223,12 +223,13 @@ def test_attention_noalloc_rejects(lib, kw, status):
 
 def test_attention_workspace_size(lib):
     lib.fp8_kv_decode_attention_workspace_size.restype = ctypes.c_size_t
-    # 64 query heads, 131072 tokens: 64 splits of 2048 tokens, 130 floats each
-    assert lib.fp8_kv_decode_attention_workspace_size(64, 131072) == 64 * 64 * 130 * 4
+    # 64 query heads, 131072 tokens: 94 splits of 1408 tokens (the last one
+    # 128 tokens), 130 floats each
+    assert lib.fp8_kv_decode_attention_workspace_size(64, 131072) == 64 * 94 * 130 * 4
     assert lib.fp8_kv_decode_attention_workspace_size(8, 1) == 8 * 1 * 130 * 4
-    assert lib.fp8_kv_decode_attention_workspace_size(8, 2048) == 8 * 1 * 130 * 4
-    assert lib.fp8_kv_decode_attention_workspace_size(8, 2049) == 8 * 2 * 130 * 4
-    assert lib.fp8_kv_decode_attention_workspace_size(8, 4097) == 8 * 3 * 130 * 4
+    assert lib.fp8_kv_decode_attention_workspace_size(8, 1408) == 8 * 1 * 130 * 4
+    assert lib.fp8_kv_decode_attention_workspace_size(8, 1409) == 8 * 2 * 130 * 4
+    assert lib.fp8_kv_decode_attention_workspace_size(8, 2817) == 8 * 3 * 130 * 4
     assert lib.fp8_kv_decode_attention_workspace_size(0, 5) == 0
 
 

@@ -59,12 +59,12 @@ def test_noalloc_equals_workspace_entry_point(gpu_lib, fmt, out_dtype):
 
 
 def test_noalloc_rejects_partials_beyond_the_fixed_workspace(gpu_lib):
-    """128 query heads over 260,000 tokens need 128 * 127 = 16256 split
-    partials of 2048 tokens, more than the 16131 the 8 MiB array holds:
+    """128 query heads over 266,113 tokens need 128 * 190 = 24320 split
+    partials of 1408 tokens, more than the 24197 the 12 MiB array holds:
     refused on the host (no kernel runs, the output keeps its contents)."""
     lib = gpu_lib.load_library()
-    hq, hkv, t = 128, 8, 260000
-    assert lib.fp8_kv_decode_attention_workspace_size(hq, t) > 8 << 20
+    hq, hkv, t = 128, 8, 189 * 1408 + 1
+    assert lib.fp8_kv_decode_attention_workspace_size(hq, t) > 12 << 20
     kc = torch.zeros((hkv, t, 128), dtype=torch.uint8, device=DEV)
     ks = torch.zeros((hkv, (t + 127) // 128), dtype=torch.float32, device=DEV)
     q = torch.zeros((hq, 128), dtype=torch.bfloat16, device=DEV)
@@ -74,5 +74,5 @@ def test_noalloc_rejects_partials_beyond_the_fixed_workspace(gpu_lib):
     assert "fixed workspace" in lib.fp8blk_last_error().decode()
     torch.cuda.synchronize()
     assert bool(torch.all(out == 7.0))
-    # one split fewer fits: 128 heads over 126 * 2048 tokens
-    assert lib.fp8_kv_decode_attention_workspace_size(hq, 126 * 2048) <= 8 << 20
+    # one split fewer fits: 128 heads over 189 * 1408 tokens
+    assert lib.fp8_kv_decode_attention_workspace_size(hq, 189 * 1408) <= 12 << 20
