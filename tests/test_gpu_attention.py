@@ -5,7 +5,7 @@ attends over the same codes and scales in float64. Acceptance per output:
 |o - o_ref| <= 1e-3 * T_o with T_o = sum_t p_t |v_hat_t| (the oracle's), plus
 half a bf16 ulp for a bf16 output. Covers ragged token counts (1, a partial
 32-token unit, a partial 352-token wave range, a partial 1408-token split,
-several splits with a ragged last one),
+several splits with a ragged last one, 129 splits),
 1 to 16 query heads per kv head,
 both FP8 formats, both output dtypes, and the full [8, 131072, 128] cache
 with 64 query heads.
@@ -45,7 +45,7 @@ def _check(got, ref, t_o, bf16, what):
 
 
 @pytest.mark.parametrize("t", [1, 31, 32, 33, 300, 351, 352, 353, 511, 513, 1025, 1407, 1408, 1409, 2047, 2048, 2049,
-                               2816, 2817, 4096, 4097, 9000])
+                               2816, 2817, 4096, 4097, 9000, 181000])
 def test_token_counts(gpu_lib, t):
     got, ref, t_o = _run(gpu_lib, 8, 1, t, "e4m3", torch.float32, variant=t)
     _check(got, ref, t_o, False, f"T={t}")
