@@ -19,10 +19,10 @@
 //   the 32 bytes of a key that it multiplies), the V codes into a ring of 3
 //   LDS stages of the wave's own by direct global -> LDS copies; both carry
 //   the non-temporal hint. Keeping K out of the LDS is what lets three
-//   workgroups share a compute unit. V rows are 128 bytes; logical 16-byte chunk c of
-//   row r is stored at c ^ (r % 8), so that 16 lanes reading one chunk of 16
-//   consecutive rows hit distinct banks. The kernel is bound by reading the
-//   codes from HBM.
+//   workgroups share a compute unit. V rows are 128 bytes; logical 16-byte
+//   chunk c of row r is stored at c ^ (r % 8), so that 16 lanes reading one
+//   chunk of 16 consecutive rows hit distinct banks. The kernel is bound by
+//   reading the codes from HBM.
 // * Scores S^T = K Q^T on the bf16 MFMA (16 x 16 x 32): FP8 codes convert to
 //   bf16 exactly and the query is bf16; the 16 MFMA columns are the G query
 //   heads that share the kv head (G <= 16). Head_dim is permuted the same way
